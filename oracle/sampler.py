@@ -1,0 +1,148 @@
+"""Canvas update, stop rule and the block loop, in float64 (test infrastructure only).
+
+Page tags as in oracle.model.  The loop follows the pages' account:
+  * prompt read into the KV cache once, then a 256-slot canvas of random
+    vocabulary tokens ([P5] "How block diffusion works");
+  * each pass predicts every slot, keeps the most confident ones and
+    re-randomises the others ([P5] "How block diffusion works"; [P3] "How
+    diffusion text generation differs");
+  * stop when the mean canvas entropy is below a threshold, or when the
+    predictions are unchanged over two consecutive passes, or after 48 passes
+    ([P2] "How Diffusion Changes the Equation"; the three triggers are OR-ed);
+  * the finished block joins the context (KV cache) and a fresh canvas starts
+    ([P2] "How Diffusion Changes the Equation"; [P3] "How diffusion text
+    generation differs").
+Readings: keep count k_t = min(S, t * n_new) with no freezing (every pass
+re-ranks all slots, since the pages say any slot can be revised later); ranking
+by fp32 confidence, descending, ties to the lower slot, NaN last; stability
+compares predictions (not the canvas) and can first fire at t = 2; the
+committed block is the last pass's predictions, written to the cache by a
+causal forward over the block.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+
+from .model import KVCache, Model
+from .numerics import f32
+from .philox import uniform_tokens
+
+STOP_NONE, STOP_ENTROPY, STOP_STABLE, STOP_CAP, STOP_FIXED = 0, 1, 2, 3, 4
+
+
+@dataclass
+class Sampler:
+    n_new: int
+    max_steps: int = 48
+    entropy_threshold: float = 0.05
+    fixed_steps: int = 0          # >0: run exactly this many passes (timing mode), no early stop
+    seed: int = 1
+    inv_temperature: float = 1.0
+
+
+def keep_count(step: int, n_new: int, slots: int) -> int:
+    """k_t = min(S, t * n_new) slots kept after pass t."""
+    return min(slots, step * n_new)
+
+
+def keep_mask(conf, k: int) -> np.ndarray:
+    """The k slots of highest fp32 confidence; ties to the lower slot; NaN ranks last."""
+    c = f32(conf)
+    key = np.where(np.isnan(c), -np.inf, c)
+    order = np.argsort(-key, kind="stable")
+    mask = np.zeros(c.shape[0], dtype=bool)
+    mask[order[:k]] = True
+    return mask
+
+
+def initial_canvas(seed: int, block: int, slots: int, vocab: int) -> np.ndarray:
+    return uniform_tokens(seed, block, 0, np.arange(slots), vocab)
+
+
+def canvas_update(pred, conf, k: int, seed: int, block: int, step: int, vocab: int):
+    """Kept slots take the prediction; every other slot takes a fresh uniform draw."""
+    mask = keep_mask(conf, k)
+    fresh = uniform_tokens(seed, block, step, np.arange(len(mask)), vocab)
+    return np.where(mask, np.asarray(pred, dtype=np.int64), fresh), mask
+
+
+def stop_reason(step: int, mean_entropy: float, pred, prev_pred, s: Sampler) -> int:
+    if s.fixed_steps > 0:
+        return STOP_FIXED if step >= s.fixed_steps else STOP_NONE
+    if mean_entropy < s.entropy_threshold:
+        return STOP_ENTROPY
+    if prev_pred is not None and step >= 2 and np.array_equal(pred, prev_pred):
+        return STOP_STABLE
+    if step >= s.max_steps:
+        return STOP_CAP
+    return STOP_NONE
+
+
+@dataclass
+class PassRecord:
+    canvas: np.ndarray
+    pred: np.ndarray
+    conf: np.ndarray
+    ent: np.ndarray
+    margin: np.ndarray
+    keep: Optional[np.ndarray] = None
+    traces: list = field(default_factory=list)
+
+
+@dataclass
+class BlockResult:
+    tokens: np.ndarray
+    steps: int
+    reason: int
+    mean_entropy: float
+    passes: List[PassRecord]
+
+
+def denoise_pass(model: Model, kv: KVCache, canvas, inv_temperature: float = 1.0, keep_traces: bool = False):
+    """One pass: embed the canvas, run every block bidirectionally over cache + canvas, then the head."""
+    x = model.embed(canvas)
+    x, traces = model.body(x, kv, causal=False, append=False)
+    pred, conf, ent, margin = model.head(x, inv_temperature)
+    rec = PassRecord(canvas=np.asarray(canvas), pred=pred, conf=conf, ent=ent, margin=margin)
+    if keep_traces:
+        rec.traces = traces
+    return rec, x
+
+
+def prefill(model: Model, kv: KVCache, tokens) -> None:
+    """Causal forward of ``tokens`` appended after the cached rows; writes their keys/values."""
+    x = model.embed(tokens)
+    model.body(x, kv, causal=True, append=True)
+
+
+def commit(model: Model, kv: KVCache, block_tokens) -> None:
+    prefill(model, kv, block_tokens)
+
+
+def generate_block(model: Model, kv: KVCache, s: Sampler, block: int, keep_traces: bool = False,
+                   do_commit: bool = True) -> BlockResult:
+    d = model.d
+    canvas = initial_canvas(s.seed, block, d.canvas, d.vocab)
+    prev = None
+    passes: List[PassRecord] = []
+    step = 0
+    reason = STOP_NONE
+    mean_ent = float("nan")
+    while True:
+        step += 1
+        rec, _ = denoise_pass(model, kv, canvas, s.inv_temperature, keep_traces)
+        passes.append(rec)
+        mean_ent = float(np.mean(rec.ent))
+        reason = stop_reason(step, mean_ent, rec.pred, prev, s)
+        if reason != STOP_NONE:
+            break
+        k = keep_count(step, s.n_new, d.canvas)
+        canvas, rec.keep = canvas_update(rec.pred, rec.conf, k, s.seed, block, step, d.vocab)
+        prev = rec.pred
+    tokens = passes[-1].pred.copy()
+    if do_commit:
+        commit(model, kv, tokens)
+    return BlockResult(tokens=tokens, steps=step, reason=reason, mean_entropy=mean_ent, passes=passes)
