@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-diffusion denoising step on one MI355X.
+
+Workload (N=1): the 30-layer bf16 MoE model (d 2816, 16 q / 8 KV heads of dim
+128, 128 experts top-8 + 1 shared, 262144-token tied vocabulary) with a
+4096-token uniform-random prompt prefilled into the KV cache, random-init
+weights from the seeded generator.  One timed step is one whole 256-slot
+block at a fixed T=10: the initial random canvas, 10 denoising passes, 10 stop
+checks, 9 keep/re-randomise updates, and the commit of the block into the KV
+cache (the cache length is reset to the prompt before each step, so every step
+does identical work).  Reported value: canvas tokens per second = 256 / (block
+time); also ms per denoising pass.
+
+Extra objects on the JSON line:
+  roofline     — the dominant kernel (routed-expert gate/up projection),
+                 algorithmic bytes per launch / its average duration from HIP
+                 events recorded on the launch stream during the timed region;
+                 traffic from the committed rocprofv3 counter summary when it
+                 matches the current kernel source, else null
+  cpu_baseline — the CPU oracle timed on a bounded sample (one layer of the
+                 pass plus the head on 16 slots), extrapolated to a block
+  kernels      — per-kernel-class time per pass from an instrumented extra block
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "canvas tokens/sec at batch 1 (256-slot block, T=10) + ms/denoising step"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moe_gate_up_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("k_gemm.hip", "dg_device.h"):
+        with open(os.path.join(ROOT, "block_diffusion_decoding_step_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def gate_up_bytes(d, experts_hit: float, pairs: int) -> float:
+    """Algorithmic bytes of one routed gate/up launch: each hit expert's [2*fe, d] weights once, the
+    normalised canvas rows once, the SwiGLU products written once."""
+    w = experts_hit * 2 * d.ffn_expert * d.d_model * 2
+    x = d.canvas * d.d_model * 2
+    h = pairs * d.ffn_expert * 2
+    return w + x + h
+
+
+def read_traffic(bytes_per_launch: float):
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, log_fn) -> dict:
+    """Oracle on the host: one layer of a denoising pass over a 4096-key cache plus the head on 16 slots,
+    extrapolated to a block (10 passes of 30 layers and 256 head slots, plus a 30-layer commit)."""
+    import numpy as np
+
+    import dg_inputs
+    from dg_inputs import recipe
+    from oracle import model as om
+    from oracle import numerics
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    d = wl.dims
+    log_fn("cpu baseline: generating one layer + embedding on the host")
+    lw = {n: numerics.from_storage(a, "bf16") for n, a in dg_inputs.layer_weights_host(d, 0).items()}
+    E = numerics.from_storage(dg_inputs.embed_host(d), "bf16")
+    d1 = om.Dims(**{f: getattr(d, f) for f in om.Dims.__dataclass_fields__})
+    d1.n_layers = 1
+    model = om.Model(d1, {"embed": E, "final_norm": np.ones(d.d_model), "layers": [lw]})
+    kv = om.KVCache(1, d.n_kv_heads, d.head_dim)
+    kv.k[0] = numerics.from_storage(dg_inputs.normal((d.n_kv_heads, wl.prefix, d.head_dim), 1,
+                                                     recipe.STREAM_PREFIX_K, 1.0, "bf16"), "bf16")
+    kv.v[0] = numerics.from_storage(dg_inputs.normal((d.n_kv_heads, wl.prefix, d.head_dim), 1,
+                                                     recipe.STREAM_PREFIX_V, 1.0, "bf16"), "bf16")
+    x = numerics.from_storage(dg_inputs.hidden((d.canvas, d.d_model), "bf16"), "bf16")
+    log_fn("cpu baseline: timing the oracle")
+    t0 = time.perf_counter()
+    xo, _ = model.layer(0, x, kv, causal=False, append=False)
+    t_layer = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    model.head(xo[:16])
+    t_head16 = time.perf_counter() - t0
+    t_pass = d.n_layers * t_layer + (d.canvas / 16) * t_head16
+    t_block = wl.fixed_steps * t_pass + d.n_layers * t_layer
+    return {"value": d.canvas / t_block, "unit": "canvas tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"one bidirectional layer over a {wl.prefix}-key cache ({t_layer:.2f} s) and the vocab head "
+                       f"on 16 slots ({t_head16:.2f} s), float64 numpy; extrapolated to {wl.fixed_steps} passes x "
+                       f"{d.n_layers} layers x {d.canvas} head slots + a {d.n_layers}-layer commit"),
+            "ms_per_denoising_step": t_pass * 1e3}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="full_loop_bf16", choices=["full_loop_bf16", "long_context_bf16"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one MI355X only: this build runs the whole denoising step on a single GPU "
+              f"with no collectives (asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import block_diffusion_decoding_step_amd as dg
+    import dg_inputs
+    from dg_inputs import device as gdev
+    from dg_inputs import recipe
+
+    wl = recipe.WORKLOADS[args.workload]
+    d = wl.dims
+    T = wl.fixed_steps
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    log(f"bench: {wl.name} on {torch.cuda.get_device_name(0)}; generating weights on the device")
+    w = gdev.model_weights_device(d)
+    weights = dg.Weights(w["embed"], w["final_norm"], w["layers"])
+    cfg = dg.make_config(d)
+    cap = ((wl.prefix + wl.blocks * d.canvas + 31) // 32) * 32
+    k, v = gdev.kv_tensors(d, cap)
+    kv = dg.KV(k, v, cap, 0)
+    chunk = 2048
+    ws_bytes = dg.dg_workspace_size(cfg, max(d.canvas, chunk))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    prompt = gdev.uniform_tensor(wl.prefix, recipe.INPUT_SEED, recipe.STREAM_PROMPT, d.vocab)
+    log(f"bench: prefill {wl.prefix} tokens")
+    t0 = time.perf_counter()
+    dg.dg_prefill_kv(cfg, weights, kv, prompt, wl.prefix, ws, ws_bytes)
+    torch.cuda.synchronize()
+    t_prefill = time.perf_counter() - t0
+    P = kv.len
+    sampler = dg.make_sampler(wl.n_new, fixed_steps=T, seed=recipe.INPUT_SEED)
+    tokens = torch.empty(d.canvas, dtype=torch.int32, device="cuda")
+
+    def block(i):
+        kv.len = P
+        return dg.dg_generate_block(cfg, weights, kv, sampler, i, tokens, ws, ws_bytes)
+
+    log(f"bench: warmup {args.warmup} blocks")
+    for i in range(args.warmup):
+        block(i)
+    torch.cuda.synchronize()
+
+    # timed region: K blocks; HIP events around the dominant kernel's launches on the launch stream
+    dg.dg_timing_start(["moe_gate_up"])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    statuses = [block(i) for i in range(args.steps)]
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t0
+    tim = dg.dg_timing_stop()
+    assert all(s.steps == T and s.reason == dg.DG_STOP_FIXED for s in statuses)
+    block_ms = t_total / args.steps * 1e3
+    value = d.canvas * args.steps / t_total
+
+    # ms per denoising pass alone (the same kernels, no update/commit)
+    canvas = torch.empty(d.canvas, dtype=torch.int32, device="cuda")
+    dg.dg_canvas_update(cfg, None, None, 0, recipe.INPUT_SEED, 0, 0, canvas)
+    pred = torch.empty(d.canvas, dtype=torch.int32, device="cuda")
+    conf = torch.empty(d.canvas, dtype=torch.float32, device="cuda")
+    ent = torch.empty(d.canvas, dtype=torch.float32, device="cuda")
+    kv.len = P
+    n_pass = args.steps * T
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_pass):
+        dg.dg_denoise_step(cfg, weights, kv, canvas, 1.0, pred, conf, ent, None, ws, ws_bytes)
+    torch.cuda.synchronize()
+    pass_ms = (time.perf_counter() - t0) / n_pass * 1e3
+
+    # routing of one pass: experts hit per layer (for the algorithmic bytes)
+    ridx = torch.empty((d.n_layers, d.canvas, d.top_k), dtype=torch.int32, device="cuda")
+    dg.dg_denoise_step(cfg, weights, kv, canvas, 1.0, pred, conf, ent, {"route_idx": ridx}, ws, ws_bytes)
+    torch.cuda.synchronize()
+    ri = ridx.cpu().numpy()
+    experts_hit = float(np.mean([len(np.unique(ri[l])) for l in range(d.n_layers)]))
+
+    # per-kernel breakdown from one extra instrumented block (outside the timed region)
+    dg.dg_timing_start(list(dg.KERNELS))
+    block(0)
+    torch.cuda.synchronize()
+    breakdown = dg.dg_timing_stop()
+
+    g_ms, g_n = tim["moe_gate_up"]
+    g_avg = g_ms / g_n
+    g_bytes = gate_up_bytes(d, experts_hit, d.canvas * d.top_k)
+    achieved = g_bytes / (g_avg * 1e-3) / 1e9
+    traffic = read_traffic(g_bytes)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "canvas tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(block_ms, 4),
+        "ms_per_denoising_step": round(pass_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": d.n_layers, "d_model": d.d_model,
+                   "heads": f"{d.n_heads}q/{d.n_kv_heads}kv x {d.head_dim}",
+                   "experts": f"{d.n_experts} top-{d.top_k} + 1 shared", "ffn_expert": d.ffn_expert,
+                   "vocab": d.vocab, "canvas": d.canvas, "prefix": wl.prefix, "T": T, "batch": 1,
+                   "step": "one block: 10 passes + stop checks + 9 keep/re-randomise updates + commit",
+                   "canvas_tokens_per_s_without_commit": round(d.canvas / (T * pass_ms * 1e-3), 2),
+                   "prefill_s": round(t_prefill, 3)},
+        "roofline": {"kernel": "k_moe_gate_up", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "bytes_per_launch": g_bytes, "avg_launch_ms": round(g_avg, 5),
+                     "launches": g_n, "experts_hit_per_layer": experts_hit},
+        "kernels": {k: {"ms_per_pass": round(v[0] / T, 4), "launches_per_pass": v[1] / T}
+                    for k, v in sorted(breakdown.items(), key=lambda kv_: -kv_[1][0])},
+    }
+    if not args.no_cpu_baseline:
+        try:
+            out["cpu_baseline"] = cpu_baseline(wl, log)
+        except MemoryError:  # pragma: no cover
+            out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,571 @@
+// dg_api.cpp — host side of libdg: argument validation, workspace carving and the
+// sequencing of one denoising pass, prefill/commit and the block loop.
+//
+// Page tags: [P2] "DiffusionGemma 26B: How Google's Text Diffusion Model Generates
+// Tokens in Parallel"; [P3] "DiffusionGemma local text generation" (ctxwire);
+// [P5] "When to use a diffusion LLM: I compared DiffusionGemma and Gemma 4".
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+#include "../../include/dg.h"
+#include "dg_kernels.h"
+
+using namespace dg;
+
+namespace {
+
+thread_local int g_hip_error = 0;
+
+#define DG_TRY(expr)                          \
+  do {                                        \
+    hipError_t e_ = (expr);                   \
+    if (e_ != hipSuccess) {                   \
+      g_hip_error = (int)e_;                  \
+      return DG_ERR_HIP;                      \
+    }                                         \
+  } while (0)
+
+#define DG_CHECK(expr)               \
+  do {                               \
+    int r_ = (expr);                 \
+    if (r_ != DG_OK) return r_;      \
+  } while (0)
+
+// ------------------------------------------------------------------ kernel timing (measurement support)
+struct TimerRec {
+  int id;
+  hipEvent_t a, b;
+};
+struct Timer {
+  uint64_t mask = 0;
+  std::vector<TimerRec> recs;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+thread_local Timer g_timer;
+
+// Records an event pair around one launch when its kernel class is selected.
+struct TimeScope {
+  int id;
+  hipStream_t s;
+  hipEvent_t a = nullptr;
+  TimeScope(int id_, hipStream_t s_) : id(id_), s(s_) {
+    if ((g_timer.mask >> id) & 1ull) {
+      a = g_timer.get();
+      if (a) (void)hipEventRecord(a, s);
+    }
+  }
+  ~TimeScope() {
+    if (!a) return;
+    hipEvent_t b = g_timer.get();
+    if (!b) return;
+    (void)hipEventRecord(b, s);
+    g_timer.recs.push_back({id, a, b});
+  }
+};
+
+#define DG_LAUNCH(id, s, expr)    \
+  do {                            \
+    TimeScope ts_((int)(id), (s)); \
+    DG_TRY(expr);                 \
+  } while (0)
+
+constexpr int kMaxSplit = 16;
+constexpr int64_t kPartialRows = 4096;  // attention split partials hold n_split * rows <= max(this, rows)
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline size_t esize(const dg_config* c) { return c->dtype == DG_BF16 ? 2 : 4; }
+inline bool aligned16(const void* p) { return p && ((uintptr_t)p & 15u) == 0; }
+
+// ------------------------------------------------------------------ workspace
+struct Ws {
+  void* X;
+  void* Xn;
+  void* Q;
+  void* O;
+  float* opart;
+  float* mlpart;
+  float* rlog;
+  int32_t* ridx;
+  float* rw;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* pos;
+  int4* tiles;
+  int32_t* n_tiles;
+  void* Hp;
+  void* Yp;
+  void* Hs;
+  void* Ys;
+  float4* hpart;
+  dg_block_status* status;
+  int32_t* prev_pred;
+  int32_t* canvas;
+  int32_t* pred;
+  float* conf;
+  float* ent;
+  size_t bytes;
+  int64_t rows;
+};
+
+// Lays out every buffer for calls of up to M rows.  With base == nullptr only sizes.
+Ws carve(const dg_config* c, int64_t M, char* base) {
+  Ws w{};
+  size_t off = 0;
+  auto take = [&](size_t n) -> void* {
+    void* p = base ? base + off : nullptr;
+    off += align256(n);
+    return p;
+  };
+  const size_t es = esize(c);
+  const int64_t d = c->d_model, E = c->n_experts, k = c->top_k;
+  const int64_t hd = (int64_t)c->n_heads * c->head_dim;
+  const int64_t prow = std::max<int64_t>(kPartialRows, M);
+  const int64_t pairs = M * k;
+  w.rows = M;
+  w.X = take(M * d * es);
+  w.Xn = take(M * d * es);
+  w.Q = take(M * hd * es);
+  w.O = take(M * hd * es);
+  w.opart = (float*)take(prow * hd * 4);
+  w.mlpart = (float*)take(prow * c->n_heads * 2 * 4);
+  w.rlog = (float*)take(M * E * 4);
+  w.ridx = (int32_t*)take(pairs * 4);
+  w.rw = (float*)take(pairs * 4);
+  w.counts = (int32_t*)take(E * 4);
+  w.offsets = (int32_t*)take((E + 1) * 4);
+  w.perm = (int32_t*)take(pairs * 4);
+  w.pos = (int32_t*)take(pairs * 4);
+  w.tiles = (int4*)take((size_t)moe_max_tiles((int)M, (int)E, (int)k) * 16);
+  w.n_tiles = (int32_t*)take(4);
+  w.Hp = take(pairs * c->ffn_expert * es);
+  w.Yp = take(pairs * d * es);
+  w.Hs = take(M * c->ffn_shared * es);
+  w.Ys = take(M * d * es);
+  w.hpart = (float4*)take((size_t)head_groups(c->vocab) * M * 16);
+  w.status = (dg_block_status*)take(sizeof(dg_block_status));
+  w.prev_pred = (int32_t*)take(c->canvas * 4);
+  w.canvas = (int32_t*)take(c->canvas * 4);
+  w.pred = (int32_t*)take(c->canvas * 4);
+  w.conf = (float*)take(c->canvas * 4);
+  w.ent = (float*)take(c->canvas * 4);
+  w.bytes = off;
+  return w;
+}
+
+// ------------------------------------------------------------------ validation
+int check_cfg(const dg_config* c) {
+  if (!c) return DG_ERR_INVALID;
+  if (c->n_layers < 0 || c->d_model <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
+      c->n_experts <= 0 || c->top_k <= 0 || c->ffn_expert <= 0 || c->ffn_shared <= 0 || c->vocab <= 0 ||
+      c->canvas <= 0)
+    return DG_ERR_INVALID;
+  if (c->dtype != DG_F32 && c->dtype != DG_BF16) return DG_ERR_INVALID;
+  if (!(c->rms_eps >= 0.f)) return DG_ERR_INVALID;
+  if (c->top_k > c->n_experts) return DG_ERR_INVALID;
+  if (c->n_heads % c->n_kv_heads) return DG_ERR_INVALID;
+  if (c->rope_theta != 0.f) return DG_ERR_UNSUPPORTED;
+  if (c->d_model % 32 || c->ffn_expert % 32 || c->ffn_shared % 32) return DG_ERR_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128) return DG_ERR_UNSUPPORTED;
+  const int G = c->n_heads / c->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4) return DG_ERR_UNSUPPORTED;
+  if (c->n_experts > 256 || c->top_k > 16) return DG_ERR_UNSUPPORTED;
+  if (c->canvas > 1024 || c->canvas > moe_max_rows(c->n_experts)) return DG_ERR_UNSUPPORTED;
+  return DG_OK;
+}
+
+int check_layer_weights(const dg_layer_weights& l) {
+  const void* p[] = {l.attn_norm, l.wqkv, l.wo, l.ffn_norm, l.w_router, l.w_gate_up, l.w_down, l.ws_gate_up,
+                     l.ws_down};
+  for (const void* q : p)
+    if (!aligned16(q)) return DG_ERR_INVALID;
+  return DG_OK;
+}
+
+int check_weights(const dg_config* c, const dg_weights* w, bool need_layers, bool need_head) {
+  if (!w) return DG_ERR_INVALID;
+  if (!aligned16(w->embed)) return DG_ERR_INVALID;
+  if (need_head && !aligned16(w->final_norm)) return DG_ERR_INVALID;
+  if (need_layers && c->n_layers > 0) {
+    if (!w->h_layers) return DG_ERR_INVALID;
+    for (int l = 0; l < c->n_layers; ++l) DG_CHECK(check_layer_weights(w->h_layers[l]));
+  }
+  return DG_OK;
+}
+
+int check_kv(const dg_kv* kv, int64_t rows) {
+  if (!kv || !aligned16(kv->k) || !aligned16(kv->v)) return DG_ERR_INVALID;
+  if (kv->capacity <= 0 || kv->capacity % 32 || kv->len < 0) return DG_ERR_INVALID;
+  if (kv->len + rows > kv->capacity) return DG_ERR_KV_FULL;
+  return DG_OK;
+}
+
+int check_ws(const dg_config* c, int64_t rows, void* ws, size_t ws_bytes) {
+  if (!ws || ((uintptr_t)ws & 255u)) return DG_ERR_WORKSPACE;
+  if (carve(c, rows, nullptr).bytes > ws_bytes) return DG_ERR_WORKSPACE;
+  return DG_OK;
+}
+
+// Largest row count (<= limit) whose workspace fits in ws_bytes; 0 if none.
+int64_t rows_supported(const dg_config* c, size_t ws_bytes, int64_t limit) {
+  int64_t lo = 0, hi = limit;
+  while (lo < hi) {
+    int64_t mid = (lo + hi + 1) / 2;
+    if (carve(c, mid, nullptr).bytes <= ws_bytes) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ------------------------------------------------------------------ one transformer block
+template <typename T>
+int layer_t(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int64_t pos0, int64_t M, bool causal,
+            const Ws& ws, hipStream_t s) {
+  const dg_layer_weights& L = w->h_layers[l];
+  const int d = c->d_model, hq = c->n_heads, hkv = c->n_kv_heads, dh = c->head_dim;
+  const int E = c->n_experts, k = c->top_k;
+  const int Mi = (int)M;
+  const size_t es = sizeof(T);
+  char* kbase = (char*)kv->k + (size_t)l * hkv * kv->capacity * dh * es;
+  char* vbase = (char*)kv->v + (size_t)l * hkv * dh * kv->capacity * es;
+
+  // attention half
+  DG_LAUNCH(DG_K_RMSNORM, s, launch_rmsnorm<T>((const T*)ws.X, (const T*)L.attn_norm, (T*)ws.Xn, Mi, d, c->rms_eps, s));
+  GemmArgs g{};
+  g.A = ws.Xn; g.B = L.wqkv; g.M = Mi; g.N = (hq + 2 * hkv) * dh; g.K = d; g.lda = d; g.ldb = d;
+  g.q = ws.Q; g.kc = kbase; g.vc = vbase; g.n_heads = hq; g.n_kv_heads = hkv; g.head_dim = dh; g.q_rows = Mi;
+  g.cap = kv->capacity; g.pos0 = pos0;
+  DG_LAUNCH(DG_K_GEMM_QKV, s, launch_gemm<T>(GemmEpi::QKV, g, s));
+
+  AttnArgs at{};
+  at.q = ws.Q; at.kc = kbase; at.vc = vbase; at.o_part = ws.opart; at.ml_part = ws.mlpart; at.o = ws.O;
+  at.q_rows = Mi; at.n_heads = hq; at.n_kv_heads = hkv; at.head_dim = dh; at.cap = kv->capacity;
+  at.n_keys = pos0 + M; at.q_pos0 = pos0; at.causal = causal ? 1 : 0;
+  const int max_split = (int)std::min<int64_t>(kMaxSplit, std::max<int64_t>(1, std::max(kPartialRows, M) / M));
+  at.n_split = attention_splits(at.n_keys, Mi, hq, hkv, at.causal, max_split);
+  DG_LAUNCH(DG_K_ATTENTION, s, launch_attention<T>(at, s));
+  DG_LAUNCH(DG_K_ATTN_MERGE, s, launch_attention_merge<T>(at, s));
+
+  g = GemmArgs{};
+  g.A = ws.O; g.B = L.wo; g.C = ws.X; g.M = Mi; g.N = d; g.K = hq * dh; g.lda = hq * dh; g.ldb = hq * dh; g.ldc = d;
+  DG_LAUNCH(DG_K_GEMM_O, s, launch_gemm<T>(GemmEpi::Resid, g, s));
+
+  // MoE half ([P2] "Architecture Details": 8 routed experts of 128, plus 1 shared)
+  DG_LAUNCH(DG_K_RMSNORM, s, launch_rmsnorm<T>((const T*)ws.X, (const T*)L.ffn_norm, (T*)ws.Xn, Mi, d, c->rms_eps, s));
+  g = GemmArgs{};
+  g.A = ws.Xn; g.B = L.w_router; g.C = ws.rlog; g.M = Mi; g.N = E; g.K = d; g.lda = d; g.ldb = d; g.ldc = E;
+  DG_LAUNCH(DG_K_GEMM_ROUTER, s, launch_gemm<T>(GemmEpi::StoreF32, g, s));
+  DG_LAUNCH(DG_K_ROUTER_TOPK, s, launch_router_topk(ws.rlog, Mi, E, k, ws.ridx, ws.rw, s));
+  DG_LAUNCH(DG_K_MOE_PERMUTE, s, launch_moe_permute(ws.ridx, Mi, E, k, ws.counts, ws.offsets, ws.perm, ws.pos, ws.tiles, ws.n_tiles, s));
+
+  MoeArgs ma{};
+  ma.tiles = ws.tiles; ma.n_tiles = ws.n_tiles; ma.max_tiles = moe_max_tiles(Mi, E, k); ma.perm = ws.perm;
+  ma.X = ws.Xn; ma.W = L.w_gate_up; ma.out = ws.Hp; ma.d = d; ma.F = c->ffn_expert;
+  DG_LAUNCH(DG_K_MOE_GATE_UP, s, launch_moe_gate_up<T>(ma, s));
+  ma.X = ws.Hp; ma.W = L.w_down; ma.out = ws.Yp;
+  DG_LAUNCH(DG_K_MOE_DOWN, s, launch_moe_down<T>(ma, s));
+
+  g = GemmArgs{};
+  g.A = ws.Xn; g.B = L.ws_gate_up; g.C = ws.Hs; g.M = Mi; g.N = c->ffn_shared; g.K = d; g.lda = d; g.ldb = d;
+  g.ldc = c->ffn_shared;
+  DG_LAUNCH(DG_K_SHARED_GATE_UP, s, launch_gemm<T>(GemmEpi::SwiGLU, g, s));
+  g = GemmArgs{};
+  g.A = ws.Hs; g.B = L.ws_down; g.C = ws.Ys; g.M = Mi; g.N = d; g.K = c->ffn_shared; g.lda = c->ffn_shared;
+  g.ldb = c->ffn_shared; g.ldc = d;
+  DG_LAUNCH(DG_K_SHARED_DOWN, s, launch_gemm<T>(GemmEpi::Store, g, s));
+
+  DG_LAUNCH(DG_K_MOE_COMBINE, s, launch_moe_combine<T>((T*)ws.X, (const T*)ws.Ys, (const T*)ws.Yp, ws.pos, ws.rw, Mi, d, k, s));
+  return DG_OK;
+}
+
+int layer(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int64_t pos0, int64_t M, bool causal,
+          const Ws& ws, hipStream_t s) {
+  if (c->dtype == DG_BF16) return layer_t<bf16>(c, w, l, kv, pos0, M, causal, ws, s);
+  return layer_t<float>(c, w, l, kv, pos0, M, causal, ws, s);
+}
+
+int embed(const dg_config* c, const dg_weights* w, const int32_t* tok, int64_t M, const Ws& ws, hipStream_t s) {
+  if (c->dtype == DG_BF16)
+    DG_LAUNCH(DG_K_EMBED, s, launch_embed<bf16>(tok, (const bf16*)w->embed, (bf16*)ws.X, (int)M, c->d_model, c->vocab, s));
+  else
+    DG_LAUNCH(DG_K_EMBED, s, launch_embed<float>(tok, (const float*)w->embed, (float*)ws.X, (int)M, c->d_model, c->vocab, s));
+  return DG_OK;
+}
+
+// final norm + fused head over M rows of ws.X
+int head(const dg_config* c, const dg_weights* w, int64_t M, float inv_temp, int32_t* pred, float* conf, float* ent,
+         const Ws& ws, hipStream_t s) {
+  HeadArgs h{};
+  h.x = ws.Xn; h.E = w->embed; h.part = ws.hpart; h.n = (int)M; h.d = c->d_model; h.V = c->vocab;
+  h.n_groups = head_groups(c->vocab); h.beta_log2e = inv_temp * 1.4426950408889634f;
+  h.pred = pred; h.conf = conf; h.ent = ent;
+  if (c->dtype == DG_BF16) {
+    DG_LAUNCH(DG_K_RMSNORM, s, launch_rmsnorm<bf16>((const bf16*)ws.X, (const bf16*)w->final_norm, (bf16*)ws.Xn, (int)M, c->d_model,
+                                c->rms_eps, s));
+    DG_LAUNCH(DG_K_VOCAB_HEAD, s, launch_vocab_head<bf16>(h, s));
+  } else {
+    DG_LAUNCH(DG_K_RMSNORM, s, launch_rmsnorm<float>((const float*)ws.X, (const float*)w->final_norm, (float*)ws.Xn, (int)M, c->d_model,
+                                 c->rms_eps, s));
+    DG_LAUNCH(DG_K_VOCAB_HEAD, s, launch_vocab_head<float>(h, s));
+  }
+  DG_LAUNCH(DG_K_HEAD_MERGE, s, launch_head_merge(h, s));
+  return DG_OK;
+}
+
+// denoising pass with an already-validated configuration
+int denoise(const dg_config* c, const dg_weights* w, const dg_kv* kv, const int32_t* canvas, float inv_temp,
+            int32_t* pred, float* conf, float* ent, const dg_debug* dbg, const Ws& ws, hipStream_t s) {
+  const int64_t S = c->canvas;
+  DG_CHECK(embed(c, w, canvas, S, ws, s));
+  for (int l = 0; l < c->n_layers; ++l) {
+    DG_CHECK(layer(c, w, l, kv, kv->len, S, false, ws, s));
+    if (dbg) {
+      const size_t hb = (size_t)S * c->d_model * esize(c);
+      if (dbg->hidden) DG_TRY(hipMemcpyAsync((char*)dbg->hidden + l * hb, ws.X, hb, hipMemcpyDeviceToDevice, s));
+      const size_t rb = (size_t)S * c->top_k * 4;
+      if (dbg->route_idx)
+        DG_TRY(hipMemcpyAsync((char*)dbg->route_idx + l * rb, ws.ridx, rb, hipMemcpyDeviceToDevice, s));
+      if (dbg->route_w) DG_TRY(hipMemcpyAsync((char*)dbg->route_w + l * rb, ws.rw, rb, hipMemcpyDeviceToDevice, s));
+    }
+  }
+  return head(c, w, S, inv_temp, pred, conf, ent, ws, s);
+}
+
+// causal forward of n tokens at kv->len.., chunked to the workspace; does not change kv->len
+int prefill(const dg_config* c, const dg_weights* w, const dg_kv* kv, const int32_t* tokens, int64_t n, void* wsp,
+            size_t ws_bytes, hipStream_t s) {
+  const int64_t chunk = rows_supported(c, ws_bytes, moe_max_rows(c->n_experts));
+  if (chunk < 1) return DG_ERR_WORKSPACE;
+  for (int64_t r0 = 0; r0 < n; r0 += chunk) {
+    const int64_t m = std::min(chunk, n - r0);
+    Ws ws = carve(c, m, (char*)wsp);
+    DG_CHECK(embed(c, w, tokens + r0, m, ws, s));
+    for (int l = 0; l < c->n_layers; ++l) DG_CHECK(layer(c, w, l, kv, kv->len + r0, m, true, ws, s));
+  }
+  return DG_OK;
+}
+
+StopParams stop_params(const dg_config* c, const dg_sampler* sp) {
+  StopParams p;
+  p.threshold = sp->entropy_threshold;
+  p.ln_vocab = logf((float)c->vocab);
+  p.max_steps = sp->max_steps;
+  p.fixed_steps = sp->fixed_steps;
+  return p;
+}
+
+int check_sampler(const dg_config* c, const dg_sampler* sp) {
+  if (!sp) return DG_ERR_INVALID;
+  if (sp->n_new < 0 || sp->max_steps < 1 || sp->fixed_steps < 0 || sp->flags != 0) return DG_ERR_INVALID;
+  if (!(sp->inv_temperature > 0.f) || std::isnan(sp->entropy_threshold)) return DG_ERR_INVALID;
+  (void)c;
+  return DG_OK;
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+extern "C" {
+
+int dg_workspace_size(const dg_config* cfg, int64_t max_tokens, size_t* h_bytes) {
+  DG_CHECK(check_cfg(cfg));
+  if (!h_bytes || max_tokens < 1 || max_tokens > moe_max_rows(cfg->n_experts)) return DG_ERR_INVALID;
+  *h_bytes = carve(cfg, std::max<int64_t>(max_tokens, 1), nullptr).bytes;
+  return DG_OK;
+}
+
+int dg_prefill_kv(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const int32_t* tokens, int64_t n, void* ws,
+                  size_t ws_bytes, void* stream) {
+  DG_CHECK(check_cfg(cfg));
+  DG_CHECK(check_weights(cfg, w, true, false));
+  if (n < 0 || (n > 0 && !tokens)) return DG_ERR_INVALID;
+  DG_CHECK(check_kv(kv, n));
+  if (n == 0) return DG_OK;
+  if (!ws || ((uintptr_t)ws & 255u) || rows_supported(cfg, ws_bytes, 1) < 1) return DG_ERR_WORKSPACE;
+  DG_CHECK(prefill(cfg, w, kv, tokens, n, ws, ws_bytes, (hipStream_t)stream));
+  kv->len += n;
+  return DG_OK;
+}
+
+int dg_denoise_step(const dg_config* cfg, const dg_weights* w, const dg_kv* kv, const int32_t* canvas,
+                    float inv_temperature, int32_t* pred, float* conf, float* entropy, const dg_debug* dbg, void* ws,
+                    size_t ws_bytes, void* stream) {
+  DG_CHECK(check_cfg(cfg));
+  DG_CHECK(check_weights(cfg, w, true, true));
+  if (!canvas || !pred || !conf || !entropy) return DG_ERR_INVALID;
+  if (!(inv_temperature > 0.f)) return DG_ERR_INVALID;
+  DG_CHECK(check_kv(kv, cfg->canvas));
+  DG_CHECK(check_ws(cfg, cfg->canvas, ws, ws_bytes));
+  Ws wsv = carve(cfg, cfg->canvas, (char*)ws);
+  return denoise(cfg, w, kv, canvas, inv_temperature, pred, conf, entropy, dbg, wsv, (hipStream_t)stream);
+}
+
+int dg_canvas_update(const dg_config* cfg, const int32_t* pred, const float* conf, int32_t keep_count, uint64_t seed,
+                     uint32_t block, uint32_t step, int32_t* canvas_out, uint8_t* keep_mask, void* stream) {
+  DG_CHECK(check_cfg(cfg));
+  if (!canvas_out || keep_count < 0 || keep_count > cfg->canvas) return DG_ERR_INVALID;
+  if (keep_count > 0 && (!pred || !conf)) return DG_ERR_INVALID;
+  DG_LAUNCH(DG_K_CANVAS_UPDATE, (hipStream_t)stream,
+            launch_canvas_update(pred, conf, cfg->canvas, keep_count, seed, block, step, (uint32_t)cfg->vocab,
+                                 canvas_out, keep_mask, (hipStream_t)stream));
+  return DG_OK;
+}
+
+int dg_commit_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const int32_t* block_tokens, void* ws,
+                    size_t ws_bytes, void* stream) {
+  return dg_prefill_kv(cfg, w, kv, block_tokens, cfg ? cfg->canvas : 0, ws, ws_bytes, stream);
+}
+
+int dg_generate_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const dg_sampler* sp, uint32_t block,
+                      int32_t* tokens_out, dg_block_status* h_status, void* ws, size_t ws_bytes, void* stream) {
+  DG_CHECK(check_cfg(cfg));
+  DG_CHECK(check_weights(cfg, w, true, true));
+  DG_CHECK(check_sampler(cfg, sp));
+  if (!tokens_out || !h_status) return DG_ERR_INVALID;
+  DG_CHECK(check_kv(kv, cfg->canvas));
+  DG_CHECK(check_ws(cfg, cfg->canvas, ws, ws_bytes));
+  hipStream_t s = (hipStream_t)stream;
+  const int S = cfg->canvas;
+  Ws wsv = carve(cfg, S, (char*)ws);
+  const StopParams stp = stop_params(cfg, sp);
+  const bool fixed = sp->fixed_steps > 0;
+  const int limit = fixed ? sp->fixed_steps : sp->max_steps;
+
+  DG_LAUNCH(DG_K_CANVAS_UPDATE, s,
+            launch_canvas_update(nullptr, nullptr, S, 0, sp->seed, block, 0, (uint32_t)cfg->vocab, wsv.canvas,
+                                 nullptr, s));
+  dg_block_status st{};
+  for (int t = 1;; ++t) {
+    DG_CHECK(denoise(cfg, w, kv, wsv.canvas, sp->inv_temperature, wsv.pred, wsv.conf, wsv.ent, nullptr, wsv, s));
+    DG_LAUNCH(DG_K_STOP_CHECK, s, launch_stop_check(wsv.ent, wsv.pred, wsv.prev_pred, S, t, stp, wsv.status, s));
+    bool stop;
+    if (fixed) {
+      stop = t >= limit;
+    } else {
+      DG_TRY(hipMemcpyAsync(&st, wsv.status, sizeof(st), hipMemcpyDeviceToHost, s));
+      DG_TRY(hipStreamSynchronize(s));
+      stop = st.reason != DG_STOP_NONE;
+    }
+    if (stop) break;
+    const int keep = (int)std::min<int64_t>(S, (int64_t)t * sp->n_new);
+    DG_LAUNCH(DG_K_CANVAS_UPDATE, s,
+              launch_canvas_update(wsv.pred, wsv.conf, S, keep, sp->seed, block, (uint32_t)t, (uint32_t)cfg->vocab,
+                                   wsv.canvas, nullptr, s));
+  }
+  DG_TRY(hipMemcpyAsync(tokens_out, wsv.pred, (size_t)S * 4, hipMemcpyDeviceToDevice, s));
+  // read the status before the commit reuses the workspace
+  if (fixed) DG_TRY(hipMemcpyAsync(&st, wsv.status, sizeof(st), hipMemcpyDeviceToHost, s));
+  DG_CHECK(prefill(cfg, w, kv, tokens_out, S, ws, ws_bytes, s));
+  kv->len += S;
+  DG_TRY(hipStreamSynchronize(s));
+  *h_status = st;
+  return DG_OK;
+}
+
+int dg_layer_forward(const dg_config* cfg, const dg_weights* w, int32_t layer_i, const dg_kv* kv, const void* x_in,
+                     void* x_out, int64_t n, int32_t causal, const dg_debug* dbg, void* ws, size_t ws_bytes,
+                     void* stream) {
+  DG_CHECK(check_cfg(cfg));
+  if (!w || !w->h_layers || layer_i < 0 || layer_i >= cfg->n_layers) return DG_ERR_INVALID;
+  DG_CHECK(check_layer_weights(w->h_layers[layer_i]));
+  if (!aligned16(x_in) || !aligned16(x_out) || n < 1 || n > moe_max_rows(cfg->n_experts)) return DG_ERR_INVALID;
+  if (causal != 0 && causal != 1) return DG_ERR_INVALID;
+  DG_CHECK(check_kv(kv, n));
+  DG_CHECK(check_ws(cfg, n, ws, ws_bytes));
+  hipStream_t s = (hipStream_t)stream;
+  Ws wsv = carve(cfg, n, (char*)ws);
+  const size_t hb = (size_t)n * cfg->d_model * esize(cfg);
+  DG_TRY(hipMemcpyAsync(wsv.X, x_in, hb, hipMemcpyDeviceToDevice, s));
+  DG_CHECK(layer(cfg, w, layer_i, kv, kv->len, n, causal != 0, wsv, s));
+  DG_TRY(hipMemcpyAsync(x_out, wsv.X, hb, hipMemcpyDeviceToDevice, s));
+  if (dbg) {
+    const size_t rb = (size_t)n * cfg->top_k * 4;
+    if (dbg->route_idx) DG_TRY(hipMemcpyAsync(dbg->route_idx, wsv.ridx, rb, hipMemcpyDeviceToDevice, s));
+    if (dbg->route_w) DG_TRY(hipMemcpyAsync(dbg->route_w, wsv.rw, rb, hipMemcpyDeviceToDevice, s));
+  }
+  return DG_OK;
+}
+
+int dg_vocab_head(const dg_config* cfg, const dg_weights* w, const void* x, int64_t n, float inv_temperature,
+                  int32_t* pred, float* conf, float* entropy, void* ws, size_t ws_bytes, void* stream) {
+  DG_CHECK(check_cfg(cfg));
+  DG_CHECK(check_weights(cfg, w, false, true));
+  if (!aligned16(x) || !pred || !conf || !entropy || n < 1 || n > moe_max_rows(cfg->n_experts))
+    return DG_ERR_INVALID;
+  if (!(inv_temperature > 0.f)) return DG_ERR_INVALID;
+  DG_CHECK(check_ws(cfg, n, ws, ws_bytes));
+  hipStream_t s = (hipStream_t)stream;
+  Ws wsv = carve(cfg, n, (char*)ws);
+  DG_TRY(hipMemcpyAsync(wsv.X, x, (size_t)n * cfg->d_model * esize(cfg), hipMemcpyDeviceToDevice, s));
+  return head(cfg, w, n, inv_temperature, pred, conf, entropy, wsv, s);
+}
+
+int dg_stop_check(const dg_config* cfg, const dg_sampler* sampler, int32_t step, const float* entropy,
+                  const int32_t* pred, int32_t* prev_pred, dg_block_status* d_status, void* stream) {
+  DG_CHECK(check_cfg(cfg));
+  DG_CHECK(check_sampler(cfg, sampler));
+  if (step < 1 || !entropy || !pred || !prev_pred || !d_status) return DG_ERR_INVALID;
+  DG_LAUNCH(DG_K_STOP_CHECK, (hipStream_t)stream,
+            launch_stop_check(entropy, pred, prev_pred, cfg->canvas, step, stop_params(cfg, sampler), d_status,
+                              (hipStream_t)stream));
+  return DG_OK;
+}
+
+int dg_timing_start(uint64_t kernel_mask) {
+  g_timer.mask = kernel_mask;
+  return DG_OK;
+}
+
+int dg_timing_stop(double* h_ms, int64_t* h_launches) {
+  g_timer.mask = 0;
+  if (h_ms)
+    for (int i = 0; i < DG_K_COUNT; ++i) h_ms[i] = 0.0;
+  if (h_launches)
+    for (int i = 0; i < DG_K_COUNT; ++i) h_launches[i] = 0;
+  int rc = DG_OK;
+  for (const TimerRec& r : g_timer.recs) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) {
+      g_hip_error = (int)e;
+      rc = DG_ERR_HIP;
+    }
+    if (h_ms) h_ms[r.id] += ms;
+    if (h_launches) h_launches[r.id] += 1;
+    g_timer.pool.push_back(r.a);
+    g_timer.pool.push_back(r.b);
+  }
+  g_timer.recs.clear();
+  return rc;
+}
+
+const char* dg_status_string(int status) {
+  switch (status) {
+    case DG_OK: return "ok";
+    case DG_ERR_INVALID: return "invalid argument";
+    case DG_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DG_ERR_KV_FULL: return "KV cache capacity exceeded";
+    case DG_ERR_WORKSPACE: return "workspace missing or too small";
+    case DG_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int dg_last_hip_error(void) { return g_hip_error; }
+
+}  // extern "C"

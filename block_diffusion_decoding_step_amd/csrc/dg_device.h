@@ -1,0 +1,142 @@
+// dg_device.h — gfx950 (CDNA4) device primitives shared by the libdg kernels.
+//
+// Matrix-core convention (v_mfma_f32_16x16x32_bf16 and v_mfma_f32_16x16x4_f32):
+//   A fragment: lane l holds row (l & 15) and 8 consecutive K elements at
+//               k0 + 8*(l >> 4) .. +8 (one 16-byte load for bf16, two for fp32)
+//   B fragment: lane l holds column (l & 15), same 8 K elements
+//   C tile    : lane l holds column (l & 15), rows 4*(l >> 4) + r, r = 0..3
+// A 32-wide K step is one bf16 MFMA, or eight fp32 MFMAs that each take the
+// j-th of the lane's 8 elements (the K order inside a step is a permutation
+// applied identically to A and B, so the sum is unchanged).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+__device__ __forceinline__ int wave_id() { return (int)(threadIdx.x >> 6); }
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // round to nearest even
+
+// ---------------------------------------------------------------- fragments
+template <typename T>
+struct Frag;
+
+template <>
+struct Frag<bf16> {
+  bf16x8 v;
+  __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+  __device__ __forceinline__ void zero() {
+    u32x4 z = {0u, 0u, 0u, 0u};
+    v = __builtin_bit_cast(bf16x8, z);
+  }
+  __device__ __forceinline__ void set(int j, float x) { v[j] = (bf16)x; }
+  __device__ __forceinline__ float get(int j) const { return (float)v[j]; }
+};
+
+template <>
+struct Frag<float> {
+  f32x4 lo, hi;
+  __device__ __forceinline__ void load(const float* p) {
+    lo = *reinterpret_cast<const f32x4*>(p);
+    hi = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  __device__ __forceinline__ void zero() {
+    lo = f32x4{0.f, 0.f, 0.f, 0.f};
+    hi = lo;
+  }
+  __device__ __forceinline__ void set(int j, float x) {
+    if (j < 4) lo[j] = x; else hi[j - 4] = x;
+  }
+  __device__ __forceinline__ float get(int j) const { return j < 4 ? lo[j] : hi[j - 4]; }
+};
+
+// acc += A(16 x 32) * B(32 x 16) for one 32-wide K step
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<bf16>& a, const Frag<bf16>& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[j], b.lo[j], acc, 0, 0, 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[j], b.hi[j], acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---------------------------------------------------------------- 8-wide vector IO
+template <typename T>
+struct Vec8;
+template <>
+struct Vec8<bf16> {
+  static __device__ __forceinline__ void load(const bf16* p, float* out) {
+    bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) out[j] = (float)v[j];
+  }
+  static __device__ __forceinline__ void store(bf16* p, const float* in) {
+    bf16x8 v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (bf16)in[j];
+    *reinterpret_cast<bf16x8*>(p) = v;
+  }
+};
+template <>
+struct Vec8<float> {
+  static __device__ __forceinline__ void load(const float* p, float* out) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { out[j] = a[j]; out[j + 4] = b[j]; }
+  }
+  static __device__ __forceinline__ void store(float* p, const float* in) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{in[0], in[1], in[2], in[3]};
+    *reinterpret_cast<f32x4*>(p + 4) = f32x4{in[4], in[5], in[6], in[7]};
+  }
+};
+
+// ---------------------------------------------------------------- wave reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Remap a linear workgroup id so that each of the 8 XCDs (dispatched round-robin
+// by workgroup id) receives one contiguous range of logical tiles; tiles that
+// share operands then share an L2.
+__device__ __forceinline__ int xcd_remap(int b, int total) {
+  const int nx = 8;
+  int per = total / nx, rem = total % nx;
+  int x = b % nx, i = b / nx;
+  // XCD x owns per + (x < rem) tiles starting at x*per + min(x, rem)
+  int start = x * per + (x < rem ? x : rem);
+  int cnt = per + (x < rem ? 1 : 0);
+  return i < cnt ? start + i : b;  // b beyond the balanced split keeps its own id
+}
+
+}  // namespace dg

@@ -1,0 +1,131 @@
+// dg_kernels.h — host-side launchers of the libdg kernels (internal to libdg).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dg.h"
+
+namespace dg {
+
+typedef __bf16 bf16;
+
+// limits of the single-workgroup token->expert permutation
+constexpr int kPermMaxRows = 2048;
+constexpr int kPermBitWords = 8192;
+constexpr int kPermMasks = 4096;
+
+// rows per routed-expert work tile, and the bound on the number of tiles
+constexpr int kMoeTileRows = 32;
+inline int moe_max_tiles(int M, int E, int k) { return E + (M * k + kMoeTileRows - 1) / kMoeTileRows; }
+
+inline int moe_max_rows(int E) {
+  int words = (E + 31) / 32;
+  int r = kPermMaxRows;
+  if (r > kPermBitWords / words) r = kPermBitWords / words;
+  int by_masks = 64 * (kPermMasks / E);
+  if (r > by_masks) r = by_masks;
+  return r;
+}
+
+struct StopParams {
+  float threshold;
+  float ln_vocab;
+  int max_steps;
+  int fixed_steps;
+};
+
+// ---- k_misc.hip
+template <typename T>
+hipError_t launch_embed(const int32_t* tok, const T* E, T* X, int M, int d, int V, hipStream_t s);
+template <typename T>
+hipError_t launch_rmsnorm(const T* X, const T* g, T* Y, int M, int d, float eps, hipStream_t s);
+hipError_t launch_router_topk(const float* logits, int M, int E, int k, int32_t* idx, float* w, hipStream_t s);
+hipError_t launch_moe_permute(const int32_t* idx, int M, int E, int k, int32_t* counts, int32_t* offsets,
+                              int32_t* perm, int32_t* pos, int4* tiles, int32_t* n_tiles, hipStream_t s);
+template <typename T>
+hipError_t launch_moe_combine(T* X, const T* Ys, const T* Yp, const int32_t* pos, const float* w, int M, int d,
+                              int k, hipStream_t s);
+hipError_t launch_stop_check(const float* ent, const int32_t* pred, int32_t* prev, int S, int step, StopParams sp,
+                             dg_block_status* out, hipStream_t s);
+hipError_t launch_canvas_update(const int32_t* pred, const float* conf, int S, int keep, uint64_t seed,
+                                uint32_t block, uint32_t step, uint32_t V, int32_t* canvas, uint8_t* keep_mask,
+                                hipStream_t s);
+
+// ---- k_gemm.hip
+enum class GemmEpi { Store, StoreF32, Resid, QKV, SwiGLU };
+
+struct GemmArgs {
+  const void* A;   // [M, K] rows, lda elements apart
+  const void* B;   // [N, K] rows (weights, [out, in])
+  void* C;         // output (meaning depends on the epilogue)
+  int M, N, K;
+  int lda, ldb, ldc;
+  // QKV epilogue
+  void* q;         // [Hq][q_rows][Dh]
+  void* kc;        // key cache of this layer   [Hkv][cap][Dh]
+  void* vc;        // value cache of this layer [Hkv][Dh][cap]
+  int n_heads, n_kv_heads, head_dim;
+  int q_rows;
+  int64_t cap, pos0;
+  // SwiGLU epilogue: N = F (output width); B holds 2F rows: gate rows then up rows
+};
+
+template <typename T>
+hipError_t launch_gemm(GemmEpi epi, const GemmArgs& a, hipStream_t s);
+
+struct MoeArgs {
+  const int4* tiles;      // (expert, first pair, rows, 0)
+  const int32_t* n_tiles;
+  int max_tiles;
+  const int32_t* perm;    // pair -> token (gate_up gathers rows through it)
+  const void* X;          // gate_up: normalised hidden [M, d]; down: H [pairs, F]
+  const void* W;          // gate_up: [E][2F][d]; down: [E][d][F]
+  void* out;              // gate_up: H [pairs, F]; down: Yp [pairs, d]
+  int d, F;
+};
+template <typename T>
+hipError_t launch_moe_gate_up(const MoeArgs& a, hipStream_t s);
+template <typename T>
+hipError_t launch_moe_down(const MoeArgs& a, hipStream_t s);
+
+// ---- k_attn.hip
+struct AttnArgs {
+  const void* q;      // [Hq][q_rows][Dh]
+  const void* kc;     // [Hkv][cap][Dh]
+  const void* vc;     // [Hkv][Dh][cap]
+  float* o_part;      // [n_split][Hq][q_rows][Dh]
+  float* ml_part;     // [n_split][Hq][q_rows][2]  (running max in log2 units, sum)
+  void* o;            // [q_rows][Hq*Dh]
+  int q_rows;         // M
+  int n_heads, n_kv_heads, head_dim;
+  int64_t cap;
+  int64_t n_keys;     // keys visible: [0, n_keys)
+  int64_t q_pos0;     // absolute position of query row 0 (causal)
+  int causal;
+  int n_split;
+};
+template <typename T>
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+template <typename T>
+hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t s);
+int attention_splits(int64_t n_keys, int q_rows, int n_heads, int n_kv_heads, int causal, int max_split);
+
+// ---- k_head.hip
+struct HeadArgs {
+  const void* x;      // normalised hidden [n, d]
+  const void* E;      // [V, d]
+  float4* part;       // [n_groups][n] partials (max, argmax bits, Z, S1), log2 units
+  int n, d, V;
+  int n_groups;
+  float beta_log2e;   // inv_temperature * log2(e)
+  int32_t* pred;
+  float* conf;
+  float* ent;
+};
+template <typename T>
+hipError_t launch_vocab_head(const HeadArgs& a, hipStream_t s);
+hipError_t launch_head_merge(const HeadArgs& a, hipStream_t s);
+int head_groups(int V);
+
+}  // namespace dg

@@ -63,6 +63,7 @@ def _dev_lib():
     if _dev is None:
         if not os.path.exists(DEV_LIB):
             raise RuntimeError(f"{DEV_LIB} is not built; run __graft_entry__.build() first")
+        import torch  # noqa: F401  (bind to the HIP runtime torch has loaded, see the libdg binding)
         lib = ctypes.CDLL(DEV_LIB)
         i64, u64, f32, vp, u32 = ctypes.c_int64, ctypes.c_uint64, ctypes.c_float, ctypes.c_void_p, ctypes.c_uint32
         for name in ("dgi_dev_normal_f32", "dgi_dev_normal_bf16"):

@@ -1,0 +1,291 @@
+/* dg.h — C ABI of the MI355X block-diffusion denoising library (libdg.so).
+ *
+ * One denoising pass of a DiffusionGemma-style block-diffusion model at batch 1,
+ * plus the canvas update, the stop rule, prompt prefill and block commit.
+ * Page references:
+ *   [P1] "DiffusionGemma: When Text Generation Stops Being Sequential" (blog)
+ *   [P2] "DiffusionGemma 26B: How Google's Text Diffusion Model Generates Tokens
+ *        in Parallel" (dev.to)
+ *   [P3] "DiffusionGemma local text generation" (ctxwire)
+ *   [P5] "When to use a diffusion LLM: I compared DiffusionGemma and Gemma 4"
+ *
+ * Conventions for every call
+ *   - Pointers are DEVICE pointers unless the name starts with h_.
+ *   - The caller owns all memory (weights, KV cache, inputs, outputs, workspace);
+ *     the library never allocates device memory and keeps no device state.
+ *   - Calls are stream-ordered and return after enqueueing on `stream` (a
+ *     hipStream_t passed as void*; NULL = the default stream).  Exceptions:
+ *     dg_generate_block in adaptive mode waits once per pass for a 16-byte status,
+ *     and dg_workspace_size / dg_status_string are host-only.
+ *   - Return value: DG_OK (0) or a negative dg_status.  Arguments are validated
+ *     before any HIP call, so a validation error enqueues nothing and writes
+ *     nothing.  DG_ERR_HIP keeps the HIP error code for dg_last_hip_error().
+ *   - Calls on distinct workspaces and streams may run concurrently; two calls
+ *     sharing one workspace must be ordered on one stream.
+ *
+ * Tensor layouts (row-major, dtype = cfg->dtype unless stated):
+ *   hidden states      [n, d_model]
+ *   embed (tied head)  [vocab, d_model]
+ *   wqkv               [(n_heads + 2*n_kv_heads)*head_dim, d_model]
+ *                      rows: query heads, then key heads, then value heads
+ *   wo                 [d_model, n_heads*head_dim]
+ *   w_router           [n_experts, d_model]
+ *   w_gate_up          [n_experts, 2*ffn_expert, d_model]  gate rows, then up rows
+ *   w_down             [n_experts, d_model, ffn_expert]
+ *   ws_gate_up         [2*ffn_shared, d_model]             gate rows, then up rows
+ *   ws_down            [d_model, ffn_shared]
+ *   norm gains         [d_model]
+ *   KV cache  k        [n_layers][n_kv_heads][capacity][head_dim]
+ *             v        [n_layers][n_kv_heads][head_dim][capacity]   (positions contiguous)
+ *   tokens / canvas    int32 [n]
+ * All matrices are [out, in]: y = x W^T.
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dg_status {
+  DG_OK = 0,
+  DG_ERR_INVALID = -1,     /* null pointer, bad dimension, out-of-range argument */
+  DG_ERR_UNSUPPORTED = -2, /* valid but not built: e.g. head_dim not 64/128, rope_theta != 0 */
+  DG_ERR_KV_FULL = -3,     /* kv->len + rows > kv->capacity */
+  DG_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than dg_workspace_size() */
+  DG_ERR_HIP = -5          /* a HIP runtime/launch call failed; see dg_last_hip_error() */
+} dg_status;
+
+typedef enum dg_dtype { DG_F32 = 0, DG_BF16 = 1 } dg_dtype;
+
+/* Why a block stopped ([P2] "How Diffusion Changes the Equation": entropy below a
+ * threshold, or predictions unchanged over two consecutive passes, or 48 passes;
+ * the three are OR-ed).  FIXED = a fixed pass count requested by the caller. */
+typedef enum dg_stop {
+  DG_STOP_NONE = 0,
+  DG_STOP_ENTROPY = 1,
+  DG_STOP_STABLE = 2,
+  DG_STOP_CAP = 3,
+  DG_STOP_FIXED = 4
+} dg_stop;
+
+/* Model dimensions.  The pages give a 128-expert MoE with 8 routed + 1 shared
+ * expert, a 262K vocabulary and a 256-slot canvas ([P2] "Architecture Details");
+ * the per-layer widths are the caller's.  Constraints: d_model, ffn_expert and
+ * ffn_shared multiples of 32; head_dim 64 or 128; n_heads a multiple of
+ * n_kv_heads with n_heads/n_kv_heads in {1, 2, 4}; top_k <= n_experts <= 256,
+ * top_k <= 16; canvas <= 1024; rope_theta must be 0 (no positional term). */
+typedef struct dg_config {
+  int32_t n_layers;
+  int32_t d_model;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t n_experts;
+  int32_t top_k;
+  int32_t ffn_expert;
+  int32_t ffn_shared;
+  int32_t vocab;
+  int32_t canvas;
+  int32_t dtype;      /* dg_dtype: storage type of weights, activations and KV */
+  float rms_eps;      /* RMSNorm epsilon */
+  float rope_theta;   /* reserved; must be 0 */
+} dg_config;
+
+typedef struct dg_layer_weights {
+  const void* attn_norm;
+  const void* wqkv;
+  const void* wo;
+  const void* ffn_norm;
+  const void* w_router;
+  const void* w_gate_up;
+  const void* w_down;
+  const void* ws_gate_up;
+  const void* ws_down;
+} dg_layer_weights;
+
+typedef struct dg_weights {
+  const void* embed;                 /* [vocab, d_model], also the output head (tied) */
+  const void* final_norm;            /* [d_model] */
+  const dg_layer_weights* h_layers;  /* HOST array of n_layers entries of device pointers */
+} dg_weights;
+
+/* KV cache.  len and capacity are host values; capacity must be a multiple of 32.
+ * Rows [0, len) hold committed context (prompt and finished blocks). */
+typedef struct dg_kv {
+  void* k;
+  void* v;
+  int64_t len;
+  int64_t capacity;
+} dg_kv;
+
+/* Sampler of dg_generate_block.
+ *   keep count after pass t: k_t = min(canvas, t * n_new) ([P5] "How block diffusion
+ *   works": keep the most confident slots, re-randomise the rest);
+ *   fixed_steps > 0: run exactly that many passes (timing mode, reason FIXED);
+ *   otherwise stop on mean entropy < entropy_threshold, on two equal consecutive
+ *   predictions, or at max_steps (<= 48 by default, any value >= 1 accepted).
+ *   seed keys the Philox canvas draws; inv_temperature scales the logits. */
+typedef struct dg_sampler {
+  int32_t n_new;
+  int32_t max_steps;
+  int32_t fixed_steps;
+  float entropy_threshold;
+  float inv_temperature;
+  uint32_t flags;       /* reserved, must be 0 */
+  uint64_t seed;
+} dg_sampler;
+
+/* Block status (host struct for dg_generate_block; device struct for dg_stop_check). */
+typedef struct dg_block_status {
+  int32_t steps;         /* passes run */
+  int32_t reason;        /* dg_stop */
+  float mean_entropy;    /* mean over all canvas slots of the last pass, nats */
+  uint32_t flags;        /* DG_WARN_* bits */
+} dg_block_status;
+
+#define DG_WARN_NUMERIC 0x1u /* some slot entropy was NaN or outside [0, ln V] */
+
+/* Optional per-layer dumps of dg_denoise_step (parity tests); any field may be NULL.
+ *   hidden    [n_layers, canvas, d_model]  residual stream after each layer (dtype)
+ *   route_idx [n_layers, canvas, top_k]    int32 chosen experts, descending logit
+ *   route_w   [n_layers, canvas, top_k]    float routing weights */
+typedef struct dg_debug {
+  void* hidden;
+  int32_t* route_idx;
+  float* route_w;
+} dg_debug;
+
+/* Bytes of workspace needed by any call that processes up to max_tokens rows at
+ * once (use cfg->canvas for denoising; a prefill chunk size for prefill/commit;
+ * the larger of the two for both).  Host-only.  Longer prefills are split into
+ * chunks of the largest row count the given workspace supports. */
+int dg_workspace_size(const dg_config* cfg, int64_t max_tokens, size_t* h_bytes);
+
+/* Prompt prefill: a causal forward of n tokens placed at positions
+ * kv->len .. kv->len+n-1; writes their keys/values for every layer and, on
+ * success, sets kv->len += n.  The prompt is read into the KV cache once
+ * ([P5] "How block diffusion works"; [P2] "Architecture Details": an
+ * autoregressive pass caches the prompt context).  Query i sees cache rows
+ * 0 .. kv->len + i.  Tokens outside [0, vocab) are clamped into range. */
+int dg_prefill_kv(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const int32_t* tokens, int64_t n,
+                  void* ws, size_t ws_bytes, void* stream);
+
+/* One denoising pass over the canvas ([P2] "How Diffusion Changes the Equation":
+ * bidirectional attention over the whole block; [P5] "How block diffusion works"):
+ * embed the canvas, run every layer with canvas queries attending to cache rows
+ * [0, kv->len) and to all canvas slots (no mask), route each slot to top_k experts
+ * plus the shared expert, then the final norm and the tied vocab head.  Per slot
+ * it writes pred (argmax token, ties to the lowest id), conf (largest softmax
+ * probability) and entropy (nats).  The canvas keys/values are written to cache
+ * rows [kv->len, kv->len + canvas) as scratch; kv->len is unchanged, so this needs
+ * kv->len + canvas <= capacity.  inv_temperature multiplies the logits. */
+int dg_denoise_step(const dg_config* cfg, const dg_weights* w, const dg_kv* kv, const int32_t* canvas,
+                    float inv_temperature, int32_t* pred, float* conf, float* entropy, const dg_debug* dbg,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Canvas update ([P5] "How block diffusion works": keep the most confident slots,
+ * re-randomise the others; any slot may change on a later pass).  The keep_count
+ * slots of highest conf (ties to the lower slot, NaN last) take pred; every other
+ * slot i takes U(seed, block, step, i) = floor(w0 * vocab / 2^32), w0 the first
+ * output word of Philox4x32-10 (Salmon et al., SC'11) with key (seed low, seed high)
+ * and counter (i, step, block, 0).  keep_count = 0 with step = 0 gives the initial
+ * random canvas (pred and conf may then be NULL).  keep_mask (uint8, may be NULL)
+ * receives 1 for kept slots.  0 <= keep_count <= canvas. */
+int dg_canvas_update(const dg_config* cfg, const int32_t* pred, const float* conf, int32_t keep_count,
+                     uint64_t seed, uint32_t block, uint32_t step, int32_t* canvas_out, uint8_t* keep_mask,
+                     void* stream);
+
+/* Commit a finished block ([P2] "How Diffusion Changes the Equation": each 256-token
+ * block is committed to the KV cache before the next; [P3] "How diffusion text
+ * generation differs").  Same as dg_prefill_kv of the canvas tokens: a causal
+ * forward at positions kv->len .. kv->len+canvas-1; on success kv->len += canvas. */
+int dg_commit_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const int32_t* block_tokens,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* One whole block: initial random canvas, passes t = 1, 2, ... each followed by
+ * the stop check and, if not stopping, the canvas update with k_t; then the last
+ * pass's predictions are written to tokens_out [canvas] and committed (kv->len
+ * grows by canvas).  h_status (host) receives steps, reason and mean entropy.
+ * Adaptive mode synchronises `stream` once per pass to read a 16-byte status;
+ * fixed mode (sampler->fixed_steps > 0) synchronises once at the end. */
+int dg_generate_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const dg_sampler* sampler,
+                      uint32_t block, int32_t* tokens_out, dg_block_status* h_status, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* --- finer-grained calls of the same path (each is one stage of dg_denoise_step) --- */
+
+/* One transformer block `layer` over n hidden rows x_in -> x_out ([n, d_model];
+ * x_out may equal x_in).  Rows sit at cache positions kv->len .. kv->len+n-1 and
+ * their keys/values are written there for this layer; kv->len is unchanged.
+ * causal = 0: every row sees all cache rows and all n rows (canvas pass);
+ * causal = 1: row i sees cache rows 0 .. kv->len + i (prefill/commit).
+ * dbg (may be NULL): route_idx / route_w receive this layer's [n, top_k] routing;
+ * its hidden field is ignored (x_out already holds the result). */
+int dg_layer_forward(const dg_config* cfg, const dg_weights* w, int32_t layer, const dg_kv* kv,
+                     const void* x_in, void* x_out, int64_t n, int32_t causal, const dg_debug* dbg, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* Final RMSNorm + tied vocab projection fused with the per-slot softmax
+ * statistics: for each of n rows, pred/conf/entropy as in dg_denoise_step.  The
+ * n x vocab logits are never written to memory. */
+int dg_vocab_head(const dg_config* cfg, const dg_weights* w, const void* x, int64_t n, float inv_temperature,
+                  int32_t* pred, float* conf, float* entropy, void* ws, size_t ws_bytes, void* stream);
+
+/* Stop check after pass `step` (1-based): writes a dg_block_status to d_status
+ * (device) with reason ENTROPY if mean(entropy) < threshold, else STABLE if
+ * step >= 2 and pred equals prev_pred on every slot, else CAP if step >= max_steps,
+ * else NONE (fixed_steps > 0: FIXED when step >= fixed_steps, else NONE).  Then
+ * copies pred into prev_pred.  Uses cfg->canvas slots. */
+int dg_stop_check(const dg_config* cfg, const dg_sampler* sampler, int32_t step, const float* entropy,
+                  const int32_t* pred, int32_t* prev_pred, dg_block_status* d_status, void* stream);
+
+/* --- measurement support: HIP-event timing of kernel classes --------------------- */
+
+/* Kernel classes of one pass, for dg_timing_*. */
+typedef enum dg_kernel {
+  DG_K_EMBED = 0,
+  DG_K_RMSNORM,
+  DG_K_GEMM_QKV,
+  DG_K_ATTENTION,      /* split-KV attention partials */
+  DG_K_ATTN_MERGE,
+  DG_K_GEMM_O,         /* output projection + residual */
+  DG_K_GEMM_ROUTER,
+  DG_K_ROUTER_TOPK,
+  DG_K_MOE_PERMUTE,
+  DG_K_MOE_GATE_UP,    /* routed experts, gate/up projections + SwiGLU */
+  DG_K_MOE_DOWN,       /* routed experts, down projection */
+  DG_K_SHARED_GATE_UP,
+  DG_K_SHARED_DOWN,
+  DG_K_MOE_COMBINE,
+  DG_K_VOCAB_HEAD,
+  DG_K_HEAD_MERGE,
+  DG_K_STOP_CHECK,
+  DG_K_CANVAS_UPDATE,
+  DG_K_COUNT
+} dg_kernel;
+
+/* Start recording a HIP event pair around every launch, on the caller's stream, of
+ * the kernel classes whose bit (1 << dg_kernel) is set in kernel_mask, for calls
+ * made by this thread.  Events come from a host-side pool (no device memory). */
+int dg_timing_start(uint64_t kernel_mask);
+
+/* Stop recording, wait for the recorded events and return per-class totals:
+ * h_ms[DG_K_COUNT] milliseconds and h_launches[DG_K_COUNT] launch counts (either
+ * pointer may be NULL). */
+int dg_timing_stop(double* h_ms, int64_t* h_launches);
+
+/* Static description of a dg_status value. */
+const char* dg_status_string(int status);
+
+/* HIP error code of the last DG_ERR_HIP returned on this thread (0 if none). */
+int dg_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DG_H */

@@ -1,0 +1,185 @@
+"""The C ABI without a GPU: libdg.so loads, exports every call include/dg.h declares, and rejects bad
+arguments with the documented status before touching the device (no compute call is made here)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+from dataclasses import replace
+
+import pytest
+
+import block_diffusion_decoding_step_amd as dg
+from dg_inputs import recipe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dg.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_documented_calls():
+    names = _declared()
+    for n in ("dg_prefill_kv", "dg_denoise_step", "dg_canvas_update", "dg_commit_block", "dg_generate_block",
+              "dg_workspace_size", "dg_status_string"):
+        assert n in names
+    assert set(names) == set(dg.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(dg.LIB_PATH)
+    for n in _declared():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", dg.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (dg_\w+)", out))
+    assert set(_declared()) <= exported
+
+
+def test_header_compiles_as_c():
+    src = '#include "dg.h"\nint main(void){dg_config c; (void)c; return dg_status_string(0) == 0;}\n'
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-I", os.path.dirname(HEADER),
+                        "-x", "c", "-"], input=src, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_struct_layouts_match_header():
+    src = ('#include <stdio.h>\n#include <stddef.h>\n#include "dg.h"\n'
+           'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(dg_config), sizeof(dg_layer_weights),'
+           ' sizeof(dg_weights), sizeof(dg_kv), sizeof(dg_sampler), offsetof(dg_sampler, seed),'
+           ' sizeof(dg_block_status), sizeof(dg_debug)); return 0;}\n')
+    exe = "/tmp/dg_layout_probe"
+    r = subprocess.run(["gcc", "-I", os.path.dirname(HEADER), "-x", "c", "-", "-o", exe], input=src,
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    got = [int(x) for x in subprocess.run([exe], capture_output=True, text=True).stdout.split()]
+    exp = [ctypes.sizeof(dg.dg_config), ctypes.sizeof(dg.dg_layer_weights), ctypes.sizeof(dg.dg_weights),
+           ctypes.sizeof(dg.dg_kv), ctypes.sizeof(dg.dg_sampler), dg.dg_sampler.seed.offset,
+           ctypes.sizeof(dg.dg_block_status), ctypes.sizeof(dg.dg_debug)]
+    assert got == exp
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5):
+        assert dg.dg_status_string(s) and dg.dg_status_string(s) != "unknown status"
+    assert dg.dg_status_string(-99) == "unknown status"
+
+
+def _cfg(**kw):
+    return dg.make_config(replace(recipe.C0.dims, **kw))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d_model=0), dg.DG_ERR_INVALID),
+    (dict(top_k=9), dg.DG_ERR_INVALID),
+    (dict(n_heads=3), dg.DG_ERR_INVALID),
+    (dict(head_dim=96), dg.DG_ERR_UNSUPPORTED),
+    (dict(d_model=250), dg.DG_ERR_UNSUPPORTED),
+    (dict(ffn_expert=500), dg.DG_ERR_UNSUPPORTED),
+    (dict(n_heads=16, n_kv_heads=2), dg.DG_ERR_UNSUPPORTED),
+    (dict(canvas=2048), dg.DG_ERR_UNSUPPORTED),
+    (dict(n_experts=300, top_k=2), dg.DG_ERR_UNSUPPORTED),
+])
+def test_workspace_size_rejects_bad_config(kw, status):
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_workspace_size(_cfg(**kw), 32)
+    assert e.value.status == status
+
+
+def test_rope_is_unsupported():
+    c = _cfg()
+    c.rope_theta = 10000.0
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_workspace_size(c, 32)
+    assert e.value.status == dg.DG_ERR_UNSUPPORTED
+
+
+def test_workspace_size_grows_with_rows():
+    c = dg.make_config(recipe.C3.dims)
+    a = dg.dg_workspace_size(c, 256)
+    b = dg.dg_workspace_size(c, 2048)
+    assert 0 < a < b
+    with pytest.raises(dg.DGError):
+        dg.dg_workspace_size(c, 0)
+    with pytest.raises(dg.DGError):
+        dg.dg_workspace_size(c, 4096)   # above the permutation's row limit for 128 experts
+
+
+class _Fake:
+    """Aligned fake device addresses: validation runs on the host and never dereferences them."""
+
+    def __init__(self, addr):
+        self.addr = addr
+
+    def data_ptr(self):
+        return self.addr
+
+
+def _fake_weights(n_layers):
+    a = _Fake(0x10000)
+    return dg.Weights(a, a, [{f: a for f in dg.Weights.LAYER_FIELDS} for _ in range(n_layers)])
+
+
+def test_calls_validate_before_any_device_work():
+    cfg = _cfg()
+    w = _fake_weights(cfg.n_layers)
+    buf = _Fake(0x20000)
+    ws_bytes = dg.dg_workspace_size(cfg, cfg.canvas)
+    kv = dg.KV(buf, buf, capacity=96, length=80)  # 80 + 32 > 96
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_denoise_step(cfg, w, kv, buf, 1.0, buf, buf, buf, None, buf, ws_bytes, 0)
+    assert e.value.status == dg.DG_ERR_KV_FULL
+    kv = dg.KV(buf, buf, capacity=100, length=0)  # capacity not a multiple of 32
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_denoise_step(cfg, w, kv, buf, 1.0, buf, buf, buf, None, buf, ws_bytes, 0)
+    assert e.value.status == dg.DG_ERR_INVALID
+    kv = dg.KV(buf, buf, capacity=128, length=0)
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_denoise_step(cfg, w, kv, buf, 1.0, buf, buf, buf, None, buf, ws_bytes - 256, 0)
+    assert e.value.status == dg.DG_ERR_WORKSPACE
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_denoise_step(cfg, w, kv, None, 1.0, buf, buf, buf, None, buf, ws_bytes, 0)
+    assert e.value.status == dg.DG_ERR_INVALID
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_denoise_step(cfg, w, kv, buf, 0.0, buf, buf, buf, None, buf, ws_bytes, 0)
+    assert e.value.status == dg.DG_ERR_INVALID
+    with pytest.raises(dg.DGError) as e:   # misaligned weight pointer
+        dg.dg_denoise_step(cfg, _fake_weights_misaligned(cfg.n_layers), kv, buf, 1.0, buf, buf, buf, None, buf,
+                           ws_bytes, 0)
+    assert e.value.status == dg.DG_ERR_INVALID
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_prefill_kv(cfg, w, kv, buf, 200, buf, ws_bytes, 0)
+    assert e.value.status == dg.DG_ERR_KV_FULL
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_layer_forward(cfg, w, 5, kv, buf, buf, 32, 0, None, buf, ws_bytes, 0)
+    assert e.value.status == dg.DG_ERR_INVALID
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_layer_forward(cfg, w, 0, kv, buf, buf, 32, 2, None, buf, ws_bytes, 0)
+    assert e.value.status == dg.DG_ERR_INVALID
+    bad = dg.make_sampler(4)
+    bad.max_steps = 0
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_generate_block(cfg, w, kv, bad, 0, buf, buf, ws_bytes, 0)
+    assert e.value.status == dg.DG_ERR_INVALID
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_stop_check(cfg, dg.make_sampler(4), 0, buf, buf, buf, buf, 0)
+    assert e.value.status == dg.DG_ERR_INVALID
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_canvas_update(cfg, buf, buf, cfg.canvas + 1, 1, 0, 1, buf, None, 0)
+    assert e.value.status == dg.DG_ERR_INVALID
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_vocab_head(cfg, w, buf, 0, 1.0, buf, buf, buf, buf, ws_bytes, 0)
+    assert e.value.status == dg.DG_ERR_INVALID
+    # the failed commit left the committed length alone
+    assert kv.len == 0
+
+
+def _fake_weights_misaligned(n_layers):
+    a = _Fake(0x10000)
+    layers = [{f: a for f in dg.Weights.LAYER_FIELDS} for _ in range(n_layers)]
+    layers[-1]["w_down"] = _Fake(0x10008)
+    return dg.Weights(a, a, layers)
