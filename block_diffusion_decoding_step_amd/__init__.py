@@ -84,7 +84,8 @@ class dg_block_status(ctypes.Structure):
 
 
 class dg_debug(ctypes.Structure):
-    _fields_ = [("hidden", ctypes.c_void_p), ("route_idx", ctypes.c_void_p), ("route_w", ctypes.c_void_p)]
+    _fields_ = [("hidden", ctypes.c_void_p), ("route_idx", ctypes.c_void_p), ("route_w", ctypes.c_void_p),
+                ("router_logits", ctypes.c_void_p)]
 
 
 _P = ctypes.POINTER
@@ -239,7 +240,7 @@ def _dbg(dbg):
     if dbg is None:
         return None
     return ctypes.byref(dg_debug(hidden=_ptr(dbg.get("hidden")), route_idx=_ptr(dbg.get("route_idx")),
-                                 route_w=_ptr(dbg.get("route_w"))))
+                                 route_w=_ptr(dbg.get("route_w")), router_logits=_ptr(dbg.get("router_logits"))))
 
 
 def dg_layer_forward(cfg, weights, layer: int, kv, x_in, x_out, n: int, causal: int, dbg=None, ws=None,

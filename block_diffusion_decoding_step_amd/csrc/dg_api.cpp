@@ -340,6 +340,9 @@ int denoise(const dg_config* c, const dg_weights* w, const dg_kv* kv, const int3
       if (dbg->route_idx)
         DG_TRY(hipMemcpyAsync((char*)dbg->route_idx + l * rb, ws.ridx, rb, hipMemcpyDeviceToDevice, s));
       if (dbg->route_w) DG_TRY(hipMemcpyAsync((char*)dbg->route_w + l * rb, ws.rw, rb, hipMemcpyDeviceToDevice, s));
+      const size_t lb = (size_t)S * c->n_experts * 4;
+      if (dbg->router_logits)
+        DG_TRY(hipMemcpyAsync((char*)dbg->router_logits + l * lb, ws.rlog, lb, hipMemcpyDeviceToDevice, s));
     }
   }
   return head(c, w, S, inv_temp, pred, conf, ent, ws, s);
@@ -496,6 +499,9 @@ int dg_layer_forward(const dg_config* cfg, const dg_weights* w, int32_t layer_i,
     const size_t rb = (size_t)n * cfg->top_k * 4;
     if (dbg->route_idx) DG_TRY(hipMemcpyAsync(dbg->route_idx, wsv.ridx, rb, hipMemcpyDeviceToDevice, s));
     if (dbg->route_w) DG_TRY(hipMemcpyAsync(dbg->route_w, wsv.rw, rb, hipMemcpyDeviceToDevice, s));
+    if (dbg->router_logits)
+      DG_TRY(hipMemcpyAsync(dbg->router_logits, wsv.rlog, (size_t)n * cfg->n_experts * 4, hipMemcpyDeviceToDevice,
+                            s));
   }
   return DG_OK;
 }

@@ -150,13 +150,15 @@ typedef struct dg_block_status {
 #define DG_WARN_NUMERIC 0x1u /* some slot entropy was NaN or outside [0, ln V] */
 
 /* Optional per-layer dumps of dg_denoise_step (parity tests); any field may be NULL.
- *   hidden    [n_layers, canvas, d_model]  residual stream after each layer (dtype)
- *   route_idx [n_layers, canvas, top_k]    int32 chosen experts, descending logit
- *   route_w   [n_layers, canvas, top_k]    float routing weights */
+ *   hidden        [n_layers, canvas, d_model]    residual stream after each layer (dtype)
+ *   route_idx     [n_layers, canvas, top_k]      int32 chosen experts, descending logit
+ *   route_w       [n_layers, canvas, top_k]      float routing weights
+ *   router_logits [n_layers, canvas, n_experts]  float router logits the choice was made on */
 typedef struct dg_debug {
   void* hidden;
   int32_t* route_idx;
   float* route_w;
+  float* router_logits;
 } dg_debug;
 
 /* Bytes of workspace needed by any call that processes up to max_tokens rows at
@@ -223,8 +225,9 @@ int dg_generate_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, cons
  * their keys/values are written there for this layer; kv->len is unchanged.
  * causal = 0: every row sees all cache rows and all n rows (canvas pass);
  * causal = 1: row i sees cache rows 0 .. kv->len + i (prefill/commit).
- * dbg (may be NULL): route_idx / route_w receive this layer's [n, top_k] routing;
- * its hidden field is ignored (x_out already holds the result). */
+ * dbg (may be NULL): route_idx / route_w / router_logits receive this layer's
+ * [n, top_k] routing and [n, n_experts] logits; its hidden field is ignored
+ * (x_out already holds the result). */
 int dg_layer_forward(const dg_config* cfg, const dg_weights* w, int32_t layer, const dg_kv* kv,
                      const void* x_in, void* x_out, int64_t n, int32_t causal, const dg_debug* dbg, void* ws,
                      size_t ws_bytes, void* stream);

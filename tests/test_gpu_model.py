@@ -54,13 +54,27 @@ def _c0_pair(d=None, storage=None, prefix=None):
     return sess, model, kv
 
 
-def _check_kv(sess, kv, tol):
+def _check_kv(sess, kv, tol, keep_rows=None):
+    """Cache parity; keep_rows[l] (optional) selects the rows compared at layer l."""
     torch.cuda.synchronize()
     assert sess.kv.len == kv.length
     for l in range(sess.d.n_layers):
         gk, gv = sess.kv_numpy(l, kv.length)
-        assert allclose_report(gk, kv.k[l], *tol)[0], f"K layer {l}"
-        assert allclose_report(gv, kv.v[l], *tol)[0], f"V layer {l}"
+        ok = np.ones(kv.length, dtype=bool) if keep_rows is None else keep_rows[l]
+        rk = allclose_report(gk[:, ok], kv.k[l][:, ok], *tol)
+        rv = allclose_report(gv[:, ok], kv.v[l][:, ok], *tol)
+        assert rk[0], f"K layer {l}: worst excess {rk[1]:.3e} at {rk[2]} (rows compared {int(ok.sum())})"
+        assert rv[0], f"V layer {l}: worst excess {rv[1]:.3e} at {rv[2]} (rows compared {int(ok.sum())})"
+
+
+def _near_tie_rows(traces, thr):
+    """keep_rows[l]: rows with no routing gap below thr at any layer before l (a near-tie upstream makes
+    the two sides legitimately route that token differently)."""
+    n = traces[0].gap.shape[0]
+    keep = [np.ones(n, dtype=bool)]
+    for tr in traces[:-1]:
+        keep.append(keep[-1] & (tr.gap >= thr))
+    return keep
 
 
 def test_c0_prefill_matches_oracle():
@@ -87,14 +101,14 @@ def test_c0_pass_matches_oracle_layer_by_layer():
     d = recipe.C0.dims
     sess, model, kv = _c0_pair()
     canvas = osm.initial_canvas(recipe.INPUT_SEED, 0, d.canvas, d.vocab)
-    hid = torch.empty((d.n_layers, d.canvas, d.d_model), dtype=torch.float32, device="cuda")
-    ridx = torch.empty((d.n_layers, d.canvas, d.top_k), dtype=torch.int32, device="cuda")
-    rw = torch.empty((d.n_layers, d.canvas, d.top_k), dtype=torch.float32, device="cuda")
-    pred, conf, ent = sess.denoise(canvas, dbg={"hidden": hid, "route_idx": ridx, "route_w": rw})
+    dbg = _dbg(d, torch.float32)
+    pred, conf, ent = sess.denoise(canvas, dbg=dbg)
     torch.cuda.synchronize()
+    hid, ridx, rw, rlog = dbg["hidden"], dbg["route_idx"], dbg["route_w"], dbg["router_logits"]
     rec, _ = osm.denoise_pass(model, kv, canvas, keep_traces=True)
     for l, tr in enumerate(rec.traces):
-        compare_routing(ridx[l].cpu().numpy(), rw[l].cpu().numpy(), tr.idx, tr.w, tr.gap, 1e-5)
+        compare_routing(ridx[l].cpu().numpy(), rw[l].cpu().numpy(), rlog[l].cpu().numpy(), tr.router_logits,
+                        tr.idx, F32_TOL)
         ok, worst, at = allclose_report(to_f64(hid[l]), tr.hidden, *F32_TOL)
         assert ok, (l, worst, at)
     sel = rec.margin > MARGIN
@@ -102,6 +116,14 @@ def test_c0_pass_matches_oracle_layer_by_layer():
     assert allclose_report(to_f64(ent), rec.ent, *F32_TOL)[0]
     assert allclose_report(to_f64(conf), rec.conf, 1e-7, 1e-4)[0]
     assert kv.length == sess.kv.len == recipe.C0.prefix   # a pass does not commit
+
+
+def _dbg(d, dtype):
+    L, S = d.n_layers, d.canvas
+    return {"hidden": torch.empty((L, S, d.d_model), dtype=dtype, device="cuda"),
+            "route_idx": torch.empty((L, S, d.top_k), dtype=torch.int32, device="cuda"),
+            "route_w": torch.empty((L, S, d.top_k), dtype=torch.float32, device="cuda"),
+            "router_logits": torch.empty((L, S, d.n_experts), dtype=torch.float32, device="cuda")}
 
 
 def _gpu_block_loop(sess, sampler_args, block):
@@ -243,25 +265,29 @@ def test_full_width_two_layers_end_to_end():
     prompt = dg_inputs.prompt_tokens(P, d.vocab)
     sess.prefill(prompt)
     canvas = osm.initial_canvas(recipe.INPUT_SEED, 0, d.canvas, d.vocab)
-    hid = torch.empty((d.n_layers, d.canvas, d.d_model), dtype=torch.bfloat16, device="cuda")
-    ridx = torch.empty((d.n_layers, d.canvas, d.top_k), dtype=torch.int32, device="cuda")
-    rw = torch.empty((d.n_layers, d.canvas, d.top_k), dtype=torch.float32, device="cuda")
-    pred, conf, ent = sess.denoise(canvas, dbg={"hidden": hid, "route_idx": ridx, "route_w": rw})
+    dbg = _dbg(d, torch.bfloat16)
+    pred, conf, ent = sess.denoise(canvas, dbg=dbg)
     torch.cuda.synchronize()
+    hid, ridx, rw, rlog = dbg["hidden"], dbg["route_idx"], dbg["route_w"], dbg["router_logits"]
     log("full-width: host weights + oracle")
     model = oracle_model(d)
     kv = om.KVCache(d.n_layers, d.n_kv_heads, d.head_dim)
-    osm.prefill(model, kv, prompt)
-    _check_kv(sess, kv, BF16_TOL)
+    _, ptraces = model.body(model.embed(prompt), kv, causal=True, append=True)
+    keep = _near_tie_rows(ptraces, 2 * BF16_TOL[0])  # tie zone: twice the logit tolerance
+    log(f"full-width: prefill rows compared per layer {[int(k.sum()) for k in keep]}")
+    _check_kv(sess, kv, BF16_TOL, keep)
     x = model.embed(canvas)
     x, traces = model.body(x, kv, causal=False, append=False)
     flips = 0
+    downstream = np.ones(d.canvas, dtype=bool)
     for l, tr in enumerate(traces):
-        same = compare_routing(ridx[l].cpu().numpy(), rw[l].cpu().numpy(), tr.idx, tr.w, tr.gap, 5e-3)
+        same = compare_routing(ridx[l].cpu().numpy(), rw[l].cpu().numpy(), rlog[l].cpu().numpy(),
+                               tr.router_logits, tr.idx, BF16_TOL)
         flips += int((~same).sum())
-        ok, worst, at = allclose_report(to_f64(hid[l])[same], tr.hidden[same], *BF16_TOL)
+        downstream &= same
+        ok, worst, at = allclose_report(to_f64(hid[l])[downstream], tr.hidden[downstream], *BF16_TOL)
         assert ok, (l, worst, at)
-    rows = np.array([0, 3, 77, 128, 255])
+    rows = np.array([r for r in (0, 3, 77, 128, 255, 17, 200, 99) if downstream[r]][:5])
     opred, oconf, oent, margin = om.head_stats(x[rows], model.w["final_norm"], model.w["embed"], 1.0, d.rms_eps,
                                                numerics.bf16_round)
     sel = margin > MARGIN
@@ -282,11 +308,10 @@ def test_c3_bench_configuration_layer0_and_properties():
     log("C3: prefill 4096")
     sess.prefill(prompt)
     canvas = osm.initial_canvas(recipe.INPUT_SEED, 0, d.canvas, d.vocab)
-    hid = torch.empty((d.n_layers, d.canvas, d.d_model), dtype=torch.bfloat16, device="cuda")
-    ridx = torch.empty((d.n_layers, d.canvas, d.top_k), dtype=torch.int32, device="cuda")
-    rw = torch.empty((d.n_layers, d.canvas, d.top_k), dtype=torch.float32, device="cuda")
-    pred, conf, ent = sess.denoise(canvas, dbg={"hidden": hid, "route_idx": ridx, "route_w": rw})
+    dbg = _dbg(d, torch.bfloat16)
+    pred, conf, ent = sess.denoise(canvas, dbg=dbg)
     torch.cuda.synchronize()
+    hid, ridx, rw, rlog = dbg["hidden"], dbg["route_idx"], dbg["route_w"], dbg["router_logits"]
     e = to_f64(ent)
     assert np.all(np.isfinite(to_f64(hid)))
     assert np.all(e >= 0) and np.all(e <= math.log(d.vocab) + 1e-4)
@@ -308,7 +333,8 @@ def test_c3_bench_configuration_layer0_and_properties():
     gk, gv = sess.kv_numpy(0, wl.prefix)
     assert allclose_report(gk, kv.k[0], *BF16_TOL)[0] and allclose_report(gv, kv.v[0], *BF16_TOL)[0]
     x0, tr = model.layer(0, E_rows[wl.prefix:], kv, causal=False, append=False)
-    same = compare_routing(ridx[0].cpu().numpy(), rw[0].cpu().numpy(), tr.idx, tr.w, tr.gap, 5e-3)
+    same = compare_routing(ridx[0].cpu().numpy(), rw[0].cpu().numpy(), rlog[0].cpu().numpy(), tr.router_logits,
+                           tr.idx, BF16_TOL)
     assert allclose_report(to_f64(hid[0])[same], x0[same], *BF16_TOL)[0]
     # fixed T=10 block + commit
     out = sess.i32(d.canvas)
