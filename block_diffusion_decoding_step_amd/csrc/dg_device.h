@@ -45,6 +45,10 @@ template <>
 struct Frag<bf16> {
   bf16x8 v;
   __device__ __forceinline__ void load(const bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+  // streaming (non-temporal) load: data read once should not displace reused data in the caches
+  __device__ __forceinline__ void load_nt(const bf16* p) {
+    v = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+  }
   __device__ __forceinline__ void zero() {
     u32x4 z = {0u, 0u, 0u, 0u};
     v = __builtin_bit_cast(bf16x8, z);
@@ -59,6 +63,10 @@ struct Frag<float> {
   __device__ __forceinline__ void load(const float* p) {
     lo = *reinterpret_cast<const f32x4*>(p);
     hi = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  __device__ __forceinline__ void load_nt(const float* p) {
+    lo = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    hi = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
   }
   __device__ __forceinline__ void zero() {
     lo = f32x4{0.f, 0.f, 0.f, 0.f};

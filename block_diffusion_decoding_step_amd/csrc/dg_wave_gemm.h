@@ -1,0 +1,61 @@
+// dg_wave_gemm.h — one wave's share of a K-contiguous GEMM on the gfx950 matrix core.
+#pragma once
+
+#include "dg_device.h"
+
+namespace dg {
+
+// ---------------------------------------------------------------- wave GEMM core
+// acc[mt][nt] += sum_k A[row(mt)][k] * B[col(nt)][k] over ksteps 32-wide steps.
+// ap[mt] / bp[nt] point at this lane's row start plus its 8*(lane>>4) K offset.
+// Software pipeline with a ring of DEPTH register buffers and no branches in the
+// steady state: step s + DEPTH is loaded into the buffer step s just used, at an
+// index clamped to the last step (the few clamped reloads at the end are never
+// consumed), so the compiler can wait for exactly the oldest loads in flight.
+template <bool STREAM, typename T>
+__device__ __forceinline__ void frag_load(Frag<T>& f, const T* p) {
+  if constexpr (STREAM) f.load_nt(p); else f.load(p);
+}
+
+// SA / SB: operand read once per launch (weights), loaded non-temporally.
+template <typename T, int MT, int NT, int DEPTH, bool SA = false, bool SB = false>
+__device__ __forceinline__ void wave_gemm(f32x4 (&acc)[MT][NT], const T* const (&ap)[MT], const T* const (&bp)[NT],
+                                          int ksteps) {
+  Frag<T> fa[DEPTH][MT];
+  Frag<T> fb[DEPTH][NT];
+  const int last = ksteps - 1;
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) {
+    const int s = min(d, last);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) frag_load<SA>(fa[d][mt], ap[mt] + 32 * s);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) frag_load<SB>(fb[d][nt], bp[nt] + 32 * s);
+  }
+  int s0 = 0;
+  for (; s0 + DEPTH <= ksteps; s0 += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) mma(acc[mt][nt], fa[d][mt], fb[d][nt]);
+      const int sn = min(s0 + DEPTH + d, last);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) frag_load<SA>(fa[d][mt], ap[mt] + 32 * sn);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) frag_load<SB>(fb[d][nt], bp[nt] + 32 * sn);
+    }
+  }
+  const int rem = ksteps - s0;  // steps s0 .. ksteps-1 sit in buffers 0 .. rem-1
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d)
+    if (d < rem) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) mma(acc[mt][nt], fa[d][mt], fb[d][nt]);
+    }
+}
+
+}  // namespace dg

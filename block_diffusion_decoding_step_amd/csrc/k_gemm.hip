@@ -18,233 +18,243 @@
 // tiles written by the permutation kernel, so the host never reads routing.
 #include "dg_device.h"
 #include "dg_kernels.h"
+#include "dg_wave_gemm.h"
 
 namespace dg {
-
-// ---------------------------------------------------------------- wave GEMM core
-// acc[mt][nt] += sum_k A[row(mt)][k] * B[col(nt)][k] over ksteps 32-wide steps.
-// ap[mt] / bp[nt] point at this lane's row start plus its 8*(lane>>4) K offset.
-template <typename T, int MT, int NT, int DEPTH>
-__device__ __forceinline__ void wave_gemm(f32x4 (&acc)[MT][NT], const T* const (&ap)[MT], const T* const (&bp)[NT],
-                                          int ksteps, int mt_active) {
-  Frag<T> fa[DEPTH][MT];
-  Frag<T> fb[DEPTH][NT];
-#pragma unroll
-  for (int d = 0; d < DEPTH; ++d) {
-    if (d < ksteps) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        if (mt < mt_active) fa[d][mt].load(ap[mt] + 32 * d);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) fb[d][nt].load(bp[nt] + 32 * d);
-    }
-  }
-  for (int s0 = 0; s0 < ksteps; s0 += DEPTH) {
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      const int s = s0 + d;
-      if (s < ksteps) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          if (mt < mt_active) {
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) mma(acc[mt][nt], fa[d][mt], fb[d][nt]);
-          }
-        const int sn = s + DEPTH;
-        if (sn < ksteps) {
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            if (mt < mt_active) fa[d][mt].load(ap[mt] + 32 * sn);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) fb[d][nt].load(bp[nt] + 32 * sn);
-        }
-      }
-    }
-  }
-}
 
 template <typename T>
 struct Depth;
 template <>
-struct Depth<bf16> { static constexpr int v = 8; };
+struct Depth<bf16> {
+  static constexpr int v = 2;     // dense tiles (4 A + 4 B fragments per step)
+  static constexpr int moe1 = 4;  // routed experts, one 16-row M-tile
+  static constexpr int moe2 = 2;  // routed experts, two 16-row M-tiles
+};
 template <>
-struct Depth<float> { static constexpr int v = 2; };
+struct Depth<float> {
+  static constexpr int v = 1;
+  static constexpr int moe1 = 1;
+  static constexpr int moe2 = 1;
+};
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 // ---------------------------------------------------------------- dense GEMM
-// Workgroup = 4 waves = (16*MT) rows x (64*NT) columns; wave w owns columns
-// [n0 + 16*NT*w, +16*NT).  SwiGLU: the output column c pairs B row c (gate) with
-// B row F + c (up), NT = 1 column tile per wave and two B streams.
+// Workgroup tile = (16*MT) rows x (16*NT) columns; the 4 waves split the K range
+// four ways (each wave reads a distinct quarter of both operands, so nothing is
+// loaded twice inside a workgroup) and their partial tiles are summed through
+// LDS in fixed wave order.  Tiles are ordered so that the row tiles sharing a
+// weight tile run on one XCD and share its L2.  SwiGLU: output column c pairs
+// B row c (gate) with B row N + c (up); the first NT/2 column tiles are gate
+// rows and the last NT/2 the matching up rows, so the tile covers 8*NT outputs.
 template <typename T, int MT, int NT, GemmEpi EPI>
 __global__ __launch_bounds__(256) void k_gemm_dense(GemmArgs a) {
   constexpr bool SW = EPI == GemmEpi::SwiGLU;
-  constexpr int NB = SW ? 2 : NT;  // B streams per wave
+  constexpr int OUTC = SW ? 8 * NT : 16 * NT;  // output columns per tile
+  __shared__ f32x4 red[4][MT * NT][64];
   const int lane = lane_id(), w = wave_id();
   const int row16 = lane & 15, kq = (lane >> 4) * 8;
   const int n_mtiles = (a.M + 16 * MT - 1) / (16 * MT);
-  const int n_ntiles = (a.N + 64 * NT - 1) / (64 * NT);
+  const int n_ntiles = (a.N + OUTC - 1) / OUTC;
   const int t = xcd_remap(blockIdx.x, n_mtiles * n_ntiles);
   const int mtile = t % n_mtiles, ntile = t / n_mtiles;
   const int m0 = mtile * 16 * MT;
-  const int nw0 = ntile * 64 * NT + w * 16 * NT;  // first output column of this wave
-  if (nw0 >= a.N) return;
-  const int mt_active = min(MT, (a.M - m0 + 15) / 16);
+  const int c0 = ntile * OUTC;  // first output column of the tile
+  const int ks = a.K / 32, q = (ks + 3) / 4;
+  const int sb = min(w * q, ks), se = min(sb + q, ks);
 
   const T* A = (const T*)a.A;
   const T* B = (const T*)a.B;
   const T* ap[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    int r = min(m0 + 16 * mt + row16, a.M - 1);
-    ap[mt] = A + (int64_t)r * a.lda + kq;
+    const int r = min(m0 + 16 * mt + row16, a.M - 1);
+    ap[mt] = A + (int64_t)r * a.lda + 32 * sb + kq;
   }
-  const T* bp[NB];
+  const T* bp[NT];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    int c = SW ? nw0 + row16 + (nb ? a.N : 0) : nw0 + 16 * nb + row16;
-    int cmax = SW ? 2 * a.N - 1 : a.N - 1;
-    bp[nb] = B + (int64_t)min(c, cmax) * a.ldb + kq;
+  for (int nt = 0; nt < NT; ++nt) {
+    int brow;
+    if constexpr (SW) {
+      const int c = min(c0 + 16 * (nt % (NT / 2)) + row16, a.N - 1);
+      brow = nt < NT / 2 ? c : a.N + c;
+    } else {
+      brow = min(c0 + 16 * nt + row16, a.N - 1);
+    }
+    bp[nt] = B + (int64_t)brow * a.ldb + 32 * sb + kq;
   }
-  f32x4 acc[MT][NB];
+  f32x4 acc[MT][NT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[mt][nb] = zero4();
-  wave_gemm<T, MT, NB, Depth<T>::v>(acc, ap, bp, a.K / 32, mt_active);
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = zero4();
+  if (se > sb) wave_gemm<T, MT, NT, Depth<T>::v>(acc, ap, bp, se - sb);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) red[w][mt * NT + nt][lane] = acc[mt][nt];
+  __syncthreads();
 
-  // epilogue: lane holds column (lane & 15) and rows 4*(lane>>4) + r of each tile
+  // epilogue: wave w finishes output tiles w, w+4, ...; lane holds column (lane & 15),
+  // rows 4*(lane>>4) + r of each 16x16 tile
   const int rq = (lane >> 4) * 4;
+  constexpr int OT = SW ? MT * NT / 2 : MT * NT;  // output tiles
+  for (int o = w; o < OT; o += 4) {
+    const int mt = o / (SW ? NT / 2 : NT), nt = o % (SW ? NT / 2 : NT);
+    f32x4 v = red[0][mt * NT + nt][lane] + red[1][mt * NT + nt][lane] + red[2][mt * NT + nt][lane] +
+              red[3][mt * NT + nt][lane];
+    f32x4 u = zero4();
+    if constexpr (SW) {
+      const int ut = mt * NT + nt + NT / 2;
+      u = red[0][ut][lane] + red[1][ut][lane] + red[2][ut][lane] + red[3][ut][lane];
+    }
+    const int n = c0 + 16 * nt + row16;
+    if (n >= a.N) continue;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    if (mt >= mt_active) continue;
-#pragma unroll
-    for (int nt = 0; nt < (SW ? 1 : NT); ++nt) {
-      const int n = nw0 + 16 * nt + row16;
-      if (n >= a.N) continue;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + 16 * mt + rq + r;
-        if (m >= a.M) continue;
-        float v = acc[mt][nt][r];
-        if constexpr (EPI == GemmEpi::Store) {
-          ((T*)a.C)[(int64_t)m * a.ldc + n] = from_f32<T>(v);
-        } else if constexpr (EPI == GemmEpi::StoreF32) {
-          ((float*)a.C)[(int64_t)m * a.ldc + n] = v;
-        } else if constexpr (EPI == GemmEpi::Resid) {
-          T* c = (T*)a.C + (int64_t)m * a.ldc + n;
-          *c = from_f32<T>(to_f32(*c) + v);
-        } else if constexpr (EPI == GemmEpi::SwiGLU) {
-          ((T*)a.C)[(int64_t)m * a.ldc + n] = from_f32<T>(silu(v) * acc[mt][1][r]);
-        } else {  // QKV scatter
-          const int dh = a.head_dim;
-          const int hq = a.n_heads, hkv = a.n_kv_heads;
-          if (n < hq * dh) {
-            int h = n / dh, c = n % dh;
-            ((T*)a.q)[((int64_t)h * a.q_rows + m) * dh + c] = from_f32<T>(v);
-          } else if (n < (hq + hkv) * dh) {
-            int h = (n - hq * dh) / dh, c = (n - hq * dh) % dh;
-            ((T*)a.kc)[((int64_t)h * a.cap + a.pos0 + m) * dh + c] = from_f32<T>(v);
-          } else {
-            int h = (n - (hq + hkv) * dh) / dh, c = (n - (hq + hkv) * dh) % dh;
-            ((T*)a.vc)[((int64_t)h * dh + c) * a.cap + a.pos0 + m] = from_f32<T>(v);
-          }
+    for (int r = 0; r < 4; ++r) {
+      const int m = m0 + 16 * mt + rq + r;
+      if (m >= a.M) continue;
+      const float x = v[r];
+      if constexpr (EPI == GemmEpi::Store) {
+        ((T*)a.C)[(int64_t)m * a.ldc + n] = from_f32<T>(x);
+      } else if constexpr (EPI == GemmEpi::StoreF32) {
+        ((float*)a.C)[(int64_t)m * a.ldc + n] = x;
+      } else if constexpr (EPI == GemmEpi::Resid) {
+        T* c = (T*)a.C + (int64_t)m * a.ldc + n;
+        *c = from_f32<T>(to_f32(*c) + x);
+      } else if constexpr (EPI == GemmEpi::SwiGLU) {
+        ((T*)a.C)[(int64_t)m * a.ldc + n] = from_f32<T>(silu(x) * u[r]);
+      } else {  // QKV scatter: queries [h][m][dh], keys [h][pos][dh], values [h][dh][pos]
+        const int dh = a.head_dim;
+        const int hq = a.n_heads, hkv = a.n_kv_heads;
+        if (n < hq * dh) {
+          const int h = n / dh, c = n % dh;
+          ((T*)a.q)[((int64_t)h * a.q_rows + m) * dh + c] = from_f32<T>(x);
+        } else if (n < (hq + hkv) * dh) {
+          const int h = (n - hq * dh) / dh, c = (n - hq * dh) % dh;
+          ((T*)a.kc)[((int64_t)h * a.cap + a.pos0 + m) * dh + c] = from_f32<T>(x);
+        } else {
+          const int h = (n - (hq + hkv) * dh) / dh, c = (n - (hq + hkv) * dh) % dh;
+          ((T*)a.vc)[((int64_t)h * dh + c) * a.cap + a.pos0 + m] = from_f32<T>(x);
         }
       }
     }
   }
 }
 
+template <typename T, int MT, int NT, GemmEpi EPI>
+static void launch_dense_t(const GemmArgs& a, hipStream_t s) {
+  constexpr int OUTC = EPI == GemmEpi::SwiGLU ? 8 * NT : 16 * NT;
+  const int tiles = ((a.M + 16 * MT - 1) / (16 * MT)) * ((a.N + OUTC - 1) / OUTC);
+  hipLaunchKernelGGL((k_gemm_dense<T, MT, NT, EPI>), dim3(tiles), dim3(256), 0, s, a);
+}
+
+// 64x64 tiles when the output is wide; 16x32 tiles for narrow outputs (the router)
+template <typename T, GemmEpi EPI>
+static void launch_dense_pick(const GemmArgs& a, hipStream_t s) {
+  if (a.N >= 512)
+    launch_dense_t<T, 4, 4, EPI>(a, s);
+  else
+    launch_dense_t<T, 1, 2, EPI>(a, s);
+}
+
 template <typename T>
 hipError_t launch_gemm(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
-  constexpr int MT = 4;
-  auto grid_for = [&](int nt) {
-    int mt = (a.M + 16 * MT - 1) / (16 * MT);
-    int ntl = (a.N + 64 * nt - 1) / (64 * nt);
-    return dim3(mt * ntl);
-  };
   switch (epi) {
-    case GemmEpi::Store:
-      hipLaunchKernelGGL((k_gemm_dense<T, MT, 1, GemmEpi::Store>), grid_for(1), dim3(256), 0, s, a);
-      break;
-    case GemmEpi::StoreF32:
-      hipLaunchKernelGGL((k_gemm_dense<T, MT, 1, GemmEpi::StoreF32>), grid_for(1), dim3(256), 0, s, a);
-      break;
-    case GemmEpi::Resid:
-      hipLaunchKernelGGL((k_gemm_dense<T, MT, 1, GemmEpi::Resid>), grid_for(1), dim3(256), 0, s, a);
-      break;
-    case GemmEpi::QKV:
-      hipLaunchKernelGGL((k_gemm_dense<T, MT, 1, GemmEpi::QKV>), grid_for(1), dim3(256), 0, s, a);
-      break;
-    case GemmEpi::SwiGLU:
-      hipLaunchKernelGGL((k_gemm_dense<T, MT, 1, GemmEpi::SwiGLU>), grid_for(1), dim3(256), 0, s, a);
-      break;
+    case GemmEpi::Store: launch_dense_pick<T, GemmEpi::Store>(a, s); break;
+    case GemmEpi::StoreF32: launch_dense_pick<T, GemmEpi::StoreF32>(a, s); break;
+    case GemmEpi::Resid: launch_dense_pick<T, GemmEpi::Resid>(a, s); break;
+    case GemmEpi::QKV: launch_dense_pick<T, GemmEpi::QKV>(a, s); break;
+    case GemmEpi::SwiGLU: launch_dense_pick<T, GemmEpi::SwiGLU>(a, s); break;
   }
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- routed experts
 // grid = (column tiles, max tiles).  Tile (e, p0, rows): pairs p0 .. p0+rows-1 all
-// routed to expert e.  gate_up: wave owns H columns [c0, c0+16) and reads gate
-// rows c0.. and up rows F+c0.. of expert e; A rows are the routed tokens' rows.
-template <typename T>
-__global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
-  constexpr int MT = kMoeTileRows / 16;
-  const int tile_i = blockIdx.y;
-  if (tile_i >= *a.n_tiles) return;
-  const int4 tile = a.tiles[tile_i];
-  const int e = tile.x, p0 = tile.y, rows = tile.z;
+// routed to expert e (rows <= 32, so one or two 16-row M-tiles).
+//
+// gate_up: a workgroup owns 64 H columns of expert e, i.e. 4 gate and the 4
+// matching up 16-row weight tiles; its 4 waves split K = d_model four ways, so
+// every weight byte and every token-row byte is loaded exactly once per
+// workgroup.  Partial tiles are summed through LDS (one 16-row M-tile per round)
+// and the SwiGLU product is formed on the sum.
+template <typename T, int MT>
+__device__ __forceinline__ void moe_gate_up_body(const MoeArgs& a, f32x4 (*red)[8][64], int e, int p0, int rows,
+                                                 int c0) {
+  constexpr int NT = 8;
   const int lane = lane_id(), w = wave_id();
   const int row16 = lane & 15, kq = (lane >> 4) * 8;
-  const int c0 = blockIdx.x * 64 + w * 16;
-  if (c0 >= a.F) return;
-  const int mt_active = (rows + 15) / 16;
+  const int ks = a.d / 32, q = (ks + 3) / 4;
+  const int sb = min(w * q, ks), se = min(sb + q, ks);
   const T* X = (const T*)a.X;
   const T* W = (const T*)a.W + (int64_t)e * 2 * a.F * a.d;
   const T* ap[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    int r = min(16 * mt + row16, rows - 1);
-    int tok = a.perm[p0 + r];
-    ap[mt] = X + (int64_t)tok * a.d + kq;
+    const int r = min(16 * mt + row16, rows - 1);
+    ap[mt] = X + (int64_t)a.perm[p0 + r] * a.d + 32 * sb + kq;
   }
-  const T* bp[2] = {W + (int64_t)(c0 + row16) * a.d + kq, W + (int64_t)(a.F + c0 + row16) * a.d + kq};
-  f32x4 acc[MT][2];
+  const T* bp[NT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) { acc[mt][0] = zero4(); acc[mt][1] = zero4(); }
-  wave_gemm<T, MT, 2, Depth<T>::v>(acc, ap, bp, a.d / 32, mt_active);
+  for (int j = 0; j < 4; ++j) {
+    const int c = min(c0 + 16 * j + row16, a.F - 1);
+    bp[j] = W + (int64_t)c * a.d + 32 * sb + kq;
+    bp[4 + j] = W + (int64_t)(a.F + c) * a.d + 32 * sb + kq;
+  }
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = zero4();
+  if (se > sb) wave_gemm<T, MT, NT, (MT == 1 ? Depth<T>::moe1 : Depth<T>::moe2)>(acc, ap, bp, se - sb);
   T* H = (T*)a.out;
   const int rq = (lane >> 4) * 4;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    if (mt >= mt_active) continue;
+    if (mt) __syncthreads();
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      int rr = 16 * mt + rq + r;
-      if (rr < rows) H[(int64_t)(p0 + rr) * a.F + c0 + row16] = from_f32<T>(silu(acc[mt][0][r]) * acc[mt][1][r]);
+    for (int nt = 0; nt < NT; ++nt) red[w][nt][lane] = acc[mt][nt];
+    __syncthreads();
+    const int c = c0 + 16 * w + row16;  // wave w finishes gate tile w with up tile 4 + w
+    const f32x4 g = red[0][w][lane] + red[1][w][lane] + red[2][w][lane] + red[3][w][lane];
+    const f32x4 u = red[0][4 + w][lane] + red[1][4 + w][lane] + red[2][4 + w][lane] + red[3][4 + w][lane];
+    if (c < a.F) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rr = 16 * mt + rq + r;
+        if (rr < rows) H[(int64_t)(p0 + rr) * a.F + c] = from_f32<T>(silu(g[r]) * u[r]);
+      }
     }
   }
 }
 
-// down: wave owns output columns [c0, c0+32) (two tiles) of expert e's [d][F] matrix.
 template <typename T>
-__global__ __launch_bounds__(256) void k_moe_down(MoeArgs a) {
-  constexpr int MT = kMoeTileRows / 16, NT = 2;
+__global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
+  __shared__ f32x4 red[4][8][64];
   const int tile_i = blockIdx.y;
   if (tile_i >= *a.n_tiles) return;
   const int4 tile = a.tiles[tile_i];
-  const int e = tile.x, p0 = tile.y, rows = tile.z;
-  const int lane = lane_id(), w = wave_id();
+  const int c0 = blockIdx.x * 64;
+  if (tile.z > 16)
+    moe_gate_up_body<T, 2>(a, red, tile.x, tile.y, tile.z, c0);
+  else
+    moe_gate_up_body<T, 1>(a, red, tile.x, tile.y, tile.z, c0);
+}
+
+// down: wave owns output columns [c0, c0+64) (four tiles) of expert e's [d][F]
+// matrix over the full K = F; a workgroup covers 256 columns.
+template <typename T, int MT>
+__device__ __forceinline__ void moe_down_body(const MoeArgs& a, int e, int p0, int rows, int c0) {
+  constexpr int NT = 4;
+  const int lane = lane_id();
   const int row16 = lane & 15, kq = (lane >> 4) * 8;
-  const int c0 = blockIdx.x * 128 + w * 32;
-  if (c0 >= a.d) return;
-  const int mt_active = (rows + 15) / 16;
   const T* H = (const T*)a.X;
   const T* W = (const T*)a.W + (int64_t)e * a.d * a.F;
   const T* ap[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    int r = min(16 * mt + row16, rows - 1);
+    const int r = min(16 * mt + row16, rows - 1);
     ap[mt] = H + (int64_t)(p0 + r) * a.F + kq;
   }
   const T* bp[NT];
@@ -255,23 +265,35 @@ __global__ __launch_bounds__(256) void k_moe_down(MoeArgs a) {
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = zero4();
-  wave_gemm<T, MT, NT, Depth<T>::v>(acc, ap, bp, a.F / 32, mt_active);
+  wave_gemm<T, MT, NT, Depth<T>::moe1>(acc, ap, bp, a.F / 32);
   T* Y = (T*)a.out;
   const int rq = (lane >> 4) * 4;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    if (mt >= mt_active) continue;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      int c = c0 + 16 * nt + row16;
+      const int c = c0 + 16 * nt + row16;
       if (c >= a.d) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        int rr = 16 * mt + rq + r;
+        const int rr = 16 * mt + rq + r;
         if (rr < rows) Y[(int64_t)(p0 + rr) * a.d + c] = from_f32<T>(acc[mt][nt][r]);
       }
     }
   }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_moe_down(MoeArgs a) {
+  const int tile_i = blockIdx.y;
+  if (tile_i >= *a.n_tiles) return;
+  const int4 tile = a.tiles[tile_i];
+  const int c0 = blockIdx.x * 256 + wave_id() * 64;
+  if (c0 >= a.d) return;
+  if (tile.z > 16)
+    moe_down_body<T, 2>(a, tile.x, tile.y, tile.z, c0);
+  else
+    moe_down_body<T, 1>(a, tile.x, tile.y, tile.z, c0);
 }
 
 template <typename T>
@@ -282,7 +304,7 @@ hipError_t launch_moe_gate_up(const MoeArgs& a, hipStream_t s) {
 }
 template <typename T>
 hipError_t launch_moe_down(const MoeArgs& a, hipStream_t s) {
-  dim3 grid((a.d + 127) / 128, a.max_tiles);
+  dim3 grid((a.d + 255) / 256, a.max_tiles);
   hipLaunchKernelGGL(k_moe_down<T>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -21,6 +21,7 @@
 // a merge kernel combines the groups in fixed order (deterministic).
 #include "dg_device.h"
 #include "dg_kernels.h"
+#include "dg_wave_gemm.h"
 
 namespace dg {
 
@@ -47,36 +48,6 @@ __device__ __forceinline__ void stat_merge(Stat& x, const Stat& y) {
   x.m = m;
   x.z = z;
   x.s1 = s1;
-}
-
-template <typename T, int DEPTH>
-__device__ __forceinline__ void wave_gemm_head(f32x4 (&acc)[4][4], const T* const (&ap)[4], const T* const (&bp)[4],
-                                               int ksteps) {
-  Frag<T> fa[DEPTH][4];
-  Frag<T> fb[DEPTH][4];
-#pragma unroll
-  for (int d = 0; d < DEPTH; ++d)
-    if (d < ksteps) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { fa[d][i].load(ap[i] + 32 * d); fb[d][i].load(bp[i] + 32 * d); }
-    }
-  for (int s0 = 0; s0 < ksteps; s0 += DEPTH) {
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      const int s = s0 + d;
-      if (s < ksteps) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) mma(acc[mt][nt], fa[d][mt], fb[d][nt]);
-        const int sn = s + DEPTH;
-        if (sn < ksteps) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) { fa[d][i].load(ap[i] + 32 * sn); fb[d][i].load(bp[i] + 32 * sn); }
-        }
-      }
-    }
-  }
 }
 
 template <typename T>
@@ -113,7 +84,7 @@ __global__ __launch_bounds__(256) void k_vocab_head(HeadArgs a) {
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = zero4();
-    wave_gemm_head<T, HeadDepth<T>::v>(acc, ap, bp, a.d / 32);
+    wave_gemm<T, 4, 4, HeadDepth<T>::v>(acc, ap, bp, a.d / 32);
     // lane holds, for slot (slot0 + 16*nt + row16), tokens v0 + 16*mt + 4*quad + r
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
