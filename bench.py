@@ -141,7 +141,7 @@ def main() -> int:
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
     log(f"bench: {wl.name} on {torch.cuda.get_device_name(0)}; generating weights on the device")
-    w = gdev.model_weights_device(d)
+    w = gdev.packed_model_weights_device(d)
     weights = dg.Weights(w["embed"], w["final_norm"], w["layers"])
     cfg = dg.make_config(d)
     cap = ((wl.prefix + wl.blocks * d.canvas + 31) // 32) * 32

@@ -31,7 +31,7 @@ DG_STOP_NONE, DG_STOP_ENTROPY, DG_STOP_STABLE, DG_STOP_CAP, DG_STOP_FIXED = 0, 1
 DG_WARN_NUMERIC = 0x1
 EXPORTED = ("dg_workspace_size", "dg_prefill_kv", "dg_denoise_step", "dg_canvas_update", "dg_commit_block",
             "dg_generate_block", "dg_layer_forward", "dg_vocab_head", "dg_stop_check", "dg_status_string",
-            "dg_last_hip_error", "dg_timing_start", "dg_timing_stop")
+            "dg_last_hip_error", "dg_timing_start", "dg_timing_stop", "dg_packed_elems", "dg_pack_matrix")
 # kernel classes of dg_timing_* (dg_kernel in dg.h), in enum order
 KERNELS = ("embed", "rmsnorm", "gemm_qkv", "attention", "attn_merge", "gemm_o", "gemm_router", "router_topk",
            "moe_permute", "moe_gate_up", "moe_down", "shared_gate_up", "shared_down", "moe_combine", "vocab_head",
@@ -104,6 +104,8 @@ _SIGS = {
                          _sz, _vp],
     "dg_vocab_head": [_P(dg_config), _P(dg_weights), _vp, _i64, _f32, _vp, _vp, _vp, _vp, _sz, _vp],
     "dg_stop_check": [_P(dg_config), _P(dg_sampler), _i32, _vp, _vp, _vp, _vp, _vp],
+    "dg_packed_elems": [_i64, _i64, _P(_i64)],
+    "dg_pack_matrix": [_vp, _vp, _i64, _i64, _i64, _i32, _vp],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -291,3 +293,39 @@ def dg_timing_stop() -> Dict[str, tuple]:
     cnt = (ctypes.c_int64 * n)()
     _check("dg_timing_stop", _lib.dg_timing_stop(ms, cnt))
     return {KERNELS[i]: (float(ms[i]), int(cnt[i])) for i in range(n) if cnt[i]}
+
+
+def dg_packed_elems(rows: int, cols: int) -> int:
+    out = ctypes.c_int64(0)
+    _check("dg_packed_elems", _lib.dg_packed_elems(rows, cols, ctypes.byref(out)))
+    return int(out.value)
+
+
+def dg_pack_matrix(src, dst, batch: int, rows: int, cols: int, dtype: int, stream=None) -> None:
+    _check("dg_pack_matrix", _lib.dg_pack_matrix(_ptr(src), _ptr(dst), batch, rows, cols, dtype, _stream(stream)))
+
+
+MATRIX_FIELDS = ("wqkv", "wo", "w_router", "w_gate_up", "w_down", "ws_gate_up", "ws_down")
+
+
+def pack_tensor(t):
+    """A 2-D [rows, cols] or 3-D [batch, rows, cols] row-major device tensor -> its fragment-tiled copy (1-D)."""
+    import torch
+    rows, cols = int(t.shape[-2]), int(t.shape[-1])
+    batch = int(t.shape[0]) if t.dim() == 3 else 1
+    dt = DG_BF16 if t.dtype == torch.bfloat16 else DG_F32
+    out = torch.empty(batch * dg_packed_elems(rows, cols), dtype=t.dtype, device=t.device)
+    dg_pack_matrix(t.contiguous(), out, batch, rows, cols, dt)
+    return out
+
+
+def pack_layer(layer: Dict[str, object]) -> Dict[str, object]:
+    """One layer's weights with every matrix converted to the library's layout (norm gains unchanged)."""
+    return {k: (pack_tensor(v) if k in MATRIX_FIELDS else v) for k, v in layer.items()}
+
+
+def pack_weights(natural: dict) -> dict:
+    """{"embed", "final_norm", "layers": [...]} of row-major device tensors -> the library's layout."""
+    return {"embed": pack_tensor(natural["embed"]) if natural.get("embed") is not None else None,
+            "final_norm": natural["final_norm"],
+            "layers": [pack_layer(l) for l in natural["layers"]]}

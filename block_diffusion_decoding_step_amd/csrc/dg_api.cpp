@@ -531,6 +531,30 @@ int dg_stop_check(const dg_config* cfg, const dg_sampler* sampler, int32_t step,
   return DG_OK;
 }
 
+int dg_packed_elems(int64_t rows, int64_t cols, int64_t* h_elems) {
+  if (!h_elems) return DG_ERR_INVALID;
+  *h_elems = 0;
+  if (rows < 1 || cols < 32 || cols % 32) return DG_ERR_INVALID;
+  *h_elems = (rows + 15) / 16 * 16 * cols;
+  return DG_OK;
+}
+
+int dg_pack_matrix(const void* src, void* dst, int64_t batch, int64_t rows, int64_t cols, int32_t dtype,
+                   void* stream) {
+  int64_t per = 0;
+  DG_CHECK(dg_packed_elems(rows, cols, &per));
+  if (batch < 1 || !aligned16(src) || !aligned16(dst) || (dtype != DG_BF16 && dtype != DG_F32)) return DG_ERR_INVALID;
+  const size_t es = dtype == DG_BF16 ? 2 : 4;
+  const uintptr_t s0 = (uintptr_t)src, s1 = s0 + (size_t)(batch * rows * cols) * es;
+  const uintptr_t d0 = (uintptr_t)dst, d1 = d0 + (size_t)(batch * per) * es;
+  if (s0 < d1 && d0 < s1) return DG_ERR_INVALID;
+  if (dtype == DG_BF16)
+    DG_TRY(launch_pack<bf16>((const bf16*)src, (bf16*)dst, batch, rows, cols, (hipStream_t)stream));
+  else
+    DG_TRY(launch_pack<float>((const float*)src, (float*)dst, batch, rows, cols, (hipStream_t)stream));
+  return DG_OK;
+}
+
 int dg_timing_start(uint64_t kernel_mask) {
   g_timer.mask = kernel_mask;
   return DG_OK;

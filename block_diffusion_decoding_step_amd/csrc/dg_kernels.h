@@ -39,6 +39,8 @@ struct StopParams {
 template <typename T>
 hipError_t launch_embed(const int32_t* tok, const T* E, T* X, int M, int d, int V, hipStream_t s);
 template <typename T>
+hipError_t launch_pack(const T* src, T* dst, int64_t batch, int64_t rows, int64_t cols, hipStream_t s);
+template <typename T>
 hipError_t launch_rmsnorm(const T* X, const T* g, T* Y, int M, int d, float eps, hipStream_t s);
 hipError_t launch_router_topk(const float* logits, int M, int E, int k, int32_t* idx, float* w, hipStream_t s);
 hipError_t launch_moe_permute(const int32_t* idx, int M, int E, int k, int32_t* counts, int32_t* offsets,

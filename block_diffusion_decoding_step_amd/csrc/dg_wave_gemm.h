@@ -5,9 +5,20 @@
 
 namespace dg {
 
+// Fragment-tiled matrices: 16-row x 32-column blocks of kFragElems elements.
+constexpr int kFragElems = 512;
+
+// Pointer to this lane's part of fragment (row tile rt, K step s) of a tiled matrix with ks K steps.
+template <typename T>
+__device__ __forceinline__ const T* tiled_frag(const T* base, int64_t rt, int ks, int s) {
+  return base + ((rt * ks + s) * kFragElems + (int64_t)lane_id() * 8);
+}
+
 // ---------------------------------------------------------------- wave GEMM core
 // acc[mt][nt] += sum_k A[row(mt)][k] * B[col(nt)][k] over ksteps 32-wide steps.
-// ap[mt] / bp[nt] point at this lane's row start plus its 8*(lane>>4) K offset.
+// ap[mt] / bp[nt] point at this lane's first fragment; consecutive K steps are sa
+// (A) and sb (B) elements apart: 32 for a row-major operand, 512 for a
+// fragment-tiled one (one contiguous 16x32 fragment per step).
 // Software pipeline with a ring of DEPTH register buffers and no branches in the
 // steady state: step s + DEPTH is loaded into the buffer step s just used, at an
 // index clamped to the last step (the few clamped reloads at the end are never
@@ -20,7 +31,7 @@ __device__ __forceinline__ void frag_load(Frag<T>& f, const T* p) {
 // SA / SB: operand read once per launch (weights), loaded non-temporally.
 template <typename T, int MT, int NT, int DEPTH, bool SA = false, bool SB = false>
 __device__ __forceinline__ void wave_gemm(f32x4 (&acc)[MT][NT], const T* const (&ap)[MT], const T* const (&bp)[NT],
-                                          int ksteps) {
+                                          int ksteps, int sa = 32, int sb = 32) {
   Frag<T> fa[DEPTH][MT];
   Frag<T> fb[DEPTH][NT];
   const int last = ksteps - 1;
@@ -28,9 +39,9 @@ __device__ __forceinline__ void wave_gemm(f32x4 (&acc)[MT][NT], const T* const (
   for (int d = 0; d < DEPTH; ++d) {
     const int s = min(d, last);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) frag_load<SA>(fa[d][mt], ap[mt] + 32 * s);
+    for (int mt = 0; mt < MT; ++mt) frag_load<SA>(fa[d][mt], ap[mt] + (int64_t)sa * s);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) frag_load<SB>(fb[d][nt], bp[nt] + 32 * s);
+    for (int nt = 0; nt < NT; ++nt) frag_load<SB>(fb[d][nt], bp[nt] + (int64_t)sb * s);
   }
   int s0 = 0;
   for (; s0 + DEPTH <= ksteps; s0 += DEPTH) {
@@ -42,9 +53,9 @@ __device__ __forceinline__ void wave_gemm(f32x4 (&acc)[MT][NT], const T* const (
         for (int nt = 0; nt < NT; ++nt) mma(acc[mt][nt], fa[d][mt], fb[d][nt]);
       const int sn = min(s0 + DEPTH + d, last);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) frag_load<SA>(fa[d][mt], ap[mt] + 32 * sn);
+      for (int mt = 0; mt < MT; ++mt) frag_load<SA>(fa[d][mt], ap[mt] + (int64_t)sa * sn);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) frag_load<SB>(fb[d][nt], bp[nt] + 32 * sn);
+      for (int nt = 0; nt < NT; ++nt) frag_load<SB>(fb[d][nt], bp[nt] + (int64_t)sb * sn);
     }
   }
   const int rem = ksteps - s0;  // steps s0 .. ksteps-1 sit in buffers 0 .. rem-1

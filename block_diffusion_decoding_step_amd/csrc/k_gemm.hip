@@ -48,7 +48,7 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z));
 // B row c (gate) with B row N + c (up); the first NT/2 column tiles are gate
 // rows and the last NT/2 the matching up rows, so the tile covers 8*NT outputs.
 template <typename T, int MT, int NT, GemmEpi EPI>
-__global__ __launch_bounds__(256) void k_gemm_dense(GemmArgs a) {
+__global__ __launch_bounds__(256, 2) void k_gemm_dense(GemmArgs a) {
   constexpr bool SW = EPI == GemmEpi::SwiGLU;
   constexpr int OUTC = SW ? 8 * NT : 16 * NT;  // output columns per tile
   __shared__ f32x4 red[4][MT * NT][64];
@@ -71,24 +71,26 @@ __global__ __launch_bounds__(256) void k_gemm_dense(GemmArgs a) {
     const int r = min(m0 + 16 * mt + row16, a.M - 1);
     ap[mt] = A + (int64_t)r * a.lda + 32 * sb + kq;
   }
+  // weights are fragment-tiled: one row tile per 16 output columns
+  const int last_rt = (a.N + 15) / 16 - 1;
   const T* bp[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    int brow;
+    int rt;
     if constexpr (SW) {
-      const int c = min(c0 + 16 * (nt % (NT / 2)) + row16, a.N - 1);
-      brow = nt < NT / 2 ? c : a.N + c;
+      const int ct = min(c0 / 16 + nt % (NT / 2), last_rt);
+      rt = nt < NT / 2 ? ct : a.N / 16 + ct;
     } else {
-      brow = min(c0 + 16 * nt + row16, a.N - 1);
+      rt = min(c0 / 16 + nt, last_rt);
     }
-    bp[nt] = B + (int64_t)brow * a.ldb + 32 * sb + kq;
+    bp[nt] = tiled_frag(B, rt, ks, sb);
   }
   f32x4 acc[MT][NT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = zero4();
-  if (se > sb) wave_gemm<T, MT, NT, Depth<T>::v>(acc, ap, bp, se - sb);
+  if (se > sb) wave_gemm<T, MT, NT, Depth<T>::v>(acc, ap, bp, se - sb, 32, kFragElems);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -198,16 +200,16 @@ __device__ __forceinline__ void moe_gate_up_body(const MoeArgs& a, f32x4 (*red)[
   const T* bp[NT];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int c = min(c0 + 16 * j + row16, a.F - 1);
-    bp[j] = W + (int64_t)c * a.d + 32 * sb + kq;
-    bp[4 + j] = W + (int64_t)(a.F + c) * a.d + 32 * sb + kq;
+    const int ct = min(c0 / 16 + j, a.F / 16 - 1);
+    bp[j] = tiled_frag(W, ct, ks, sb);
+    bp[4 + j] = tiled_frag(W, a.F / 16 + ct, ks, sb);
   }
   f32x4 acc[MT][NT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = zero4();
-  if (se > sb) wave_gemm<T, MT, NT, (MT == 1 ? Depth<T>::moe1 : Depth<T>::moe2)>(acc, ap, bp, se - sb);
+  if (se > sb) wave_gemm<T, MT, NT, (MT == 1 ? Depth<T>::moe1 : Depth<T>::moe2)>(acc, ap, bp, se - sb, 32, kFragElems);
   T* H = (T*)a.out;
   const int rq = (lane >> 4) * 4;
 #pragma unroll
@@ -230,7 +232,7 @@ __device__ __forceinline__ void moe_gate_up_body(const MoeArgs& a, f32x4 (*red)[
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void k_moe_gate_up(MoeArgs a) {
+__global__ __launch_bounds__(256, 2) void k_moe_gate_up(MoeArgs a) {
   __shared__ f32x4 red[4][8][64];
   const int tile_i = blockIdx.y;
   if (tile_i >= *a.n_tiles) return;
@@ -257,15 +259,16 @@ __device__ __forceinline__ void moe_down_body(const MoeArgs& a, int e, int p0, i
     const int r = min(16 * mt + row16, rows - 1);
     ap[mt] = H + (int64_t)(p0 + r) * a.F + kq;
   }
+  const int ks = a.F / 32;
   const T* bp[NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) bp[nt] = W + (int64_t)min(c0 + 16 * nt + row16, a.d - 1) * a.F + kq;
+  for (int nt = 0; nt < NT; ++nt) bp[nt] = tiled_frag(W, min(c0 / 16 + nt, a.d / 16 - 1), ks, 0);
   f32x4 acc[MT][NT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = zero4();
-  wave_gemm<T, MT, NT, Depth<T>::moe1>(acc, ap, bp, a.F / 32);
+  wave_gemm<T, MT, NT, Depth<T>::moe1>(acc, ap, bp, ks, 32, kFragElems);
   T* Y = (T*)a.out;
   const int rq = (lane >> 4) * 4;
 #pragma unroll

@@ -76,15 +76,15 @@ __global__ __launch_bounds__(256) void k_vocab_head(HeadArgs a) {
   const int n_vt = (a.V + 63) / 64;
   for (int vt = blockIdx.x; vt < n_vt; vt += a.n_groups) {
     const int v0 = vt * 64;
-    const T* ap[4];
+    const T* ap[4];  // E is fragment-tiled: one row tile per 16 tokens
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) ap[mt] = E + (int64_t)min(v0 + 16 * mt + row16, a.V - 1) * a.d + quad * 8;
+    for (int mt = 0; mt < 4; ++mt) ap[mt] = tiled_frag(E, min(v0 / 16 + mt, (a.V + 15) / 16 - 1), a.d / 32, 0);
     f32x4 acc[4][4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = zero4();
-    wave_gemm<T, 4, 4, HeadDepth<T>::v>(acc, ap, bp, a.d / 32);
+    wave_gemm<T, 4, 4, HeadDepth<T>::v>(acc, ap, bp, a.d / 32, kFragElems, 32);
     // lane holds, for slot (slot0 + 16*nt + row16), tokens v0 + 16*mt + 4*quad + r
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {

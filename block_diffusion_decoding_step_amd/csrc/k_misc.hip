@@ -10,18 +10,45 @@
 namespace dg {
 
 // ============================================================== embedding
-// X[m, :] = E[tok[m], :]; tokens outside [0, V) are clamped into range.
+// X[m, :] = E[tok[m], :] with E fragment-tiled; tokens outside [0, V) are clamped
+// into range.  Thread i copies the 8 elements (K step i/4, quarter i%4) of its row.
 template <typename T>
 __global__ __launch_bounds__(256) void k_embed(const int32_t* __restrict__ tok, const T* __restrict__ E,
                                                T* __restrict__ X, int M, int d, int V) {
-  int m = blockIdx.x;
+  const int m = blockIdx.x;
   if (m >= M) return;
   int t = tok[m];
   t = t < 0 ? 0 : (t >= V ? V - 1 : t);
-  const u32x4* src = reinterpret_cast<const u32x4*>(E + (int64_t)t * d);
-  u32x4* dst = reinterpret_cast<u32x4*>(X + (int64_t)m * d);
-  int n16 = d * (int)sizeof(T) / 16;
-  for (int i = threadIdx.x; i < n16; i += blockDim.x) dst[i] = src[i];
+  const int ks = d / 32;
+  const T* tile = E + (int64_t)(t >> 4) * ks * 512;
+  for (int i = threadIdx.x; i < d / 8; i += blockDim.x) {
+    const int s = i >> 2, q = i & 3;
+    float v[8];
+    Vec8<T>::load(tile + ((int64_t)s * 512 + ((t & 15) + 16 * q) * 8), v);
+    Vec8<T>::store(X + (int64_t)m * d + 8 * i, v);
+  }
+}
+
+// ============================================================== weight packing
+// Row-major [rows, cols] -> fragment-tiled (see dg.h); thread i writes 8 elements:
+// fragment i/64 (row tile, K step) and lane i%64 of it.
+template <typename T>
+__global__ __launch_bounds__(256) void k_pack(const T* __restrict__ src, T* __restrict__ dst, int64_t batch,
+                                              int64_t rows, int64_t cols, int64_t rows_p) {
+  const int64_t ks = cols / 32;
+  const int64_t per = rows_p / 16 * ks * 64;  // 8-element chunks per matrix
+  const int64_t total = batch * per;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int64_t b = i / per, rem = i % per;
+    const int lane = (int)(rem & 63);
+    const int64_t frag = rem >> 6;
+    const int64_t s = frag % ks, rt = frag / ks;
+    const int64_t r = rt * 16 + (lane & 15), c = s * 32 + (lane >> 4) * 8;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (r < rows) Vec8<T>::load(src + (b * rows + r) * cols + c, v);
+    Vec8<T>::store(dst + b * rows_p * cols + rem * 8, v);
+  }
 }
 
 // ============================================================== RMSNorm
@@ -146,31 +173,39 @@ __global__ __launch_bounds__(1024) void k_moe_permute(const int32_t* __restrict_
     }
   }
   __syncthreads();
-  // per-expert totals and chunk prefixes
-  for (int e = tid; e < E; e += blockDim.x) {
-    int run = 0;
+  // per-expert totals and chunk prefixes (thread e walks its expert's chunks)
+  int n_e = 0;
+  if (tid < E) {
     for (int c = 0; c < chunks; ++c) {
-      int n = pre[e * chunks + c];
-      pre[e * chunks + c] = run;
-      run += n;
+      const int n = pre[tid * chunks + c];
+      pre[tid * chunks + c] = n_e;
+      n_e += n;
     }
-    counts[e] = run;
-    off_s[e] = run;
+    counts[tid] = n_e;
   }
+  // exclusive scans over experts of (pairs, tiles): wave prefix sums, then wave totals (E <= 256)
+  const int t_e = (n_e + kMoeTileRows - 1) / kMoeTileRows;
+  int inc_n = n_e, inc_t = t_e;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int yn = __shfl_up(inc_n, o, 64), yt = __shfl_up(inc_t, o, 64);
+    if (l >= o) { inc_n += yn; inc_t += yt; }
+  }
+  __shared__ int wsum_n[4], wsum_t[4];
+  if (tid < 256 && l == 63) { wsum_n[tid >> 6] = inc_n; wsum_t[tid >> 6] = inc_t; }
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    int nt = 0;
-    for (int e = 0; e < E; ++e) {
-      int n = off_s[e];
-      off_s[e] = run;
-      offsets[e] = run;
-      for (int r0 = 0; r0 < n; r0 += kMoeTileRows) tiles[nt++] = make_int4(e, run + r0, min(kMoeTileRows, n - r0), 0);
-      run += n;
+  if (tid < E) {
+    int base_n = 0, base_t = 0;
+    for (int wv = 0; wv < (tid >> 6); ++wv) { base_n += wsum_n[wv]; base_t += wsum_t[wv]; }
+    const int off = base_n + inc_n - n_e, toff = base_t + inc_t - t_e;
+    off_s[tid] = off;
+    offsets[tid] = off;
+    for (int i = 0; i < t_e; ++i)
+      tiles[toff + i] = make_int4(tid, off + i * kMoeTileRows, min(kMoeTileRows, n_e - i * kMoeTileRows), 0);
+    if (tid == E - 1) {
+      offsets[E] = off + n_e;
+      *n_tiles = toff + t_e;
     }
-    off_s[E] = run;
-    offsets[E] = run;
-    *n_tiles = nt;
   }
   __syncthreads();
   for (int p = tid; p < M * k; p += blockDim.x) {
@@ -323,6 +358,16 @@ hipError_t launch_embed(const int32_t* tok, const T* E, T* X, int M, int d, int 
   return hipGetLastError();
 }
 template <typename T>
+hipError_t launch_pack(const T* src, T* dst, int64_t batch, int64_t rows, int64_t cols, hipStream_t s) {
+  const int64_t rows_p = (rows + 15) / 16 * 16;
+  const int64_t chunks = batch * rows_p / 16 * (cols / 32) * 64;
+  int64_t g = (chunks + 255) / 256;
+  if (g > 65536) g = 65536;
+  if (g < 1) g = 1;
+  hipLaunchKernelGGL(k_pack<T>, dim3((unsigned)g), dim3(256), 0, s, src, dst, batch, rows, cols, rows_p);
+  return hipGetLastError();
+}
+template <typename T>
 hipError_t launch_rmsnorm(const T* X, const T* g, T* Y, int M, int d, float eps, hipStream_t s) {
   hipLaunchKernelGGL(k_rmsnorm<T>, dim3((M + 3) / 4), dim3(256), 0, s, X, g, Y, M, d, eps);
   return hipGetLastError();
@@ -360,6 +405,8 @@ hipError_t launch_canvas_update(const int32_t* pred, const float* conf, int S, i
 }
 
 template hipError_t launch_embed<float>(const int32_t*, const float*, float*, int, int, int, hipStream_t);
+template hipError_t launch_pack<float>(const float*, float*, int64_t, int64_t, int64_t, hipStream_t);
+template hipError_t launch_pack<bf16>(const bf16*, bf16*, int64_t, int64_t, int64_t, hipStream_t);
 template hipError_t launch_embed<bf16>(const int32_t*, const bf16*, bf16*, int, int, int, hipStream_t);
 template hipError_t launch_rmsnorm<float>(const float*, const float*, float*, int, int, float, hipStream_t);
 template hipError_t launch_rmsnorm<bf16>(const bf16*, const bf16*, bf16*, int, int, float, hipStream_t);

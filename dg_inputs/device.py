@@ -67,3 +67,24 @@ def kv_tensors(d: Dims, capacity: int):
     k = torch.zeros((max(d.n_layers, 1), d.n_kv_heads, capacity, d.head_dim), dtype=dt, device="cuda")
     v = torch.zeros((max(d.n_layers, 1), d.n_kv_heads, d.head_dim, capacity), dtype=dt, device="cuda")
     return k, v
+
+
+def packed_model_weights_device(d: Dims, seed: int = recipe.WEIGHT_SEED) -> dict:
+    """Device weights in the library's fragment-tiled layout, generated and converted one tensor at a time
+    so that the peak memory is the packed model plus one natural tensor."""
+    import block_diffusion_decoding_step_amd as dg
+    emb = normal_tensor((d.vocab, d.d_model), seed, recipe.STREAM_EMBED, recipe.WEIGHT_SIGMA, d.dtype)
+    out = {"embed": dg.pack_tensor(emb), "final_norm": torch.ones(d.d_model, dtype=torch_dtype(d.dtype), device="cuda"),
+           "layers": []}
+    del emb
+    for l in range(d.n_layers):
+        layer = {}
+        for name, shape in layer_shapes(d).items():
+            if name in recipe.NORM_TENSORS:
+                layer[name] = torch.ones(shape, dtype=torch_dtype(d.dtype), device="cuda")
+            else:
+                t = normal_tensor(shape, seed, layer_stream(l, name), recipe.WEIGHT_SIGMA, d.dtype)
+                layer[name] = dg.pack_tensor(t)
+                del t
+        out["layers"].append(layer)
+    return out

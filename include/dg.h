@@ -23,22 +23,31 @@
  *   - Calls on distinct workspaces and streams may run concurrently; two calls
  *     sharing one workspace must be ordered on one stream.
  *
- * Tensor layouts (row-major, dtype = cfg->dtype unless stated):
- *   hidden states      [n, d_model]
+ * Tensor layouts (dtype = cfg->dtype unless stated):
+ *   hidden states      [n, d_model] row-major
+ *   norm gains         [d_model]
+ *   KV cache  k        [n_layers][n_kv_heads][capacity][head_dim] row-major
+ *             v        [n_layers][n_kv_heads][head_dim][capacity] (positions contiguous)
+ *   tokens / canvas    int32 [n]
+ * Weight matrices, logically [out, in] (y = x W^T):
  *   embed (tied head)  [vocab, d_model]
  *   wqkv               [(n_heads + 2*n_kv_heads)*head_dim, d_model]
  *                      rows: query heads, then key heads, then value heads
  *   wo                 [d_model, n_heads*head_dim]
  *   w_router           [n_experts, d_model]
- *   w_gate_up          [n_experts, 2*ffn_expert, d_model]  gate rows, then up rows
- *   w_down             [n_experts, d_model, ffn_expert]
- *   ws_gate_up         [2*ffn_shared, d_model]             gate rows, then up rows
+ *   w_gate_up          n_experts x [2*ffn_expert, d_model]  gate rows, then up rows
+ *   w_down             n_experts x [d_model, ffn_expert]
+ *   ws_gate_up         [2*ffn_shared, d_model]              gate rows, then up rows
  *   ws_down            [d_model, ffn_shared]
- *   norm gains         [d_model]
- *   KV cache  k        [n_layers][n_kv_heads][capacity][head_dim]
- *             v        [n_layers][n_kv_heads][head_dim][capacity]   (positions contiguous)
- *   tokens / canvas    int32 [n]
- * All matrices are [out, in]: y = x W^T.
+ * are stored in the FRAGMENT-TILED layout that dg_pack_matrix produces from a
+ * row-major matrix: with R rows padded up to a multiple of 16 and C columns (a
+ * multiple of 32), element (r, c) sits at
+ *     ((r/16)*(C/32) + c/32)*512 + ((r%16) + 16*((c%32)/8))*8 + c%8,
+ * i.e. each 16-row x 32-column block is one contiguous 512-element fragment in
+ * the matrix cores' operand order (a 1 KB bf16 block that one 64-lane wave reads
+ * with a single contiguous 16-byte-per-lane load).  Padded rows are zero.
+ * Batched weights (w_gate_up, w_down) are n_experts such tiled matrices back to
+ * back.
  */
 #ifndef DG_H
 #define DG_H
@@ -160,6 +169,18 @@ typedef struct dg_debug {
   float* route_w;
   float* router_logits;
 } dg_debug;
+
+/* Elements of the fragment-tiled form of a rows x cols matrix (rows rounded up to
+ * 16; cols must be a positive multiple of 32, else 0 is written and DG_ERR_INVALID
+ * returned).  Host-only. */
+int dg_packed_elems(int64_t rows, int64_t cols, int64_t* h_elems);
+
+/* Convert `batch` row-major [rows, cols] matrices at src (dtype DG_BF16 or DG_F32)
+ * into the fragment-tiled layout at dst (batch * dg_packed_elems elements; padded
+ * rows are written as zeros).  src and dst must not overlap; both 16-byte aligned.
+ * This is how callers bring weights into the layout dg_weights expects. */
+int dg_pack_matrix(const void* src, void* dst, int64_t batch, int64_t rows, int64_t cols, int32_t dtype,
+                   void* stream);
 
 /* Bytes of workspace needed by any call that processes up to max_tokens rows at
  * once (use cfg->canvas for denoising; a prefill chunk size for prefill/commit;

@@ -13,11 +13,15 @@ class Session:
     """Device model + KV cache + workspace for one set of dimensions."""
 
     def __init__(self, d: recipe.Dims, capacity: int, max_tokens: int = None, weights: dict = None,
-                 kv_capacity_round: int = 32):
+                 kv_capacity_round: int = 32, packed: bool = False):
+        """weights: natural (row-major) device weights, converted here unless packed=True; None builds the
+        seeded model directly in the library's layout."""
         self.d = d
         self.cfg = dg.make_config(d)
         if weights is None:
-            weights = gdev.model_weights_device(d)
+            weights = gdev.packed_model_weights_device(d)
+        elif not packed:
+            weights = dg.pack_weights(weights)
         self.w = weights
         self.weights = dg.Weights(weights["embed"], weights["final_norm"], weights["layers"])
         cap = ((capacity + kv_capacity_round - 1) // kv_capacity_round) * kv_capacity_round
@@ -64,7 +68,7 @@ def allclose_report(got: np.ndarray, ref: np.ndarray, atol: float, rtol: float):
 
 
 def compare_routing(g_idx: np.ndarray, g_w: np.ndarray, g_logits: np.ndarray, o_logits: np.ndarray,
-                    o_idx: np.ndarray, logit_tol) -> np.ndarray:
+                    o_idx: np.ndarray, logit_tol, rows=None) -> np.ndarray:
     """Routing parity in three parts.
 
     1. The GPU's decision is exact on its own logits: its expert list is the top-k of its fp32 logits in
@@ -72,7 +76,8 @@ def compare_routing(g_idx: np.ndarray, g_w: np.ndarray, g_logits: np.ndarray, o_
     2. Its logits match the oracle's within ``logit_tol`` = (atol, rtol).
     3. The chosen SET matches the oracle's wherever the oracle's k-th/(k+1)-th gap exceeds twice the
        token's largest logit difference (otherwise the two sides legitimately sit on either side of a tie).
-    Returns the mask of tokens whose sets match.
+    ``rows`` (optional mask): parts 2 and 3 only on these rows (rows whose inputs already diverged at an
+    earlier near-tie are not comparable).  Returns the mask of compared tokens whose sets match.
     """
     n, k = g_idx.shape
     E = g_logits.shape[1]
@@ -82,6 +87,9 @@ def compare_routing(g_idx: np.ndarray, g_w: np.ndarray, g_logits: np.ndarray, o_
     ex = np.exp(sel - sel[:, :1])
     np.testing.assert_allclose(g_w, ex / ex.sum(axis=1, keepdims=True), rtol=1e-5, atol=1e-6)
     atol, rtol = logit_tol
+    if rows is not None:
+        g_idx, g_logits, o_logits, o_idx = g_idx[rows], g_logits[rows], o_logits[rows], o_idx[rows]
+        n = int(np.sum(rows))
     diff = np.abs(g_logits.astype(np.float64) - o_logits)
     assert np.all(diff <= atol + rtol * np.abs(o_logits)), f"router logits differ by up to {diff.max():.3e}"
     srt = -np.sort(-o_logits, axis=1)
@@ -89,4 +97,8 @@ def compare_routing(g_idx: np.ndarray, g_w: np.ndarray, g_logits: np.ndarray, o_
     same = np.all(np.sort(g_idx, axis=1) == np.sort(o_idx, axis=1), axis=1)
     bad = ~same & (gap > 2 * diff.max(axis=1))
     assert not bad.any(), f"expert sets differ away from a tie: tokens {np.nonzero(bad)[0][:10]}"
+    if rows is not None:
+        full = np.zeros(rows.shape[0], dtype=bool)
+        full[np.nonzero(rows)[0]] = same
+        return full
     return same

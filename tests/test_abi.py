@@ -183,3 +183,20 @@ def _fake_weights_misaligned(n_layers):
     layers = [{f: a for f in dg.Weights.LAYER_FIELDS} for _ in range(n_layers)]
     layers[-1]["w_down"] = _Fake(0x10008)
     return dg.Weights(a, a, layers)
+
+
+def test_packed_elems():
+    assert dg.dg_packed_elems(16, 32) == 512
+    assert dg.dg_packed_elems(8, 256) == 16 * 256
+    assert dg.dg_packed_elems(262144, 2816) == 262144 * 2816
+    for rows, cols in ((0, 32), (16, 30), (16, 0)):
+        with pytest.raises(dg.DGError):
+            dg.dg_packed_elems(rows, cols)
+
+
+def test_pack_rejects_overlap_and_bad_dtype():
+    a = _Fake(0x100000)
+    with pytest.raises(dg.DGError):
+        dg.dg_pack_matrix(a, _Fake(0x100000 + 64), 1, 16, 32, dg.DG_BF16, 0)
+    with pytest.raises(dg.DGError):
+        dg.dg_pack_matrix(a, _Fake(0x900000), 1, 16, 32, 7, 0)

@@ -256,9 +256,14 @@ def test_deterministic_bitwise():
 
 
 def test_full_width_two_layers_end_to_end():
-    """C3 widths (d 2816, 128 experts, 262144 vocab, bf16) with 2 layers and a 256-token prompt: prefill
-    cache, per-layer hidden states and routing, and sampled head outputs against the oracle."""
-    d = replace(recipe.C3.dims, n_layers=2)
+    """Two layers at the full widths (d 2816, 16 q / 8 KV heads of 128, 262144 vocab, bf16) with a 256-token
+    prompt, every row compared: prefill cache, per-layer hidden states, routing and sampled head outputs.
+
+    Routing here selects all 16 of 16 experts, so no expert choice can sit on either side of a tie and the
+    two sides stay comparable through both layers (with top-8 of 128, a single tie flip at layer 0 legitimately
+    moves that token, and through attention its neighbours, beyond tolerance at layer 1; the top-8-of-128
+    decision itself is checked layer by layer in the C1 and C3 tests)."""
+    d = replace(recipe.C3.dims, n_layers=2, n_experts=16, top_k=16)
     P = 256
     log("full-width: device weights")
     sess = Session(d, capacity=P + d.canvas, max_tokens=d.canvas)
@@ -272,45 +277,43 @@ def test_full_width_two_layers_end_to_end():
     log("full-width: host weights + oracle")
     model = oracle_model(d)
     kv = om.KVCache(d.n_layers, d.n_kv_heads, d.head_dim)
-    _, ptraces = model.body(model.embed(prompt), kv, causal=True, append=True)
-    # the prompt again, one causal layer at a time, to see the GPU's own routing of the prompt rows
-    sess2 = Session(d, capacity=P + d.canvas, max_tokens=d.canvas, weights=sess.w)
-    x = torch.from_numpy(dg_inputs.embed_host(d, rows=prompt).view(np.int16)).cuda().view(torch.bfloat16)
-    keep = [np.ones(P, dtype=bool)]
-    for l in range(d.n_layers):
-        pd = {"route_idx": torch.empty((P, d.top_k), dtype=torch.int32, device="cuda"),
-              "route_w": torch.empty((P, d.top_k), dtype=torch.float32, device="cuda"),
-              "router_logits": torch.empty((P, d.n_experts), dtype=torch.float32, device="cuda")}
-        y = torch.empty_like(x)
-        dg.dg_layer_forward(sess2.cfg, sess2.weights, l, sess2.kv, x, y, P, 1, pd, sess2.ws, sess2.ws_bytes)
-        torch.cuda.synchronize()
-        same = compare_routing(pd["route_idx"].cpu().numpy(), pd["route_w"].cpu().numpy(),
-                               pd["router_logits"].cpu().numpy(), ptraces[l].router_logits, ptraces[l].idx, BF16_TOL)
-        keep.append(keep[-1] & same)
-        x = y
-    sess2.kv.len = P
-    for l in range(d.n_layers):   # layer-by-layer replay == one prefill call, bit for bit
-        assert torch.equal(sess2.k[l, :, :P], sess.k[l, :, :P]) and torch.equal(sess2.v[l, :, :, :P], sess.v[l, :, :, :P])
-    log(f"full-width: prefill rows compared per layer {[int(k.sum()) for k in keep[:-1]]}")
-    _check_kv(sess, kv, BF16_TOL, keep)
+    osm.prefill(model, kv, prompt)
+    _check_kv(sess, kv, BF16_TOL)
     x = model.embed(canvas)
     x, traces = model.body(x, kv, causal=False, append=False)
-    flips = 0
-    downstream = np.ones(d.canvas, dtype=bool)
     for l, tr in enumerate(traces):
         same = compare_routing(ridx[l].cpu().numpy(), rw[l].cpu().numpy(), rlog[l].cpu().numpy(),
                                tr.router_logits, tr.idx, BF16_TOL)
-        flips += int((~same).sum())
-        downstream &= same
-        ok, worst, at = allclose_report(to_f64(hid[l])[downstream], tr.hidden[downstream], *BF16_TOL)
+        assert same.all()
+        ok, worst, at = allclose_report(to_f64(hid[l]), tr.hidden, *BF16_TOL)
         assert ok, (l, worst, at)
-    rows = np.array([r for r in (0, 3, 77, 128, 255, 17, 200, 99) if downstream[r]][:5])
+    rows = np.array([0, 3, 77, 128, 255])
     opred, oconf, oent, margin = om.head_stats(x[rows], model.w["final_norm"], model.w["embed"], 1.0, d.rms_eps,
                                                numerics.bf16_round)
     sel = margin > MARGIN
     assert np.array_equal(pred.cpu().numpy()[rows][sel], opred[sel])
     assert allclose_report(to_f64(ent)[rows], oent, *BF16_TOL)[0]
-    log(f"full-width: routing near-tie flips {flips}; {int(sel.sum())}/{len(rows)} argmax compared")
+    log(f"full-width: {int(sel.sum())}/{len(rows)} argmax compared")
+
+
+def test_prefill_equals_layer_by_layer_replay():
+    """dg_prefill_kv and a causal dg_layer_forward replay of the same prompt write identical caches (bf16,
+    full widths, top-8 of 128)."""
+    d = replace(recipe.C3.dims, n_layers=2)
+    P = 256
+    sess = Session(d, capacity=P + d.canvas, max_tokens=d.canvas)
+    prompt = dg_inputs.prompt_tokens(P, d.vocab)
+    sess.prefill(prompt)
+    sess2 = Session(d, capacity=P + d.canvas, max_tokens=d.canvas, weights=sess.w, packed=True)
+    x = torch.from_numpy(dg_inputs.embed_host(d, rows=prompt).view(np.int16)).cuda().view(torch.bfloat16)
+    for l in range(d.n_layers):
+        y = torch.empty_like(x)
+        dg.dg_layer_forward(sess2.cfg, sess2.weights, l, sess2.kv, x, y, P, 1, None, sess2.ws, sess2.ws_bytes)
+        x = y
+    torch.cuda.synchronize()
+    for l in range(d.n_layers):
+        assert torch.equal(sess2.k[l, :, :P], sess.k[l, :, :P])
+        assert torch.equal(sess2.v[l, :, :, :P], sess.v[l, :, :, :P])
 
 
 def test_c3_bench_configuration_layer0_and_properties():

@@ -51,6 +51,29 @@ def test_device_generator_matches_host():
     assert np.array_equal(u.cpu().numpy(), dg_inputs.uniform_int(5000, 1, 1, 262144))
 
 
+# ----------------------------------------------------------------------------- weight layout
+
+@pytest.mark.parametrize("dtype,batch,rows,cols", [("bf16", 1, 48, 64), ("f32", 2, 40, 96), ("bf16", 3, 8, 32)])
+def test_pack_matrix_layout(dtype, batch, rows, cols):
+    """Fragment-tiled layout: element (r, c) of each matrix at ((r/16)*(C/32) + c/32)*512 + ((r%16) + 16*((c%32)/8))*8
+    + c%8, padded rows zero."""
+    src = gdev.normal_tensor((batch, rows, cols), 3, 7, 1.0, dtype)
+    out = dg.pack_tensor(src if batch > 1 else src[0])
+    torch.cuda.synchronize()
+    a = src.float().cpu().numpy()
+    got = out.float().cpu().numpy()
+    rows_p = (rows + 15) // 16 * 16
+    per = rows_p * cols
+    assert got.size == batch * per
+    exp = np.zeros(batch * per, dtype=np.float32)
+    for b in range(batch):
+        for r in range(rows):
+            for c in range(cols):
+                i = ((r // 16) * (cols // 32) + c // 32) * 512 + ((r % 16) + 16 * ((c % 32) // 8)) * 8 + c % 8
+                exp[b * per + i] = a[b, r, c]
+    assert np.array_equal(got, exp)
+
+
 # ----------------------------------------------------------------------------- canvas update
 
 @pytest.mark.parametrize("S,V", [(32, 4096), (256, 262144), (200, 1000)])
