@@ -14,8 +14,11 @@
 //     shuffles, and the probabilities are already in the B-operand layout of
 //     O^T = V^T P^T.  The value cache is stored [dh][position], so the A operand
 //     of that product is a contiguous 16-byte load per lane.  No LDS, no
-//     transposes; probabilities stay in registers (rounded to the storage type
-//     for the second product).
+//     transposes; probabilities stay in registers.  For bf16 storage each
+//     probability is split into a bf16 high part and a bf16 remainder and P V
+//     takes two matrix-core products, so P keeps ~16 significant bits instead of
+//     8 (rounding P to bf16 alone shifts the attention output by ~0.1%, enough to
+//     move a visible fraction of bf16 hidden states by one unit in the last place).
 //   * Scores use base-2 exponentials with log2(e)/sqrt(Dh) folded into the scale.
 //   * Splits write unnormalised partials (O, running max, running sum); a merge
 //     kernel combines them in fixed split order (deterministic) and normalises.
@@ -27,6 +30,7 @@ namespace dg {
 template <typename T, int DH, int HG>
 __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   constexpr int KS = DH / 32;   // 32-wide K steps over the head dimension
+  constexpr bool kExactP = sizeof(T) == 4;  // fp32 storage holds P exactly
   constexpr int MTD = DH / 16;  // 16-row tiles of O^T along the head dimension
   const int lane = lane_id(), row16 = lane & 15, quad = lane >> 4;
   const int G = a.n_heads / a.n_kv_heads;
@@ -124,13 +128,14 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
       const float m_new = fmaxf(m_run[j], mx);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = exp2f(m_run[j] - m_use);
-      Frag<T> pf;
+      Frag<T> pf, pl;
       float psum = 0.f;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         float p = ok[t] ? exp2f(sc[t] - m_use) : 0.f;
         psum += p;
         pf.set(t, p);
+        if constexpr (!kExactP) pl.set(t, p - pf.get(t));
       }
       l_run[j] = l_run[j] * alpha + psum;
       m_run[j] = m_new;
@@ -138,6 +143,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
       for (int mt = 0; mt < MTD; ++mt) {
         o[j][mt] *= alpha;
         mma(o[j][mt], vf[mt], pf);
+        if constexpr (!kExactP) mma(o[j][mt], vf[mt], pl);
       }
     }
   }
