@@ -120,6 +120,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="full_loop_bf16", choices=["full_loop_bf16", "long_context_bf16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (reference for HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -202,6 +204,14 @@ def main() -> int:
     torch.cuda.synchronize()
     ri = ridx.cpu().numpy()
     experts_hit = float(np.mean([len(np.unique(ri[l])) for l in range(d.n_layers)]))
+
+    if args.copy_calibration_mib > 0:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters give the scale of the byte counters
+        src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # per-kernel breakdown from one extra instrumented block (outside the timed region)
     dg.dg_timing_start(list(dg.KERNELS))
