@@ -45,7 +45,7 @@ def log(*a):
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("k_gemm.hip", "dg_device.h"):
+    for f in ("k_gemm.hip", "dg_device.h", "dg_wave_gemm.h", "dg_kernels.h"):
         with open(os.path.join(ROOT, "block_diffusion_decoding_step_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
