@@ -117,7 +117,7 @@ int attention_splits(int64_t n_keys, int q_rows, int n_heads, int n_kv_heads, in
 struct HeadArgs {
   const void* x;      // normalised hidden [n, d]
   const void* E;      // [V, d]
-  float4* part;       // [n_groups][n] partials (max, argmax bits, Z, S1), log2 units
+  float4* part;       // [n_groups][n] partials (max, argmax bits, Z, S1), natural units
   int n, d, V;
   int n_groups;
   float beta_log2e;   // inv_temperature * log2(e)

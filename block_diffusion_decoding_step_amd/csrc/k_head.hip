@@ -14,11 +14,17 @@
 //     S1 = e^(ma-m) (S1a + (ma-m) Za) + e^(mb-m) (S1b + (mb-m) Zb).
 // Finally conf = 1/Z and entropy = ln Z - S1/Z.
 //
-// logits^T = E_tile X^T on the matrix core: a wave owns 64 vocabulary rows x 64
-// slots, so each lane holds one slot (lane & 15 of each slot tile) and 16 of its
-// logits per tile.  A workgroup (4 waves = 256 slots) walks vocabulary tiles
-// group, group + n_groups, ...; each group writes one partial state per slot and
-// a merge kernel combines the groups in fixed order (deterministic).
+// logits^T = E_tile X^T on the matrix core, LDS-tiled.  A workgroup (8 waves)
+// owns 256 slots and walks 256-token vocabulary tiles blockIdx.x, +gridDim.x, ...
+// For each pair of 32-wide K steps it stages the tiles' fragments of E (16 row
+// fragments, read once from HBM) and of X (16 slot fragments, from L2) in LDS,
+// double-buffered so that the next stage's global loads are in flight while
+// the matrix core works on this one.  Wave w computes 64 tokens (w % 4) x 128
+// slots (w / 4): each lane holds one slot per 16-slot fragment and 16 of its
+// logits per tile, folds them into a running per-slot state, and at the end the
+// four quads of a wave and the four token waves of a slot are merged in fixed
+// order into one partial per (workgroup, slot).  A merge kernel combines the
+// workgroups in fixed order (deterministic).
 #include "dg_device.h"
 #include "dg_kernels.h"
 #include "dg_wave_gemm.h"
@@ -51,84 +57,178 @@ __device__ __forceinline__ void stat_merge(Stat& x, const Stat& y) {
 }
 
 template <typename T>
-struct HeadDepth;
-template <>
-struct HeadDepth<bf16> { static constexpr int v = 4; };
-template <>
-struct HeadDepth<float> { static constexpr int v = 1; };
+struct HeadCfg {
+  static constexpr int KC = sizeof(T) == 2 ? 2 : 1;   // K steps per stage
+  static constexpr int FB = kFragElems * (int)sizeof(T);  // bytes per fragment
+  static constexpr int STAGE = KC * 32 * FB;           // 16 E + 16 X fragments per K step: 64 KB
+  static constexpr int UPL = FB / 64 / 16;             // 16-byte units per lane per fragment
+  static constexpr int LOADS = STAGE / 16 / 512;       // 16-byte loads per thread per stage
+};
 
-// grid = (n_groups, ceil(n / 256)); block = 256 (4 waves x 64 slots)
+constexpr int kHeadSlots = 256;    // slots per workgroup
+constexpr int kHeadTokens = 256;   // vocabulary rows per tile
+constexpr int kHeadMaxGroups = 256;
+
+// grid = (n_groups, ceil(n / 256)); block = 512
 template <typename T>
-__global__ __launch_bounds__(256) void k_vocab_head(HeadArgs a) {
-  const int lane = lane_id(), w = wave_id();
-  const int row16 = lane & 15, quad = lane >> 4;
-  const int slot0 = blockIdx.y * 256 + w * 64;
-  if (slot0 >= a.n) return;
-  const T* X = (const T*)a.x;
+__global__ __launch_bounds__(512, 1) void k_vocab_head(HeadArgs a) {
+  using C = HeadCfg<T>;
+  static_assert(C::LOADS == 8, "stage layout");
+  __shared__ uint4 lds[2 * C::STAGE / 16];
+  const int t = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int wv = w & 3, wsl = w >> 2;  // token quarter, slot half
+  const int quad = lane >> 4, row16 = lane & 15;
+  const int slot_base = blockIdx.y * kHeadSlots;
+  const int ks = a.d / 32;
+  const int nch = (ks + C::KC - 1) / C::KC;
+  const int n_tiles = (a.V + kHeadTokens - 1) / kHeadTokens;
+  const int G = gridDim.x;
+  const int my_tiles = (n_tiles - (int)blockIdx.x + G - 1) / G;
+  const int total = my_tiles * nch;
+  const int last_rt = (a.V + 15) / 16 - 1;
   const T* E = (const T*)a.E;
-  const T* bp[4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) bp[nt] = X + (int64_t)min(slot0 + 16 * nt + row16, a.n - 1) * a.d + quad * 8;
-  Stat st[4];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) st[nt] = Stat{-INFINITY, 0.f, 0.f, 0x7fffffff};
+  const T* X = (const T*)a.x;
   const float beta = a.beta_log2e * 0.6931471805599453f;  // inverse temperature
-  const int n_vt = (a.V + 63) / 64;
-  for (int vt = blockIdx.x; vt < n_vt; vt += a.n_groups) {
-    const int v0 = vt * 64;
-    const T* ap[4];  // E is fragment-tiled: one row tile per 16 tokens
+
+  // Stage q = (tile blockIdx.x + (q / nch) * G, chunk q % nch).  Thread t moves the
+  // 16-byte units j*512 + t of the stage: unit u is byte 16u of the stage, i.e.
+  // fragment u / (64*UPL) (K step, then 16 E fragments, then 16 X fragments),
+  // lane (u % (64*UPL)) / UPL of it, part u % UPL of that lane's 8 elements.
+  auto issue = [&](int q, uint4 (&r)[C::LOADS]) {
+    const int tile = (int)blockIdx.x + (q / nch) * G, c = q % nch;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) ap[mt] = tiled_frag(E, min(v0 / 16 + mt, (a.V + 15) / 16 - 1), a.d / 32, 0);
-    f32x4 acc[4][4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = zero4();
-    wave_gemm<T, 4, 4, HeadDepth<T>::v>(acc, ap, bp, a.d / 32, kFragElems, 32);
-    // lane holds, for slot (slot0 + 16*nt + row16), tokens v0 + 16*mt + 4*quad + r
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      Stat loc{-INFINITY, 0.f, 0.f, 0x7fffffff};
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int v = v0 + 16 * mt + 4 * quad + r;
-          const float l = acc[mt][nt][r] * beta;
-          if (v < a.V && l > loc.m) { loc.m = l; loc.a = v; }
-        }
-      if (loc.m != -INFINITY) {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int v = v0 + 16 * mt + 4 * quad + r;
-            if (v < a.V) {
-              const float dl = acc[mt][nt][r] * beta - loc.m;
-              const float e = exp2f(dl * 1.4426950408889634f);
-              loc.z += e;
-              loc.s1 += e * dl;
-            }
-          }
+    for (int j = 0; j < C::LOADS; ++j) {
+      const int u = j * 512 + t;
+      const int g = u / (64 * C::UPL), qq = u % (64 * C::UPL);
+      const int fl = qq / C::UPL, part = qq % C::UPL;
+      const int kk = g >> 5, which = (g >> 4) & 1, idx = g & 15;
+      const int s = c * C::KC + kk;
+      const T* src;
+      if (which == 0) {
+        const int rt = min(tile * (kHeadTokens / 16) + idx, last_rt);
+        src = E + ((int64_t)rt * ks + min(s, ks - 1)) * kFragElems + fl * 8;
+      } else {
+        const int row = min(slot_base + 16 * idx + (fl & 15), a.n - 1);
+        src = X + (int64_t)row * a.d + 32 * min(s, ks - 1) + 8 * (fl >> 4);
       }
-      stat_merge(st[nt], loc);
+      src += part * (16 / (int)sizeof(T));
+      r[j] = s < ks ? *reinterpret_cast<const uint4*>(src) : uint4{0u, 0u, 0u, 0u};
     }
-  }
-  // combine the four quads that share a slot, then write one partial per slot
+  };
+  auto commit = [&](int buf, const uint4 (&r)[C::LOADS]) {
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+    for (int j = 0; j < C::LOADS; ++j) lds[buf * (C::STAGE / 16) + j * 512 + t] = r[j];
+  };
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = zero4();
+  Stat st[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) st[j] = Stat{-INFINITY, 0.f, 0.f, 0x7fffffff};
+
+  uint4 r[C::LOADS];
+  if (total > 0) {
+    issue(0, r);
+    commit(0, r);
+  }
+  __syncthreads();
+  for (int q = 0; q < total; ++q) {
+    if (q + 1 < total) issue(q + 1, r);
+    const T* base = reinterpret_cast<const T*>(lds) + (q & 1) * (C::STAGE / (int)sizeof(T));
+#pragma unroll
+    for (int kk = 0; kk < C::KC; ++kk) {
+      const T* kb = base + kk * 32 * kFragElems + lane * 8;
+      Frag<T> fa[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[i].load(kb + (4 * wv + i) * kFragElems);
+      if constexpr (sizeof(T) == 2) {
+        Frag<T> fb[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) fb[j].load(kb + (16 + 8 * wsl + j) * kFragElems);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) mma(acc[i][j], fa[i], fb[j]);
+      } else {  // fp32 fragments are twice the size: one slot fragment at a time
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          Frag<T> fb;
+          fb.load(kb + (16 + 8 * wsl + j) * kFragElems);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mma(acc[i][j], fa[i], fb);
+        }
+      }
+    }
+    if (q % nch == nch - 1) {
+      // tile finished: lane holds, for slot slot_base + 128*wsl + 16*j + row16,
+      // tokens v0 + 16*i + 4*quad + rr
+      const int v0 = ((int)blockIdx.x + (q / nch) * G) * kHeadTokens + 64 * wv;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        Stat loc{-INFINITY, 0.f, 0.f, 0x7fffffff};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int v = v0 + 16 * i + 4 * quad + rr;
+            const float l = acc[i][j][rr] * beta;
+            if (v < a.V && l > loc.m) { loc.m = l; loc.a = v; }
+          }
+        if (loc.m != -INFINITY) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const int v = v0 + 16 * i + 4 * quad + rr;
+              if (v < a.V) {
+                const float dl = acc[i][j][rr] * beta - loc.m;
+                const float e = exp2f(dl * 1.4426950408889634f);
+                loc.z += e;
+                loc.s1 += e * dl;
+              }
+            }
+        }
+        stat_merge(st[j], loc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i][j] = zero4();
+      }
+    }
+    if (q + 1 < total) commit((q + 1) & 1, r);
+    __syncthreads();
+  }
+  // merge the four quads (lanes 16 apart hold the same slot), then the four token waves
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
 #pragma unroll
     for (int o = 16; o <= 32; o <<= 1) {
       Stat y;
-      y.m = __shfl_xor(st[nt].m, o, 64);
-      y.z = __shfl_xor(st[nt].z, o, 64);
-      y.s1 = __shfl_xor(st[nt].s1, o, 64);
-      y.a = __shfl_xor(st[nt].a, o, 64);
-      stat_merge(st[nt], y);
+      y.m = __shfl_xor(st[j].m, o, 64);
+      y.z = __shfl_xor(st[j].z, o, 64);
+      y.s1 = __shfl_xor(st[j].s1, o, 64);
+      y.a = __shfl_xor(st[j].a, o, 64);
+      stat_merge(st[j], y);
     }
-    const int slot = slot0 + 16 * nt + row16;
-    if (quad == 0 && slot < a.n)
-      a.part[(int64_t)blockIdx.x * a.n + slot] = make_float4(st[nt].m, __int_as_float(st[nt].a), st[nt].z, st[nt].s1);
+  }
+  float4* red = reinterpret_cast<float4*>(lds);  // [4 token waves][256 slots]; stages are no longer read
+  if (quad == 0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      red[wv * kHeadSlots + 128 * wsl + 16 * j + row16] =
+          make_float4(st[j].m, __int_as_float(st[j].a), st[j].z, st[j].s1);
+  }
+  __syncthreads();
+  if (t < kHeadSlots && slot_base + t < a.n) {
+    float4 p = red[t];
+    Stat x{p.x, p.z, p.w, __float_as_int(p.y)};
+#pragma unroll
+    for (int k = 1; k < 4; ++k) {
+      p = red[k * kHeadSlots + t];
+      stat_merge(x, Stat{p.x, p.z, p.w, __float_as_int(p.y)});
+    }
+    a.part[(int64_t)blockIdx.x * a.n + slot_base + t] = make_float4(x.m, __int_as_float(x.a), x.z, x.s1);
   }
 }
 
@@ -161,14 +261,14 @@ __global__ __launch_bounds__(256) void k_head_merge(HeadArgs a) {
 }
 
 int head_groups(int V) {
-  const int n_vt = (V + 63) / 64;
-  return n_vt < 1024 ? n_vt : 1024;
+  const int n_tiles = (V + kHeadTokens - 1) / kHeadTokens;
+  return n_tiles < kHeadMaxGroups ? n_tiles : kHeadMaxGroups;
 }
 
 template <typename T>
 hipError_t launch_vocab_head(const HeadArgs& a, hipStream_t s) {
-  dim3 grid(a.n_groups, (a.n + 255) / 256);
-  hipLaunchKernelGGL(k_vocab_head<T>, grid, dim3(256), 0, s, a);
+  dim3 grid(a.n_groups, (a.n + kHeadSlots - 1) / kHeadSlots);
+  hipLaunchKernelGGL(k_vocab_head<T>, grid, dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
