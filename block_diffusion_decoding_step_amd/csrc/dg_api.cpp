@@ -84,7 +84,6 @@ struct TimeScope {
     DG_TRY(expr);                 \
   } while (0)
 
-constexpr int kMaxSplit = 16;
 constexpr int64_t kPartialRows = 4096;  // attention split partials hold n_split * rows <= max(this, rows)
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -255,7 +254,7 @@ int layer_t(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int
   at.q = ws.Q; at.kc = kbase; at.vc = vbase; at.o_part = ws.opart; at.ml_part = ws.mlpart; at.o = ws.O;
   at.q_rows = Mi; at.n_heads = hq; at.n_kv_heads = hkv; at.head_dim = dh; at.cap = kv->capacity;
   at.n_keys = pos0 + M; at.q_pos0 = pos0; at.causal = causal ? 1 : 0;
-  const int max_split = (int)std::min<int64_t>(kMaxSplit, std::max<int64_t>(1, std::max(kPartialRows, M) / M));
+  const int max_split = (int)std::min<int64_t>(kAttnMaxSplit, std::max<int64_t>(1, std::max(kPartialRows, M) / M));
   at.n_split = attention_splits(at.n_keys, Mi, hq, hkv, at.causal, max_split);
   DG_LAUNCH(DG_K_ATTENTION, s, launch_attention<T>(at, s));
   DG_LAUNCH(DG_K_ATTN_MERGE, s, launch_attention_merge<T>(at, s));

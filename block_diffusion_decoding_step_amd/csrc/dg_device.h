@@ -122,6 +122,10 @@ struct Vec8<float> {
   }
 };
 
+// 64-bit integer min / max as plain compares (the generic min/max overloads may go through double)
+__device__ __forceinline__ int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
+__device__ __forceinline__ int64_t imax64(int64_t a, int64_t b) { return a > b ? a : b; }
+
 // ---------------------------------------------------------------- wave reductions
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

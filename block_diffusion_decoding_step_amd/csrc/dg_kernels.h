@@ -111,6 +111,7 @@ template <typename T>
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 template <typename T>
 hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t s);
+constexpr int kAttnMaxSplit = 16;  // key splits of one attention launch (partials per row)
 int attention_splits(int64_t n_keys, int q_rows, int n_heads, int n_kv_heads, int causal, int max_split);
 
 // ---- k_head.hip

@@ -7,161 +7,317 @@
 // (query i sees keys up to its own position) serves prompt prefill and block commit.
 //
 // Design
-//   * One wave = 16 query rows x HG query heads of one KV head (GQA packing: the
-//     HG heads share every K/V fragment) x one split of the key range.
-//   * S^T = K Q^T on the matrix core, so each lane ends up holding 8 consecutive
-//     keys of ONE query (its lane & 15): the online softmax needs only two xor
-//     shuffles, and the probabilities are already in the B-operand layout of
-//     O^T = V^T P^T.  The value cache is stored [dh][position], so the A operand
-//     of that product is a contiguous 16-byte load per lane.  No LDS, no
-//     transposes; probabilities stay in registers.  For bf16 storage each
-//     probability is split into a bf16 high part and a bf16 remainder and P V
-//     takes two matrix-core products, so P keeps ~16 significant bits instead of
-//     8 (rounding P to bf16 alone shifts the attention output by ~0.1%, enough to
-//     move a visible fraction of bf16 hidden states by one unit in the last place).
-//   * Scores use base-2 exponentials with log2(e)/sqrt(Dh) folded into the scale.
-//   * Splits write unnormalised partials (O, running max, running sum); a merge
-//     kernel combines them in fixed split order (deterministic) and normalises.
+//   * A workgroup of 8 waves takes 256 (head, query) rows of ONE KV head -- every
+//     query head of the GQA group reads the same keys -- and one split of the key
+//     range.  Each wave owns 32 consecutive queries of one head (two 16-row tiles).
+//   * The key range is walked in chunks of 128 keys.  Each chunk's K and V
+//     fragments are copied once from global memory straight into LDS (no register
+//     staging), double-buffered so that the copy of the next chunk is in flight
+//     while this one is computed, and read by all 8 waves: K/V leave L2 once per
+//     workgroup.  In LDS every fragment is stored in the matrix core's operand order
+//     (one contiguous 16-byte read per lane, no bank conflicts).
+//   * S^T = K Q^T on the matrix core, with the key rows of each K fragment
+//     permuted so that each lane ends up holding 8 consecutive keys of ONE query
+//     (its lane & 15), already in the B-operand layout of O^T = V^T P^T.  The value
+//     cache is stored [dh][position], so V^T fragments are contiguous 16-byte rows.
+//     For bf16 storage each probability is split into a bf16 high part and a bf16
+//     remainder and P V takes two matrix-core products, so P keeps ~16 significant
+//     bits instead of 8 (rounding P to bf16 alone perturbs the attention output by
+//     ~0.1%, enough to flip downstream bf16 roundings and routing decisions).
+//   * Online softmax in base 2 with log2(e)/sqrt(Dh) folded into one FMA per score,
+//     against a lazily updated reference max: the exact row max (two shuffles) and
+//     the rescale of O are only computed when some probability would exceed 2^8.
+//   * Splits write unnormalised partials (O, reference max, sum); a merge kernel
+//     combines them in fixed split order (deterministic) and normalises.
 #include "dg_device.h"
 #include "dg_kernels.h"
+#include "dg_wave_gemm.h"
 
 namespace dg {
 
-template <typename T, int DH, int HG>
-__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
-  constexpr int KS = DH / 32;   // 32-wide K steps over the head dimension
-  constexpr bool kExactP = sizeof(T) == 4;  // fp32 storage holds P exactly
-  constexpr int MTD = DH / 16;  // 16-row tiles of O^T along the head dimension
-  const int lane = lane_id(), row16 = lane & 15, quad = lane >> 4;
+constexpr int kAttnWaves = 8;     // waves per workgroup
+constexpr int kAttnRows = 32;     // (head, query) rows per wave
+constexpr int kAttnChunk = 128;   // keys per LDS stage (four 32-key steps; two for fp32 at Dh 128)
+constexpr bool kAttnSplitP = true;   // bf16 P as high + remainder parts (two products)
+constexpr uint32_t kAttnLazyBits = 0x43800000u;  // 256.0f: probabilities stay below 2^8 of the reference
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <typename T, int DH>
+struct AttnCfg {
+  static constexpr int SUBS = (sizeof(T) == 4 && DH == 128) ? 2 : kAttnChunk / 32;  // 32-key steps per chunk
+  static constexpr int CHUNK = 32 * SUBS;
+  static constexpr int KF = DH / 32;                 // K fragments per 16-key tile (32-wide dh steps)
+  static constexpr int MTD = DH / 16;                // 16-row dh tiles of O^T
+  static constexpr int NKF = SUBS * 2 * KF;          // K fragments per chunk (2 key tiles per step)
+  static constexpr int NVF = SUBS * MTD;             // V^T fragments per chunk
+  static constexpr int NF = NKF + NVF;
+  static constexpr int FB = kFragElems * (int)sizeof(T);
+  static constexpr int STAGE = NF * FB;              // bytes per stage
+  static constexpr int UPL = FB / 64 / 16;           // 16-byte units per lane per fragment
+  static constexpr int LOADS = STAGE / 16 / (64 * kAttnWaves);  // 1 KB copies per wave per stage
+  static_assert(LOADS * 16 * 64 * kAttnWaves == STAGE, "stage split");
+  static_assert(2 * STAGE <= 131072, "LDS");
+};
+
+// Workgroup -> (row block, split, KV head), row block fastest, XCD-aware so that
+// the row blocks and splits of one KV head share an L2.
+template <typename T, int DH>
+__global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
+  using C = AttnCfg<T, DH>;
+  constexpr bool kSplitP = sizeof(T) == 2 && kAttnSplitP;
+  constexpr int EPU = 16 / (int)sizeof(T);  // elements per 16-byte unit
+  __shared__ uint4 lds0[C::STAGE / 16];
+  __shared__ uint4 lds1[C::STAGE / 16];
+  const int lane = lane_id(), w = wave_id();
+  const int row16 = lane & 15, quad = lane >> 4;
   const int G = a.n_heads / a.n_kv_heads;
-  const int hsub = G / HG;                      // head sub-groups per KV head
-  const int n_rt = (a.q_rows + 15) / 16;        // query row tiles
-  const int tasks = a.n_kv_heads * hsub * a.n_split * n_rt;
-  const int n_wg = (tasks + 3) / 4;
-  const int task = xcd_remap(blockIdx.x, n_wg) * 4 + wave_id();
-  if (task >= tasks) return;
-  const int rt = task % n_rt;
-  int rest = task / n_rt;
-  const int split = rest % a.n_split;
-  rest /= a.n_split;
-  const int hs = rest % hsub;
-  const int g = rest / hsub;
-  const int r0 = rt * 16;
-  const int mq = r0 + row16;                     // this lane's query row
-  const int mq_ld = min(mq, a.q_rows - 1);
+  const int qt32 = (a.q_rows + kAttnRows - 1) / kAttnRows;   // 32-query tiles per head
+  const int n_wt = G * qt32;                                 // wave tasks per KV head
+  const int nb = (n_wt + kAttnWaves - 1) / kAttnWaves;       // row blocks per KV head
+  const int n_wg = nb * a.n_split * a.n_kv_heads;
+  const int id = xcd_remap(blockIdx.x, n_wg);
+  const int rb = id % nb;
+  const int split = (id / nb) % a.n_split;
+  const int g = id / (nb * a.n_split);
 
-  const int64_t n_chunks = (a.n_keys + 31) / 32;
-  const int64_t per = (n_chunks + a.n_split - 1) / a.n_split;
-  int64_t c_begin = split * per;
-  int64_t c_end = min(n_chunks, c_begin + per);
+  const int wt = rb * kAttnWaves + w;
+  const bool active = wt < n_wt;
+  const int j = active ? wt / qt32 : 0;           // head within the group
+  const int q0 = active ? (wt % qt32) * kAttnRows : 0;
+  const int h = g * G + j;
+
+  // keys this workgroup may need: all of them, or (causal) up to its furthest query
+  int64_t key_end = a.n_keys;
   if (a.causal) {
-    int64_t last_pos = a.q_pos0 + min(r0 + 15, a.q_rows - 1);  // furthest key any row of the tile sees
-    c_end = min(c_end, last_pos / 32 + 1);
+    int qmax = 0;
+    for (int x = 0; x < kAttnWaves; ++x) {
+      const int wx = rb * kAttnWaves + x;
+      if (wx < n_wt) qmax = max(qmax, min((wx % qt32) * kAttnRows + kAttnRows - 1, a.q_rows - 1));
+    }
+    key_end = imin64(key_end, a.q_pos0 + qmax + 1);
   }
-  const int64_t my_pos = a.q_pos0 + mq;
+  const int64_t n_ch = (key_end + C::CHUNK - 1) / C::CHUNK;
+  const int64_t per = (n_ch + a.n_split - 1) / a.n_split;
+  const int64_t ch_begin = imin64(n_ch, (int64_t)split * per);
+  const int64_t ch_end = imin64(n_ch, ch_begin + per);
+  const int n_my = (int)(ch_end - ch_begin);
 
-  const T* Q = (const T*)a.q;
   const T* K = (const T*)a.kc + (int64_t)g * a.cap * DH;
   const T* Vt = (const T*)a.vc + (int64_t)g * DH * a.cap;
 
-  Frag<T> qf[HG][KS];
+  // Stage layout: fragment f < NKF is K for (32-key step f / (2 KF), key tile (f / KF) % 2,
+  // dh step f % KF); fragment NKF + f' is V^T for (32-key step f' / MTD, dh tile f' % MTD).
+  // Unit u (16 bytes at byte 16u) is lane (u % (64 UPL)) / UPL, part u % UPL, of fragment
+  // u / (64 UPL).  Wave w copies units (jj * 8 + w) * 64 + lane straight from global memory
+  // into LDS (one contiguous 1 KB per instruction).  Addresses are clamped into the cache
+  // row; keys at or past n_keys are masked out of the scores, and their values are zeroed in
+  // LDS before use (memory there may hold anything).
+  auto unit_src = [&](int64_t c0, int u) -> const T* {
+    const int f = u / (64 * C::UPL), qq = u % (64 * C::UPL);
+    const int l = qq / C::UPL, part = qq % C::UPL;
+    if (f < C::NKF) {
+      const int sub = f / (2 * C::KF), i = (f / C::KF) % 2, ks = f % C::KF;
+      const int lr = l & 15;
+      const int64_t key = imin64(c0 + 32 * sub + 8 * (lr >> 2) + (lr & 3) + 4 * i, a.cap - 1);
+      return K + key * DH + 32 * ks + 8 * (l >> 4) + part * EPU;
+    }
+    const int ff = f - C::NKF;
+    const int sub = ff / C::MTD, mt = ff % C::MTD;
+    const int64_t key0 = imin64(c0 + 32 * sub + 8 * (l >> 4) + part * EPU, a.cap - EPU);
+    return Vt + (int64_t)(16 * mt + (l & 15)) * a.cap + key0;
+  };
+  auto issue = [&](int64_t ch, uint4* buf) {
+    const int64_t c0 = ch * C::CHUNK;
 #pragma unroll
-  for (int j = 0; j < HG; ++j) {
-    const int h = g * G + hs * HG + j;
-    const T* qrow = Q + ((int64_t)h * a.q_rows + mq_ld) * DH + quad * 8;
+    for (int jj = 0; jj < C::LOADS; ++jj) {
+      const int u0 = (jj * kAttnWaves + w) * 64;
+      __builtin_amdgcn_global_load_lds((const void*)unit_src(c0, u0 + lane), (lds_void*)(buf + u0), 16, 0, 0);
+    }
+  };
+  // zero V^T entries of keys >= n_keys in a staged chunk (only the chunk holding the last key)
+  auto fix_tail = [&](int64_t ch, uint4* buf) {
+    const int64_t c0 = ch * C::CHUNK;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[j][ks].load(qrow + 32 * ks);
+    for (int jj = 0; jj < C::LOADS; ++jj) {
+      const int u = (jj * kAttnWaves + w) * 64 + lane;
+      const int f = u / (64 * C::UPL), qq = u % (64 * C::UPL);
+      if (f < C::NKF) continue;
+      const int l = qq / C::UPL, part = qq % C::UPL;
+      const int sub = (f - C::NKF) / C::MTD;
+      const int64_t key0 = c0 + 32 * sub + 8 * (l >> 4) + part * EPU;
+      if (key0 + EPU > a.n_keys) {
+        uint4 v = buf[u];
+        T* e = reinterpret_cast<T*>(&v);
+#pragma unroll
+        for (int x = 0; x < EPU; ++x)
+          if (key0 + x >= a.n_keys) e[x] = from_f32<T>(0.f);
+        buf[u] = v;
+      }
+    }
+  };
+
+  Frag<T> qf[2][C::KF];
+  int64_t my_pos[2];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int mq = q0 + 16 * qt + row16;
+    my_pos[qt] = a.q_pos0 + mq;
+    const T* qrow = (const T*)a.q + ((int64_t)h * a.q_rows + min(mq, a.q_rows - 1)) * DH + quad * 8;
+#pragma unroll
+    for (int ks = 0; ks < C::KF; ++ks) qf[qt][ks].load(qrow + 32 * ks);
   }
   const float scale = 1.4426950408889634f / sqrtf((float)DH);
+  const int64_t wave_last = a.q_pos0 + min(q0 + kAttnRows - 1, a.q_rows - 1);  // furthest key this wave sees
 
-  float m_run[HG], l_run[HG];
-  f32x4 o[HG][MTD];
+  float m_run[2], l_run[2];
+  f32x4 o[2][C::MTD];
 #pragma unroll
-  for (int j = 0; j < HG; ++j) {
-    m_run[j] = -INFINITY;
-    l_run[j] = 0.f;
+  for (int qt = 0; qt < 2; ++qt) {
+    m_run[qt] = -INFINITY;
+    l_run[qt] = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < MTD; ++mt) o[j][mt] = zero4();
-  }
-  // A-operand row of S^T tile i for this lane: key kbase + 8*(row16/4) + 4*i + row16%4,
-  // so that C register r of tile i on this lane is key kbase + 8*quad + 4*i + r.
-  const int krow = 8 * (row16 >> 2) + (row16 & 3);
-
-  for (int64_t c = c_begin; c < c_end; ++c) {
-    const int64_t kbase = c * 32;
-    Frag<T> kf[2][KS];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const T* kr = K + (kbase + krow + 4 * i) * DH + quad * 8;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kf[i][ks].load(kr + 32 * ks);
-    }
-    Frag<T> vf[MTD];
-#pragma unroll
-    for (int mt = 0; mt < MTD; ++mt) vf[mt].load(Vt + (int64_t)(16 * mt + row16) * a.cap + kbase + quad * 8);
-    if (kbase + 32 > a.n_keys) {  // zero values past the last key (memory there may hold anything)
-#pragma unroll
-      for (int mt = 0; mt < MTD; ++mt)
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-          if (kbase + quad * 8 + t >= a.n_keys) vf[mt].set(t, 0.f);
-    }
-#pragma unroll
-    for (int j = 0; j < HG; ++j) {
-      f32x4 s[2] = {zero4(), zero4()};
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) mma(s[i], kf[i][ks], qf[j][ks]);
-      float sc[8];
-      bool ok[8];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int64_t key = kbase + quad * 8 + t;
-        ok[t] = key < a.n_keys && (!a.causal || key <= my_pos);
-        sc[t] = s[t >> 2][t & 3] * scale;
-        if (ok[t]) mx = fmaxf(mx, sc[t]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run[j], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m_run[j] - m_use);
-      Frag<T> pf, pl;
-      float psum = 0.f;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        float p = ok[t] ? exp2f(sc[t] - m_use) : 0.f;
-        psum += p;
-        pf.set(t, p);
-        if constexpr (!kExactP) pl.set(t, p - pf.get(t));
-      }
-      l_run[j] = l_run[j] * alpha + psum;
-      m_run[j] = m_new;
-#pragma unroll
-      for (int mt = 0; mt < MTD; ++mt) {
-        o[j][mt] *= alpha;
-        mma(o[j][mt], vf[mt], pf);
-        if constexpr (!kExactP) mma(o[j][mt], vf[mt], pl);
-      }
-    }
+    for (int mt = 0; mt < C::MTD; ++mt) o[qt][mt] = zero4();
   }
 
-  // partials: O^T tile register r of tile mt on this lane = (query mq, dh 16*mt + 4*quad + r)
+  // S^T tiles of both query tiles for 32-key step `sub` of a staged chunk
+  auto scores = [&](const T* base, int sub, f32x4 (&sv)[2][2]) {
+    Frag<T> kf[2][C::KF];
 #pragma unroll
-  for (int j = 0; j < HG; ++j) {
-    float l_tot = l_run[j];
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int ks = 0; ks < C::KF; ++ks) kf[i][ks].load(base + ((sub * 2 + i) * C::KF + ks) * kFragElems);
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        sv[qt][i] = zero4();
+#pragma unroll
+        for (int ks = 0; ks < C::KF; ++ks) mma(sv[qt][i], kf[i][ks], qf[qt][ks]);
+      }
+  };
+
+  // One staged chunk, 32-key step by 32-key step (steps past the wave's last visible key are skipped).
+  auto compute = [&](int64_t ch, const uint4* buf) {
+    const int64_t c0 = ch * C::CHUNK;
+    if (!active || c0 >= a.n_keys || (a.causal && c0 > wave_last)) return;  // wave-uniform
+    const T* base = reinterpret_cast<const T*>(buf) + lane * 8;
+#pragma unroll
+    for (int sub = 0; sub < C::SUBS; ++sub) {
+      const int64_t kbase = c0 + 32 * sub;
+      if (kbase >= a.n_keys || (a.causal && kbase > wave_last)) continue;  // wave-uniform
+      f32x4 svc[2][2];
+      scores(base, sub, svc);
+      Frag<T> vf[C::MTD];
+#pragma unroll
+      for (int mt = 0; mt < C::MTD; ++mt) vf[mt].load(base + (C::NKF + sub * C::MTD + mt) * kFragElems);
+      // keys [kbase, kbase + rel) exist; a step needs no mask when all 32 exist and (causal)
+      // every query of the wave sees all of them
+      const int rel = (int)imin64(a.n_keys - kbase, 32);
+      const bool full = rel == 32 && (!a.causal || kbase + 31 <= a.q_pos0 + q0);
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        // lane holds raw scores of keys kbase + 8*quad + x, x = 0..7, of its query
+        float sr[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) sr[x] = svc[qt][x >> 2][x & 3];
+        bool has_valid = true;
+        if (!full) {
+          const int lim = a.causal ? (int)imin64(rel, my_pos[qt] - kbase + 1) : rel;
+#pragma unroll
+          for (int x = 0; x < 8; ++x)
+            if (quad * 8 + x >= lim) sr[x] = -INFINITY;
+          has_valid = lim > quad * 8;
+        }
+        // Lazy softmax reference: probabilities are formed against the running reference
+        // m_run, which moves only when some probability would exceed 2^8 (or on the row's
+        // first keys).  Only then does the wave take the exact row max (two shuffles) and
+        // rescale O; otherwise no max, shuffle or rescale is needed.  Same softmax.
+        float pv[8];
+        uint32_t pm = 0;
+        {
+          const float m_use = m_run[qt] == -INFINITY ? 0.f : m_run[qt];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            pv[x] = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[x], scale, -m_use));
+            pm = max(pm, __float_as_uint(pv[x]));  // p >= 0 (or NaN): bit order is value order
+          }
+        }
+        const bool need = m_run[qt] == -INFINITY ? has_valid : pm > kAttnLazyBits;
+        if (__any(need)) {
+          float mx = fmaxf(fmaxf(fmaxf(sr[0], sr[1]), fmaxf(sr[2], sr[3])), fmaxf(fmaxf(sr[4], sr[5]), fmaxf(sr[6], sr[7])));
+          mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          const float m_new = fmaxf(m_run[qt], mx * scale);  // log2 units
+          const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[qt] - m_new);
+          l_run[qt] *= alpha;
+          m_run[qt] = m_new;
+#pragma unroll
+          for (int mt = 0; mt < C::MTD; ++mt) o[qt][mt] *= alpha;
+          const float m_use = m_new == -INFINITY ? 0.f : m_new;
+#pragma unroll
+          for (int x = 0; x < 8; ++x) pv[x] = __builtin_amdgcn_exp2f(__builtin_fmaf(sr[x], scale, -m_use));
+        }
+        Frag<T> pf, pl;
+        float psum = 0.f;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const float p = pv[x];
+          pf.set(x, p);
+          if constexpr (kSplitP) {
+            psum += p;
+            pl.set(x, p - pf.get(x));
+          } else {
+            psum += pf.get(x);  // normalise with the same (rounded) weights that multiply V
+          }
+        }
+        l_run[qt] += psum;
+#pragma unroll
+        for (int mt = 0; mt < C::MTD; ++mt) {
+          mma(o[qt][mt], vf[mt], pf);
+          if constexpr (kSplitP) mma(o[qt][mt], vf[mt], pl);
+        }
+      }
+    }
+  };
+
+  // Double-buffered walk: the copy of chunk q+1 is in flight while chunk q is computed; the
+  // barrier after each chunk both completes that copy and frees the buffer just read.
+  if (n_my > 0) issue(ch_begin, lds0);
+  __syncthreads();
+  for (int q = 0; q < n_my; q += 2) {
+    if (q + 1 < n_my) issue(ch_begin + q + 1, lds1);
+    if ((ch_begin + q + 1) * C::CHUNK > a.n_keys) {
+      fix_tail(ch_begin + q, lds0);
+      __syncthreads();
+    }
+    compute(ch_begin + q, lds0);
+    __syncthreads();
+    if (q + 1 >= n_my) break;
+    if (q + 2 < n_my) issue(ch_begin + q + 2, lds0);
+    if ((ch_begin + q + 2) * C::CHUNK > a.n_keys) {
+      fix_tail(ch_begin + q + 1, lds1);
+      __syncthreads();
+    }
+    compute(ch_begin + q + 1, lds1);
+    __syncthreads();
+  }
+
+  if (!active) return;
+  // partials: O^T tile register x of tile mt on this lane = (query q0 + 16 qt + row16, dh 16 mt + 4 quad + x)
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    float l_tot = l_run[qt];
     l_tot += __shfl_xor(l_tot, 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
+    const int mq = q0 + 16 * qt + row16;
     if (mq < a.q_rows) {
-      const int h = g * G + hs * HG + j;
       const int64_t row = ((int64_t)split * a.n_heads + h) * a.q_rows + mq;
       float* op = a.o_part + row * DH + quad * 4;
 #pragma unroll
-      for (int mt = 0; mt < MTD; ++mt) *reinterpret_cast<f32x4*>(op + 16 * mt) = o[j][mt];
+      for (int mt = 0; mt < C::MTD; ++mt) *reinterpret_cast<f32x4*>(op + 16 * mt) = o[qt][mt];
       if (quad == 0) {
-        a.ml_part[row * 2] = m_run[j];
+        a.ml_part[row * 2] = m_run[qt];
         a.ml_part[row * 2 + 1] = l_tot;
       }
     }
@@ -169,6 +325,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
 }
 
 // Merge split partials in split order and normalise: one thread per (row, head, 8 dh).
+// All splits' loads are issued before any is used (n_split <= kAttnMaxSplit).
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const int per_row = DH / 8;
@@ -179,22 +336,37 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const int64_t hm = i / per_row;
   const int h = (int)(hm % a.n_heads);
   const int m = (int)(hm / a.n_heads);
+  float ms[kAttnMaxSplit], ls[kAttnMaxSplit];
   float mx = -INFINITY;
-  for (int s = 0; s < a.n_split; ++s) {
-    const int64_t row = ((int64_t)s * a.n_heads + h) * a.q_rows + m;
-    mx = fmaxf(mx, a.ml_part[row * 2]);
+#pragma unroll
+  for (int s = 0; s < kAttnMaxSplit; ++s) {
+    ms[s] = -INFINITY;
+    ls[s] = 0.f;
+    if (s < a.n_split) {
+      const int64_t row = ((int64_t)s * a.n_heads + h) * a.q_rows + m;
+      const float2 p = *reinterpret_cast<const float2*>(a.ml_part + row * 2);
+      ms[s] = p.x;
+      ls[s] = p.y;
+      mx = fmaxf(mx, p.x);
+    }
   }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
-  for (int s = 0; s < a.n_split; ++s) {
-    const int64_t row = ((int64_t)s * a.n_heads + h) * a.q_rows + m;
-    const float ms = a.ml_part[row * 2];
-    if (ms == -INFINITY) continue;
-    const float f = exp2f(ms - mx);
-    L += a.ml_part[row * 2 + 1] * f;
-    const float* op = a.o_part + row * DH + c;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) acc[t] += op[t] * f;
+  for (int s = 0; s < kAttnMaxSplit; ++s) {
+    if (s < a.n_split && ms[s] != -INFINITY) {
+      const int64_t row = ((int64_t)s * a.n_heads + h) * a.q_rows + m;
+      const float f = exp2f(ms[s] - mx);
+      L += ls[s] * f;
+      const float* op = a.o_part + row * DH + c;
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(op);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(op + 4);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        acc[t] += x0[t] * f;
+        acc[t + 4] += x1[t] * f;
+      }
+    }
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
 #pragma unroll
@@ -202,34 +374,34 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   Vec8<T>::store((T*)a.o + (int64_t)m * a.n_heads * DH + h * DH + c, acc);
 }
 
+// Key splits: enough workgroups to cover the chip (~256), at least two key chunks per split.
 int attention_splits(int64_t n_keys, int q_rows, int n_heads, int n_kv_heads, int causal, int max_split) {
   (void)causal;
-  const int64_t n_chunks = (n_keys + 31) / 32;
-  const int base = n_kv_heads * ((q_rows + 15) / 16) * (n_heads / n_kv_heads >= 2 ? n_heads / n_kv_heads / 2 : 1);
-  int s = (2048 + base - 1) / base;
+  const int64_t n_ch = (n_keys + kAttnChunk - 1) / kAttnChunk;
+  const int n_wt = (n_heads / n_kv_heads) * ((q_rows + kAttnRows - 1) / kAttnRows);
+  const int base = n_kv_heads * ((n_wt + kAttnWaves - 1) / kAttnWaves);
+  int s = (256 + base - 1) / base;
   if (s > max_split) s = max_split;
-  int64_t by_chunks = n_chunks / 4;  // at least 4 chunks (128 keys) per split
+  if (s > kAttnMaxSplit) s = kAttnMaxSplit;
+  const int64_t by_chunks = n_ch / 2;
   if (s > by_chunks) s = (int)by_chunks;
   if (s < 1) s = 1;
   return s;
 }
 
-template <typename T, int DH, int HG>
+template <typename T, int DH>
 static void launch_attn_t(const AttnArgs& a, hipStream_t s) {
-  const int G = a.n_heads / a.n_kv_heads;
-  const int tasks = a.n_kv_heads * (G / HG) * a.n_split * ((a.q_rows + 15) / 16);
-  hipLaunchKernelGGL((k_attn<T, DH, HG>), dim3((tasks + 3) / 4), dim3(256), 0, s, a);
+  const int n_wt = (a.n_heads / a.n_kv_heads) * ((a.q_rows + kAttnRows - 1) / kAttnRows);
+  const int nb = (n_wt + kAttnWaves - 1) / kAttnWaves;
+  hipLaunchKernelGGL((k_attn<T, DH>), dim3(nb * a.n_split * a.n_kv_heads), dim3(64 * kAttnWaves), 0, s, a);
 }
 
 template <typename T>
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
-  const int G = a.n_heads / a.n_kv_heads;
-  const bool pair = G % 2 == 0;
-  if (a.head_dim == 128) {
-    if (pair) launch_attn_t<T, 128, 2>(a, s); else launch_attn_t<T, 128, 1>(a, s);
-  } else {
-    if (pair) launch_attn_t<T, 64, 2>(a, s); else launch_attn_t<T, 64, 1>(a, s);
-  }
+  if (a.head_dim == 128)
+    launch_attn_t<T, 128>(a, s);
+  else
+    launch_attn_t<T, 64>(a, s);
   return hipGetLastError();
 }
 
