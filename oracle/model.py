@@ -42,23 +42,27 @@ def silu(z: np.ndarray) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
 
-def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal_offset: Optional[int] = None) -> np.ndarray:
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal_offset: Optional[int] = None,
+              q_pos: Optional[np.ndarray] = None) -> np.ndarray:
     """softmax(Q K^T / sqrt(Dh)) V per query head, GQA head grouping, fp64.
 
     q: [Hq, n, Dh]; k, v: [Hkv, m, Dh].  With ``causal_offset = P`` query i sits at
-    absolute position P + i and sees keys 0..P+i; with None every query sees every
-    key — the bidirectional canvas attention of [P2] "How Diffusion Changes the
-    Equation" and [P5] "How block diffusion works" (no mask inside the canvas).
+    absolute position P + i (or ``q_pos[i]`` when given) and sees keys up to its own
+    position; with None every query sees every key — the bidirectional canvas
+    attention of [P2] "How Diffusion Changes the Equation" and [P5] "How block
+    diffusion works" (no mask inside the canvas).
     Returns [n, Hq*Dh] (token-major, heads concatenated).
     """
     hq, n, dh = q.shape
     hkv, m, _ = k.shape
     out = np.empty((n, hq, dh))
+    if causal_offset is not None and q_pos is None:
+        q_pos = causal_offset + np.arange(n)
     for h in range(hq):
         g = h * hkv // hq
         s = q[h] @ k[g].T / np.sqrt(dh)
         if causal_offset is not None:
-            allowed = np.arange(m)[None, :] <= (causal_offset + np.arange(n))[:, None]
+            allowed = np.arange(m)[None, :] <= np.asarray(q_pos)[:, None]
             s = np.where(allowed, s, -np.inf)
         s = s - s.max(axis=1, keepdims=True)
         p = np.exp(s)
@@ -202,6 +206,34 @@ class Model:
         if append:
             kv.append(l, k, v)
         return x, LayerTrace(idx=idx, w=rw, router_logits=rlog, gap=gap, hidden=x)
+
+    def layer_rows(self, l: int, x: np.ndarray, kv: KVCache, causal: bool, rows: np.ndarray):
+        """``layer(l, x, kv, causal, append=False)`` evaluated for the rows ``rows`` only.
+
+        Every row's keys and values are still formed (all of them take part in the
+        attention of the rows asked for); everything after the attention is per row.
+        Returns (x_out[rows], LayerTrace of those rows)."""
+        d, w, rnd = self.d, self.w["layers"][l], self.rnd
+        hq, hkv, dh = d.n_heads, d.n_kv_heads, d.head_dim
+        rows = np.asarray(rows, dtype=np.int64)
+        n = x.shape[0]
+        p0 = kv.k[l].shape[1]
+        xn = rnd(rmsnorm(x, w["attn_norm"], d.rms_eps))
+        kvp = xn @ w["wqkv"][hq * dh:].T
+        k = rnd(kvp[:, :hkv * dh]).reshape(n, hkv, dh).transpose(1, 0, 2)
+        v = rnd(kvp[:, hkv * dh:]).reshape(n, hkv, dh).transpose(1, 0, 2)
+        q = rnd(xn[rows] @ w["wqkv"][:hq * dh].T).reshape(len(rows), hq, dh).transpose(1, 0, 2)
+        k_all = np.concatenate([kv.k[l], k], axis=1)
+        v_all = np.concatenate([kv.v[l], v], axis=1)
+        o = rnd(attention(q, k_all, v_all, causal_offset=p0 if causal else None,
+                          q_pos=(p0 + rows) if causal else None))
+        xr = rnd(x[rows] + o @ w["wo"].T)
+        xn2 = rnd(rmsnorm(xr, w["ffn_norm"], d.rms_eps))
+        idx, rw, rlog, gap = route(xn2, w["w_router"], d.top_k)
+        y = moe_routed(xn2, idx, rw, w["w_gate_up"], w["w_down"], rnd)
+        ys = swiglu_ffn(xn2, w["ws_gate_up"], w["ws_down"], rnd)
+        xr = rnd(xr + ys + y)
+        return xr, LayerTrace(idx=idx, w=rw, router_logits=rlog, gap=gap, hidden=xr)
 
     def embed(self, tokens) -> np.ndarray:
         return self.w["embed"][np.asarray(tokens, dtype=np.int64)]

@@ -201,6 +201,38 @@ def test_attention_special_cases():
         np.testing.assert_allclose(out[0, h], v[h // 2, 0], atol=1e-14)
 
 
+def test_attention_explicit_query_positions():
+    """Queries given by explicit positions equal the same rows of the consecutive-position call (catches a
+    mask built from row numbers instead of positions)."""
+    rng = np.random.default_rng(5)
+    q = rng.normal(size=(4, 7, 3))
+    k = rng.normal(size=(2, 12, 3))
+    v = rng.normal(size=(2, 12, 3))
+    full = om.attention(q, k, v, causal_offset=5)
+    rows = np.array([6, 0, 3])
+    sub = om.attention(q[:, rows], k, v, causal_offset=5, q_pos=5 + rows)
+    np.testing.assert_allclose(sub, full[rows], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(sub, _attn_loops(q, k, v, 5)[rows], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_layer_rows_equals_full_layer(causal):
+    """The row-subset layer used for long-context sampling equals the full layer on those rows."""
+    dd = small_dims(dtype="bf16")
+    d = oracle_dims(dd)
+    m = oracle_model(dd)
+    kv = om.KVCache(1, d.n_kv_heads, d.head_dim)
+    rng = np.random.default_rng(6)
+    kv.k[0] = numerics.bf16_round(rng.normal(size=(d.n_kv_heads, 9, d.head_dim)))
+    kv.v[0] = numerics.bf16_round(rng.normal(size=(d.n_kv_heads, 9, d.head_dim)))
+    x = numerics.bf16_round(rng.normal(size=(10, d.d_model)))
+    full, trf = m.layer(0, x, kv, causal, append=False)
+    rows = np.array([9, 2, 5])
+    sub, trs = m.layer_rows(0, x, kv, causal, rows)
+    np.testing.assert_allclose(sub, full[rows], rtol=1e-12, atol=1e-12)
+    assert np.array_equal(trs.idx, trf.idx[rows])
+
+
 def test_rmsnorm_constant_input():
     for c in (0.5, -3.0, 1e-4):
         g = np.linspace(0.5, 2.0, 10)
