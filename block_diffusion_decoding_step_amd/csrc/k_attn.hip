@@ -36,16 +36,17 @@
 namespace dg {
 
 constexpr int kAttnWaves = 8;     // waves per workgroup
-constexpr int kAttnRows = 32;     // (head, query) rows per wave
+constexpr int kAttnQT = 2;        // 16-query tiles per wave
+constexpr int kAttnRows = 16 * kAttnQT;  // (head, query) rows per wave
 constexpr int kAttnChunk = 128;   // keys per LDS stage (four 32-key steps; two for fp32 at Dh 128)
 constexpr bool kAttnSplitP = true;   // bf16 P as high + remainder parts (two products)
 constexpr uint32_t kAttnLazyBits = 0x43800000u;  // 256.0f: probabilities stay below 2^8 of the reference
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <typename T, int DH>
+template <typename T, int DH, int NW = kAttnWaves, int SUBS_ = 4>
 struct AttnCfg {
-  static constexpr int SUBS = (sizeof(T) == 4 && DH == 128) ? 2 : kAttnChunk / 32;  // 32-key steps per chunk
+  static constexpr int SUBS = (sizeof(T) == 4 && DH == 128) ? (SUBS_ < 2 ? SUBS_ : 2) : SUBS_;  // 32-key steps per chunk
   static constexpr int CHUNK = 32 * SUBS;
   static constexpr int KF = DH / 32;                 // K fragments per 16-key tile (32-wide dh steps)
   static constexpr int MTD = DH / 16;                // 16-row dh tiles of O^T
@@ -55,16 +56,17 @@ struct AttnCfg {
   static constexpr int FB = kFragElems * (int)sizeof(T);
   static constexpr int STAGE = NF * FB;              // bytes per stage
   static constexpr int UPL = FB / 64 / 16;           // 16-byte units per lane per fragment
-  static constexpr int LOADS = STAGE / 16 / (64 * kAttnWaves);  // 1 KB copies per wave per stage
-  static_assert(LOADS * 16 * 64 * kAttnWaves == STAGE, "stage split");
+  static constexpr int LOADS = STAGE / 16 / (64 * NW);  // 1 KB copies per wave per stage
+  static_assert(LOADS * 16 * 64 * NW == STAGE, "stage split");
   static_assert(2 * STAGE <= 131072, "LDS");
 };
 
 // Workgroup -> (row block, split, KV head), row block fastest, XCD-aware so that
 // the row blocks and splits of one KV head share an L2.
-template <typename T, int DH>
-__global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
-  using C = AttnCfg<T, DH>;
+template <typename T, int DH, int NW, int SUBS, int QT>
+__global__ __launch_bounds__(64 * NW, 1) void k_attn(AttnArgs a) {
+  using C = AttnCfg<T, DH, NW, SUBS>;
+  constexpr int ROWS = 16 * QT;  // (head, query) rows per wave
   constexpr bool kSplitP = sizeof(T) == 2 && kAttnSplitP;
   constexpr int EPU = 16 / (int)sizeof(T);  // elements per 16-byte unit
   __shared__ uint4 lds0[C::STAGE / 16];
@@ -72,28 +74,28 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
   const int lane = lane_id(), w = wave_id();
   const int row16 = lane & 15, quad = lane >> 4;
   const int G = a.n_heads / a.n_kv_heads;
-  const int qt32 = (a.q_rows + kAttnRows - 1) / kAttnRows;   // 32-query tiles per head
+  const int qt32 = (a.q_rows + ROWS - 1) / ROWS;   // 32-query tiles per head
   const int n_wt = G * qt32;                                 // wave tasks per KV head
-  const int nb = (n_wt + kAttnWaves - 1) / kAttnWaves;       // row blocks per KV head
+  const int nb = (n_wt + NW - 1) / NW;       // row blocks per KV head
   const int n_wg = nb * a.n_split * a.n_kv_heads;
   const int id = xcd_remap(blockIdx.x, n_wg);
   const int rb = id % nb;
   const int split = (id / nb) % a.n_split;
   const int g = id / (nb * a.n_split);
 
-  const int wt = rb * kAttnWaves + w;
+  const int wt = rb * NW + w;
   const bool active = wt < n_wt;
   const int j = active ? wt / qt32 : 0;           // head within the group
-  const int q0 = active ? (wt % qt32) * kAttnRows : 0;
+  const int q0 = active ? (wt % qt32) * ROWS : 0;
   const int h = g * G + j;
 
   // keys this workgroup may need: all of them, or (causal) up to its furthest query
   int64_t key_end = a.n_keys;
   if (a.causal) {
     int qmax = 0;
-    for (int x = 0; x < kAttnWaves; ++x) {
-      const int wx = rb * kAttnWaves + x;
-      if (wx < n_wt) qmax = max(qmax, min((wx % qt32) * kAttnRows + kAttnRows - 1, a.q_rows - 1));
+    for (int x = 0; x < NW; ++x) {
+      const int wx = rb * NW + x;
+      if (wx < n_wt) qmax = max(qmax, min((wx % qt32) * ROWS + ROWS - 1, a.q_rows - 1));
     }
     key_end = imin64(key_end, a.q_pos0 + qmax + 1);
   }
@@ -131,7 +133,7 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
     const int64_t c0 = ch * C::CHUNK;
 #pragma unroll
     for (int jj = 0; jj < C::LOADS; ++jj) {
-      const int u0 = (jj * kAttnWaves + w) * 64;
+      const int u0 = (jj * NW + w) * 64;
       __builtin_amdgcn_global_load_lds((const void*)unit_src(c0, u0 + lane), (lds_void*)(buf + u0), 16, 0, 0);
     }
   };
@@ -140,7 +142,7 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
     const int64_t c0 = ch * C::CHUNK;
 #pragma unroll
     for (int jj = 0; jj < C::LOADS; ++jj) {
-      const int u = (jj * kAttnWaves + w) * 64 + lane;
+      const int u = (jj * NW + w) * 64 + lane;
       const int f = u / (64 * C::UPL), qq = u % (64 * C::UPL);
       if (f < C::NKF) continue;
       const int l = qq / C::UPL, part = qq % C::UPL;
@@ -157,10 +159,10 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
     }
   };
 
-  Frag<T> qf[2][C::KF];
-  int64_t my_pos[2];
+  Frag<T> qf[QT][C::KF];
+  int64_t my_pos[QT];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < QT; ++qt) {
     const int mq = q0 + 16 * qt + row16;
     my_pos[qt] = a.q_pos0 + mq;
     const T* qrow = (const T*)a.q + ((int64_t)h * a.q_rows + min(mq, a.q_rows - 1)) * DH + quad * 8;
@@ -168,12 +170,12 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
     for (int ks = 0; ks < C::KF; ++ks) qf[qt][ks].load(qrow + 32 * ks);
   }
   const float scale = 1.4426950408889634f / sqrtf((float)DH);
-  const int64_t wave_last = a.q_pos0 + min(q0 + kAttnRows - 1, a.q_rows - 1);  // furthest key this wave sees
+  const int64_t wave_last = a.q_pos0 + min(q0 + ROWS - 1, a.q_rows - 1);  // furthest key this wave sees
 
-  float m_run[2], l_run[2];
-  f32x4 o[2][C::MTD];
+  float m_run[QT], l_run[QT];
+  f32x4 o[QT][C::MTD];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < QT; ++qt) {
     m_run[qt] = -INFINITY;
     l_run[qt] = 0.f;
 #pragma unroll
@@ -181,14 +183,14 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
   }
 
   // S^T tiles of both query tiles for 32-key step `sub` of a staged chunk
-  auto scores = [&](const T* base, int sub, f32x4 (&sv)[2][2]) {
+  auto scores = [&](const T* base, int sub, f32x4 (&sv)[QT][2]) {
     Frag<T> kf[2][C::KF];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int ks = 0; ks < C::KF; ++ks) kf[i][ks].load(base + ((sub * 2 + i) * C::KF + ks) * kFragElems);
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
+    for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         sv[qt][i] = zero4();
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
     for (int sub = 0; sub < C::SUBS; ++sub) {
       const int64_t kbase = c0 + 32 * sub;
       if (kbase >= a.n_keys || (a.causal && kbase > wave_last)) continue;  // wave-uniform
-      f32x4 svc[2][2];
+      f32x4 svc[QT][2];
       scores(base, sub, svc);
       Frag<T> vf[C::MTD];
 #pragma unroll
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
       const int rel = (int)imin64(a.n_keys - kbase, 32);
       const bool full = rel == 32 && (!a.causal || kbase + 31 <= a.q_pos0 + q0);
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
+      for (int qt = 0; qt < QT; ++qt) {
         // lane holds raw scores of keys kbase + 8*quad + x, x = 0..7, of its query
         float sr[8];
 #pragma unroll
@@ -306,7 +308,7 @@ __global__ __launch_bounds__(512, 1) void k_attn(AttnArgs a) {
   if (!active) return;
   // partials: O^T tile register x of tile mt on this lane = (query q0 + 16 qt + row16, dh 16 mt + 4 quad + x)
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < QT; ++qt) {
     float l_tot = l_run[qt];
     l_tot += __shfl_xor(l_tot, 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
@@ -393,7 +395,8 @@ template <typename T, int DH>
 static void launch_attn_t(const AttnArgs& a, hipStream_t s) {
   const int n_wt = (a.n_heads / a.n_kv_heads) * ((a.q_rows + kAttnRows - 1) / kAttnRows);
   const int nb = (n_wt + kAttnWaves - 1) / kAttnWaves;
-  hipLaunchKernelGGL((k_attn<T, DH>), dim3(nb * a.n_split * a.n_kv_heads), dim3(64 * kAttnWaves), 0, s, a);
+  hipLaunchKernelGGL((k_attn<T, DH, kAttnWaves, kAttnChunk / 32, kAttnQT>), dim3(nb * a.n_split * a.n_kv_heads),
+                     dim3(64 * kAttnWaves), 0, s, a);
 }
 
 template <typename T>
