@@ -212,6 +212,9 @@ def main() -> int:
     torch.cuda.synchronize()
     ri = ridx.cpu().numpy()
     experts_hit = float(np.mean([len(np.unique(ri[l])) for l in range(d.n_layers)]))
+    counts = [np.bincount(ri[l].ravel(), minlength=d.n_experts) for l in range(d.n_layers)]
+    expert_tiles = float(np.mean([np.sum((c + 31) // 32) for c in counts]))  # 32-row tiles (weight reads)
+    max_pairs = int(max(c.max() for c in counts))
 
     if args.copy_calibration_mib > 0:
         # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters give the scale of the byte counters
@@ -254,7 +257,8 @@ def main() -> int:
         "roofline": {"kernel": "k_moe_gate_up", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "bytes_per_launch": g_bytes, "avg_launch_ms": round(g_avg, 5),
-                     "launches": g_n, "experts_hit_per_layer": experts_hit},
+                     "launches": g_n, "experts_hit_per_layer": experts_hit,
+                     "expert_tiles_per_layer": expert_tiles, "max_pairs_per_expert": max_pairs},
         "kernels": {k: {"ms_per_pass": round(v[0] / T, 4), "launches_per_pass": v[1] / T}
                     for k, v in sorted(breakdown.items(), key=lambda kv_: -kv_[1][0])},
     }

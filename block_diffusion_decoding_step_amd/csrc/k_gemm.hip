@@ -173,7 +173,7 @@ hipError_t launch_gemm(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------- routed experts
-// grid = (column tiles, max tiles).  Tile (e, p0, rows): pairs p0 .. p0+rows-1 all
+// Tile (e, p0, rows): pairs p0 .. p0+rows-1 all
 // routed to expert e (rows <= 32, so one or two 16-row M-tiles).
 //
 // gate_up: a workgroup owns 64 H columns of expert e, i.e. 4 gate and the 4
@@ -231,13 +231,25 @@ __device__ __forceinline__ void moe_gate_up_body(const MoeArgs& a, f32x4 (*red)[
   }
 }
 
+// Routed-expert grids are 1-D: 8 * ceil(max_tiles / 8) * ncols workgroups.  Workgroup b runs on XCD
+// b % 8 (round-robin dispatch); XCD x takes tiles x, x + 8, ... (of the device-side, data-dependent
+// tile count) with all ncols column blocks of a tile back to back, so the workgroups that share a
+// tile's activation rows share one L2 and every XCD gets an equal share of the tiles.
+__device__ __forceinline__ bool moe_tile_col(int ncols, int n_tiles, int& tile, int& col) {
+  const int b = (int)blockIdx.x, x = b & 7, i = b >> 3;
+  tile = x + 8 * (i / ncols);
+  col = i % ncols;
+  return tile < n_tiles;
+}
+static inline int moe_grid(int max_tiles, int ncols) { return 8 * ((max_tiles + 7) / 8) * ncols; }
+
 template <typename T>
 __global__ __launch_bounds__(256, 2) void k_moe_gate_up(MoeArgs a) {
   __shared__ f32x4 red[4][8][64];
-  const int tile_i = blockIdx.y;
-  if (tile_i >= *a.n_tiles) return;
+  int tile_i, col;
+  if (!moe_tile_col((a.F + 63) / 64, min(*a.n_tiles, a.max_tiles), tile_i, col)) return;
   const int4 tile = a.tiles[tile_i];
-  const int c0 = blockIdx.x * 64;
+  const int c0 = col * 64;
   if (tile.z > 16)
     moe_gate_up_body<T, 2>(a, red, tile.x, tile.y, tile.z, c0);
   else
@@ -288,10 +300,10 @@ __device__ __forceinline__ void moe_down_body(const MoeArgs& a, int e, int p0, i
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_moe_down(MoeArgs a) {
-  const int tile_i = blockIdx.y;
-  if (tile_i >= *a.n_tiles) return;
+  int tile_i, col;
+  if (!moe_tile_col((a.d + 255) / 256, min(*a.n_tiles, a.max_tiles), tile_i, col)) return;
   const int4 tile = a.tiles[tile_i];
-  const int c0 = blockIdx.x * 256 + wave_id() * 64;
+  const int c0 = col * 256 + wave_id() * 64;
   if (c0 >= a.d) return;
   if (tile.z > 16)
     moe_down_body<T, 2>(a, tile.x, tile.y, tile.z, c0);
@@ -301,14 +313,12 @@ __global__ __launch_bounds__(256) void k_moe_down(MoeArgs a) {
 
 template <typename T>
 hipError_t launch_moe_gate_up(const MoeArgs& a, hipStream_t s) {
-  dim3 grid((a.F + 63) / 64, a.max_tiles);
-  hipLaunchKernelGGL(k_moe_gate_up<T>, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_moe_gate_up<T>, dim3(moe_grid(a.max_tiles, (a.F + 63) / 64)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 template <typename T>
 hipError_t launch_moe_down(const MoeArgs& a, hipStream_t s) {
-  dim3 grid((a.d + 255) / 256, a.max_tiles);
-  hipLaunchKernelGGL(k_moe_down<T>, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_moe_down<T>, dim3(moe_grid(a.max_tiles, (a.d + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
