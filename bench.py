@@ -1,25 +1,32 @@
 #!/usr/bin/env python3
 """Benchmark of the block-diffusion denoising step on one MI355X.
 
-Workload (N=1): the 30-layer bf16 MoE model (d 2816, 16 q / 8 KV heads of dim
-128, 128 experts top-8 + 1 shared, 262144-token tied vocabulary) with a
-4096-token uniform-random prompt prefilled into the KV cache, random-init
-weights from the seeded generator.  One timed step is one whole 256-slot
-block at a fixed T=10: the initial random canvas, 10 denoising passes, 10 stop
-checks, 9 keep/re-randomise updates, and the commit of the block into the KV
-cache (the cache length is reset to the prompt before each step, so every step
-does identical work).  Reported value: canvas tokens per second = 256 / (block
-time); also ms per denoising pass.
+Workload (N=1, default full_loop_bf16): the 30-layer bf16 MoE model (d 2816,
+16 q / 8 KV heads of dim 128, 128 experts top-8 + 1 shared, 262144-token tied
+vocabulary) with a 4096-token uniform-random prompt prefilled into the KV
+cache, random-init weights from the seeded generator.  One timed step is one
+whole 256-slot block at a fixed T=10: the initial random canvas, 10 denoising
+passes, 10 stop checks, 9 keep/re-randomise updates, and the commit of the
+block into the KV cache (the cache length is reset to the prompt before each
+step, so every step does identical work).  With --workload long_context_bf16
+the prompt is 131072 tokens and one step is 4 consecutive blocks, each
+committed before the next.  Reported value: canvas tokens per second =
+256 * blocks / (step time); also ms per denoising pass.
 
 Extra objects on the JSON line:
-  roofline     — the dominant kernel (routed-expert gate/up projection),
-                 algorithmic bytes per launch / its average duration from HIP
-                 events recorded on the launch stream during the timed region;
-                 traffic from the committed rocprofv3 counter summary when it
-                 matches the current kernel source, else null
+  roofline     — the dominant kernel (routed-expert gate/up projection, HBM
+                 bound; attention, matrix-core bound, on the long-context
+                 workload): algorithmic bytes or FLOPs per launch / its average
+                 duration from HIP events recorded on the launch stream during
+                 the timed region; traffic from the committed rocprofv3 counter
+                 summary when it matches the current kernel source, else null
   cpu_baseline — the CPU oracle timed on a bounded sample (one layer of the
-                 pass plus the head on 16 slots), extrapolated to a block
-  kernels      — per-kernel-class time per pass from an instrumented extra block
+                 pass plus the head on a few slots), extrapolated to a step
+  kernels      — per-kernel-class time of one instrumented denoising pass
+  mfma, hbm    — achieved bf16 matrix-core TFLOP/s of attention, the expert
+                 GEMMs, the dense projections and the vocab GEMM, and HBM GB/s
+                 of the expert-weight stream, from that pass, as fractions of
+                 MI355X peak (algorithmic FLOPs / bytes)
 """
 from __future__ import annotations
 
@@ -36,6 +43,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "canvas tokens/sec at batch 1 (256-slot block, T=10) + ms/denoising step"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moe_gate_up_traffic.json")
 
 
@@ -58,6 +66,28 @@ def gate_up_bytes(d, experts_hit: float, pairs: int) -> float:
     x = d.canvas * d.d_model * 2
     h = pairs * d.ffn_expert * 2
     return w + x + h
+
+
+def attention_flops(d, keys: int, causal: bool) -> float:
+    """Algorithmic FLOPs of one attention launch over the canvas: Q K^T and P V for every visible key."""
+    if causal:  # query i (0-based) of the block sees keys - S + i + 1 keys
+        visible = d.canvas * (keys - d.canvas) + d.canvas * (d.canvas + 1) / 2
+    else:
+        visible = d.canvas * keys
+    return 4.0 * d.n_heads * d.head_dim * visible
+
+
+def pass_flops(d, keys: int, pairs: int) -> dict:
+    """Algorithmic FLOPs of one denoising pass by kernel class."""
+    S, L = d.canvas, d.n_layers
+    qkv = 2 * S * d.d_model * (d.n_heads + 2 * d.n_kv_heads) * d.head_dim
+    o = 2 * S * d.n_heads * d.head_dim * d.d_model
+    shared = 2 * S * d.d_model * 3 * d.ffn_shared
+    router = 2 * S * d.d_model * d.n_experts
+    return {"attention": L * attention_flops(d, keys, False),
+            "experts": L * 2 * pairs * 3 * d.ffn_expert * d.d_model,
+            "dense": L * (qkv + o + shared + router),
+            "vocab_head": 2 * S * d.vocab * d.d_model}
 
 
 def read_traffic(bytes_per_launch: float):
@@ -170,26 +200,31 @@ def main() -> int:
     sampler = dg.make_sampler(wl.n_new, fixed_steps=T, seed=recipe.INPUT_SEED)
     tokens = torch.empty(d.canvas, dtype=torch.int32, device="cuda")
 
-    def block(i):
-        kv.len = P
-        return dg.dg_generate_block(cfg, weights, kv, sampler, i, tokens, ws, ws_bytes)
+    blocks = wl.blocks
 
-    log(f"bench: warmup {args.warmup} blocks")
+    def step(i):
+        """One timed step: `blocks` consecutive blocks, each committed before the next."""
+        kv.len = P
+        return [dg.dg_generate_block(cfg, weights, kv, sampler, i * blocks + b, tokens, ws, ws_bytes)
+                for b in range(blocks)]
+
+    log(f"bench: warmup {args.warmup} steps of {blocks} block(s)")
     for i in range(args.warmup):
-        block(i)
+        step(i)
     torch.cuda.synchronize()
 
-    # timed region: K blocks; HIP events around the dominant kernel's launches on the launch stream
-    dg.dg_timing_start(["moe_gate_up"])
+    # timed region: K steps; HIP events around the dominant kernel's launches on the launch stream
+    dom = "attention" if wl.prefix > 65536 else "moe_gate_up"
+    dg.dg_timing_start([dom])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    statuses = [block(i) for i in range(args.steps)]
+    statuses = [st for i in range(args.steps) for st in step(i)]
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t0
     tim = dg.dg_timing_stop()
     assert all(s.steps == T and s.reason == dg.DG_STOP_FIXED for s in statuses)
     block_ms = t_total / args.steps * 1e3
-    value = d.canvas * args.steps / t_total
+    value = d.canvas * blocks * args.steps / t_total
 
     # ms per denoising pass alone (the same kernels, no update/commit)
     canvas = torch.empty(d.canvas, dtype=torch.int32, device="cuda")
@@ -224,17 +259,51 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    # per-kernel breakdown from one extra instrumented block (outside the timed region)
+    # per-kernel breakdown from one extra instrumented denoising pass (outside the timed region)
+    kv.len = P
     dg.dg_timing_start(list(dg.KERNELS))
-    block(0)
+    dg.dg_denoise_step(cfg, weights, kv, canvas, 1.0, pred, conf, ent, None, ws, ws_bytes)
     torch.cuda.synchronize()
     breakdown = dg.dg_timing_stop()
 
-    g_ms, g_n = tim["moe_gate_up"]
+    pairs = d.canvas * d.top_k
+    fl = pass_flops(d, P + d.canvas, pairs)
+    cls = {"attention": ("attention", "attn_merge"), "experts": ("moe_gate_up", "moe_down"),
+           "dense": ("gemm_qkv", "gemm_o", "gemm_router", "shared_gate_up", "shared_down"),
+           "vocab_head": ("vocab_head", "head_merge")}
+    mfma = {}
+    for name, ks in cls.items():
+        ms = sum(breakdown.get(k, (0.0, 0))[0] for k in ks)
+        tf = fl[name] / (ms * 1e-3) / 1e12 if ms > 0 else 0.0
+        mfma[name] = {"tflops": round(tf, 1), "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "ms_per_pass": round(ms, 4),
+                      "kernels": list(ks)}
+    ex_ms = sum(breakdown.get(k, (0.0, 0))[0] for k in ("moe_gate_up", "moe_down"))
+    ex_bytes = d.n_layers * experts_hit * 3 * d.ffn_expert * d.d_model * 2
+    hbm = {"experts": {"gbs": round(ex_bytes / (ex_ms * 1e-3) / 1e9, 1),
+                       "frac": round(ex_bytes / (ex_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "bytes_per_pass": ex_bytes, "kernels": ["moe_gate_up", "moe_down"]}}
+
+    g_ms, g_n = tim[dom]
     g_avg = g_ms / g_n
-    g_bytes = gate_up_bytes(d, experts_hit, d.canvas * d.top_k)
-    achieved = g_bytes / (g_avg * 1e-3) / 1e9
-    traffic = read_traffic(g_bytes)
+    if dom == "moe_gate_up":
+        g_work = gate_up_bytes(d, experts_hit, pairs)
+        achieved = g_work / (g_avg * 1e-3) / 1e9
+        roof = {"kernel": "k_moe_gate_up", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(g_work),
+                "bytes_per_launch": g_work}
+    else:
+        # launches of one step: per block b, T passes over P_b + S keys and one causal commit
+        works = []
+        for b in range(blocks):
+            pb = P + b * d.canvas
+            works += [attention_flops(d, pb + d.canvas, False)] * T + [attention_flops(d, pb + d.canvas, True)]
+        g_work = sum(works) / len(works)
+        achieved = g_work / (g_avg * 1e-3) / 1e12
+        roof = {"kernel": "k_attn", "bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": g_work}
+    roof.update({"avg_launch_ms": round(g_avg, 5), "launches": g_n, "experts_hit_per_layer": experts_hit,
+                 "expert_tiles_per_layer": expert_tiles, "max_pairs_per_expert": max_pairs})
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -250,16 +319,15 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "description": wl.description,
-                   "canvas": d.canvas, "prefix": wl.prefix, "T": T, "batch": 1,
-                   "step": "one block: 10 passes + stop checks + 9 keep/re-randomise updates + commit",
+                   "canvas": d.canvas, "prefix": wl.prefix, "T": T, "batch": 1, "blocks_per_step": blocks,
+                   "step": (f"{blocks} block(s), each: 10 passes + stop checks + 9 keep/re-randomise updates "
+                            f"+ commit"),
                    "canvas_tokens_per_s_without_commit": round(d.canvas / (T * pass_ms * 1e-3), 2),
                    "prefill_s": round(t_prefill, 3)},
-        "roofline": {"kernel": "k_moe_gate_up", "bound": "hbm", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "bytes_per_launch": g_bytes, "avg_launch_ms": round(g_avg, 5),
-                     "launches": g_n, "experts_hit_per_layer": experts_hit,
-                     "expert_tiles_per_layer": expert_tiles, "max_pairs_per_expert": max_pairs},
-        "kernels": {k: {"ms_per_pass": round(v[0] / T, 4), "launches_per_pass": v[1] / T}
+        "roofline": roof,
+        "mfma": mfma,
+        "hbm": hbm,
+        "kernels": {k: {"ms_per_pass": round(v[0], 4), "launches_per_pass": v[1]}
                     for k, v in sorted(breakdown.items(), key=lambda kv_: -kv_[1][0])},
     }
     if not args.no_cpu_baseline:
