@@ -92,10 +92,11 @@ inline bool aligned16(const void* p) { return p && ((uintptr_t)p & 15u) == 0; }
 
 // ------------------------------------------------------------------ workspace
 struct Ws {
-  void* X;
-  void* Xn;
+  void* X;   // residual stream [M, d]
+  void* Xn;  // normalised rows [M, d] (routed-expert gathers, head)
+  void* Xt;  // normalised rows, fragment-tiled (dense GEMM A operand)
   void* Q;
-  void* O;
+  void* O;   // attention output, fragment-tiled
   float* opart;
   float* mlpart;
   float* rlog;
@@ -137,10 +138,12 @@ Ws carve(const dg_config* c, int64_t M, char* base) {
   const int64_t prow = std::max<int64_t>(kPartialRows, M);
   const int64_t pairs = M * k;
   w.rows = M;
+  const int64_t Mp = (M + 15) / 16 * 16;  // rows of the fragment-tiled activations
   w.X = take(M * d * es);
   w.Xn = take(M * d * es);
+  w.Xt = take(Mp * d * es);
   w.Q = take(M * hd * es);
-  w.O = take(M * hd * es);
+  w.O = take(Mp * hd * es);
   w.opart = (float*)take(prow * hd * 4);
   w.mlpart = (float*)take(prow * c->n_heads * 2 * 4);
   w.rlog = (float*)take(M * E * 4);
@@ -154,7 +157,7 @@ Ws carve(const dg_config* c, int64_t M, char* base) {
   w.n_tiles = (int32_t*)take(4);
   w.Hp = take(pairs * c->ffn_expert * es);
   w.Yp = take(pairs * d * es);
-  w.Hs = take(M * c->ffn_shared * es);
+  w.Hs = take(Mp * c->ffn_shared * es);
   w.Ys = take(M * d * es);
   w.hpart = (float4*)take((size_t)head_groups(c->vocab) * M * 16);
   w.status = (dg_block_status*)take(sizeof(dg_block_status));
@@ -243,9 +246,10 @@ int layer_t(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int
   char* vbase = (char*)kv->v + (size_t)l * hkv * dh * kv->capacity * es;
 
   // attention half
-  DG_LAUNCH(DG_K_RMSNORM, s, launch_rmsnorm<T>((const T*)ws.X, (const T*)L.attn_norm, (T*)ws.Xn, Mi, d, c->rms_eps, s));
+  DG_LAUNCH(DG_K_RMSNORM, s, launch_rmsnorm<T>((const T*)ws.X, (const T*)L.attn_norm, nullptr, (T*)ws.Xt, Mi, d,
+                                                c->rms_eps, s));
   GemmArgs g{};
-  g.A = ws.Xn; g.B = L.wqkv; g.M = Mi; g.N = (hq + 2 * hkv) * dh; g.K = d; g.lda = d; g.ldb = d;
+  g.A = ws.Xt; g.a_tiled = 1; g.B = L.wqkv; g.M = Mi; g.N = (hq + 2 * hkv) * dh; g.K = d; g.lda = d; g.ldb = d;
   g.q = ws.Q; g.kc = kbase; g.vc = vbase; g.n_heads = hq; g.n_kv_heads = hkv; g.head_dim = dh; g.q_rows = Mi;
   g.cap = kv->capacity; g.pos0 = pos0;
   DG_LAUNCH(DG_K_GEMM_QKV, s, launch_gemm<T>(GemmEpi::QKV, g, s));
@@ -260,13 +264,14 @@ int layer_t(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int
   DG_LAUNCH(DG_K_ATTN_MERGE, s, launch_attention_merge<T>(at, s));
 
   g = GemmArgs{};
-  g.A = ws.O; g.B = L.wo; g.C = ws.X; g.M = Mi; g.N = d; g.K = hq * dh; g.lda = hq * dh; g.ldb = hq * dh; g.ldc = d;
+  g.A = ws.O; g.a_tiled = 1; g.B = L.wo; g.C = ws.X; g.M = Mi; g.N = d; g.K = hq * dh; g.lda = hq * dh; g.ldb = hq * dh; g.ldc = d;
   DG_LAUNCH(DG_K_GEMM_O, s, launch_gemm<T>(GemmEpi::Resid, g, s));
 
   // MoE half ([P2] "Architecture Details": 8 routed experts of 128, plus 1 shared)
-  DG_LAUNCH(DG_K_RMSNORM, s, launch_rmsnorm<T>((const T*)ws.X, (const T*)L.ffn_norm, (T*)ws.Xn, Mi, d, c->rms_eps, s));
+  DG_LAUNCH(DG_K_RMSNORM, s, launch_rmsnorm<T>((const T*)ws.X, (const T*)L.ffn_norm, (T*)ws.Xn, (T*)ws.Xt, Mi, d,
+                                                c->rms_eps, s));
   g = GemmArgs{};
-  g.A = ws.Xn; g.B = L.w_router; g.C = ws.rlog; g.M = Mi; g.N = E; g.K = d; g.lda = d; g.ldb = d; g.ldc = E;
+  g.A = ws.Xt; g.a_tiled = 1; g.B = L.w_router; g.C = ws.rlog; g.M = Mi; g.N = E; g.K = d; g.lda = d; g.ldb = d; g.ldc = E;
   DG_LAUNCH(DG_K_GEMM_ROUTER, s, launch_gemm<T>(GemmEpi::StoreF32, g, s));
   DG_LAUNCH(DG_K_ROUTER_TOPK, s, launch_router_topk(ws.rlog, Mi, E, k, ws.ridx, ws.rw, s));
   DG_LAUNCH(DG_K_MOE_PERMUTE, s, launch_moe_permute(ws.ridx, Mi, E, k, ws.counts, ws.offsets, ws.perm, ws.pos, ws.tiles, ws.n_tiles, s));
@@ -279,11 +284,11 @@ int layer_t(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int
   DG_LAUNCH(DG_K_MOE_DOWN, s, launch_moe_down<T>(ma, s));
 
   g = GemmArgs{};
-  g.A = ws.Xn; g.B = L.ws_gate_up; g.C = ws.Hs; g.M = Mi; g.N = c->ffn_shared; g.K = d; g.lda = d; g.ldb = d;
+  g.A = ws.Xt; g.a_tiled = 1; g.B = L.ws_gate_up; g.C = ws.Hs; g.M = Mi; g.N = c->ffn_shared; g.K = d; g.lda = d; g.ldb = d;
   g.ldc = c->ffn_shared;
   DG_LAUNCH(DG_K_SHARED_GATE_UP, s, launch_gemm<T>(GemmEpi::SwiGLU, g, s));
   g = GemmArgs{};
-  g.A = ws.Hs; g.B = L.ws_down; g.C = ws.Ys; g.M = Mi; g.N = d; g.K = c->ffn_shared; g.lda = c->ffn_shared;
+  g.A = ws.Hs; g.a_tiled = 1; g.B = L.ws_down; g.C = ws.Ys; g.M = Mi; g.N = d; g.K = c->ffn_shared; g.lda = c->ffn_shared;
   g.ldb = c->ffn_shared; g.ldc = d;
   DG_LAUNCH(DG_K_SHARED_DOWN, s, launch_gemm<T>(GemmEpi::Store, g, s));
 
@@ -313,11 +318,11 @@ int head(const dg_config* c, const dg_weights* w, int64_t M, float inv_temp, int
   h.n_groups = head_groups(c->vocab); h.beta_log2e = inv_temp * 1.4426950408889634f;
   h.pred = pred; h.conf = conf; h.ent = ent;
   if (c->dtype == DG_BF16) {
-    DG_LAUNCH(DG_K_RMSNORM, s, launch_rmsnorm<bf16>((const bf16*)ws.X, (const bf16*)w->final_norm, (bf16*)ws.Xn, (int)M, c->d_model,
+    DG_LAUNCH(DG_K_RMSNORM, s, launch_rmsnorm<bf16>((const bf16*)ws.X, (const bf16*)w->final_norm, (bf16*)ws.Xn, nullptr, (int)M, c->d_model,
                                 c->rms_eps, s));
     DG_LAUNCH(DG_K_VOCAB_HEAD, s, launch_vocab_head<bf16>(h, s));
   } else {
-    DG_LAUNCH(DG_K_RMSNORM, s, launch_rmsnorm<float>((const float*)ws.X, (const float*)w->final_norm, (float*)ws.Xn, (int)M, c->d_model,
+    DG_LAUNCH(DG_K_RMSNORM, s, launch_rmsnorm<float>((const float*)ws.X, (const float*)w->final_norm, (float*)ws.Xn, nullptr, (int)M, c->d_model,
                                  c->rms_eps, s));
     DG_LAUNCH(DG_K_VOCAB_HEAD, s, launch_vocab_head<float>(h, s));
   }

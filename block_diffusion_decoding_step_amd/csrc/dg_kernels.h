@@ -40,8 +40,9 @@ template <typename T>
 hipError_t launch_embed(const int32_t* tok, const T* E, T* X, int M, int d, int V, hipStream_t s);
 template <typename T>
 hipError_t launch_pack(const T* src, T* dst, int64_t batch, int64_t rows, int64_t cols, hipStream_t s);
+// Y (row-major) and / or Yt (fragment-tiled, rows padded to 16); either may be null
 template <typename T>
-hipError_t launch_rmsnorm(const T* X, const T* g, T* Y, int M, int d, float eps, hipStream_t s);
+hipError_t launch_rmsnorm(const T* X, const T* g, T* Y, T* Yt, int M, int d, float eps, hipStream_t s);
 hipError_t launch_router_topk(const float* logits, int M, int E, int k, int32_t* idx, float* w, hipStream_t s);
 hipError_t launch_moe_permute(const int32_t* idx, int M, int E, int k, int32_t* counts, int32_t* offsets,
                               int32_t* perm, int32_t* pos, int4* tiles, int32_t* n_tiles, hipStream_t s);
@@ -58,7 +59,8 @@ hipError_t launch_canvas_update(const int32_t* pred, const float* conf, int S, i
 enum class GemmEpi { Store, StoreF32, Resid, QKV, SwiGLU };
 
 struct GemmArgs {
-  const void* A;   // [M, K] rows, lda elements apart
+  const void* A;   // [M, K] rows, lda elements apart; or fragment-tiled (a_tiled, rows padded to 16)
+  int a_tiled;
   const void* B;   // [N, K] rows (weights, [out, in])
   void* C;         // output (meaning depends on the epilogue)
   int M, N, K;
@@ -70,7 +72,8 @@ struct GemmArgs {
   int n_heads, n_kv_heads, head_dim;
   int q_rows;
   int64_t cap, pos0;
-  // SwiGLU epilogue: N = F (output width); B holds 2F rows: gate rows then up rows
+  // SwiGLU epilogue: N = F (output width); B holds 2F rows: gate rows then up rows; the output
+  // [M, F] is stored fragment-tiled (its only reader is the next GEMM's A operand)
 };
 
 template <typename T>
@@ -98,7 +101,7 @@ struct AttnArgs {
   const void* vc;     // [Hkv][Dh][cap]
   float* o_part;      // [n_split][Hq][q_rows][Dh]
   float* ml_part;     // [n_split][Hq][q_rows][2]  (running max in log2 units, sum)
-  void* o;            // [q_rows][Hq*Dh]
+  void* o;            // [q_rows][Hq*Dh], fragment-tiled (rows padded to 16)
   int q_rows;         // M
   int n_heads, n_kv_heads, head_dim;
   int64_t cap;

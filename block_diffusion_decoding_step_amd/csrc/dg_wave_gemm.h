@@ -8,6 +8,12 @@ namespace dg {
 // Fragment-tiled matrices: 16-row x 32-column blocks of kFragElems elements.
 constexpr int kFragElems = 512;
 
+// Element (r, c) of a fragment-tiled [rows, K] matrix (K a multiple of 32, rows padded to 16): the
+// 16-row x 32-column block (r/16, c/32) is one contiguous fragment in the matrix cores' operand order.
+__device__ __forceinline__ int64_t tiled_offset(int64_t r, int c, int K) {
+  return ((r >> 4) * (K >> 5) + (c >> 5)) * (int64_t)kFragElems + ((r & 15) + 16 * ((c & 31) >> 3)) * 8 + (c & 7);
+}
+
 // Pointer to this lane's part of fragment (row tile rt, K step s) of a tiled matrix with ks K steps.
 template <typename T>
 __device__ __forceinline__ const T* tiled_frag(const T* base, int64_t rt, int ks, int s) {

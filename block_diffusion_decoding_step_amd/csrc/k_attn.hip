@@ -326,7 +326,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn(AttnArgs a) {
   }
 }
 
-// Merge split partials in split order and normalise: one thread per (row, head, 8 dh).
+// Merge split partials in split order and normalise: one thread per (row, head, 8 dh).  O is
+// written fragment-tiled for the output projection's A operand.
 // All splits' loads are issued before any is used (n_split <= kAttnMaxSplit).
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
@@ -373,7 +374,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const float inv = L > 0.f ? 1.0f / L : 0.f;
 #pragma unroll
   for (int t = 0; t < 8; ++t) acc[t] *= inv;
-  Vec8<T>::store((T*)a.o + (int64_t)m * a.n_heads * DH + h * DH + c, acc);
+  Vec8<T>::store((T*)a.o + tiled_offset(m, h * DH + c, a.n_heads * DH), acc);
 }
 
 // Key splits: enough workgroups to cover the chip (~256), at least two key chunks per split.

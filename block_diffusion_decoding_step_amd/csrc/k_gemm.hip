@@ -47,7 +47,7 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z));
 // weight tile run on one XCD and share its L2.  SwiGLU: output column c pairs
 // B row c (gate) with B row N + c (up); the first NT/2 column tiles are gate
 // rows and the last NT/2 the matching up rows, so the tile covers 8*NT outputs.
-template <typename T, int MT, int NT, GemmEpi EPI>
+template <typename T, int MT, int NT, GemmEpi EPI, int DEPTH = Depth<T>::v, bool A_TILED = false>
 __global__ __launch_bounds__(256, 2) void k_gemm_dense(GemmArgs a) {
   constexpr bool SW = EPI == GemmEpi::SwiGLU;
   constexpr int OUTC = SW ? 8 * NT : 16 * NT;  // output columns per tile
@@ -68,8 +68,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm_dense(GemmArgs a) {
   const T* ap[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int r = min(m0 + 16 * mt + row16, a.M - 1);
-    ap[mt] = A + (int64_t)r * a.lda + 32 * sb + kq;
+    if constexpr (A_TILED) {
+      ap[mt] = tiled_frag(A, min(m0 / 16 + mt, (a.M + 15) / 16 - 1), ks, sb);
+    } else {
+      const int r = min(m0 + 16 * mt + row16, a.M - 1);
+      ap[mt] = A + (int64_t)r * a.lda + 32 * sb + kq;
+    }
   }
   // weights are fragment-tiled: one row tile per 16 output columns
   const int last_rt = (a.N + 15) / 16 - 1;
@@ -90,7 +94,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_dense(GemmArgs a) {
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = zero4();
-  if (se > sb) wave_gemm<T, MT, NT, Depth<T>::v>(acc, ap, bp, se - sb, 32, kFragElems);
+  if (se > sb) wave_gemm<T, MT, NT, DEPTH>(acc, ap, bp, se - sb, A_TILED ? kFragElems : 32, kFragElems);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -125,7 +129,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_dense(GemmArgs a) {
         T* c = (T*)a.C + (int64_t)m * a.ldc + n;
         *c = from_f32<T>(to_f32(*c) + x);
       } else if constexpr (EPI == GemmEpi::SwiGLU) {
-        ((T*)a.C)[(int64_t)m * a.ldc + n] = from_f32<T>(silu(x) * u[r]);
+        ((T*)a.C)[tiled_offset(m, n, a.N)] = from_f32<T>(silu(x) * u[r]);
       } else {  // QKV scatter: queries [h][m][dh], keys [h][pos][dh], values [h][dh][pos]
         const int dh = a.head_dim;
         const int hq = a.n_heads, hkv = a.n_kv_heads;
@@ -148,7 +152,10 @@ template <typename T, int MT, int NT, GemmEpi EPI>
 static void launch_dense_t(const GemmArgs& a, hipStream_t s) {
   constexpr int OUTC = EPI == GemmEpi::SwiGLU ? 8 * NT : 16 * NT;
   const int tiles = ((a.M + 16 * MT - 1) / (16 * MT)) * ((a.N + OUTC - 1) / OUTC);
-  hipLaunchKernelGGL((k_gemm_dense<T, MT, NT, EPI>), dim3(tiles), dim3(256), 0, s, a);
+  if (a.a_tiled)
+    hipLaunchKernelGGL((k_gemm_dense<T, MT, NT, EPI, Depth<T>::v, true>), dim3(tiles), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_gemm_dense<T, MT, NT, EPI>), dim3(tiles), dim3(256), 0, s, a);
 }
 
 // 64x64 tiles when the output is wide; 16x32 tiles for narrow outputs (the router)

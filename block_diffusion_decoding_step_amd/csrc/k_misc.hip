@@ -6,6 +6,7 @@
 // and Gemma 4".
 #include "dg_device.h"
 #include "dg_kernels.h"
+#include "dg_wave_gemm.h"
 
 namespace dg {
 
@@ -52,10 +53,11 @@ __global__ __launch_bounds__(256) void k_pack(const T* __restrict__ src, T* __re
 }
 
 // ============================================================== RMSNorm
-// Y = X / sqrt(mean(X^2) + eps) * g, fp32 statistics, one wave per row.
+// Y = X / sqrt(mean(X^2) + eps) * g, fp32 statistics, one wave per row.  Written row-major to Y
+// and / or fragment-tiled to Yt (the layout the matrix-core GEMMs read their A operand in).
 template <typename T>
 __global__ __launch_bounds__(256) void k_rmsnorm(const T* __restrict__ X, const T* __restrict__ g,
-                                                 T* __restrict__ Y, int M, int d, float eps) {
+                                                 T* __restrict__ Y, T* __restrict__ Yt, int M, int d, float eps) {
   int row = blockIdx.x * 4 + wave_id();
   if (row >= M) return;
   int l = lane_id();
@@ -69,14 +71,14 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const T* __restrict__ X, const 
   }
   ss = wave_sum(ss);
   float r = 1.0f / sqrtf(ss / (float)d + eps);
-  T* y = Y + (int64_t)row * d;
   for (int c = l * 8; c < d; c += 64 * 8) {
     float v[8], gv[8];
     Vec8<T>::load(x + c, v);
     Vec8<T>::load(g + c, gv);
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = v[j] * r * gv[j];
-    Vec8<T>::store(y + c, v);
+    if (Y) Vec8<T>::store(Y + (int64_t)row * d + c, v);
+    if (Yt) Vec8<T>::store(Yt + tiled_offset(row, c, d), v);
   }
 }
 
@@ -368,8 +370,8 @@ hipError_t launch_pack(const T* src, T* dst, int64_t batch, int64_t rows, int64_
   return hipGetLastError();
 }
 template <typename T>
-hipError_t launch_rmsnorm(const T* X, const T* g, T* Y, int M, int d, float eps, hipStream_t s) {
-  hipLaunchKernelGGL(k_rmsnorm<T>, dim3((M + 3) / 4), dim3(256), 0, s, X, g, Y, M, d, eps);
+hipError_t launch_rmsnorm(const T* X, const T* g, T* Y, T* Yt, int M, int d, float eps, hipStream_t s) {
+  hipLaunchKernelGGL(k_rmsnorm<T>, dim3((M + 3) / 4), dim3(256), 0, s, X, g, Y, Yt, M, d, eps);
   return hipGetLastError();
 }
 hipError_t launch_router_topk(const float* logits, int M, int E, int k, int32_t* idx, float* w, hipStream_t s) {
@@ -408,8 +410,8 @@ template hipError_t launch_embed<float>(const int32_t*, const float*, float*, in
 template hipError_t launch_pack<float>(const float*, float*, int64_t, int64_t, int64_t, hipStream_t);
 template hipError_t launch_pack<bf16>(const bf16*, bf16*, int64_t, int64_t, int64_t, hipStream_t);
 template hipError_t launch_embed<bf16>(const int32_t*, const bf16*, bf16*, int, int, int, hipStream_t);
-template hipError_t launch_rmsnorm<float>(const float*, const float*, float*, int, int, float, hipStream_t);
-template hipError_t launch_rmsnorm<bf16>(const bf16*, const bf16*, bf16*, int, int, float, hipStream_t);
+template hipError_t launch_rmsnorm<float>(const float*, const float*, float*, float*, int, int, float, hipStream_t);
+template hipError_t launch_rmsnorm<bf16>(const bf16*, const bf16*, bf16*, bf16*, int, int, float, hipStream_t);
 template hipError_t launch_moe_combine<float>(float*, const float*, const float*, const int32_t*, const float*, int,
                                               int, int, hipStream_t);
 template hipError_t launch_moe_combine<bf16>(bf16*, const bf16*, const bf16*, const int32_t*, const float*, int, int,
