@@ -183,6 +183,7 @@ int check_cfg(const dg_config* c) {
   if (c->n_heads % c->n_kv_heads) return DG_ERR_INVALID;
   if (c->rope_theta != 0.f) return DG_ERR_UNSUPPORTED;
   if (c->d_model % 32 || c->ffn_expert % 32 || c->ffn_shared % 32) return DG_ERR_UNSUPPORTED;
+  if (c->d_model > 8192) return DG_ERR_UNSUPPORTED;  // row kernels: one thread per 8 columns, <= 1024 threads
   if (c->head_dim != 64 && c->head_dim != 128) return DG_ERR_UNSUPPORTED;
   const int G = c->n_heads / c->n_kv_heads;
   if (G != 1 && G != 2 && G != 4) return DG_ERR_UNSUPPORTED;
@@ -234,9 +235,13 @@ int64_t rows_supported(const dg_config* c, size_t ws_bytes, int64_t limit) {
 }
 
 // ------------------------------------------------------------------ one transformer block
+// What the layer's final combine also produces: nothing, the next layer's attention-normalised rows
+// (fragment-tiled, so that layer skips its own RMSNorm), or the final-normalised rows for the head.
+enum class Next { None, NextLayer, Head };
+
 template <typename T>
 int layer_t(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int64_t pos0, int64_t M, bool causal,
-            const Ws& ws, hipStream_t s) {
+            bool normed_in, Next next, const Ws& ws, hipStream_t s) {
   const dg_layer_weights& L = w->h_layers[l];
   const int d = c->d_model, hq = c->n_heads, hkv = c->n_kv_heads, dh = c->head_dim;
   const int E = c->n_experts, k = c->top_k;
@@ -245,9 +250,10 @@ int layer_t(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int
   char* kbase = (char*)kv->k + (size_t)l * hkv * kv->capacity * dh * es;
   char* vbase = (char*)kv->v + (size_t)l * hkv * dh * kv->capacity * es;
 
-  // attention half
-  DG_LAUNCH(DG_K_RMSNORM, s, launch_rmsnorm<T>((const T*)ws.X, (const T*)L.attn_norm, nullptr, (T*)ws.Xt, Mi, d,
-                                                c->rms_eps, s));
+  // attention half (normed_in: the previous layer's combine already wrote attn_norm(X) to ws.Xt)
+  if (!normed_in)
+    DG_LAUNCH(DG_K_RMSNORM, s, launch_rmsnorm<T>((const T*)ws.X, (const T*)L.attn_norm, nullptr, (T*)ws.Xt, Mi, d,
+                                                  c->rms_eps, s));
   GemmArgs g{};
   g.A = ws.Xt; g.a_tiled = 1; g.B = L.wqkv; g.M = Mi; g.N = (hq + 2 * hkv) * dh; g.K = d; g.lda = d; g.ldb = d;
   g.q = ws.Q; g.kc = kbase; g.vc = vbase; g.n_heads = hq; g.n_kv_heads = hkv; g.head_dim = dh; g.q_rows = Mi;
@@ -274,7 +280,8 @@ int layer_t(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int
   g.A = ws.Xt; g.a_tiled = 1; g.B = L.w_router; g.C = ws.rlog; g.M = Mi; g.N = E; g.K = d; g.lda = d; g.ldb = d; g.ldc = E;
   DG_LAUNCH(DG_K_GEMM_ROUTER, s, launch_gemm<T>(GemmEpi::StoreF32, g, s));
   DG_LAUNCH(DG_K_ROUTER_TOPK, s, launch_router_topk(ws.rlog, Mi, E, k, ws.ridx, ws.rw, s));
-  DG_LAUNCH(DG_K_MOE_PERMUTE, s, launch_moe_permute(ws.ridx, Mi, E, k, ws.counts, ws.offsets, ws.perm, ws.pos, ws.tiles, ws.n_tiles, s));
+  DG_LAUNCH(DG_K_MOE_PERMUTE, s, launch_moe_permute(ws.ridx, Mi, E, k, ws.counts, ws.offsets, ws.perm, ws.pos,
+                                                    ws.tiles, ws.n_tiles, s));
 
   MoeArgs ma{};
   ma.tiles = ws.tiles; ma.n_tiles = ws.n_tiles; ma.max_tiles = moe_max_tiles(Mi, E, k); ma.perm = ws.perm;
@@ -292,14 +299,20 @@ int layer_t(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int
   g.ldb = c->ffn_shared; g.ldc = d;
   DG_LAUNCH(DG_K_SHARED_DOWN, s, launch_gemm<T>(GemmEpi::Store, g, s));
 
-  DG_LAUNCH(DG_K_MOE_COMBINE, s, launch_moe_combine<T>((T*)ws.X, (const T*)ws.Ys, (const T*)ws.Yp, ws.pos, ws.rw, Mi, d, k, s));
+  const T* g_next = next == Next::NextLayer ? (const T*)w->h_layers[l + 1].attn_norm
+                    : next == Next::Head      ? (const T*)w->final_norm
+                                              : nullptr;
+  T* y_next = next == Next::NextLayer ? (T*)ws.Xt : (T*)ws.Xn;
+  DG_LAUNCH(DG_K_MOE_COMBINE, s,
+            launch_moe_combine<T>((T*)ws.X, (const T*)ws.Ys, (const T*)ws.Yp, ws.pos, ws.rw, Mi, d, k, g_next, y_next,
+                                  next == Next::NextLayer ? 1 : 0, c->rms_eps, s));
   return DG_OK;
 }
 
 int layer(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int64_t pos0, int64_t M, bool causal,
-          const Ws& ws, hipStream_t s) {
-  if (c->dtype == DG_BF16) return layer_t<bf16>(c, w, l, kv, pos0, M, causal, ws, s);
-  return layer_t<float>(c, w, l, kv, pos0, M, causal, ws, s);
+          bool normed_in, Next next, const Ws& ws, hipStream_t s) {
+  if (c->dtype == DG_BF16) return layer_t<bf16>(c, w, l, kv, pos0, M, causal, normed_in, next, ws, s);
+  return layer_t<float>(c, w, l, kv, pos0, M, causal, normed_in, next, ws, s);
 }
 
 int embed(const dg_config* c, const dg_weights* w, const int32_t* tok, int64_t M, const Ws& ws, hipStream_t s) {
@@ -310,20 +323,22 @@ int embed(const dg_config* c, const dg_weights* w, const int32_t* tok, int64_t M
   return DG_OK;
 }
 
-// final norm + fused head over M rows of ws.X
+// final norm (unless normed: ws.Xn already holds it) + fused head over M rows of ws.X
 int head(const dg_config* c, const dg_weights* w, int64_t M, float inv_temp, int32_t* pred, float* conf, float* ent,
-         const Ws& ws, hipStream_t s) {
+         bool normed, const Ws& ws, hipStream_t s) {
   HeadArgs h{};
   h.x = ws.Xn; h.E = w->embed; h.part = ws.hpart; h.n = (int)M; h.d = c->d_model; h.V = c->vocab;
   h.n_groups = head_groups(c->vocab); h.beta_log2e = inv_temp * 1.4426950408889634f;
   h.pred = pred; h.conf = conf; h.ent = ent;
   if (c->dtype == DG_BF16) {
-    DG_LAUNCH(DG_K_RMSNORM, s, launch_rmsnorm<bf16>((const bf16*)ws.X, (const bf16*)w->final_norm, (bf16*)ws.Xn, nullptr, (int)M, c->d_model,
-                                c->rms_eps, s));
+    if (!normed)
+      DG_LAUNCH(DG_K_RMSNORM, s, launch_rmsnorm<bf16>((const bf16*)ws.X, (const bf16*)w->final_norm, (bf16*)ws.Xn,
+                                                       nullptr, (int)M, c->d_model, c->rms_eps, s));
     DG_LAUNCH(DG_K_VOCAB_HEAD, s, launch_vocab_head<bf16>(h, s));
   } else {
-    DG_LAUNCH(DG_K_RMSNORM, s, launch_rmsnorm<float>((const float*)ws.X, (const float*)w->final_norm, (float*)ws.Xn, nullptr, (int)M, c->d_model,
-                                 c->rms_eps, s));
+    if (!normed)
+      DG_LAUNCH(DG_K_RMSNORM, s, launch_rmsnorm<float>((const float*)ws.X, (const float*)w->final_norm, (float*)ws.Xn,
+                                                        nullptr, (int)M, c->d_model, c->rms_eps, s));
     DG_LAUNCH(DG_K_VOCAB_HEAD, s, launch_vocab_head<float>(h, s));
   }
   DG_LAUNCH(DG_K_HEAD_MERGE, s, launch_head_merge(h, s));
@@ -335,8 +350,9 @@ int denoise(const dg_config* c, const dg_weights* w, const dg_kv* kv, const int3
             int32_t* pred, float* conf, float* ent, const dg_debug* dbg, const Ws& ws, hipStream_t s) {
   const int64_t S = c->canvas;
   DG_CHECK(embed(c, w, canvas, S, ws, s));
-  for (int l = 0; l < c->n_layers; ++l) {
-    DG_CHECK(layer(c, w, l, kv, kv->len, S, false, ws, s));
+  const int L = c->n_layers;
+  for (int l = 0; l < L; ++l) {
+    DG_CHECK(layer(c, w, l, kv, kv->len, S, false, l > 0, l + 1 < L ? Next::NextLayer : Next::Head, ws, s));
     if (dbg) {
       const size_t hb = (size_t)S * c->d_model * esize(c);
       if (dbg->hidden) DG_TRY(hipMemcpyAsync((char*)dbg->hidden + l * hb, ws.X, hb, hipMemcpyDeviceToDevice, s));
@@ -349,7 +365,7 @@ int denoise(const dg_config* c, const dg_weights* w, const dg_kv* kv, const int3
         DG_TRY(hipMemcpyAsync((char*)dbg->router_logits + l * lb, ws.rlog, lb, hipMemcpyDeviceToDevice, s));
     }
   }
-  return head(c, w, S, inv_temp, pred, conf, ent, ws, s);
+  return head(c, w, S, inv_temp, pred, conf, ent, L > 0, ws, s);
 }
 
 // causal forward of n tokens at kv->len.., chunked to the workspace; does not change kv->len
@@ -361,7 +377,9 @@ int prefill(const dg_config* c, const dg_weights* w, const dg_kv* kv, const int3
     const int64_t m = std::min(chunk, n - r0);
     Ws ws = carve(c, m, (char*)wsp);
     DG_CHECK(embed(c, w, tokens + r0, m, ws, s));
-    for (int l = 0; l < c->n_layers; ++l) DG_CHECK(layer(c, w, l, kv, kv->len + r0, m, true, ws, s));
+    const int L = c->n_layers;
+    for (int l = 0; l < L; ++l)
+      DG_CHECK(layer(c, w, l, kv, kv->len + r0, m, true, l > 0, l + 1 < L ? Next::NextLayer : Next::None, ws, s));
   }
   return DG_OK;
 }
@@ -497,7 +515,7 @@ int dg_layer_forward(const dg_config* cfg, const dg_weights* w, int32_t layer_i,
   Ws wsv = carve(cfg, n, (char*)ws);
   const size_t hb = (size_t)n * cfg->d_model * esize(cfg);
   DG_TRY(hipMemcpyAsync(wsv.X, x_in, hb, hipMemcpyDeviceToDevice, s));
-  DG_CHECK(layer(cfg, w, layer_i, kv, kv->len, n, causal != 0, wsv, s));
+  DG_CHECK(layer(cfg, w, layer_i, kv, kv->len, n, causal != 0, false, Next::None, wsv, s));
   DG_TRY(hipMemcpyAsync(x_out, wsv.X, hb, hipMemcpyDeviceToDevice, s));
   if (dbg) {
     const size_t rb = (size_t)n * cfg->top_k * 4;
@@ -521,7 +539,7 @@ int dg_vocab_head(const dg_config* cfg, const dg_weights* w, const void* x, int6
   hipStream_t s = (hipStream_t)stream;
   Ws wsv = carve(cfg, n, (char*)ws);
   DG_TRY(hipMemcpyAsync(wsv.X, x, (size_t)n * cfg->d_model * esize(cfg), hipMemcpyDeviceToDevice, s));
-  return head(cfg, w, n, inv_temperature, pred, conf, entropy, wsv, s);
+  return head(cfg, w, n, inv_temperature, pred, conf, entropy, false, wsv, s);
 }
 
 int dg_stop_check(const dg_config* cfg, const dg_sampler* sampler, int32_t step, const float* entropy,

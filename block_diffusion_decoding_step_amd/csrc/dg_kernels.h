@@ -46,9 +46,10 @@ hipError_t launch_rmsnorm(const T* X, const T* g, T* Y, T* Yt, int M, int d, flo
 hipError_t launch_router_topk(const float* logits, int M, int E, int k, int32_t* idx, float* w, hipStream_t s);
 hipError_t launch_moe_permute(const int32_t* idx, int M, int E, int k, int32_t* counts, int32_t* offsets,
                               int32_t* perm, int32_t* pos, int4* tiles, int32_t* n_tiles, hipStream_t s);
+// X += Ys + sum_j w_j Yp[pos_j]; with g != null also Yn = RMSNorm(X) * g (tiled or row-major)
 template <typename T>
 hipError_t launch_moe_combine(T* X, const T* Ys, const T* Yp, const int32_t* pos, const float* w, int M, int d,
-                              int k, hipStream_t s);
+                              int k, const T* g, T* Yn, int yn_tiled, float eps, hipStream_t s);
 hipError_t launch_stop_check(const float* ent, const int32_t* pred, int32_t* prev, int S, int step, StopParams sp,
                              dg_block_status* out, hipStream_t s);
 hipError_t launch_canvas_update(const int32_t* pred, const float* conf, int S, int keep, uint64_t seed,

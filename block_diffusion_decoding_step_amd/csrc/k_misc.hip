@@ -53,33 +53,48 @@ __global__ __launch_bounds__(256) void k_pack(const T* __restrict__ src, T* __re
 }
 
 // ============================================================== RMSNorm
-// Y = X / sqrt(mean(X^2) + eps) * g, fp32 statistics, one wave per row.  Written row-major to Y
-// and / or fragment-tiled to Yt (the layout the matrix-core GEMMs read their A operand in).
+// Y = X / sqrt(mean(X^2) + eps) * g, fp32 statistics.  One workgroup per row, one thread per 8
+// consecutive columns (blockDim = 64 * ceil(d / 512)); the sum of squares is reduced in a fixed
+// order (within each wave, then across waves in wave order), shared with the combine kernel's fused
+// normalisation below so that both give bit-identical rows.  Written row-major to Y and / or
+// fragment-tiled to Yt (the layout the matrix-core GEMMs read their A operand in).
+__device__ __forceinline__ float row_sum_sq(float ss) {
+  __shared__ float part[16];
+  ss = wave_sum(ss);
+  if (lane_id() == 0) part[wave_id()] = ss;
+  __syncthreads();
+  float t = 0.f;
+  const int nw = (int)(blockDim.x >> 6);
+  for (int i = 0; i < nw; ++i) t += part[i];
+  return t;
+}
+
 template <typename T>
-__global__ __launch_bounds__(256) void k_rmsnorm(const T* __restrict__ X, const T* __restrict__ g,
-                                                 T* __restrict__ Y, T* __restrict__ Yt, int M, int d, float eps) {
-  int row = blockIdx.x * 4 + wave_id();
-  if (row >= M) return;
-  int l = lane_id();
-  const T* x = X + (int64_t)row * d;
+__device__ __forceinline__ void store_norm_row(const float (&v)[8], float r, const T* __restrict__ g, int c, int row,
+                                               int d, T* __restrict__ Y, T* __restrict__ Yt) {
+  float gv[8], o[8];
+  Vec8<T>::load(g + c, gv);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = v[j] * r * gv[j];
+  if (Y) Vec8<T>::store(Y + (int64_t)row * d + c, o);
+  if (Yt) Vec8<T>::store(Yt + tiled_offset(row, c, d), o);
+}
+
+template <typename T>
+__global__ __launch_bounds__(1024) void k_rmsnorm(const T* __restrict__ X, const T* __restrict__ g,
+                                                  T* __restrict__ Y, T* __restrict__ Yt, int M, int d, float eps) {
+  const int row = blockIdx.x;
+  const int c = threadIdx.x * 8;
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float ss = 0.f;
-  for (int c = l * 8; c < d; c += 64 * 8) {
-    float v[8];
-    Vec8<T>::load(x + c, v);
+  if (c < d) {
+    Vec8<T>::load(X + (int64_t)row * d + c, v);
 #pragma unroll
     for (int j = 0; j < 8; ++j) ss += v[j] * v[j];
   }
-  ss = wave_sum(ss);
-  float r = 1.0f / sqrtf(ss / (float)d + eps);
-  for (int c = l * 8; c < d; c += 64 * 8) {
-    float v[8], gv[8];
-    Vec8<T>::load(x + c, v);
-    Vec8<T>::load(g + c, gv);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = v[j] * r * gv[j];
-    if (Y) Vec8<T>::store(Y + (int64_t)row * d + c, v);
-    if (Yt) Vec8<T>::store(Yt + tiled_offset(row, c, d), v);
-  }
+  ss = row_sum_sq(ss);
+  const float r = 1.0f / sqrtf(ss / (float)d + eps);
+  if (c < d) store_norm_row<T>(v, r, g, c, row, d, Y, Yt);
 }
 
 // ============================================================== router top-k
@@ -97,7 +112,8 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ l
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     int e = l + 64 * i;
-    v[i] = e < E ? r[e] : -INFINITY;
+    const float x = e < E ? r[e] : -INFINITY;
+    v[i] = x != x ? -INFINITY : x;  // a NaN logit counts as -inf, so a valid expert is always chosen
     used[i] = e >= E;
   }
   float sel_v[16];
@@ -221,30 +237,55 @@ __global__ __launch_bounds__(1024) void k_moe_permute(const int32_t* __restrict_
   }
 }
 
-// ============================================================== combine + residual
-// X[t] = X[t] + Ys[t] + sum_j w[t,j] * Yp[pos[t,j]], in fp32, j in fixed order.
+// ============================================================== combine + residual (+ next RMSNorm)
+// X[t] = X[t] + Ys[t] + sum_j w[t,j] * Yp[pos[t,j]], in fp32, j in fixed order, stored in the storage
+// type.  With g != null the same kernel also forms the RMSNorm of the stored row with gain g (the next
+// layer's attention norm, or the final norm before the head) and writes it to Yn, fragment-tiled
+// (yn_tiled) or row-major, with k_rmsnorm's exact reduction order (bit-identical to normalising the
+// stored X separately).  One workgroup per row, one thread per 8 columns.
 template <typename T>
-__global__ __launch_bounds__(256) void k_moe_combine(T* __restrict__ X, const T* __restrict__ Ys,
-                                                     const T* __restrict__ Yp, const int32_t* __restrict__ pos,
-                                                     const float* __restrict__ w, int M, int d, int k) {
-  int per_row = d / 8;
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)M * per_row) return;
-  int t = (int)(i / per_row);
-  int c = (int)(i % per_row) * 8;
-  float acc[8], v[8];
-  Vec8<T>::load(X + (int64_t)t * d + c, acc);
-  Vec8<T>::load(Ys + (int64_t)t * d + c, v);
+__global__ __launch_bounds__(1024) void k_moe_combine(T* __restrict__ X, const T* __restrict__ Ys,
+                                                      const T* __restrict__ Yp, const int32_t* __restrict__ pos,
+                                                      const float* __restrict__ w, int M, int d, int k,
+                                                      const T* __restrict__ g, T* __restrict__ Yn, int yn_tiled,
+                                                      float eps) {
+  const int row = blockIdx.x;
+  const int c = threadIdx.x * 8;
+  int pj[16];
+  float wj[16];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] += v[j];
-  for (int j = 0; j < k; ++j) {
-    int p = pos[(int64_t)t * k + j];
-    float wj = w[(int64_t)t * k + j];
-    Vec8<T>::load(Yp + (int64_t)p * d + c, v);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] += wj * v[q];
+  for (int j = 0; j < 16; ++j) {
+    pj[j] = j < k ? pos[(int64_t)row * k + j] : 0;
+    wj[j] = j < k ? w[(int64_t)row * k + j] : 0.f;
   }
-  Vec8<T>::store(X + (int64_t)t * d + c, acc);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float ss = 0.f;
+  if (c < d) {
+    T* x = X + (int64_t)row * d + c;
+    float v[8];
+    Vec8<T>::load(x, acc);
+    Vec8<T>::load(Ys + (int64_t)row * d + c, v);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] += v[q];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j < k) {
+        Vec8<T>::load(Yp + (int64_t)pj[j] * d + c, v);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] += wj[j] * v[q];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      acc[q] = to_f32(from_f32<T>(acc[q]));  // the stored value
+      ss += acc[q] * acc[q];
+    }
+    Vec8<T>::store(x, acc);
+  }
+  if (!g) return;  // uniform over the workgroup
+  ss = row_sum_sq(ss);
+  const float r = 1.0f / sqrtf(ss / (float)d + eps);
+  if (c < d) store_norm_row<T>(acc, r, g, c, row, d, yn_tiled ? nullptr : Yn, yn_tiled ? Yn : nullptr);
 }
 
 // ============================================================== stop check
@@ -369,9 +410,11 @@ hipError_t launch_pack(const T* src, T* dst, int64_t batch, int64_t rows, int64_
   hipLaunchKernelGGL(k_pack<T>, dim3((unsigned)g), dim3(256), 0, s, src, dst, batch, rows, cols, rows_p);
   return hipGetLastError();
 }
+static inline int row_threads(int d) { return 64 * ((d + 511) / 512); }
+
 template <typename T>
 hipError_t launch_rmsnorm(const T* X, const T* g, T* Y, T* Yt, int M, int d, float eps, hipStream_t s) {
-  hipLaunchKernelGGL(k_rmsnorm<T>, dim3((M + 3) / 4), dim3(256), 0, s, X, g, Y, Yt, M, d, eps);
+  hipLaunchKernelGGL(k_rmsnorm<T>, dim3(M), dim3(row_threads(d)), 0, s, X, g, Y, Yt, M, d, eps);
   return hipGetLastError();
 }
 hipError_t launch_router_topk(const float* logits, int M, int E, int k, int32_t* idx, float* w, hipStream_t s) {
@@ -386,10 +429,9 @@ hipError_t launch_moe_permute(const int32_t* idx, int M, int E, int k, int32_t* 
 }
 template <typename T>
 hipError_t launch_moe_combine(T* X, const T* Ys, const T* Yp, const int32_t* pos, const float* w, int M, int d,
-                              int k, hipStream_t s) {
-  int64_t n = (int64_t)M * (d / 8);
-  hipLaunchKernelGGL(k_moe_combine<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, X, Ys, Yp, pos, w, M, d,
-                     k);
+                              int k, const T* g, T* Yn, int yn_tiled, float eps, hipStream_t s) {
+  hipLaunchKernelGGL(k_moe_combine<T>, dim3(M), dim3(row_threads(d)), 0, s, X, Ys, Yp, pos, w, M, d, k, g, Yn,
+                     yn_tiled, eps);
   return hipGetLastError();
 }
 hipError_t launch_stop_check(const float* ent, const int32_t* pred, int32_t* prev, int S, int step, StopParams sp,
@@ -413,8 +455,8 @@ template hipError_t launch_embed<bf16>(const int32_t*, const bf16*, bf16*, int, 
 template hipError_t launch_rmsnorm<float>(const float*, const float*, float*, float*, int, int, float, hipStream_t);
 template hipError_t launch_rmsnorm<bf16>(const bf16*, const bf16*, bf16*, bf16*, int, int, float, hipStream_t);
 template hipError_t launch_moe_combine<float>(float*, const float*, const float*, const int32_t*, const float*, int,
-                                              int, int, hipStream_t);
-template hipError_t launch_moe_combine<bf16>(bf16*, const bf16*, const bf16*, const int32_t*, const float*, int, int,
-                                             int, hipStream_t);
+                                                      int, int, const float*, float*, int, float, hipStream_t);
+template hipError_t launch_moe_combine<bf16>(bf16*, const bf16*, const bf16*, const int32_t*, const float*, int,
+                                                     int, int, const bf16*, bf16*, int, float, hipStream_t);
 
 }  // namespace dg
