@@ -40,18 +40,18 @@ struct Depth<float> {
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 // ---------------------------------------------------------------- dense GEMM
-// Workgroup tile = (16*MT) rows x (16*NT) columns; the 4 waves split the K range
-// four ways (each wave reads a distinct quarter of both operands, so nothing is
+// Workgroup tile = (16*MT) rows x (16*NT) columns; the NW waves split the K range
+// NW ways (each wave reads a distinct share of both operands, so nothing is
 // loaded twice inside a workgroup) and their partial tiles are summed through
 // LDS in fixed wave order.  Tiles are ordered so that the row tiles sharing a
 // weight tile run on one XCD and share its L2.  SwiGLU: output column c pairs
 // B row c (gate) with B row N + c (up); the first NT/2 column tiles are gate
 // rows and the last NT/2 the matching up rows, so the tile covers 8*NT outputs.
-template <typename T, int MT, int NT, GemmEpi EPI, int DEPTH = Depth<T>::v, bool A_TILED = false>
-__global__ __launch_bounds__(256, 2) void k_gemm_dense(GemmArgs a) {
+template <typename T, int MT, int NT, GemmEpi EPI, int DEPTH = Depth<T>::v, bool A_TILED = false, int NW = 4>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void k_gemm_dense(GemmArgs a) {
   constexpr bool SW = EPI == GemmEpi::SwiGLU;
   constexpr int OUTC = SW ? 8 * NT : 16 * NT;  // output columns per tile
-  __shared__ f32x4 red[4][MT * NT][64];
+  __shared__ f32x4 red[NW][MT * NT][64];
   const int lane = lane_id(), w = wave_id();
   const int row16 = lane & 15, kq = (lane >> 4) * 8;
   const int n_mtiles = (a.M + 16 * MT - 1) / (16 * MT);
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_dense(GemmArgs a) {
   const int mtile = t % n_mtiles, ntile = t / n_mtiles;
   const int m0 = mtile * 16 * MT;
   const int c0 = ntile * OUTC;  // first output column of the tile
-  const int ks = a.K / 32, q = (ks + 3) / 4;
+  const int ks = a.K / 32, q = (ks + NW - 1) / NW;
   const int sb = min(w * q, ks), se = min(sb + q, ks);
 
   const T* A = (const T*)a.A;
@@ -105,14 +105,17 @@ __global__ __launch_bounds__(256, 2) void k_gemm_dense(GemmArgs a) {
   // rows 4*(lane>>4) + r of each 16x16 tile
   const int rq = (lane >> 4) * 4;
   constexpr int OT = SW ? MT * NT / 2 : MT * NT;  // output tiles
-  for (int o = w; o < OT; o += 4) {
+  for (int o = w; o < OT; o += NW) {
     const int mt = o / (SW ? NT / 2 : NT), nt = o % (SW ? NT / 2 : NT);
-    f32x4 v = red[0][mt * NT + nt][lane] + red[1][mt * NT + nt][lane] + red[2][mt * NT + nt][lane] +
-              red[3][mt * NT + nt][lane];
+    f32x4 v = red[0][mt * NT + nt][lane];
+#pragma unroll
+    for (int x = 1; x < NW; ++x) v += red[x][mt * NT + nt][lane];
     f32x4 u = zero4();
     if constexpr (SW) {
       const int ut = mt * NT + nt + NT / 2;
-      u = red[0][ut][lane] + red[1][ut][lane] + red[2][ut][lane] + red[3][ut][lane];
+      u = red[0][ut][lane];
+#pragma unroll
+      for (int x = 1; x < NW; ++x) u += red[x][ut][lane];
     }
     const int n = c0 + 16 * nt + row16;
     if (n >= a.N) continue;
@@ -148,23 +151,29 @@ __global__ __launch_bounds__(256, 2) void k_gemm_dense(GemmArgs a) {
   }
 }
 
-template <typename T, int MT, int NT, GemmEpi EPI>
+template <typename T, int MT, int NT, GemmEpi EPI, int DEPTH = Depth<T>::v, int NW = 4>
 static void launch_dense_t(const GemmArgs& a, hipStream_t s) {
   constexpr int OUTC = EPI == GemmEpi::SwiGLU ? 8 * NT : 16 * NT;
   const int tiles = ((a.M + 16 * MT - 1) / (16 * MT)) * ((a.N + OUTC - 1) / OUTC);
   if (a.a_tiled)
-    hipLaunchKernelGGL((k_gemm_dense<T, MT, NT, EPI, Depth<T>::v, true>), dim3(tiles), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_gemm_dense<T, MT, NT, EPI, DEPTH, true, NW>), dim3(tiles), dim3(64 * NW), 0, s, a);
   else
-    hipLaunchKernelGGL((k_gemm_dense<T, MT, NT, EPI>), dim3(tiles), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_gemm_dense<T, MT, NT, EPI, DEPTH, false, NW>), dim3(tiles), dim3(64 * NW), 0, s, a);
 }
 
-// 64x64 tiles when the output is wide; 16x32 tiles for narrow outputs (the router)
+// 64x64 tiles when the output is wide (K split over 8 waves and 3 steps in flight, except the SwiGLU
+// pairs, which fill the chip with 4); 16x32 tiles for narrow outputs (the router)
 template <typename T, GemmEpi EPI>
 static void launch_dense_pick(const GemmArgs& a, hipStream_t s) {
-  if (a.N >= 512)
-    launch_dense_t<T, 4, 4, EPI>(a, s);
-  else
+  constexpr int D3 = sizeof(T) == 2 ? 3 : 1;
+  if (a.N >= 512) {
+    if constexpr (EPI == GemmEpi::SwiGLU)
+      launch_dense_t<T, 4, 4, EPI>(a, s);
+    else
+      launch_dense_t<T, 4, 4, EPI, D3, 8>(a, s);
+  } else {
     launch_dense_t<T, 1, 2, EPI>(a, s);
+  }
 }
 
 template <typename T>
