@@ -10,6 +10,9 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
 #include <vector>
 
 #include "../../include/dg.h"
@@ -77,6 +80,35 @@ struct TimeScope {
     g_timer.recs.push_back({id, a, b});
   }
 };
+
+// ------------------------------------------------------------------ side stream
+// The shared expert depends only on the FFN-normalised rows, so it runs on a side stream while the
+// caller's stream does the routing and the routed experts; the two join before the combine.  One side
+// stream (default priority, non-blocking) and a fork/join event pair per (device, caller stream),
+// created on first use and kept for the life of the process.
+struct Side {
+  hipStream_t s;
+  hipEvent_t fork, join;
+};
+std::mutex g_side_mu;
+std::map<std::pair<int, hipStream_t>, Side> g_side;
+
+int side_for(hipStream_t main, Side** out) {
+  int dev = 0;
+  DG_TRY(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  const auto key = std::make_pair(dev, main);
+  auto it = g_side.find(key);
+  if (it == g_side.end()) {
+    Side sd{};
+    DG_TRY(hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking));
+    DG_TRY(hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming));
+    DG_TRY(hipEventCreateWithFlags(&sd.join, hipEventDisableTiming));
+    it = g_side.emplace(key, sd).first;
+  }
+  *out = &it->second;
+  return DG_OK;
+}
 
 #define DG_LAUNCH(id, s, expr)    \
   do {                            \
@@ -276,6 +308,21 @@ int layer_t(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int
   // MoE half ([P2] "Architecture Details": 8 routed experts of 128, plus 1 shared)
   DG_LAUNCH(DG_K_RMSNORM, s, launch_rmsnorm<T>((const T*)ws.X, (const T*)L.ffn_norm, (T*)ws.Xn, (T*)ws.Xt, Mi, d,
                                                 c->rms_eps, s));
+  // shared expert on the side stream, concurrent with the routing and the routed experts
+  Side* sd = nullptr;
+  DG_CHECK(side_for(s, &sd));
+  DG_TRY(hipEventRecord(sd->fork, s));
+  DG_TRY(hipStreamWaitEvent(sd->s, sd->fork, 0));
+  g = GemmArgs{};
+  g.A = ws.Xt; g.a_tiled = 1; g.B = L.ws_gate_up; g.C = ws.Hs; g.M = Mi; g.N = c->ffn_shared; g.K = d; g.lda = d;
+  g.ldb = d; g.ldc = c->ffn_shared;
+  DG_LAUNCH(DG_K_SHARED_GATE_UP, sd->s, launch_gemm<T>(GemmEpi::SwiGLU, g, sd->s));
+  g = GemmArgs{};
+  g.A = ws.Hs; g.a_tiled = 1; g.B = L.ws_down; g.C = ws.Ys; g.M = Mi; g.N = d; g.K = c->ffn_shared;
+  g.lda = c->ffn_shared; g.ldb = c->ffn_shared; g.ldc = d;
+  DG_LAUNCH(DG_K_SHARED_DOWN, sd->s, launch_gemm<T>(GemmEpi::Store, g, sd->s));
+  DG_TRY(hipEventRecord(sd->join, sd->s));
+
   g = GemmArgs{};
   g.A = ws.Xt; g.a_tiled = 1; g.B = L.w_router; g.C = ws.rlog; g.M = Mi; g.N = E; g.K = d; g.lda = d; g.ldb = d; g.ldc = E;
   DG_LAUNCH(DG_K_GEMM_ROUTER, s, launch_gemm<T>(GemmEpi::StoreF32, g, s));
@@ -290,15 +337,7 @@ int layer_t(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int
   ma.X = ws.Hp; ma.W = L.w_down; ma.out = ws.Yp;
   DG_LAUNCH(DG_K_MOE_DOWN, s, launch_moe_down<T>(ma, s));
 
-  g = GemmArgs{};
-  g.A = ws.Xt; g.a_tiled = 1; g.B = L.ws_gate_up; g.C = ws.Hs; g.M = Mi; g.N = c->ffn_shared; g.K = d; g.lda = d; g.ldb = d;
-  g.ldc = c->ffn_shared;
-  DG_LAUNCH(DG_K_SHARED_GATE_UP, s, launch_gemm<T>(GemmEpi::SwiGLU, g, s));
-  g = GemmArgs{};
-  g.A = ws.Hs; g.a_tiled = 1; g.B = L.ws_down; g.C = ws.Ys; g.M = Mi; g.N = d; g.K = c->ffn_shared; g.lda = c->ffn_shared;
-  g.ldb = c->ffn_shared; g.ldc = d;
-  DG_LAUNCH(DG_K_SHARED_DOWN, s, launch_gemm<T>(GemmEpi::Store, g, s));
-
+  DG_TRY(hipStreamWaitEvent(s, sd->join, 0));  // join: the combine reads the shared expert's output
   const T* g_next = next == Next::NextLayer ? (const T*)w->h_layers[l + 1].attn_norm
                     : next == Next::Head      ? (const T*)w->final_norm
                                               : nullptr;

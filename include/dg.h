@@ -12,7 +12,11 @@
  * Conventions for every call
  *   - Pointers are DEVICE pointers unless the name starts with h_.
  *   - The caller owns all memory (weights, KV cache, inputs, outputs, workspace);
- *     the library never allocates device memory and keeps no device state.
+ *     the library never allocates device memory.  Its only state is, per (device,
+ *     caller stream), one side stream and two events, created on first use and kept
+ *     for the life of the process: each layer's shared expert runs on the side
+ *     stream, concurrent with the routed experts, and joins before the combine.
+ *     Calls on one caller stream must be issued from one host thread at a time.
  *   - Calls are stream-ordered and return after enqueueing on `stream` (a
  *     hipStream_t passed as void*; NULL = the default stream).  Exceptions:
  *     dg_generate_block in adaptive mode waits once per pass for a 16-byte status,
