@@ -232,6 +232,172 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head(HeadArgs a) {
   }
 }
 
+// bf16 variant: the vocabulary operand E is read by each wave straight from global memory into a
+// register ring (two K steps ahead; each E fragment is used by the two slot-half waves of its token
+// quarter, the second read hits L2), and only the slot operand X is staged in LDS, two K steps per
+// stage, double-buffered; the running per-slot states live in LDS.  LDS traffic per K step drops from 128 KB to 80 KB per workgroup.
+constexpr int kHeadKC = 2;     // K steps per X stage
+constexpr int kHeadEDepth = 2; // K steps of E fragments in flight per wave
+static_assert(kHeadKC % kHeadEDepth == 0, "the E ring slot of a K step is its index within the stage");
+
+__global__ __launch_bounds__(512, 1) void k_vocab_head_bf16(HeadArgs a) {
+  using T = bf16;
+  constexpr int STAGE = kHeadKC * 16 * kFragElems * 2;  // X fragments of kHeadKC steps: 64 KB
+  constexpr int LOADS = STAGE / 16 / 512;                // 16-byte units per thread per stage
+  static_assert(LOADS * 16 * 512 == STAGE, "stage layout");
+  __shared__ uint4 lds[2 * STAGE / 16];
+  __shared__ float4 run[8][128];  // running (max, argmax bits, Z, S1) per wave and slot of its half
+  const int t = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int wv = w & 3, wsl = w >> 2;  // token quarter, slot half
+  const int quad = lane >> 4;
+  const int row16 = lane & 15;
+  const int slot_base = blockIdx.y * kHeadSlots;
+  const int ks = a.d / 32;
+  const int nch = (ks + kHeadKC - 1) / kHeadKC;
+  const int n_tiles = (a.V + kHeadTokens - 1) / kHeadTokens;
+  const int G = gridDim.x;
+  const int my_tiles = (n_tiles - (int)blockIdx.x + G - 1) / G;
+  const int total = my_tiles * nch;
+  const int last_rt = (a.V + 15) / 16 - 1;
+  const T* E = (const T*)a.E;
+  const T* X = (const T*)a.x;
+  const float beta = a.beta_log2e * 0.6931471805599453f;  // inverse temperature
+
+  // X stage q = (tile q / nch, chunk q % nch): unit u = j*512 + t is lane u % 64 of X fragment u / 64
+  // (K step (u / 64) / 16 of the chunk, slot fragment (u / 64) % 16)
+  auto issue = [&](int q, uint4 (&r)[LOADS]) {
+    const int c = q % nch;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int u = j * 512 + t;
+      const int g = u >> 6, fl = u & 63;
+      const int s = c * kHeadKC + (g >> 4);
+      const int row = min(slot_base + 16 * (g & 15) + (fl & 15), a.n - 1);
+      const T* src = X + (int64_t)row * a.d + 32 * min(s, ks - 1) + 8 * (fl >> 4);
+      r[j] = s < ks ? *reinterpret_cast<const uint4*>(src) : uint4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto commit = [&](int buf, const uint4 (&r)[LOADS]) {
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) lds[buf * (STAGE / 16) + j * 512 + t] = r[j];
+  };
+  // E fragments of flat K step f (over this workgroup's tiles); steps past the end reload the last one
+  const int nsteps = my_tiles * nch * kHeadKC;
+  auto e_load = [&](int f, Frag<T> (&e)[4]) {
+    f = min(f, nsteps - 1);
+    const int tl = f / (nch * kHeadKC), s = f % (nch * kHeadKC);
+    const int tile = (int)blockIdx.x + tl * G;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rt = min(tile * (kHeadTokens / 16) + 4 * wv + i, last_rt);
+      e[i].load(tiled_frag(E, rt, ks, min(s, ks - 1)));
+    }
+  };
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = zero4();
+  if (lane < 16) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) run[w][16 * j + lane] = make_float4(-INFINITY, __int_as_float(0x7fffffff), 0.f, 0.f);
+  }
+
+  Frag<T> ering[kHeadEDepth][4];
+#pragma unroll
+  for (int dd = 0; dd < kHeadEDepth; ++dd) e_load(dd, ering[dd]);
+  uint4 r[LOADS];
+  if (total > 0) {
+    issue(0, r);
+    commit(0, r);
+  }
+  __syncthreads();
+  for (int q = 0; q < total; ++q) {
+    if (q + 1 < total) issue(q + 1, r);
+    const T* base = reinterpret_cast<const T*>(lds) + (q & 1) * (STAGE / 2) + lane * 8;
+#pragma unroll
+    for (int kk = 0; kk < kHeadKC; ++kk) {
+      const int f = q * kHeadKC + kk;
+      Frag<T> fb[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) fb[j].load(base + (kk * 16 + 8 * wsl + j) * kFragElems);
+      Frag<T>(&ea)[4] = ering[kk % kHeadEDepth];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mma(acc[i][j], ea[i], fb[j]);
+      e_load(f + kHeadEDepth, ering[kk % kHeadEDepth]);
+    }
+    if (q % nch == nch - 1) {
+      // tile finished: lane holds, for slot slot_base + 128*wsl + 16*j + row16, tokens v0 + 16*i + 4*quad + rr
+      const int v0 = ((int)blockIdx.x + (q / nch) * G) * kHeadTokens + 64 * wv;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        Stat loc{-INFINITY, 0.f, 0.f, 0x7fffffff};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int v = v0 + 16 * i + 4 * quad + rr;
+            const float l = acc[i][j][rr] * beta;
+            if (v < a.V && l > loc.m) { loc.m = l; loc.a = v; }
+          }
+        if (loc.m != -INFINITY) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const int v = v0 + 16 * i + 4 * quad + rr;
+              if (v < a.V) {
+                const float dl = acc[i][j][rr] * beta - loc.m;
+                const float e = exp2f(dl * 1.4426950408889634f);
+                loc.z += e;
+                loc.s1 += e * dl;
+              }
+            }
+        }
+        // the four quads hold the same slot: merge them, then fold into the running state
+#pragma unroll
+        for (int o = 16; o <= 32; o <<= 1) {
+          Stat y;
+          y.m = __shfl_xor(loc.m, o, 64);
+          y.z = __shfl_xor(loc.z, o, 64);
+          y.s1 = __shfl_xor(loc.s1, o, 64);
+          y.a = __shfl_xor(loc.a, o, 64);
+          stat_merge(loc, y);
+        }
+        if (quad == 0) {
+          const float4 p = run[w][16 * j + row16];
+          Stat x{p.x, p.z, p.w, __float_as_int(p.y)};
+          stat_merge(x, loc);
+          run[w][16 * j + row16] = make_float4(x.m, __int_as_float(x.a), x.z, x.s1);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i][j] = zero4();
+      }
+    }
+    if (q + 1 < total) commit((q + 1) & 1, r);
+    __syncthreads();
+  }
+  float4* red = reinterpret_cast<float4*>(lds);  // [4 token waves][256 slots]; stages are no longer read
+  if (quad == 0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) red[wv * kHeadSlots + 128 * wsl + 16 * j + row16] = run[w][16 * j + row16];
+  }
+  __syncthreads();
+  if (t < kHeadSlots && slot_base + t < a.n) {
+    float4 p = red[t];
+    Stat x{p.x, p.z, p.w, __float_as_int(p.y)};
+#pragma unroll
+    for (int k2 = 1; k2 < 4; ++k2) {
+      p = red[k2 * kHeadSlots + t];
+      stat_merge(x, Stat{p.x, p.z, p.w, __float_as_int(p.y)});
+    }
+    a.part[(int64_t)blockIdx.x * a.n + slot_base + t] = make_float4(x.m, __int_as_float(x.a), x.z, x.s1);
+  }
+}
+
 // One wave per slot: lane i merges groups i, i+64, ... in order, then a fixed
 // butterfly merges the lanes.
 __global__ __launch_bounds__(256) void k_head_merge(HeadArgs a) {
@@ -268,7 +434,10 @@ int head_groups(int V) {
 template <typename T>
 hipError_t launch_vocab_head(const HeadArgs& a, hipStream_t s) {
   dim3 grid(a.n_groups, (a.n + kHeadSlots - 1) / kHeadSlots);
-  hipLaunchKernelGGL(k_vocab_head<T>, grid, dim3(512), 0, s, a);
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL(k_vocab_head_bf16, grid, dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_vocab_head<T>, grid, dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
