@@ -242,7 +242,7 @@ static_assert(kHeadKC % kHeadEDepth == 0, "the E ring slot of a K step is its in
 
 __global__ __launch_bounds__(512, 1) void k_vocab_head_bf16(HeadArgs a) {
   using T = bf16;
-  constexpr int STAGE = kHeadKC * 16 * kFragElems * 2;  // X fragments of kHeadKC steps: 64 KB
+  constexpr int STAGE = kHeadKC * 16 * kFragElems * 2;  // X fragments of kHeadKC steps: 32 KB
   constexpr int LOADS = STAGE / 16 / 512;                // 16-byte units per thread per stage
   static_assert(LOADS * 16 * 512 == STAGE, "stage layout");
   __shared__ uint4 lds[2 * STAGE / 16];
