@@ -269,7 +269,7 @@ def main() -> int:
     pairs = d.canvas * d.top_k
     fl = pass_flops(d, P + d.canvas, pairs)
     cls = {"attention": ("attention", "attn_merge"), "experts": ("moe_gate_up", "moe_down"),
-           "dense": ("gemm_qkv", "gemm_o", "gemm_router", "shared_gate_up", "shared_down"),
+           "dense": ("gemm_qkv", "gemm_o", "route", "shared_gate_up", "shared_down"),
            "vocab_head": ("vocab_head", "head_merge")}
     mfma = {}
     for name, ks in cls.items():

@@ -140,6 +140,8 @@ struct Ws {
   int32_t* pos;
   int4* tiles;
   int32_t* n_tiles;
+  float* cand_v;
+  int32_t* cand_e;
   void* Hp;
   void* Yp;
   void* Hs;
@@ -187,6 +189,8 @@ Ws carve(const dg_config* c, int64_t M, char* base) {
   w.pos = (int32_t*)take(pairs * 4);
   w.tiles = (int4*)take((size_t)moe_max_tiles((int)M, (int)E, (int)k) * 16);
   w.n_tiles = (int32_t*)take(4);
+  w.cand_v = (float*)take((size_t)pairs * kRouteSlices * 4);
+  w.cand_e = (int32_t*)take((size_t)pairs * kRouteSlices * 4);
   w.Hp = take(pairs * c->ffn_expert * es);
   w.Yp = take(pairs * d * es);
   w.Hs = take(Mp * c->ffn_shared * es);
@@ -323,12 +327,12 @@ int layer_t(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int
   DG_LAUNCH(DG_K_SHARED_DOWN, sd->s, launch_gemm<T>(GemmEpi::Store, g, sd->s));
   DG_TRY(hipEventRecord(sd->join, sd->s));
 
-  g = GemmArgs{};
-  g.A = ws.Xt; g.a_tiled = 1; g.B = L.w_router; g.C = ws.rlog; g.M = Mi; g.N = E; g.K = d; g.lda = d; g.ldb = d; g.ldc = E;
-  DG_LAUNCH(DG_K_GEMM_ROUTER, s, launch_gemm<T>(GemmEpi::StoreF32, g, s));
-  DG_LAUNCH(DG_K_ROUTER_TOPK, s, launch_router_topk(ws.rlog, Mi, E, k, ws.ridx, ws.rw, s));
-  DG_LAUNCH(DG_K_MOE_PERMUTE, s, launch_moe_permute(ws.ridx, Mi, E, k, ws.counts, ws.offsets, ws.perm, ws.pos,
-                                                    ws.tiles, ws.n_tiles, s));
+  // router logits, top-k, softmax weights and the token->expert order
+  RouteArgs ra{};
+  ra.Xt = ws.Xt; ra.Wr = L.w_router; ra.logits = ws.rlog; ra.cand_v = ws.cand_v; ra.cand_e = ws.cand_e;
+  ra.idx = ws.ridx; ra.w = ws.rw; ra.counts = ws.counts; ra.offsets = ws.offsets; ra.perm = ws.perm;
+  ra.pos = ws.pos; ra.tiles = ws.tiles; ra.n_tiles = ws.n_tiles; ra.M = Mi; ra.d = d; ra.E = E; ra.k = k;
+  DG_LAUNCH(DG_K_ROUTE, s, launch_route<T>(ra, s));
 
   MoeArgs ma{};
   ma.tiles = ws.tiles; ma.n_tiles = ws.n_tiles; ma.max_tiles = moe_max_tiles(Mi, E, k); ma.perm = ws.perm;

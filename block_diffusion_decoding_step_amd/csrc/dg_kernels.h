@@ -10,23 +10,20 @@ namespace dg {
 
 typedef __bf16 bf16;
 
-// limits of the single-workgroup token->expert permutation
-constexpr int kPermMaxRows = 2048;
-constexpr int kPermBitWords = 8192;
-constexpr int kPermMasks = 4096;
+// limits of the routing kernels: rows per launch (two per thread of the ordering workgroup) and
+// the ordering workgroup's LDS masks, one per (expert, 64-token chunk)
+constexpr int kRouteMaxRows = 2048;
+constexpr int kRouteMasks = 4096;
 
 // rows per routed-expert work tile, and the bound on the number of tiles
 constexpr int kMoeTileRows = 32;
 inline int moe_max_tiles(int M, int E, int k) { return E + (M * k + kMoeTileRows - 1) / kMoeTileRows; }
 
 inline int moe_max_rows(int E) {
-  int words = (E + 31) / 32;
-  int r = kPermMaxRows;
-  if (r > kPermBitWords / words) r = kPermBitWords / words;
-  int by_masks = 64 * (kPermMasks / E);
-  if (r > by_masks) r = by_masks;
-  return r;
+  const int by_masks = 64 * (kRouteMasks / E);
+  return by_masks < kRouteMaxRows ? by_masks : kRouteMaxRows;
 }
+
 
 struct StopParams {
   float threshold;
@@ -43,9 +40,28 @@ hipError_t launch_pack(const T* src, T* dst, int64_t batch, int64_t rows, int64_
 // Y (row-major) and / or Yt (fragment-tiled, rows padded to 16); either may be null
 template <typename T>
 hipError_t launch_rmsnorm(const T* X, const T* g, T* Y, T* Yt, int M, int d, float eps, hipStream_t s);
-hipError_t launch_router_topk(const float* logits, int M, int E, int k, int32_t* idx, float* w, hipStream_t s);
-hipError_t launch_moe_permute(const int32_t* idx, int M, int E, int k, int32_t* counts, int32_t* offsets,
-                              int32_t* perm, int32_t* pos, int4* tiles, int32_t* n_tiles, hipStream_t s);
+
+// router logits + top-k, then softmax weights and the token->expert order (two launches;
+// E <= 256, k <= 16, M <= moe_max_rows(E), d a multiple of 32)
+struct RouteArgs {
+  const void* Xt;     // FFN-normalised rows, fragment-tiled (rows padded to 16)
+  const void* Wr;     // router weights [E, d], fragment-tiled
+  float* logits;      // [M, E] fp32
+  float* cand_v;      // [M][2][k] scratch: each expert slice's best logits, best first
+  int32_t* cand_e;    // [M][2][k] scratch: their experts (-1: none)
+  int32_t* idx;       // [M, k] chosen experts, best first
+  float* w;           // [M, k] softmax over the chosen logits
+  int32_t* counts;    // [E] pairs per expert
+  int32_t* offsets;   // [E + 1] first pair of each expert
+  int32_t* perm;      // [M * k] pair slot -> token
+  int32_t* pos;       // [M * k] (token, choice) -> pair slot
+  int4* tiles;        // work tiles (expert, first pair, rows, 0)
+  int32_t* n_tiles;
+  int M, d, E, k;
+};
+constexpr int kRouteSlices = 2;  // expert slices of the router (candidate lists per row)
+template <typename T>
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 // X += Ys + sum_j w_j Yp[pos_j]; with g != null also Yn = RMSNorm(X) * g (tiled or row-major)
 template <typename T>
 hipError_t launch_moe_combine(T* X, const T* Ys, const T* Yp, const int32_t* pos, const float* w, int M, int d,
@@ -57,7 +73,7 @@ hipError_t launch_canvas_update(const int32_t* pred, const float* conf, int S, i
                                 hipStream_t s);
 
 // ---- k_gemm.hip
-enum class GemmEpi { Store, StoreF32, Resid, QKV, SwiGLU };
+enum class GemmEpi { Store, Resid, QKV, SwiGLU };
 
 struct GemmArgs {
   const void* A;   // [M, K] rows, lda elements apart; or fragment-tiled (a_tiled, rows padded to 16)

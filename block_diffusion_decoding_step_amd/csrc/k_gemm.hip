@@ -11,11 +11,11 @@
 // Kernels
 //   k_gemm_dense  : dense projections (QKV with a scatter into Q / KV cache,
 //                   O-projection + residual, shared-expert SwiGLU and down
-//                   projection, fp32 router logits)
+//                   projection)
 //   k_moe_gate_up : routed experts, H = silu(X_e Wg^T) * (X_e Wu^T) per expert
 //   k_moe_down    : routed experts, Y = H We_down^T per expert
 // The routed kernels walk a device-side list of (expert, first pair, rows <= kMoeTileRows)
-// tiles written by the permutation kernel, so the host never reads routing.
+// tiles written by the routing kernels, so the host never reads routing.
 #include "dg_device.h"
 #include "dg_kernels.h"
 #include "dg_wave_gemm.h"
@@ -126,8 +126,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_gemm_dense(GemmArgs a) {
       const float x = v[r];
       if constexpr (EPI == GemmEpi::Store) {
         ((T*)a.C)[(int64_t)m * a.ldc + n] = from_f32<T>(x);
-      } else if constexpr (EPI == GemmEpi::StoreF32) {
-        ((float*)a.C)[(int64_t)m * a.ldc + n] = x;
       } else if constexpr (EPI == GemmEpi::Resid) {
         T* c = (T*)a.C + (int64_t)m * a.ldc + n;
         *c = from_f32<T>(to_f32(*c) + x);
@@ -162,7 +160,7 @@ static void launch_dense_t(const GemmArgs& a, hipStream_t s) {
 }
 
 // 64x64 tiles when the output is wide (K split over 8 waves and 3 steps in flight, except the SwiGLU
-// pairs, which fill the chip with 4); 16x32 tiles for narrow outputs (the router)
+// pairs, which fill the chip with 4); 16x32 tiles for narrow outputs (d_model < 512)
 template <typename T, GemmEpi EPI>
 static void launch_dense_pick(const GemmArgs& a, hipStream_t s) {
   constexpr int D3 = sizeof(T) == 2 ? 3 : 1;
@@ -180,7 +178,6 @@ template <typename T>
 hipError_t launch_gemm(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
   switch (epi) {
     case GemmEpi::Store: launch_dense_pick<T, GemmEpi::Store>(a, s); break;
-    case GemmEpi::StoreF32: launch_dense_pick<T, GemmEpi::StoreF32>(a, s); break;
     case GemmEpi::Resid: launch_dense_pick<T, GemmEpi::Resid>(a, s); break;
     case GemmEpi::QKV: launch_dense_pick<T, GemmEpi::QKV>(a, s); break;
     case GemmEpi::SwiGLU: launch_dense_pick<T, GemmEpi::SwiGLU>(a, s); break;

@@ -1,5 +1,6 @@
 // k_misc.hip — the memory-light stages of a denoising pass:
-//   embedding gather, RMSNorm, MoE routing (top-k + token->expert permutation),
+//   embedding gather, RMSNorm, MoE routing (FFN norm + router logits + top-k, then softmax and the
+//   token->expert order),
 //   MoE combine + residual, stop check and the Philox canvas update.
 // Page tags: [P2] "DiffusionGemma 26B: How Google's Text Diffusion Model Generates
 // Tokens in Parallel"; [P5] "When to use a diffusion LLM: I compared DiffusionGemma
@@ -97,143 +98,244 @@ __global__ __launch_bounds__(1024) void k_rmsnorm(const T* __restrict__ X, const
   if (c < d) store_norm_row<T>(v, r, g, c, row, d, Y, Yt);
 }
 
-// ============================================================== router top-k
-// One wave per token.  Top-k of the fp32 router logits, ties to the lower expert
-// id, then softmax over the k chosen ([P2] "Architecture Details": 8 of 128
-// experts active per token, plus one shared expert that is always applied).
-__global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ logits, int M, int E, int k,
-                                                     int32_t* __restrict__ idx, float* __restrict__ w) {
-  int t = blockIdx.x * 4 + wave_id();
-  if (t >= M) return;
-  int l = lane_id();
-  const float* r = logits + (int64_t)t * E;
-  float v[4];
-  bool used[4];
+// ============================================================== routing
+// Everything between the FFN RMSNorm and the routed experts, in two launches: the fp32 router logits, top-k with ties to the lower expert id and a softmax over the
+// k chosen ([P2] "Architecture Details": 8 of 128 experts active per token, plus one shared expert
+// that is always applied), and the order of the (token, choice) pairs by (expert, token) that the
+// grouped expert GEMMs walk, with their list of (expert, first pair, rows <= kMoeTileRows) tiles.
+//
+// k_route_logits<T, NT>: workgroup (row tile rt, expert slice es) of a ceil(M/16) x ES grid (ES <= 2
+// slices of 16*NT experts), 8 waves that split K = d eight ways; no workgroup waits for another.
+//  1. the 16 FFN-normalised rows (fragment-tiled) against the slice's NT router weight tiles, DB K
+//     steps of loads in flight; partial tiles summed in wave order through LDS: the slice's logits;
+//  2. per row, the slice's k best, best first, by k rounds of an arg-max across one 16-lane row (DPP
+//     lane exchanges).
+// k_route_order (one workgroup): per row, the k best of the slices' sorted candidates (ranked across
+// the two lists by four threads) and the softmax weights; an LDS mask of 64 tokens per (expert, 64-token chunk), built with atomic ORs, gives
+// every pair's rank among its expert's pairs as a prefix count, so the order is (expert, token).
+constexpr int kRouteWaves = 8;
+template <typename T>
+struct RouteDepth;
+template <>
+struct RouteDepth<bf16> {
+  static constexpr int b = 4;  // K steps of loads in flight
+};
+template <>
+struct RouteDepth<float> {
+  static constexpr int b = 1;
+};
+__host__ __device__ inline int route_tiles(int E) { return E <= 128 ? 4 : 8; }  // 16-expert tiles per workgroup: two slices at most
+
+// the better of two (logit, expert) candidates: larger logit, then lower expert id
+__device__ __forceinline__ bool route_better(float v, int e, float bv, int be) {
+  return v > bv || (v == bv && e < be);
+}
+// the same order over candidates that may be empty (expert -1): an empty one loses to any other
+__device__ __forceinline__ bool route_cand_better(float v, int e, float bv, int be) {
+  return e >= 0 && (be < 0 || route_better(v, e, bv, be));
+}
+// arg-max step across a 16-lane row: exchange with the lane the DPP control names
+template <int CTRL>
+__device__ __forceinline__ void route_argmax_step(float& bv, int& be) {
+  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bv), CTRL, 0xF, 0xF, false));
+  const int oe = __builtin_amdgcn_update_dpp(0, be, CTRL, 0xF, 0xF, false);
+  if (route_better(ov, oe, bv, be)) { bv = ov; be = oe; }
+}
+// every lane of each 16-lane row ends with the row's best: swap neighbours (quad_perm 1,0,3,2), pairs
+// (quad_perm 2,3,0,1), then the mirror inside each half row and inside the row (each pairs two groups
+// that already agree)
+__device__ __forceinline__ void route_argmax16(float& bv, int& be) {
+  route_argmax_step<0xB1>(bv, be);
+  route_argmax_step<0x4E>(bv, be);
+  route_argmax_step<0x141>(bv, be);
+  route_argmax_step<0x140>(bv, be);
+}
+
+template <typename T, int NT>
+__global__ __launch_bounds__(64 * kRouteWaves) void k_route_logits(RouteArgs a) {
+  constexpr int NW = kRouteWaves, DB = RouteDepth<T>::b, EPW = 16 * NT;
+  __shared__ f32x4 red[NW][NT][64];
+  __shared__ float lg[16][EPW];
+  const int lane = lane_id(), w = wave_id();
+  const int M = a.M, d = a.d, E = a.E, k = a.k;
+  const int ES = (E + EPW - 1) / EPW;
+  const int rt = (int)blockIdx.x / ES, es = (int)blockIdx.x % ES;
+  const int ks = d / 32, qw = (ks + NW - 1) / NW;
+  const int sb = min(w * qw, ks), se = min(sb + qw, ks);
+  const int row16 = lane & 15;
+
+  // 1. this wave's share of K for the tile's 16 rows and the slice's NT expert tiles
+  const T* ap[1] = {tiled_frag((const T*)a.Xt, rt, ks, sb)};
+  const T* bp[NT];
+  {
+    const int last_ct = (E + 15) / 16 - 1;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int e = l + 64 * i;
-    const float x = e < E ? r[e] : -INFINITY;
-    v[i] = x != x ? -INFINITY : x;  // a NaN logit counts as -inf, so a valid expert is always chosen
-    used[i] = e >= E;
+    for (int nt = 0; nt < NT; ++nt) bp[nt] = tiled_frag((const T*)a.Wr, min(es * NT + nt, last_ct), ks, sb);
   }
-  float sel_v[16];
-  int sel_e[16];
+  f32x4 acc[1][NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[0][nt] = zero4();
+  if (se > sb) wave_gemm<T, 1, NT, DB>(acc, ap, bp, se - sb, kFragElems, kFragElems);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) red[w][nt][lane] = acc[0][nt];
+  __syncthreads();
+
+  // 2. the slice's logits, then its k best per row
+  for (int nt = w; nt < NT; nt += NW) {
+    f32x4 v = red[0][nt][lane];
+#pragma unroll
+    for (int x = 1; x < NW; ++x) v += red[x][nt][lane];
+    const int c = 16 * nt + (lane & 15), e = EPW * es + c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * (lane >> 4) + i, tt = 16 * rt + row;
+      lg[row][c] = v[i] != v[i] ? -INFINITY : v[i];  // a NaN logit counts as -inf
+      if (e < E && tt < M) a.logits[(int64_t)tt * E + e] = v[i];
+    }
+  }
+  __syncthreads();
+  if (w >= 4) return;
+  const int row = 4 * w + (lane >> 4), tt = 16 * rt + row;
+  if (tt >= M) return;  // a whole 16-lane row leaves together
+  const int valid = min(EPW, E - EPW * es);  // experts of this slice
+  float v[NT];
+  bool used[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int c = row16 + 16 * i;
+    v[i] = lg[row][c];
+    used[i] = c >= valid;
+  }
+  float* cv = a.cand_v + ((int64_t)tt * ES + es) * k;
+  int32_t* ce = a.cand_e + ((int64_t)tt * ES + es) * k;
   for (int j = 0; j < k; ++j) {
-    // lane-local best among unused entries: larger value, then lower id
     float bv = -INFINITY;
     int be = 0x7fffffff;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int e = l + 64 * i;
-      if (!used[i] && (v[i] > bv || (v[i] == bv && e < be))) { bv = v[i]; be = e; }
-    }
+    for (int i = 0; i < NT; ++i)
+      if (!used[i] && route_better(v[i], row16 + 16 * i, bv, be)) { bv = v[i]; be = row16 + 16 * i; }
+    route_argmax16(bv, be);
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      float ov = __shfl_xor(bv, o, 64);
-      int oe = __shfl_xor(be, o, 64);
-      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (l + 64 * i == be) used[i] = true;
-    sel_v[j] = bv;
-    sel_e[j] = be;
-  }
-  if (l == 0) {
-    float mx = sel_v[0];
-    float s = 0.f, ex[16];
-    for (int j = 0; j < k; ++j) { ex[j] = expf(sel_v[j] - mx); s += ex[j]; }
-    for (int j = 0; j < k; ++j) {
-      idx[(int64_t)t * k + j] = sel_e[j];
-      w[(int64_t)t * k + j] = ex[j] / s;
+    for (int i = 0; i < NT; ++i)
+      if (be == row16 + 16 * i) used[i] = true;
+    if (row16 == 0) {  // fewer experts than k in this slice: the rest are empty (-1), never chosen
+      cv[j] = bv;
+      ce[j] = be < valid ? EPW * es + be : -1;
     }
   }
 }
 
-// ============================================================== token -> expert permutation
-// Pairs (token t, choice j) are ordered by (expert, token).  Built with wavefront
-// ballots: for expert e and a 64-token chunk c, ballot(token routes to e) gives a
-// 64-bit mask whose popcount is the chunk's count and whose prefix popcount is a
-// pair's rank inside the chunk.  All integer, deterministic.  Also emits the list
-// of (expert, first pair, rows <= kMoeTileRows) work tiles of the grouped expert GEMMs.
-// Launch: one workgroup of 1024 threads.  Limits (checked by the host, see
-// moe_max_rows): M <= 2048, M * ceil(E/32) <= 8192, E * ceil(M/64) <= 4096.
-
-__global__ __launch_bounds__(1024) void k_moe_permute(const int32_t* __restrict__ idx, int M, int E, int k,
-                                                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                                      int32_t* __restrict__ perm, int32_t* __restrict__ pos,
-                                                      int4* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
-  __shared__ uint32_t bits[kPermBitWords];  // [M][ceil(E/32)] token -> expert bitmap
-  __shared__ uint64_t masks[kPermMasks];    // [E][chunks] ballot masks
-  __shared__ int32_t pre[kPermMasks];       // [E][chunks] chunk counts, then chunk prefixes
+template <int KMAX>  // k <= KMAX
+__global__ __launch_bounds__(1024) void k_route_order(RouteArgs a) {
+  constexpr int CPT = KMAX / 2;  // candidates a thread owns: half of one slice's list
+  __shared__ unsigned long long masks[kRouteMasks];  // [E][chunks]: bit b of (e, c) set when token 64c + b routes to e
+  __shared__ int32_t pre[kRouteMasks];               // [E][chunks]: pairs of e in earlier chunks
+  __shared__ uint8_t sel_s[kRouteMaxRows * 16];      // [M][k] chosen experts, best first
   __shared__ int32_t off_s[257];
-  const int words = (E + 31) >> 5;
+  __shared__ int32_t wsum_n[4], wsum_t[4];
+  const int tid = (int)threadIdx.x, lane = lane_id(), w = wave_id();
+  const int M = a.M, E = a.E, k = a.k;
+  const int ES = (E + 16 * route_tiles(E) - 1) / (16 * route_tiles(E));
   const int chunks = (M + 63) >> 6;
-  const int tid = threadIdx.x;
-  for (int i = tid; i < M * words; i += blockDim.x) bits[i] = 0u;
+  for (int i = tid; i < E * chunks; i += 1024) masks[i] = 0ull;
   __syncthreads();
-  for (int p = tid; p < M * k; p += blockDim.x) {
-    int t = p / k;
-    int e = idx[p];
-    atomicOr(&bits[t * words + (e >> 5)], 1u << (e & 31));
-  }
-  __syncthreads();
-  const int nwaves = blockDim.x >> 6;
-  const int l = lane_id();
-  for (int ec = wave_id(); ec < E * chunks; ec += nwaves) {
-    int e = ec / chunks, c = ec % chunks;
-    int t = c * 64 + l;
-    bool hit = t < M && ((bits[t * words + (e >> 5)] >> (e & 31)) & 1u);
-    uint64_t m = __ballot(hit);
-    if (l == 0) {
-      masks[ec] = m;
-      pre[ec] = __popcll(m);
+
+  // 1. four threads per row: thread (row, L, H) owns places H*CPT .. H*CPT + CPT-1 of slice L's sorted
+  //    list; a candidate's rank among both lists is its place plus the other list's candidates that
+  //    beat it.  Softmax over the k best in fp32, shifted by the best logit; the quad adds its four
+  //    partial sums pairwise, so all four hold the same total.
+  const int L = (tid >> 1) & 1, H = tid & 1;
+  for (int t0 = 0; t0 < M; t0 += 256) {
+    const int t = t0 + (tid >> 2);
+    if (t >= M) break;  // a quad shares its row
+    const float* cv = a.cand_v + (int64_t)t * ES * k;
+    const int32_t* ce = a.cand_e + (int64_t)t * ES * k;
+    float ov[CPT], xv[KMAX];
+    int oe[CPT], xe[KMAX];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int p = H * CPT + i;
+      const bool ok = L < ES && p < k;
+      ov[i] = ok ? cv[L * k + p] : -INFINITY;
+      oe[i] = ok ? ce[L * k + p] : -1;
     }
+#pragma unroll
+    for (int o = 0; o < KMAX; ++o) {
+      const bool ok = 1 - L < ES && o < k;
+      xv[o] = ok ? cv[(1 - L) * k + o] : -INFINITY;
+      xe[o] = ok ? ce[(1 - L) * k + o] : -1;
+    }
+    const float h0 = cv[0], h1 = ES > 1 ? cv[k] : -INFINITY;
+    const float mx = ES > 1 && route_cand_better(h1, ce[k], h0, ce[0]) ? h1 : h0;
+    int rk[CPT];
+    float ex[CPT], s = 0.f;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      rk[i] = H * CPT + i;
+#pragma unroll
+      for (int o = 0; o < KMAX; ++o) rk[i] += route_cand_better(xv[o], xe[o], ov[i], oe[i]);
+      if (oe[i] < 0) rk[i] = k;  // empty: not chosen
+      ex[i] = 0.f;
+      if (rk[i] < k) {
+        ex[i] = expf(ov[i] - mx);
+        s += ex[i];
+      }
+    }
+    s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0xB1, 0xF, 0xF, false));
+    s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x4E, 0xF, 0xF, false));
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      if (rk[i] < k) {
+        const int64_t p = (int64_t)t * k + rk[i];
+        a.idx[p] = oe[i];
+        a.w[p] = ex[i] / s;
+        sel_s[p] = (uint8_t)oe[i];
+        atomicOr(&masks[oe[i] * chunks + (t >> 6)], 1ull << (t & 63));  // ds_or_b64
+      }
   }
   __syncthreads();
-  // per-expert totals and chunk prefixes (thread e walks its expert's chunks)
+
+  // 2. per expert: pairs in earlier chunks, total; exclusive scans over experts of pairs and tiles
   int n_e = 0;
   if (tid < E) {
     for (int c = 0; c < chunks; ++c) {
-      const int n = pre[tid * chunks + c];
       pre[tid * chunks + c] = n_e;
-      n_e += n;
+      n_e += __popcll(masks[tid * chunks + c]);
     }
-    counts[tid] = n_e;
+    a.counts[tid] = n_e;
   }
-  // exclusive scans over experts of (pairs, tiles): wave prefix sums, then wave totals (E <= 256)
   const int t_e = (n_e + kMoeTileRows - 1) / kMoeTileRows;
   int inc_n = n_e, inc_t = t_e;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int yn = __shfl_up(inc_n, o, 64), yt = __shfl_up(inc_t, o, 64);
-    if (l >= o) { inc_n += yn; inc_t += yt; }
+    if (lane >= o) { inc_n += yn; inc_t += yt; }
   }
-  __shared__ int wsum_n[4], wsum_t[4];
-  if (tid < 256 && l == 63) { wsum_n[tid >> 6] = inc_n; wsum_t[tid >> 6] = inc_t; }
+  if (tid < 256 && lane == 63) { wsum_n[w] = inc_n; wsum_t[w] = inc_t; }
   __syncthreads();
   if (tid < E) {
     int base_n = 0, base_t = 0;
-    for (int wv = 0; wv < (tid >> 6); ++wv) { base_n += wsum_n[wv]; base_t += wsum_t[wv]; }
+    for (int x = 0; x < w; ++x) { base_n += wsum_n[x]; base_t += wsum_t[x]; }
     const int off = base_n + inc_n - n_e, toff = base_t + inc_t - t_e;
     off_s[tid] = off;
-    offsets[tid] = off;
+    a.offsets[tid] = off;
     for (int i = 0; i < t_e; ++i)
-      tiles[toff + i] = make_int4(tid, off + i * kMoeTileRows, min(kMoeTileRows, n_e - i * kMoeTileRows), 0);
+      a.tiles[toff + i] = make_int4(tid, off + i * kMoeTileRows, min(kMoeTileRows, n_e - i * kMoeTileRows), 0);
     if (tid == E - 1) {
-      offsets[E] = off + n_e;
-      *n_tiles = toff + t_e;
+      a.offsets[E] = off + n_e;
+      *a.n_tiles = toff + t_e;
     }
   }
   __syncthreads();
-  for (int p = tid; p < M * k; p += blockDim.x) {
-    int t = p / k;
-    int e = idx[p];
-    int c = t >> 6, b = t & 63;
-    uint64_t below = b ? (masks[e * chunks + c] & ((~0ull) >> (64 - b))) : 0ull;
-    int q = off_s[e] + pre[e * chunks + c] + __popcll(below);
-    pos[p] = q;
-    perm[q] = t;
+
+  // 3. every pair's slot: its expert's offset + pairs of the expert in earlier chunks + earlier tokens
+  //    of the expert in its own chunk
+  for (int p = tid; p < M * k; p += 1024) {
+    const int t = p / k, c = t >> 6, b = t & 63, e = sel_s[p];
+    const unsigned long long below = b ? (~0ull) >> (64 - b) : 0ull;
+    const int qs = off_s[e] + pre[e * chunks + c] + __popcll(masks[e * chunks + c] & below);
+    a.pos[p] = qs;
+    a.perm[qs] = t;
   }
 }
 
@@ -417,14 +519,19 @@ hipError_t launch_rmsnorm(const T* X, const T* g, T* Y, T* Yt, int M, int d, flo
   hipLaunchKernelGGL(k_rmsnorm<T>, dim3(M), dim3(row_threads(d)), 0, s, X, g, Y, Yt, M, d, eps);
   return hipGetLastError();
 }
-hipError_t launch_router_topk(const float* logits, int M, int E, int k, int32_t* idx, float* w, hipStream_t s) {
-  hipLaunchKernelGGL(k_router_topk, dim3((M + 3) / 4), dim3(256), 0, s, logits, M, E, k, idx, w);
-  return hipGetLastError();
-}
-hipError_t launch_moe_permute(const int32_t* idx, int M, int E, int k, int32_t* counts, int32_t* offsets,
-                              int32_t* perm, int32_t* pos, int4* tiles, int32_t* n_tiles, hipStream_t s) {
-  hipLaunchKernelGGL(k_moe_permute, dim3(1), dim3(1024), 0, s, idx, M, E, k, counts, offsets, perm, pos, tiles,
-                     n_tiles);
+template <typename T>
+hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
+  if (a.M <= 0) return hipSuccess;
+  const int nt = route_tiles(a.E), slices = (a.E + 16 * nt - 1) / (16 * nt);
+  const dim3 grid(((a.M + 15) / 16) * slices), block(64 * kRouteWaves);
+  if (nt == 4)
+    hipLaunchKernelGGL((k_route_logits<T, 4>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((k_route_logits<T, 8>), grid, block, 0, s, a);
+  if (a.k <= 8)
+    hipLaunchKernelGGL(k_route_order<8>, dim3(1), dim3(1024), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_route_order<16>, dim3(1), dim3(1024), 0, s, a);
   return hipGetLastError();
 }
 template <typename T>
@@ -454,6 +561,8 @@ template hipError_t launch_pack<bf16>(const bf16*, bf16*, int64_t, int64_t, int6
 template hipError_t launch_embed<bf16>(const int32_t*, const bf16*, bf16*, int, int, int, hipStream_t);
 template hipError_t launch_rmsnorm<float>(const float*, const float*, float*, float*, int, int, float, hipStream_t);
 template hipError_t launch_rmsnorm<bf16>(const bf16*, const bf16*, bf16*, bf16*, int, int, float, hipStream_t);
+template hipError_t launch_route<float>(const RouteArgs&, hipStream_t);
+template hipError_t launch_route<bf16>(const RouteArgs&, hipStream_t);
 template hipError_t launch_moe_combine<float>(float*, const float*, const float*, const int32_t*, const float*, int,
                                                       int, int, const float*, float*, int, float, hipStream_t);
 template hipError_t launch_moe_combine<bf16>(bf16*, const bf16*, const bf16*, const int32_t*, const float*, int,

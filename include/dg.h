@@ -188,8 +188,9 @@ int dg_pack_matrix(const void* src, void* dst, int64_t batch, int64_t rows, int6
 
 /* Bytes of workspace needed by any call that processes up to max_tokens rows at
  * once (use cfg->canvas for denoising; a prefill chunk size for prefill/commit;
- * the larger of the two for both).  Host-only.  Longer prefills are split into
- * chunks of the largest row count the given workspace supports. */
+ * the larger of the two for both; 1 <= max_tokens <= min(2048, 64 * (4096 /
+ * n_experts)), the rows one routing step orders).  Host-only.  Longer prefills
+ * are split into chunks of the largest row count the given workspace supports. */
 int dg_workspace_size(const dg_config* cfg, int64_t max_tokens, size_t* h_bytes);
 
 /* Prompt prefill: a causal forward of n tokens placed at positions
@@ -281,9 +282,8 @@ typedef enum dg_kernel {
   DG_K_ATTENTION,      /* split-KV attention partials */
   DG_K_ATTN_MERGE,
   DG_K_GEMM_O,         /* output projection + residual */
-  DG_K_GEMM_ROUTER,
-  DG_K_ROUTER_TOPK,
-  DG_K_MOE_PERMUTE,
+  DG_K_ROUTE,          /* router logits and top-k; softmax and token->expert order
+                          (two launches, timed together) */
   DG_K_MOE_GATE_UP,    /* routed experts, gate/up projections + SwiGLU */
   DG_K_MOE_DOWN,       /* routed experts, down projection */
   DG_K_SHARED_GATE_UP,

@@ -156,3 +156,21 @@ def test_empty_prefill_is_a_no_op():
     torch.cuda.synchronize()
     assert sess.kv.len == 0
     assert torch.equal(before, sess.k)
+
+
+@pytest.mark.parametrize("E,k", [(160, 8), (24, 12), (256, 16)])
+def test_layer_router_slices_and_wide_top_k(E, k):
+    """Expert counts past one 64-expert router slice (two slices of 128 when E > 128, the second one
+    partly empty) and top-k past 8: one causal fp32 layer against the oracle."""
+    d = replace(recipe.C0.dims, n_layers=1, n_experts=E, top_k=k)
+    host = dg_inputs.layer_weights_host(d, 0)
+    M, P = 40, 24
+    x_host = dg_inputs.hidden((M, d.d_model), d.dtype)
+    k_host = dg_inputs.normal((d.n_kv_heads, P, d.head_dim), recipe.INPUT_SEED, recipe.STREAM_PREFIX_K, 1.0, d.dtype)
+    v_host = dg_inputs.normal((d.n_kv_heads, P, d.head_dim), recipe.INPUT_SEED, recipe.STREAM_PREFIX_V, 1.0, d.dtype)
+    log(f"router slices: E={E} k={k}")
+    y, y_ref, tr, ridx, rw, rlog = _layer_pair(d, host, x_host, P, k_host, v_host, 1)
+    same = compare_routing(ridx, rw, rlog, tr.router_logits, tr.idx, F32_TOL)
+    assert same.sum() >= M - 1
+    ok, worst, at = allclose_report(y[same], y_ref[same], *F32_TOL)
+    assert ok, (worst, at)
