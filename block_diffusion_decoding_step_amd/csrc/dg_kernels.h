@@ -55,7 +55,7 @@ struct RouteArgs {
   int32_t* offsets;   // [E + 1] first pair of each expert
   int32_t* perm;      // [M * k] pair slot -> token
   int32_t* pos;       // [M * k] (token, choice) -> pair slot
-  int4* tiles;        // work tiles (expert, first pair, rows, 0)
+  int4* tiles;        // work tiles (expert, first pair, rows, tiles of that expert)
   int32_t* n_tiles;
   int M, d, E, k;
 };
@@ -97,7 +97,7 @@ template <typename T>
 hipError_t launch_gemm(GemmEpi epi, const GemmArgs& a, hipStream_t s);
 
 struct MoeArgs {
-  const int4* tiles;      // (expert, first pair, rows, 0)
+  const int4* tiles;      // (expert, first pair, rows, tiles of that expert)
   const int32_t* n_tiles;
   int max_tiles;
   const int32_t* perm;    // pair -> token (gate_up gathers rows through it)

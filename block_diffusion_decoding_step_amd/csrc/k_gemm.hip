@@ -186,15 +186,17 @@ hipError_t launch_gemm(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------- routed experts
-// Tile (e, p0, rows): pairs p0 .. p0+rows-1 all
-// routed to expert e (rows <= 32, so one or two 16-row M-tiles).
+// Tile (e, p0, rows, n): pairs p0 .. p0+rows-1 all routed to expert e (rows <= 32, so one or two
+// 16-row M-tiles); n = tiles of expert e.  The weights of an expert with one tile are read once and
+// streamed with non-temporal loads; those of an expert with several tiles are loaded normally, so
+// its other tiles can find them in the caches.
 //
 // gate_up: a workgroup owns 64 H columns of expert e, i.e. 4 gate and the 4
 // matching up 16-row weight tiles; its 4 waves split K = d_model four ways, so
 // every weight byte and every token-row byte is loaded exactly once per
 // workgroup.  Partial tiles are summed through LDS (one 16-row M-tile per round)
 // and the SwiGLU product is formed on the sum.
-template <typename T, int MT>
+template <typename T, int MT, bool NTL>
 __device__ __forceinline__ void moe_gate_up_body(const MoeArgs& a, f32x4 (*red)[8][64], int e, int p0, int rows,
                                                  int c0) {
   constexpr int NT = 8;
@@ -222,7 +224,7 @@ __device__ __forceinline__ void moe_gate_up_body(const MoeArgs& a, f32x4 (*red)[
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = zero4();
-  if (se > sb) wave_gemm<T, MT, NT, (MT == 1 ? Depth<T>::moe1 : Depth<T>::moe2)>(acc, ap, bp, se - sb, 32, kFragElems);
+  if (se > sb) wave_gemm<T, MT, NT, (MT == 1 ? Depth<T>::moe1 : Depth<T>::moe2), false, NTL>(acc, ap, bp, se - sb, 32, kFragElems);
   T* H = (T*)a.out;
   const int rq = (lane >> 4) * 4;
 #pragma unroll
@@ -263,15 +265,18 @@ __global__ __launch_bounds__(256, 2) void k_moe_gate_up(MoeArgs a) {
   if (!moe_tile_col((a.F + 63) / 64, min(*a.n_tiles, a.max_tiles), tile_i, col)) return;
   const int4 tile = a.tiles[tile_i];
   const int c0 = col * 64;
-  if (tile.z > 16)
-    moe_gate_up_body<T, 2>(a, red, tile.x, tile.y, tile.z, c0);
-  else
-    moe_gate_up_body<T, 1>(a, red, tile.x, tile.y, tile.z, c0);
+  if (tile.w > 1) {  // weights re-read by the expert's other tiles: keep them cacheable
+    if (tile.z > 16) moe_gate_up_body<T, 2, false>(a, red, tile.x, tile.y, tile.z, c0);
+    else moe_gate_up_body<T, 1, false>(a, red, tile.x, tile.y, tile.z, c0);
+  } else {  // weights read once: streamed (non-temporal)
+    if (tile.z > 16) moe_gate_up_body<T, 2, true>(a, red, tile.x, tile.y, tile.z, c0);
+    else moe_gate_up_body<T, 1, true>(a, red, tile.x, tile.y, tile.z, c0);
+  }
 }
 
 // down: wave owns output columns [c0, c0+64) (four tiles) of expert e's [d][F]
 // matrix over the full K = F; a workgroup covers 256 columns.
-template <typename T, int MT>
+template <typename T, int MT, bool NTL>
 __device__ __forceinline__ void moe_down_body(const MoeArgs& a, int e, int p0, int rows, int c0) {
   constexpr int NT = 4;
   const int lane = lane_id();
@@ -293,7 +298,7 @@ __device__ __forceinline__ void moe_down_body(const MoeArgs& a, int e, int p0, i
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = zero4();
-  wave_gemm<T, MT, NT, Depth<T>::moe1>(acc, ap, bp, ks, 32, kFragElems);
+  wave_gemm<T, MT, NT, Depth<T>::moe1, false, NTL>(acc, ap, bp, ks, 32, kFragElems);
   T* Y = (T*)a.out;
   const int rq = (lane >> 4) * 4;
 #pragma unroll
@@ -318,10 +323,13 @@ __global__ __launch_bounds__(256) void k_moe_down(MoeArgs a) {
   const int4 tile = a.tiles[tile_i];
   const int c0 = col * 256 + wave_id() * 64;
   if (c0 >= a.d) return;
-  if (tile.z > 16)
-    moe_down_body<T, 2>(a, tile.x, tile.y, tile.z, c0);
-  else
-    moe_down_body<T, 1>(a, tile.x, tile.y, tile.z, c0);
+  if (tile.w > 1) {
+    if (tile.z > 16) moe_down_body<T, 2, false>(a, tile.x, tile.y, tile.z, c0);
+    else moe_down_body<T, 1, false>(a, tile.x, tile.y, tile.z, c0);
+  } else {
+    if (tile.z > 16) moe_down_body<T, 2, true>(a, tile.x, tile.y, tile.z, c0);
+    else moe_down_body<T, 1, true>(a, tile.x, tile.y, tile.z, c0);
+  }
 }
 
 template <typename T>

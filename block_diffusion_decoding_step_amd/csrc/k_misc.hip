@@ -99,10 +99,11 @@ __global__ __launch_bounds__(1024) void k_rmsnorm(const T* __restrict__ X, const
 }
 
 // ============================================================== routing
-// Everything between the FFN RMSNorm and the routed experts, in two launches: the fp32 router logits, top-k with ties to the lower expert id and a softmax over the
-// k chosen ([P2] "Architecture Details": 8 of 128 experts active per token, plus one shared expert
-// that is always applied), and the order of the (token, choice) pairs by (expert, token) that the
-// grouped expert GEMMs walk, with their list of (expert, first pair, rows <= kMoeTileRows) tiles.
+// Everything between the FFN RMSNorm and the routed experts, in two launches: the fp32 router
+// logits, top-k with ties to the lower expert id and a softmax over the k chosen ([P2] "Architecture
+// Details": 8 of 128 experts active per token, plus one shared expert that is always applied), and
+// the order of the (token, choice) pairs by (expert, token) that the grouped expert GEMMs walk, with
+// their list of (expert, first pair, rows <= kMoeTileRows, tiles of the expert) work tiles.
 //
 // k_route_logits<T, NT>: workgroup (row tile rt, expert slice es) of a ceil(M/16) x ES grid (ES <= 2
 // slices of 16*NT experts), 8 waves that split K = d eight ways; no workgroup waits for another.
@@ -320,7 +321,7 @@ __global__ __launch_bounds__(1024) void k_route_order(RouteArgs a) {
     off_s[tid] = off;
     a.offsets[tid] = off;
     for (int i = 0; i < t_e; ++i)
-      a.tiles[toff + i] = make_int4(tid, off + i * kMoeTileRows, min(kMoeTileRows, n_e - i * kMoeTileRows), 0);
+      a.tiles[toff + i] = make_int4(tid, off + i * kMoeTileRows, min(kMoeTileRows, n_e - i * kMoeTileRows), t_e);
     if (tid == E - 1) {
       a.offsets[E] = off + n_e;
       *a.n_tiles = toff + t_e;
