@@ -310,12 +310,12 @@ int layer_t(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int
   DG_LAUNCH(DG_K_GEMM_O, s, launch_gemm<T>(GemmEpi::Resid, g, s));
 
   // MoE half ([P2] "Architecture Details": 8 routed experts of 128, plus 1 shared)
-  DG_LAUNCH(DG_K_RMSNORM, s, launch_rmsnorm<T>((const T*)ws.X, (const T*)L.ffn_norm, (T*)ws.Xn, (T*)ws.Xt, Mi, d,
-                                                c->rms_eps, s));
-  // shared expert on the side stream, concurrent with the routing and the routed experts
+  // shared expert on the side stream, concurrent with the routing and the routed experts; the fork and
+  // join events complete with the norm and the shared down projection themselves
   Side* sd = nullptr;
   DG_CHECK(side_for(s, &sd));
-  DG_TRY(hipEventRecord(sd->fork, s));
+  DG_LAUNCH(DG_K_RMSNORM, s, launch_rmsnorm<T>((const T*)ws.X, (const T*)L.ffn_norm, (T*)ws.Xn, (T*)ws.Xt, Mi, d,
+                                                c->rms_eps, s, sd->fork));
   DG_TRY(hipStreamWaitEvent(sd->s, sd->fork, 0));
   g = GemmArgs{};
   g.A = ws.Xt; g.a_tiled = 1; g.B = L.ws_gate_up; g.C = ws.Hs; g.M = Mi; g.N = c->ffn_shared; g.K = d; g.lda = d;
@@ -324,8 +324,7 @@ int layer_t(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int
   g = GemmArgs{};
   g.A = ws.Hs; g.a_tiled = 1; g.B = L.ws_down; g.C = ws.Ys; g.M = Mi; g.N = d; g.K = c->ffn_shared;
   g.lda = c->ffn_shared; g.ldb = c->ffn_shared; g.ldc = d;
-  DG_LAUNCH(DG_K_SHARED_DOWN, sd->s, launch_gemm<T>(GemmEpi::Store, g, sd->s));
-  DG_TRY(hipEventRecord(sd->join, sd->s));
+  DG_LAUNCH(DG_K_SHARED_DOWN, sd->s, launch_gemm<T>(GemmEpi::Store, g, sd->s, sd->join));
 
   // router logits, top-k, softmax weights and the token->expert order
   RouteArgs ra{};

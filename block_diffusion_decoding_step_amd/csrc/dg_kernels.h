@@ -39,7 +39,8 @@ template <typename T>
 hipError_t launch_pack(const T* src, T* dst, int64_t batch, int64_t rows, int64_t cols, hipStream_t s);
 // Y (row-major) and / or Yt (fragment-tiled, rows padded to 16); either may be null
 template <typename T>
-hipError_t launch_rmsnorm(const T* X, const T* g, T* Y, T* Yt, int M, int d, float eps, hipStream_t s);
+hipError_t launch_rmsnorm(const T* X, const T* g, T* Y, T* Yt, int M, int d, float eps, hipStream_t s,
+                          hipEvent_t done = nullptr);  // done (optional): completes with the kernel
 
 // router logits + top-k, then softmax weights and the token->expert order (two launches;
 // E <= 256, k <= 16, M <= moe_max_rows(E), d a multiple of 32)
@@ -94,7 +95,7 @@ struct GemmArgs {
 };
 
 template <typename T>
-hipError_t launch_gemm(GemmEpi epi, const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm(GemmEpi epi, const GemmArgs& a, hipStream_t s, hipEvent_t done = nullptr);
 
 struct MoeArgs {
   const int4* tiles;      // (expert, first pair, rows, tiles of that expert)

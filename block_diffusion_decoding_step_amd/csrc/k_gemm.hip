@@ -16,6 +16,8 @@
 //   k_moe_down    : routed experts, Y = H We_down^T per expert
 // The routed kernels walk a device-side list of (expert, first pair, rows <= kMoeTileRows)
 // tiles written by the routing kernels, so the host never reads routing.
+#include <hip/hip_ext.h>
+
 #include "dg_device.h"
 #include "dg_kernels.h"
 #include "dg_wave_gemm.h"
@@ -150,37 +152,39 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_gemm_dense(GemmArgs a) {
 }
 
 template <typename T, int MT, int NT, GemmEpi EPI, int DEPTH = Depth<T>::v, int NW = 4>
-static void launch_dense_t(const GemmArgs& a, hipStream_t s) {
+static void launch_dense_t(const GemmArgs& a, hipStream_t s, hipEvent_t done) {
   constexpr int OUTC = EPI == GemmEpi::SwiGLU ? 8 * NT : 16 * NT;
   const int tiles = ((a.M + 16 * MT - 1) / (16 * MT)) * ((a.N + OUTC - 1) / OUTC);
   if (a.a_tiled)
-    hipLaunchKernelGGL((k_gemm_dense<T, MT, NT, EPI, DEPTH, true, NW>), dim3(tiles), dim3(64 * NW), 0, s, a);
+    hipExtLaunchKernelGGL((k_gemm_dense<T, MT, NT, EPI, DEPTH, true, NW>), dim3(tiles), dim3(64 * NW), 0, s, nullptr, done,
+                          0, a);
   else
-    hipLaunchKernelGGL((k_gemm_dense<T, MT, NT, EPI, DEPTH, false, NW>), dim3(tiles), dim3(64 * NW), 0, s, a);
+    hipExtLaunchKernelGGL((k_gemm_dense<T, MT, NT, EPI, DEPTH, false, NW>), dim3(tiles), dim3(64 * NW), 0, s, nullptr,
+                          done, 0, a);
 }
 
 // 64x64 tiles when the output is wide (K split over 8 waves and 3 steps in flight, except the SwiGLU
 // pairs, which fill the chip with 4); 16x32 tiles for narrow outputs (d_model < 512)
 template <typename T, GemmEpi EPI>
-static void launch_dense_pick(const GemmArgs& a, hipStream_t s) {
+static void launch_dense_pick(const GemmArgs& a, hipStream_t s, hipEvent_t done) {
   constexpr int D3 = sizeof(T) == 2 ? 3 : 1;
   if (a.N >= 512) {
     if constexpr (EPI == GemmEpi::SwiGLU)
-      launch_dense_t<T, 4, 4, EPI>(a, s);
+      launch_dense_t<T, 4, 4, EPI>(a, s, done);
     else
-      launch_dense_t<T, 4, 4, EPI, D3, 8>(a, s);
+      launch_dense_t<T, 4, 4, EPI, D3, 8>(a, s, done);
   } else {
-    launch_dense_t<T, 1, 2, EPI>(a, s);
+    launch_dense_t<T, 1, 2, EPI>(a, s, done);
   }
 }
 
 template <typename T>
-hipError_t launch_gemm(GemmEpi epi, const GemmArgs& a, hipStream_t s) {
+hipError_t launch_gemm(GemmEpi epi, const GemmArgs& a, hipStream_t s, hipEvent_t done) {
   switch (epi) {
-    case GemmEpi::Store: launch_dense_pick<T, GemmEpi::Store>(a, s); break;
-    case GemmEpi::Resid: launch_dense_pick<T, GemmEpi::Resid>(a, s); break;
-    case GemmEpi::QKV: launch_dense_pick<T, GemmEpi::QKV>(a, s); break;
-    case GemmEpi::SwiGLU: launch_dense_pick<T, GemmEpi::SwiGLU>(a, s); break;
+    case GemmEpi::Store: launch_dense_pick<T, GemmEpi::Store>(a, s, done); break;
+    case GemmEpi::Resid: launch_dense_pick<T, GemmEpi::Resid>(a, s, done); break;
+    case GemmEpi::QKV: launch_dense_pick<T, GemmEpi::QKV>(a, s, done); break;
+    case GemmEpi::SwiGLU: launch_dense_pick<T, GemmEpi::SwiGLU>(a, s, done); break;
   }
   return hipGetLastError();
 }
@@ -343,8 +347,8 @@ hipError_t launch_moe_down(const MoeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template hipError_t launch_gemm<float>(GemmEpi, const GemmArgs&, hipStream_t);
-template hipError_t launch_gemm<bf16>(GemmEpi, const GemmArgs&, hipStream_t);
+template hipError_t launch_gemm<float>(GemmEpi, const GemmArgs&, hipStream_t, hipEvent_t);
+template hipError_t launch_gemm<bf16>(GemmEpi, const GemmArgs&, hipStream_t, hipEvent_t);
 template hipError_t launch_moe_gate_up<float>(const MoeArgs&, hipStream_t);
 template hipError_t launch_moe_gate_up<bf16>(const MoeArgs&, hipStream_t);
 template hipError_t launch_moe_down<float>(const MoeArgs&, hipStream_t);

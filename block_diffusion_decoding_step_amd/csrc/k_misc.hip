@@ -5,6 +5,8 @@
 // Page tags: [P2] "DiffusionGemma 26B: How Google's Text Diffusion Model Generates
 // Tokens in Parallel"; [P5] "When to use a diffusion LLM: I compared DiffusionGemma
 // and Gemma 4".
+#include <hip/hip_ext.h>
+
 #include "dg_device.h"
 #include "dg_kernels.h"
 #include "dg_wave_gemm.h"
@@ -516,8 +518,11 @@ hipError_t launch_pack(const T* src, T* dst, int64_t batch, int64_t rows, int64_
 static inline int row_threads(int d) { return 64 * ((d + 511) / 512); }
 
 template <typename T>
-hipError_t launch_rmsnorm(const T* X, const T* g, T* Y, T* Yt, int M, int d, float eps, hipStream_t s) {
-  hipLaunchKernelGGL(k_rmsnorm<T>, dim3(M), dim3(row_threads(d)), 0, s, X, g, Y, Yt, M, d, eps);
+hipError_t launch_rmsnorm(const T* X, const T* g, T* Y, T* Yt, int M, int d, float eps, hipStream_t s, hipEvent_t done) {
+  if (done)  // the event completes with the kernel itself (no separate marker in the stream)
+    hipExtLaunchKernelGGL(k_rmsnorm<T>, dim3(M), dim3(row_threads(d)), 0, s, nullptr, done, 0, X, g, Y, Yt, M, d, eps);
+  else
+    hipLaunchKernelGGL(k_rmsnorm<T>, dim3(M), dim3(row_threads(d)), 0, s, X, g, Y, Yt, M, d, eps);
   return hipGetLastError();
 }
 template <typename T>
@@ -560,8 +565,8 @@ template hipError_t launch_embed<float>(const int32_t*, const float*, float*, in
 template hipError_t launch_pack<float>(const float*, float*, int64_t, int64_t, int64_t, hipStream_t);
 template hipError_t launch_pack<bf16>(const bf16*, bf16*, int64_t, int64_t, int64_t, hipStream_t);
 template hipError_t launch_embed<bf16>(const int32_t*, const bf16*, bf16*, int, int, int, hipStream_t);
-template hipError_t launch_rmsnorm<float>(const float*, const float*, float*, float*, int, int, float, hipStream_t);
-template hipError_t launch_rmsnorm<bf16>(const bf16*, const bf16*, bf16*, bf16*, int, int, float, hipStream_t);
+template hipError_t launch_rmsnorm<float>(const float*, const float*, float*, float*, int, int, float, hipStream_t, hipEvent_t);
+template hipError_t launch_rmsnorm<bf16>(const bf16*, const bf16*, bf16*, bf16*, int, int, float, hipStream_t, hipEvent_t);
 template hipError_t launch_route<float>(const RouteArgs&, hipStream_t);
 template hipError_t launch_route<bf16>(const RouteArgs&, hipStream_t);
 template hipError_t launch_moe_combine<float>(float*, const float*, const float*, const int32_t*, const float*, int,
