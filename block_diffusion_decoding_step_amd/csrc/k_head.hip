@@ -14,7 +14,8 @@
 //     S1 = e^(ma-m) (S1a + (ma-m) Za) + e^(mb-m) (S1b + (mb-m) Zb).
 // Finally conf = 1/Z and entropy = ln Z - S1/Z.
 //
-// logits^T = E_tile X^T on the matrix core, LDS-tiled.  A workgroup (8 waves)
+// logits^T = E_tile X^T on the matrix core.  fp32 kernel (k_vocab_head), LDS-tiled; the bf16 kernel
+// (k_vocab_head_bf16, below) reads E straight into registers.  A workgroup (8 waves)
 // owns 256 slots and walks 256-token vocabulary tiles blockIdx.x, +gridDim.x, ...
 // For each pair of 32-wide K steps it stages the tiles' fragments of E (16 row
 // fragments, read once from HBM) and of X (16 slot fragments, from L2) in LDS,
@@ -25,6 +26,8 @@
 // four quads of a wave and the four token waves of a slot are merged in fixed
 // order into one partial per (workgroup, slot).  A merge kernel combines the
 // workgroups in fixed order (deterministic).
+#include <type_traits>
+
 #include "dg_device.h"
 #include "dg_kernels.h"
 #include "dg_wave_gemm.h"
@@ -232,13 +235,16 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head(HeadArgs a) {
   }
 }
 
-// bf16 variant: the vocabulary operand E is read by each wave straight from global memory into a
-// register ring (two K steps ahead; each E fragment is used by the two slot-half waves of its token
-// quarter, the second read hits L2), and only the slot operand X is staged in LDS, two K steps per
-// stage, double-buffered; the running per-slot states live in LDS.  LDS traffic per K step drops from 128 KB to 80 KB per workgroup.
-constexpr int kHeadKC = 2;     // K steps per X stage
-constexpr int kHeadEDepth = 2; // K steps of E fragments in flight per wave
-static_assert(kHeadKC % kHeadEDepth == 0, "the E ring slot of a K step is its index within the stage");
+// bf16: wave w owns 32 tokens (two E fragments, tokens 32w .. 32w+31 of the tile) x all 256 slots, so
+// every E fragment is loaded by exactly one wave, straight into a four-deep register ring.  The slot
+// operand X (16 fragments per K step) is staged in LDS, two K steps per stage, double-buffered, and
+// read by all eight waves; its global loads (L2 hits) are issued two stages ahead of use, since one
+// stage of matrix work is shorter than their round trip while the vocabulary stream loads the memory
+// system.  The running per-slot states live in LDS and the eight token waves of a slot merge in wave
+// order.
+constexpr int kHeadKC = 2;      // K steps per X stage
+constexpr int kHeadEDepth = 4;  // K steps of E fragments in flight per wave: the two stages of a loop turn
+static_assert(kHeadEDepth == 2 * kHeadKC, "the ring slot of a K step is 2 * (stage parity) + its index in the stage");
 
 __global__ __launch_bounds__(512, 1) void k_vocab_head_bf16(HeadArgs a) {
   using T = bf16;
@@ -246,9 +252,8 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head_bf16(HeadArgs a) {
   constexpr int LOADS = STAGE / 16 / 512;                // 16-byte units per thread per stage
   static_assert(LOADS * 16 * 512 == STAGE, "stage layout");
   __shared__ uint4 lds[2 * STAGE / 16];
-  __shared__ float4 run[8][128];  // running (max, argmax bits, Z, S1) per wave and slot of its half
+  __shared__ float4 run[8][kHeadSlots];  // running (max, argmax bits, Z, S1) per token wave and slot
   const int t = threadIdx.x, lane = lane_id(), w = wave_id();
-  const int wv = w & 3, wsl = w >> 2;  // token quarter, slot half
   const int quad = lane >> 4;
   const int row16 = lane & 15;
   const int slot_base = blockIdx.y * kHeadSlots;
@@ -265,7 +270,7 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head_bf16(HeadArgs a) {
 
   // X stage q = (tile q / nch, chunk q % nch): unit u = j*512 + t is lane u % 64 of X fragment u / 64
   // (K step (u / 64) / 16 of the chunk, slot fragment (u / 64) % 16)
-  auto issue = [&](int q, uint4 (&r)[LOADS]) {
+  auto issue = [&](int q, uint4 (&r)[LOADS]) __attribute__((always_inline)) {
     const int c = q % nch;
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
@@ -277,121 +282,125 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head_bf16(HeadArgs a) {
       r[j] = s < ks ? *reinterpret_cast<const uint4*>(src) : uint4{0u, 0u, 0u, 0u};
     }
   };
-  auto commit = [&](int buf, const uint4 (&r)[LOADS]) {
+  auto commit = [&](int buf, const uint4 (&r)[LOADS]) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) lds[buf * (STAGE / 16) + j * 512 + t] = r[j];
   };
   // E fragments of flat K step f (over this workgroup's tiles); steps past the end reload the last one
-  const int nsteps = my_tiles * nch * kHeadKC;
-  auto e_load = [&](int f, Frag<T> (&e)[4]) {
+  const int nsteps = total * kHeadKC;
+  auto e_load = [&](int f, Frag<T> (&e)[2]) __attribute__((always_inline)) {
     f = min(f, nsteps - 1);
     const int tl = f / (nch * kHeadKC), s = f % (nch * kHeadKC);
     const int tile = (int)blockIdx.x + tl * G;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rt = min(tile * (kHeadTokens / 16) + 4 * wv + i, last_rt);
+    for (int i = 0; i < 2; ++i) {
+      const int rt = min(tile * (kHeadTokens / 16) + 2 * w + i, last_rt);
       e[i].load(tiled_frag(E, rt, ks, min(s, ks - 1)));
     }
   };
 
-  f32x4 acc[4][8];
+  f32x4 acc[2][16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = zero4();
-  if (lane < 16) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) run[w][16 * j + lane] = make_float4(-INFINITY, __int_as_float(0x7fffffff), 0.f, 0.f);
-  }
+    for (int j = 0; j < 16; ++j) acc[i][j] = zero4();
+  for (int i = lane; i < kHeadSlots; i += 64) run[w][i] = make_float4(-INFINITY, __int_as_float(0x7fffffff), 0.f, 0.f);
 
-  Frag<T> ering[kHeadEDepth][4];
+  // tile finished: lane holds, for slot slot_base + 16*j + row16, tokens v0 + 16*i + 4*quad + rr
+  auto fold_tile = [&](int q) __attribute__((always_inline)) {
+    const int v0 = ((int)blockIdx.x + (q / nch) * G) * kHeadTokens + 32 * w;
 #pragma unroll
-  for (int dd = 0; dd < kHeadEDepth; ++dd) e_load(dd, ering[dd]);
-  uint4 r[LOADS];
-  if (total > 0) {
-    issue(0, r);
-    commit(0, r);
-  }
-  __syncthreads();
-  for (int q = 0; q < total; ++q) {
-    if (q + 1 < total) issue(q + 1, r);
-    const T* base = reinterpret_cast<const T*>(lds) + (q & 1) * (STAGE / 2) + lane * 8;
+    for (int j = 0; j < 16; ++j) {
+      Stat loc{-INFINITY, 0.f, 0.f, 0x7fffffff};
 #pragma unroll
-    for (int kk = 0; kk < kHeadKC; ++kk) {
-      const int f = q * kHeadKC + kk;
-      Frag<T> fb[8];
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) fb[j].load(base + (kk * 16 + 8 * wsl + j) * kFragElems);
-      Frag<T>(&ea)[4] = ering[kk % kHeadEDepth];
+        for (int rr = 0; rr < 4; ++rr) {
+          const int v = v0 + 16 * i + 4 * quad + rr;
+          const float l = acc[i][j][rr] * beta;
+          if (v < a.V && l > loc.m) { loc.m = l; loc.a = v; }
+        }
+      if (loc.m != -INFINITY) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) mma(acc[i][j], ea[i], fb[j]);
-      e_load(f + kHeadEDepth, ering[kk % kHeadEDepth]);
-    }
-    if (q % nch == nch - 1) {
-      // tile finished: lane holds, for slot slot_base + 128*wsl + 16*j + row16, tokens v0 + 16*i + 4*quad + rr
-      const int v0 = ((int)blockIdx.x + (q / nch) * G) * kHeadTokens + 64 * wv;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        Stat loc{-INFINITY, 0.f, 0.f, 0x7fffffff};
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             const int v = v0 + 16 * i + 4 * quad + rr;
-            const float l = acc[i][j][rr] * beta;
-            if (v < a.V && l > loc.m) { loc.m = l; loc.a = v; }
-          }
-        if (loc.m != -INFINITY) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-              const int v = v0 + 16 * i + 4 * quad + rr;
-              if (v < a.V) {
-                const float dl = acc[i][j][rr] * beta - loc.m;
-                const float e = exp2f(dl * 1.4426950408889634f);
-                loc.z += e;
-                loc.s1 += e * dl;
-              }
+            if (v < a.V) {
+              const float dl = acc[i][j][rr] * beta - loc.m;
+              const float e = exp2f(dl * 1.4426950408889634f);
+              loc.z += e;
+              loc.s1 += e * dl;
             }
-        }
-        // the four quads hold the same slot: merge them, then fold into the running state
-#pragma unroll
-        for (int o = 16; o <= 32; o <<= 1) {
-          Stat y;
-          y.m = __shfl_xor(loc.m, o, 64);
-          y.z = __shfl_xor(loc.z, o, 64);
-          y.s1 = __shfl_xor(loc.s1, o, 64);
-          y.a = __shfl_xor(loc.a, o, 64);
-          stat_merge(loc, y);
-        }
-        if (quad == 0) {
-          const float4 p = run[w][16 * j + row16];
-          Stat x{p.x, p.z, p.w, __float_as_int(p.y)};
-          stat_merge(x, loc);
-          run[w][16 * j + row16] = make_float4(x.m, __int_as_float(x.a), x.z, x.s1);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i][j] = zero4();
+          }
       }
-    }
-    if (q + 1 < total) commit((q + 1) & 1, r);
-    __syncthreads();
-  }
-  float4* red = reinterpret_cast<float4*>(lds);  // [4 token waves][256 slots]; stages are no longer read
-  if (quad == 0) {
+      // the four quads hold the same slot: merge them, then fold into the running state
 #pragma unroll
-    for (int j = 0; j < 8; ++j) red[wv * kHeadSlots + 128 * wsl + 16 * j + row16] = run[w][16 * j + row16];
+      for (int o = 16; o <= 32; o <<= 1) {
+        Stat y;
+        y.m = __shfl_xor(loc.m, o, 64);
+        y.z = __shfl_xor(loc.z, o, 64);
+        y.s1 = __shfl_xor(loc.s1, o, 64);
+        y.a = __shfl_xor(loc.a, o, 64);
+        stat_merge(loc, y);
+      }
+      if (quad == 0) {
+        const float4 p = run[w][16 * j + row16];
+        Stat x{p.x, p.z, p.w, __float_as_int(p.y)};
+        stat_merge(x, loc);
+        run[w][16 * j + row16] = make_float4(x.m, __int_as_float(x.a), x.z, x.s1);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) acc[i][j] = zero4();
+    }
+  };
+
+  Frag<T> ering[kHeadEDepth][2];
+#pragma unroll
+  for (int dd = 0; dd < kHeadEDepth; ++dd) e_load(dd, ering[dd]);
+  // X loads run two stages ahead of their LDS stage: stage q's data is requested at the start of stage
+  // q - 2 into register set q & 1 and written to LDS buffer q & 1 at the end of stage q - 1
+  uint4 r[2][LOADS];
+  if (total > 0) {
+    issue(0, r[0]);
+    commit(0, r[0]);
   }
+  if (total > 1) issue(1, r[1]);
   __syncthreads();
+  // stage q (X buffer and register set q & 1 = B): K steps 2q, 2q+1 use ring slots 2B, 2B+1
+  auto stage = [&](int q, auto bparity) __attribute__((always_inline)) {
+    constexpr int B = decltype(bparity)::value;
+    if (q + 2 < total) issue(q + 2, r[B]);
+    const T* base = reinterpret_cast<const T*>(lds) + B * (STAGE / 2) + lane * 8;
+#pragma unroll
+    for (int kk = 0; kk < kHeadKC; ++kk) {
+      Frag<T>(&ea)[2] = ering[2 * B + kk];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        Frag<T> fb[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) fb[j].load(base + (kk * 16 + 8 * half + j) * kFragElems);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) mma(acc[i][8 * half + j], ea[i], fb[j]);
+      }
+      e_load(q * kHeadKC + kk + kHeadEDepth, ering[2 * B + kk]);
+    }
+    if (q % nch == nch - 1) fold_tile(q);
+    if (q + 1 < total) commit(1 - B, r[1 - B]);
+    __syncthreads();
+  };
+  for (int q = 0; q < total; q += 2) {
+    stage(q, std::integral_constant<int, 0>{});
+    if (q + 1 < total) stage(q + 1, std::integral_constant<int, 1>{});
+  }
   if (t < kHeadSlots && slot_base + t < a.n) {
-    float4 p = red[t];
+    float4 p = run[0][t];
     Stat x{p.x, p.z, p.w, __float_as_int(p.y)};
 #pragma unroll
-    for (int k2 = 1; k2 < 4; ++k2) {
-      p = red[k2 * kHeadSlots + t];
+    for (int k2 = 1; k2 < 8; ++k2) {
+      p = run[k2][t];
       stat_merge(x, Stat{p.x, p.z, p.w, __float_as_int(p.y)});
     }
     a.part[(int64_t)blockIdx.x * a.n + slot_base + t] = make_float4(x.m, __int_as_float(x.a), x.z, x.s1);
