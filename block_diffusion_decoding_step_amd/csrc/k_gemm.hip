@@ -91,6 +91,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_gemm_dense(GemmArgs a) {
     }
     bp[nt] = tiled_frag(B, rt, ks, sb);
   }
+  // Resid: this wave's residual inputs are requested before the K loop, so the epilogue does not wait
+  // for them (the residual rows were last written long before and are usually no longer cached)
+  const int rq = (lane >> 4) * 4;
+  constexpr int OT = SW ? MT * NT / 2 : MT * NT;  // output tiles
+  constexpr int OPW = (OT + NW - 1) / NW;          // per wave: tiles w, w + NW, ...
+  float cres[OPW][4];
+  if constexpr (EPI == GemmEpi::Resid) {
+#pragma unroll
+    for (int k = 0; k < OPW; ++k) {
+      const int o = w + NW * k, mt = (o % OT) / NT, nt = o % NT;
+      const int n = min(c0 + 16 * nt + row16, a.N - 1);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = min(m0 + 16 * mt + rq + r, a.M - 1);
+        cres[k][r] = to_f32(((const T*)a.C)[(int64_t)m * a.ldc + n]);
+      }
+    }
+  }
   f32x4 acc[MT][NT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -103,11 +121,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_gemm_dense(GemmArgs a) {
     for (int nt = 0; nt < NT; ++nt) red[w][mt * NT + nt][lane] = acc[mt][nt];
   __syncthreads();
 
-  // epilogue: wave w finishes output tiles w, w+4, ...; lane holds column (lane & 15),
+  // epilogue: wave w finishes output tiles w, w+NW, ...; lane holds column (lane & 15),
   // rows 4*(lane>>4) + r of each 16x16 tile
-  const int rq = (lane >> 4) * 4;
-  constexpr int OT = SW ? MT * NT / 2 : MT * NT;  // output tiles
-  for (int o = w; o < OT; o += NW) {
+#pragma unroll
+  for (int k = 0; k < OPW; ++k) {
+    const int o = w + NW * k;
+    if (o >= OT) break;
     const int mt = o / (SW ? NT / 2 : NT), nt = o % (SW ? NT / 2 : NT);
     f32x4 v = red[0][mt * NT + nt][lane];
 #pragma unroll
@@ -129,8 +148,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_gemm_dense(GemmArgs a) {
       if constexpr (EPI == GemmEpi::Store) {
         ((T*)a.C)[(int64_t)m * a.ldc + n] = from_f32<T>(x);
       } else if constexpr (EPI == GemmEpi::Resid) {
-        T* c = (T*)a.C + (int64_t)m * a.ldc + n;
-        *c = from_f32<T>(to_f32(*c) + x);
+        ((T*)a.C)[(int64_t)m * a.ldc + n] = from_f32<T>(cres[k][r] + x);
       } else if constexpr (EPI == GemmEpi::SwiGLU) {
         ((T*)a.C)[tiled_offset(m, n, a.N)] = from_f32<T>(silu(x) * u[r]);
       } else {  // QKV scatter: queries [h][m][dh], keys [h][pos][dh], values [h][dh][pos]
