@@ -328,7 +328,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn(AttnArgs a) {
 
 // Merge split partials in split order and normalise: one thread per (row, head, 8 dh).  O is
 // written fragment-tiled for the output projection's A operand.
-// All splits' loads are issued before any is used (n_split <= kAttnMaxSplit).
+// All of a thread's loads (every split's max, sum and partial) are issued before any is used
+// (n_split <= kAttnMaxSplit).
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const int per_row = DH / 8;
@@ -340,14 +341,19 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const int h = (int)(hm % a.n_heads);
   const int m = (int)(hm / a.n_heads);
   float ms[kAttnMaxSplit], ls[kAttnMaxSplit];
+  f32x4 x0s[kAttnMaxSplit], x1s[kAttnMaxSplit];
   float mx = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < kAttnMaxSplit; ++s) {
+  for (int s = 0; s < kAttnMaxSplit; ++s) {  // every load of the thread is in flight at once
     ms[s] = -INFINITY;
     ls[s] = 0.f;
+    x0s[s] = x1s[s] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (s < a.n_split) {
       const int64_t row = ((int64_t)s * a.n_heads + h) * a.q_rows + m;
       const float2 p = *reinterpret_cast<const float2*>(a.ml_part + row * 2);
+      const float* op = a.o_part + row * DH + c;
+      x0s[s] = *reinterpret_cast<const f32x4*>(op);
+      x1s[s] = *reinterpret_cast<const f32x4*>(op + 4);
       ms[s] = p.x;
       ls[s] = p.y;
       mx = fmaxf(mx, p.x);
@@ -358,12 +364,10 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 #pragma unroll
   for (int s = 0; s < kAttnMaxSplit; ++s) {
     if (s < a.n_split && ms[s] != -INFINITY) {
-      const int64_t row = ((int64_t)s * a.n_heads + h) * a.q_rows + m;
       const float f = exp2f(ms[s] - mx);
       L += ls[s] * f;
-      const float* op = a.o_part + row * DH + c;
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(op);
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(op + 4);
+      const f32x4 x0 = x0s[s];
+      const f32x4 x1 = x1s[s];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         acc[t] += x0[t] * f;
