@@ -15,8 +15,13 @@ typedef __bf16 bf16;
 constexpr int kRouteMaxRows = 2048;
 constexpr int kRouteMasks = 4096;
 
-// rows per routed-expert work tile, and the bound on the number of tiles
+// rows per routed-expert work tile, and the bound on the number of tiles.  A tile is the int4
+// (expert, first pair, rows, packed) with packed = tiles of that expert | (index of this tile among
+// them) << 8 | (rows of the expert's last tile) << 16; an expert holds at most 2048 pairs (64 tiles).
 constexpr int kMoeTileRows = 32;
+__host__ __device__ inline int moe_pack_tile_w(int tiles_of_expert, int index, int last_rows) {
+  return tiles_of_expert | (index << 8) | (last_rows << 16);
+}
 inline int moe_max_tiles(int M, int E, int k) { return E + (M * k + kMoeTileRows - 1) / kMoeTileRows; }
 
 inline int moe_max_rows(int E) {
@@ -56,7 +61,7 @@ struct RouteArgs {
   int32_t* offsets;   // [E + 1] first pair of each expert
   int32_t* perm;      // [M * k] pair slot -> token
   int32_t* pos;       // [M * k] (token, choice) -> pair slot
-  int4* tiles;        // work tiles (expert, first pair, rows, tiles of that expert)
+  int4* tiles;        // work tiles (expert, first pair, rows, packed as moe_pack_tile_w)
   int32_t* n_tiles;
   int M, d, E, k;
 };
@@ -98,7 +103,7 @@ template <typename T>
 hipError_t launch_gemm(GemmEpi epi, const GemmArgs& a, hipStream_t s, hipEvent_t done = nullptr);
 
 struct MoeArgs {
-  const int4* tiles;      // (expert, first pair, rows, tiles of that expert)
+  const int4* tiles;      // (expert, first pair, rows, packed as moe_pack_tile_w)
   const int32_t* n_tiles;
   int max_tiles;
   const int32_t* perm;    // pair -> token (gate_up gathers rows through it)

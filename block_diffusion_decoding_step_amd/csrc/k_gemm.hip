@@ -268,24 +268,34 @@ __device__ __forceinline__ void moe_gate_up_body(const MoeArgs& a, f32x4 (*red)[
   }
 }
 
-// Routed-expert grids are 1-D: 8 * ceil(max_tiles / 8) * ncols workgroups.  Workgroup b runs on XCD
-// b % 8 (round-robin dispatch); XCD x takes tiles x, x + 8, ... (of the device-side, data-dependent
-// tile count) with all ncols column blocks of a tile back to back, so the workgroups that share a
-// tile's activation rows share one L2 and every XCD gets an equal share of the tiles.
-__device__ __forceinline__ bool moe_tile_col(int ncols, int n_tiles, int& tile, int& col) {
+// Routed-expert grids are 1-D: 8 * ceil(max_tiles / 8) * ncols workgroups.  The work units (tile,
+// column block) are ordered expert by expert; within an expert, column block by column block, and
+// within a column block, the expert's tiles.  Workgroup b runs on XCD b % 8 (round-robin dispatch) and
+// XCD x takes the x-th of eight equal contiguous runs of that order (n_tiles is the device-side,
+// data-dependent tile count).  So the workgroups of one tile share its activation rows in one L2, and
+// the tiles of an expert routed more than 32 pairs read each weight block at about the same time on
+// one XCD, where the second read hits the first one's L2 lines.
+__device__ __forceinline__ bool moe_unit(const MoeArgs& a, int ncols, int n_tiles, int4& tile, int& col) {
   const int b = (int)blockIdx.x, x = b & 7, i = b >> 3;
-  tile = x + 8 * (i / ncols);
-  col = i % ncols;
-  return tile < n_tiles;
+  const int units = ncols * n_tiles, per = units / 8, rem = units % 8;
+  if (i >= per + (x < rem ? 1 : 0)) return false;
+  const int u = x * per + min(x, rem) + i;
+  const int4 t = a.tiles[u / ncols];  // a tile of the unit's expert
+  const int te = t.w & 255, j = (t.w >> 8) & 255, last = t.w >> 16;
+  const int r = u - ncols * (u / ncols - j);  // unit index within the expert's ncols * te units
+  const int jj = r % te;
+  col = r / te;
+  tile = make_int4(t.x, t.y + (jj - j) * kMoeTileRows, jj == te - 1 ? last : kMoeTileRows, te);
+  return true;
 }
 static inline int moe_grid(int max_tiles, int ncols) { return 8 * ((max_tiles + 7) / 8) * ncols; }
 
 template <typename T>
 __global__ __launch_bounds__(256, 2) void k_moe_gate_up(MoeArgs a) {
   __shared__ f32x4 red[4][8][64];
-  int tile_i, col;
-  if (!moe_tile_col((a.F + 63) / 64, min(*a.n_tiles, a.max_tiles), tile_i, col)) return;
-  const int4 tile = a.tiles[tile_i];
+  int4 tile;
+  int col;
+  if (!moe_unit(a, (a.F + 63) / 64, min(*a.n_tiles, a.max_tiles), tile, col)) return;
   const int c0 = col * 64;
   if (tile.w > 1) {  // weights re-read by the expert's other tiles: keep them cacheable
     if (tile.z > 16) moe_gate_up_body<T, 2, false>(a, red, tile.x, tile.y, tile.z, c0);
@@ -340,9 +350,9 @@ __device__ __forceinline__ void moe_down_body(const MoeArgs& a, int e, int p0, i
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_moe_down(MoeArgs a) {
-  int tile_i, col;
-  if (!moe_tile_col((a.d + 255) / 256, min(*a.n_tiles, a.max_tiles), tile_i, col)) return;
-  const int4 tile = a.tiles[tile_i];
+  int4 tile;
+  int col;
+  if (!moe_unit(a, (a.d + 255) / 256, min(*a.n_tiles, a.max_tiles), tile, col)) return;
   const int c0 = col * 256 + wave_id() * 64;
   if (c0 >= a.d) return;
   if (tile.w > 1) {

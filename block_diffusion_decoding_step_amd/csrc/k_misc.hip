@@ -323,7 +323,8 @@ __global__ __launch_bounds__(1024) void k_route_order(RouteArgs a) {
     off_s[tid] = off;
     a.offsets[tid] = off;
     for (int i = 0; i < t_e; ++i)
-      a.tiles[toff + i] = make_int4(tid, off + i * kMoeTileRows, min(kMoeTileRows, n_e - i * kMoeTileRows), t_e);
+      a.tiles[toff + i] = make_int4(tid, off + i * kMoeTileRows, min(kMoeTileRows, n_e - i * kMoeTileRows),
+                                    moe_pack_tile_w(t_e, i, n_e - (t_e - 1) * kMoeTileRows));
     if (tid == E - 1) {
       a.offsets[E] = off + n_e;
       *a.n_tiles = toff + t_e;

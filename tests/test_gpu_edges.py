@@ -114,10 +114,13 @@ def _layer_pair(d, storage_layer, x_host, P, k_host, v_host, causal):
 
 
 @pytest.mark.parametrize("dims,tol,M,P", [(replace(recipe.C0.dims, n_layers=1), F32_TOL, 64, 40),
-                                          (replace(recipe.C1.dims, n_layers=1), BF16_TOL, 256, 96)])
+                                          (replace(recipe.C0.dims, n_layers=1), F32_TOL, 71, 40),
+                                          (replace(recipe.C1.dims, n_layers=1), BF16_TOL, 256, 96),
+                                          (replace(recipe.C1.dims, n_layers=1), BF16_TOL, 200, 96)])
 def test_all_tokens_route_to_the_same_experts(dims, tol, M, P):
     """Zero router weights: every logit is 0, so every token picks experts 0..k-1 (ties to the lower id)
-    with weight 1/k, and those k experts each take all M tokens (the busiest possible routing)."""
+    with weight 1/k, and those k experts each take all M tokens (the busiest possible routing).  M = 71
+    and 200 leave each busy expert a short last tile (3 tiles ending in 7 rows, 7 ending in 8)."""
     d = dims
     host = dg_inputs.layer_weights_host(d, 0)
     host["w_router"] = np.zeros_like(host["w_router"])
