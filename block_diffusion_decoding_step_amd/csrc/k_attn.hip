@@ -381,7 +381,9 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   Vec8<T>::store((T*)a.o + tiled_offset(m, h * DH + c, a.n_heads * DH), acc);
 }
 
-// Key splits: enough workgroups to cover the chip (~256), at least two key chunks per split.
+// Key splits: enough workgroups to cover the chip (~256), at least two key chunks per split, and then
+// as few splits as give the same chunks per split (the longest split sets the time; fewer splits mean
+// fewer partials for the merge to read).
 int attention_splits(int64_t n_keys, int q_rows, int n_heads, int n_kv_heads, int causal, int max_split) {
   (void)causal;
   const int64_t n_ch = (n_keys + kAttnChunk - 1) / kAttnChunk;
@@ -393,7 +395,8 @@ int attention_splits(int64_t n_keys, int q_rows, int n_heads, int n_kv_heads, in
   const int64_t by_chunks = n_ch / 2;
   if (s > by_chunks) s = (int)by_chunks;
   if (s < 1) s = 1;
-  return s;
+  const int64_t per = (n_ch + s - 1) / s;
+  return (int)((n_ch + per - 1) / per);
 }
 
 template <typename T, int DH>
