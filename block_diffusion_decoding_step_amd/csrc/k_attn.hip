@@ -10,7 +10,7 @@
 //   * A workgroup of 8 waves takes 256 (head, query) rows of ONE KV head -- every
 //     query head of the GQA group reads the same keys -- and one split of the key
 //     range.  Each wave owns 32 consecutive queries of one head (two 16-row tiles).
-//   * The key range is walked in chunks of 128 keys.  Each chunk's K and V
+//   * The key range is walked in chunks of 64 keys.  Each chunk's K and V
 //     fragments are copied once from global memory straight into LDS (no register
 //     staging), double-buffered so that the copy of the next chunk is in flight
 //     while this one is computed, and read by all 8 waves: K/V leave L2 once per
@@ -38,7 +38,7 @@ namespace dg {
 constexpr int kAttnWaves = 8;     // waves per workgroup
 constexpr int kAttnQT = 2;        // 16-query tiles per wave
 constexpr int kAttnRows = 16 * kAttnQT;  // (head, query) rows per wave
-constexpr int kAttnChunk = 128;   // keys per LDS stage (four 32-key steps; two for fp32 at Dh 128)
+constexpr int kAttnChunk = 64;    // keys per LDS stage (two 32-key steps)
 constexpr bool kAttnSplitP = true;   // bf16 P as high + remainder parts (two products)
 constexpr uint32_t kAttnLazyBits = 0x43800000u;  // 256.0f: probabilities stay below 2^8 of the reference
 
