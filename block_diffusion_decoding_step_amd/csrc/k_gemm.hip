@@ -182,13 +182,14 @@ static void launch_dense_t(const GemmArgs& a, hipStream_t s, hipEvent_t done) {
 }
 
 // 64x64 tiles when the output is wide (K split over 8 waves and 3 steps in flight, except the SwiGLU
-// pairs, which fill the chip with 4); 16x32 tiles for narrow outputs (d_model < 512)
+// pairs, which fill the chip with 4 waves, also 3 steps in flight for bf16); 16x32 tiles for narrow
+// outputs (d_model < 512)
 template <typename T, GemmEpi EPI>
 static void launch_dense_pick(const GemmArgs& a, hipStream_t s, hipEvent_t done) {
   constexpr int D3 = sizeof(T) == 2 ? 3 : 1;
   if (a.N >= 512) {
     if constexpr (EPI == GemmEpi::SwiGLU)
-      launch_dense_t<T, 4, 4, EPI>(a, s, done);
+      launch_dense_t<T, 4, 4, EPI, D3>(a, s, done);
     else
       launch_dense_t<T, 4, 4, EPI, D3, 8>(a, s, done);
   } else {

@@ -121,7 +121,7 @@ template <typename T>
 struct RouteDepth;
 template <>
 struct RouteDepth<bf16> {
-  static constexpr int b = 4;  // K steps of loads in flight
+  static constexpr int b = 6;  // K steps of loads in flight (of 11 per wave at d = 2816)
 };
 template <>
 struct RouteDepth<float> {
