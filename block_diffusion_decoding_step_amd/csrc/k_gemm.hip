@@ -30,7 +30,7 @@ template <>
 struct Depth<bf16> {
   static constexpr int v = 2;     // dense tiles (4 A + 4 B fragments per step)
   static constexpr int moe1 = 4;  // routed experts, one 16-row M-tile
-  static constexpr int moe2 = 2;  // routed experts, two 16-row M-tiles
+  static constexpr int moe2 = 3;  // routed experts, two 16-row M-tiles
 };
 template <>
 struct Depth<float> {
