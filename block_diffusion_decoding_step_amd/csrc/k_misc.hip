@@ -133,9 +133,14 @@ __host__ __device__ inline int route_tiles(int E) { return E <= 128 ? 4 : 8; }  
 __device__ __forceinline__ bool route_better(float v, int e, float bv, int be) {
   return v > bv || (v == bv && e < be);
 }
-// the same order over candidates that may be empty (expert -1): an empty one loses to any other
-__device__ __forceinline__ bool route_cand_better(float v, int e, float bv, int be) {
-  return e >= 0 && (be < 0 || route_better(v, e, bv, be));
+// the same order over candidates that may be empty (expert -1, below every other), as one unsigned
+// 64-bit key (larger key = better candidate): the logit's bits mapped
+// monotonically to an unsigned word (-0 taken as +0, so equal logits tie), then the inverted expert
+// id; an empty candidate is 0, below every other
+__device__ __forceinline__ unsigned long long route_key(float v, int e) {
+  uint32_t u = __float_as_uint(v + 0.0f);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return e < 0 ? 0ull : ((unsigned long long)u << 32) | (uint32_t)(0x7fffffff - e);
 }
 // arg-max step across a 16-lane row: exchange with the lane the DPP control names
 template <int CTRL>
@@ -253,30 +258,44 @@ __global__ __launch_bounds__(1024) void k_route_order(RouteArgs a) {
     if (t >= M) break;  // a quad shares its row
     const float* cv = a.cand_v + (int64_t)t * ES * k;
     const int32_t* ce = a.cand_e + (int64_t)t * ES * k;
+    // every load is unconditional, at an index clamped into the row's lists, so that all of them are in
+    // flight at once; entries outside the lists are replaced by empty candidates afterwards
+    const int Lo = min(L, ES - 1), Lx = min(1 - L, ES - 1);
     float ov[CPT], xv[KMAX];
     int oe[CPT], xe[KMAX];
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int p = H * CPT + i;
-      const bool ok = L < ES && p < k;
-      ov[i] = ok ? cv[L * k + p] : -INFINITY;
-      oe[i] = ok ? ce[L * k + p] : -1;
+      const int pc = min(H * CPT + i, k - 1);
+      ov[i] = cv[Lo * k + pc];
+      oe[i] = ce[Lo * k + pc];
     }
 #pragma unroll
     for (int o = 0; o < KMAX; ++o) {
-      const bool ok = 1 - L < ES && o < k;
-      xv[o] = ok ? cv[(1 - L) * k + o] : -INFINITY;
-      xe[o] = ok ? ce[(1 - L) * k + o] : -1;
+      const int oc = min(o, k - 1);
+      xv[o] = cv[Lx * k + oc];
+      xe[o] = ce[Lx * k + oc];
     }
-    const float h0 = cv[0], h1 = ES > 1 ? cv[k] : -INFINITY;
-    const float mx = ES > 1 && route_cand_better(h1, ce[k], h0, ce[0]) ? h1 : h0;
+    const float hv = cv[Lo * k];  // head of this thread's list (the other list's head is xv[0])
+    const int he = ce[Lo * k];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      if (!(L < ES && H * CPT + i < k)) { ov[i] = -INFINITY; oe[i] = -1; }
+#pragma unroll
+    for (int o = 0; o < KMAX; ++o)
+      if (!(1 - L < ES && o < k)) { xv[o] = -INFINITY; xe[o] = -1; }
+    // the row's best logit (the better head), the same on all four threads of the row
+    unsigned long long xk[KMAX];
+#pragma unroll
+    for (int o = 0; o < KMAX; ++o) xk[o] = route_key(xv[o], xe[o]);
+    const float mx = xk[0] > route_key(hv, he) ? xv[0] : hv;
     int rk[CPT];
     float ex[CPT], s = 0.f;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       rk[i] = H * CPT + i;
+      const unsigned long long ok = route_key(ov[i], oe[i]);
 #pragma unroll
-      for (int o = 0; o < KMAX; ++o) rk[i] += route_cand_better(xv[o], xe[o], ov[i], oe[i]);
+      for (int o = 0; o < KMAX; ++o) rk[i] += xk[o] > ok;
       if (oe[i] < 0) rk[i] = k;  // empty: not chosen
       ex[i] = 0.f;
       if (rk[i] < k) {
