@@ -34,21 +34,23 @@ __device__ __forceinline__ void frag_load(Frag<T>& f, const T* p) {
   if constexpr (STREAM) f.load_nt(p); else f.load(p);
 }
 
-// SA / SB: operand read once per launch (weights), loaded non-temporally.
-template <typename T, int MT, int NT, int DEPTH, bool SA = false, bool SB = false>
-__device__ __forceinline__ void wave_gemm(f32x4 (&acc)[MT][NT], const T* const (&ap)[MT], const T* const (&bp)[NT],
-                                          int ksteps, int sa = 32, int sb = 32) {
-  Frag<T> fa[DEPTH][MT];
-  Frag<T> fb[DEPTH][NT];
+// The first DEPTH steps of each operand (the pipeline's fill), issued separately so that a caller
+// can start the B loads before the A addresses are known.
+template <typename T, int NT, int DEPTH, bool STREAM>
+__device__ __forceinline__ void wave_gemm_fill(Frag<T> (&f)[DEPTH][NT], const T* const (&p)[NT], int ksteps, int stride) {
   const int last = ksteps - 1;
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) {
-    const int s = min(d, last);
+  for (int d = 0; d < DEPTH; ++d)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) frag_load<SA>(fa[d][mt], ap[mt] + (int64_t)sa * s);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) frag_load<SB>(fb[d][nt], bp[nt] + (int64_t)sb * s);
-  }
+    for (int nt = 0; nt < NT; ++nt) frag_load<STREAM>(f[d][nt], p[nt] + (int64_t)stride * min(d, last));
+}
+
+// The steady state and the tail, on rings already filled by wave_gemm_fill.
+template <typename T, int MT, int NT, int DEPTH, bool SA, bool SB>
+__device__ __forceinline__ void wave_gemm_run(f32x4 (&acc)[MT][NT], Frag<T> (&fa)[DEPTH][MT], Frag<T> (&fb)[DEPTH][NT],
+                                              const T* const (&ap)[MT], const T* const (&bp)[NT], int ksteps, int sa,
+                                              int sb) {
+  const int last = ksteps - 1;
   int s0 = 0;
   for (; s0 + DEPTH <= ksteps; s0 += DEPTH) {
 #pragma unroll
@@ -73,6 +75,17 @@ __device__ __forceinline__ void wave_gemm(f32x4 (&acc)[MT][NT], const T* const (
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) mma(acc[mt][nt], fa[d][mt], fb[d][nt]);
     }
+}
+
+// SA / SB: operand read once per launch (weights), loaded non-temporally.
+template <typename T, int MT, int NT, int DEPTH, bool SA = false, bool SB = false>
+__device__ __forceinline__ void wave_gemm(f32x4 (&acc)[MT][NT], const T* const (&ap)[MT], const T* const (&bp)[NT],
+                                          int ksteps, int sa = 32, int sb = 32) {
+  Frag<T> fa[DEPTH][MT];
+  Frag<T> fb[DEPTH][NT];
+  wave_gemm_fill<T, MT, DEPTH, SA>(fa, ap, ksteps, sa);
+  wave_gemm_fill<T, NT, DEPTH, SB>(fb, bp, ksteps, sb);
+  wave_gemm_run<T, MT, NT, DEPTH, SA, SB>(acc, fa, fb, ap, bp, ksteps, sa, sb);
 }
 
 }  // namespace dg

@@ -229,12 +229,8 @@ __device__ __forceinline__ void moe_gate_up_body(const MoeArgs& a, f32x4 (*red)[
   const int sb = min(w * q, ks), se = min(sb + q, ks);
   const T* X = (const T*)a.X;
   const T* W = (const T*)a.W + (int64_t)e * 2 * a.F * a.d;
-  const T* ap[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int r = min(16 * mt + row16, rows - 1);
-    ap[mt] = X + (int64_t)a.perm[p0 + r] * a.d + 32 * sb + kq;
-  }
+  // the weight loads need only the tile: they are issued before the row gather's indices arrive
+  constexpr int D = MT == 1 ? Depth<T>::moe1 : Depth<T>::moe2;
   const T* bp[NT];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -242,12 +238,24 @@ __device__ __forceinline__ void moe_gate_up_body(const MoeArgs& a, f32x4 (*red)[
     bp[j] = tiled_frag(W, ct, ks, sb);
     bp[4 + j] = tiled_frag(W, a.F / 16 + ct, ks, sb);
   }
+  Frag<T> fb[D][NT];
+  if (se > sb) wave_gemm_fill<T, NT, D, NTL>(fb, bp, se - sb, kFragElems);
+  const T* ap[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int r = min(16 * mt + row16, rows - 1);
+    ap[mt] = X + (int64_t)a.perm[p0 + r] * a.d + 32 * sb + kq;
+  }
   f32x4 acc[MT][NT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = zero4();
-  if (se > sb) wave_gemm<T, MT, NT, (MT == 1 ? Depth<T>::moe1 : Depth<T>::moe2), false, NTL>(acc, ap, bp, se - sb, 32, kFragElems);
+  if (se > sb) {
+    Frag<T> fa[D][MT];
+    wave_gemm_fill<T, MT, D, false>(fa, ap, se - sb, 32);
+    wave_gemm_run<T, MT, NT, D, false, NTL>(acc, fa, fb, ap, bp, se - sb, 32, kFragElems);
+  }
   T* H = (T*)a.out;
   const int rq = (lane >> 4) * 4;
 #pragma unroll
