@@ -30,7 +30,7 @@ DG_F32, DG_BF16 = 0, 1
 DG_STOP_NONE, DG_STOP_ENTROPY, DG_STOP_STABLE, DG_STOP_CAP, DG_STOP_FIXED = 0, 1, 2, 3, 4
 DG_WARN_NUMERIC = 0x1
 EXPORTED = ("dg_workspace_size", "dg_prefill_kv", "dg_denoise_step", "dg_canvas_update", "dg_commit_block",
-            "dg_generate_block", "dg_layer_forward", "dg_vocab_head", "dg_stop_check", "dg_status_string",
+            "dg_generate_block", "dg_generate_block_overlapped", "dg_layer_forward", "dg_vocab_head", "dg_stop_check", "dg_status_string",
             "dg_last_hip_error", "dg_timing_start", "dg_timing_stop", "dg_packed_elems", "dg_pack_matrix")
 # kernel classes of dg_timing_* (dg_kernel in dg.h), in enum order
 KERNELS = ("embed", "rmsnorm", "gemm_qkv", "attention", "attn_merge", "gemm_o", "route",
@@ -100,6 +100,8 @@ _SIGS = {
     "dg_commit_block": [_P(dg_config), _P(dg_weights), _P(dg_kv), _vp, _vp, _sz, _vp],
     "dg_generate_block": [_P(dg_config), _P(dg_weights), _P(dg_kv), _P(dg_sampler), _u32, _vp, _P(dg_block_status),
                           _vp, _sz, _vp],
+    "dg_generate_block_overlapped": [_P(dg_config), _P(dg_weights), _P(dg_kv), _P(dg_sampler), _u32, _vp, _i32, _vp,
+                                     _P(dg_block_status), _vp, _sz, _vp],
     "dg_layer_forward": [_P(dg_config), _P(dg_weights), _i32, _P(dg_kv), _vp, _vp, _i64, _i32, _P(dg_debug), _vp,
                          _sz, _vp],
     "dg_vocab_head": [_P(dg_config), _P(dg_weights), _vp, _i64, _f32, _vp, _vp, _vp, _vp, _sz, _vp],
@@ -235,6 +237,16 @@ def dg_generate_block(cfg, weights, kv, sampler: dg_sampler, block: int, tokens_
     _check("dg_generate_block", _lib.dg_generate_block(ctypes.byref(cfg), _w(weights), _kv(kv),
                                                        ctypes.byref(sampler), block, _ptr(tokens_out),
                                                        ctypes.byref(st), _ptr(ws), ws_bytes, _stream(stream)))
+    return st
+
+
+def dg_generate_block_overlapped(cfg, weights, kv, sampler: dg_sampler, block: int, pending, defer_commit: int,
+                                 tokens_out, ws, ws_bytes: int, stream=None) -> dg_block_status:
+    st = dg_block_status()
+    _check("dg_generate_block_overlapped",
+           _lib.dg_generate_block_overlapped(ctypes.byref(cfg), _w(weights), _kv(kv), ctypes.byref(sampler), block,
+                                             _ptr(pending), defer_commit, _ptr(tokens_out), ctypes.byref(st),
+                                             _ptr(ws), ws_bytes, _stream(stream)))
     return st
 
 

@@ -275,9 +275,11 @@ int64_t rows_supported(const dg_config* c, size_t ws_bytes, int64_t limit) {
 // (fragment-tiled, so that layer skips its own RMSNorm), or the final-normalised rows for the head.
 enum class Next { None, NextLayer, Head };
 
+// One layer over M rows at cache positions pos0.. : rows [0, n_causal) attend causally (a prompt chunk
+// or a committed block), rows [n_causal, M) attend to every key [0, pos0 + M) (the canvas).
 template <typename T>
-int layer_t(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int64_t pos0, int64_t M, bool causal,
-            bool normed_in, Next next, const Ws& ws, hipStream_t s) {
+int layer_t(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int64_t pos0, int64_t M,
+            int64_t n_causal, bool normed_in, Next next, const Ws& ws, hipStream_t s) {
   const dg_layer_weights& L = w->h_layers[l];
   const int d = c->d_model, hq = c->n_heads, hkv = c->n_kv_heads, dh = c->head_dim;
   const int E = c->n_experts, k = c->top_k;
@@ -296,14 +298,23 @@ int layer_t(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int
   g.cap = kv->capacity; g.pos0 = pos0;
   DG_LAUNCH(DG_K_GEMM_QKV, s, launch_gemm<T>(GemmEpi::QKV, g, s));
 
-  AttnArgs at{};
-  at.q = ws.Q; at.kc = kbase; at.vc = vbase; at.o_part = ws.opart; at.ml_part = ws.mlpart; at.o = ws.O;
-  at.q_rows = Mi; at.n_heads = hq; at.n_kv_heads = hkv; at.head_dim = dh; at.cap = kv->capacity;
-  at.n_keys = pos0 + M; at.q_pos0 = pos0; at.causal = causal ? 1 : 0;
-  const int max_split = (int)std::min<int64_t>(kAttnMaxSplit, std::max<int64_t>(1, std::max(kPartialRows, M) / M));
-  at.n_split = attention_splits(at.n_keys, Mi, hq, hkv, at.causal, max_split);
-  DG_LAUNCH(DG_K_ATTENTION, s, launch_attention<T>(at, s));
-  DG_LAUNCH(DG_K_ATTN_MERGE, s, launch_attention_merge<T>(at, s));
+  // attention: one launch (and merge) per row range of one mask
+  auto attend = [&](int64_t row0, int64_t rows, bool causal) -> int {
+    AttnArgs at{};
+    at.q = ws.Q; at.kc = kbase; at.vc = vbase; at.o_part = ws.opart; at.ml_part = ws.mlpart; at.o = ws.O;
+    at.q_rows = (int)rows; at.q_stride = Mi; at.row0 = (int)row0; at.n_heads = hq; at.n_kv_heads = hkv;
+    at.head_dim = dh; at.cap = kv->capacity;
+    at.n_keys = causal ? pos0 + row0 + rows : pos0 + M;
+    at.q_pos0 = pos0 + row0; at.causal = causal ? 1 : 0;
+    const int max_split =
+        (int)std::min<int64_t>(kAttnMaxSplit, std::max<int64_t>(1, std::max(kPartialRows, M) / rows));
+    at.n_split = attention_splits(at.n_keys, (int)rows, hq, hkv, at.causal, max_split);
+    DG_LAUNCH(DG_K_ATTENTION, s, launch_attention<T>(at, s));
+    DG_LAUNCH(DG_K_ATTN_MERGE, s, launch_attention_merge<T>(at, s));
+    return DG_OK;
+  };
+  if (n_causal > 0) DG_CHECK(attend(0, n_causal, true));
+  if (n_causal < M) DG_CHECK(attend(n_causal, M - n_causal, false));
 
   g = GemmArgs{};
   g.A = ws.O; g.a_tiled = 1; g.B = L.wo; g.C = ws.X; g.M = Mi; g.N = d; g.K = hq * dh; g.lda = hq * dh; g.ldb = hq * dh; g.ldc = d;
@@ -351,35 +362,42 @@ int layer_t(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int
   return DG_OK;
 }
 
-int layer(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int64_t pos0, int64_t M, bool causal,
+int layer(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int64_t pos0, int64_t M, int64_t n_causal,
           bool normed_in, Next next, const Ws& ws, hipStream_t s) {
-  if (c->dtype == DG_BF16) return layer_t<bf16>(c, w, l, kv, pos0, M, causal, normed_in, next, ws, s);
-  return layer_t<float>(c, w, l, kv, pos0, M, causal, normed_in, next, ws, s);
+  if (c->dtype == DG_BF16) return layer_t<bf16>(c, w, l, kv, pos0, M, n_causal, normed_in, next, ws, s);
+  return layer_t<float>(c, w, l, kv, pos0, M, n_causal, normed_in, next, ws, s);
 }
 
-int embed(const dg_config* c, const dg_weights* w, const int32_t* tok, int64_t M, const Ws& ws, hipStream_t s) {
+// rows [row0, row0 + M) of ws.X = embeddings of tok[0, M)
+int embed(const dg_config* c, const dg_weights* w, const int32_t* tok, int64_t M, const Ws& ws, hipStream_t s,
+          int64_t row0 = 0) {
+  const int64_t off = row0 * c->d_model;
   if (c->dtype == DG_BF16)
-    DG_LAUNCH(DG_K_EMBED, s, launch_embed<bf16>(tok, (const bf16*)w->embed, (bf16*)ws.X, (int)M, c->d_model, c->vocab, s));
+    DG_LAUNCH(DG_K_EMBED, s, launch_embed<bf16>(tok, (const bf16*)w->embed, (bf16*)ws.X + off, (int)M, c->d_model,
+                                                 c->vocab, s));
   else
-    DG_LAUNCH(DG_K_EMBED, s, launch_embed<float>(tok, (const float*)w->embed, (float*)ws.X, (int)M, c->d_model, c->vocab, s));
+    DG_LAUNCH(DG_K_EMBED, s, launch_embed<float>(tok, (const float*)w->embed, (float*)ws.X + off, (int)M, c->d_model,
+                                                  c->vocab, s));
   return DG_OK;
 }
 
-// final norm (unless normed: ws.Xn already holds it) + fused head over M rows of ws.X
+// final norm (unless normed: ws.Xn already holds it) + fused head over rows [row0, row0 + M) of ws.X
 int head(const dg_config* c, const dg_weights* w, int64_t M, float inv_temp, int32_t* pred, float* conf, float* ent,
-         bool normed, const Ws& ws, hipStream_t s) {
+         bool normed, const Ws& ws, hipStream_t s, int64_t row0 = 0) {
   HeadArgs h{};
-  h.x = ws.Xn; h.E = w->embed; h.part = ws.hpart; h.n = (int)M; h.d = c->d_model; h.V = c->vocab;
+  h.x = (const char*)ws.Xn + row0 * c->d_model * esize(c); h.E = w->embed; h.part = ws.hpart; h.n = (int)M; h.d = c->d_model; h.V = c->vocab;
   h.n_groups = head_groups(c->vocab); h.beta_log2e = inv_temp * 1.4426950408889634f;
   h.pred = pred; h.conf = conf; h.ent = ent;
   if (c->dtype == DG_BF16) {
     if (!normed)
-      DG_LAUNCH(DG_K_RMSNORM, s, launch_rmsnorm<bf16>((const bf16*)ws.X, (const bf16*)w->final_norm, (bf16*)ws.Xn,
-                                                       nullptr, (int)M, c->d_model, c->rms_eps, s));
+      DG_LAUNCH(DG_K_RMSNORM, s, launch_rmsnorm<bf16>((const bf16*)ws.X + row0 * c->d_model, (const bf16*)w->final_norm,
+                                                       (bf16*)ws.Xn + row0 * c->d_model, nullptr, (int)M, c->d_model,
+                                                       c->rms_eps, s));
     DG_LAUNCH(DG_K_VOCAB_HEAD, s, launch_vocab_head<bf16>(h, s));
   } else {
     if (!normed)
-      DG_LAUNCH(DG_K_RMSNORM, s, launch_rmsnorm<float>((const float*)ws.X, (const float*)w->final_norm, (float*)ws.Xn,
+      DG_LAUNCH(DG_K_RMSNORM, s, launch_rmsnorm<float>((const float*)ws.X + row0 * c->d_model,
+                                                        (const float*)w->final_norm, (float*)ws.Xn + row0 * c->d_model,
                                                         nullptr, (int)M, c->d_model, c->rms_eps, s));
     DG_LAUNCH(DG_K_VOCAB_HEAD, s, launch_vocab_head<float>(h, s));
   }
@@ -394,7 +412,7 @@ int denoise(const dg_config* c, const dg_weights* w, const dg_kv* kv, const int3
   DG_CHECK(embed(c, w, canvas, S, ws, s));
   const int L = c->n_layers;
   for (int l = 0; l < L; ++l) {
-    DG_CHECK(layer(c, w, l, kv, kv->len, S, false, l > 0, l + 1 < L ? Next::NextLayer : Next::Head, ws, s));
+    DG_CHECK(layer(c, w, l, kv, kv->len, S, 0, l > 0, l + 1 < L ? Next::NextLayer : Next::Head, ws, s));
     if (dbg) {
       const size_t hb = (size_t)S * c->d_model * esize(c);
       if (dbg->hidden) DG_TRY(hipMemcpyAsync((char*)dbg->hidden + l * hb, ws.X, hb, hipMemcpyDeviceToDevice, s));
@@ -410,6 +428,22 @@ int denoise(const dg_config* c, const dg_weights* w, const dg_kv* kv, const int3
   return head(c, w, S, inv_temp, pred, conf, ent, L > 0, ws, s);
 }
 
+// A pass that also commits the previous block: rows [0, S) are that block's tokens at cache rows
+// len.. (causal: they become its committed keys and values), rows [S, 2S) are the canvas (scratch rows
+// len + S..).  Every weight is streamed once for both; the head runs on the canvas rows only.  The
+// caller advances kv->len by S afterwards.
+int denoise_committing(const dg_config* c, const dg_weights* w, const dg_kv* kv, const int32_t* block_tokens,
+                       const int32_t* canvas, float inv_temp, int32_t* pred, float* conf, float* ent, const Ws& ws,
+                       hipStream_t s) {
+  const int64_t S = c->canvas;
+  DG_CHECK(embed(c, w, block_tokens, S, ws, s, 0));
+  DG_CHECK(embed(c, w, canvas, S, ws, s, S));
+  const int L = c->n_layers;
+  for (int l = 0; l < L; ++l)
+    DG_CHECK(layer(c, w, l, kv, kv->len, 2 * S, S, l > 0, l + 1 < L ? Next::NextLayer : Next::Head, ws, s));
+  return head(c, w, S, inv_temp, pred, conf, ent, L > 0, ws, s, S);
+}
+
 // causal forward of n tokens at kv->len.., chunked to the workspace; does not change kv->len
 int prefill(const dg_config* c, const dg_weights* w, const dg_kv* kv, const int32_t* tokens, int64_t n, void* wsp,
             size_t ws_bytes, hipStream_t s) {
@@ -421,7 +455,7 @@ int prefill(const dg_config* c, const dg_weights* w, const dg_kv* kv, const int3
     DG_CHECK(embed(c, w, tokens + r0, m, ws, s));
     const int L = c->n_layers;
     for (int l = 0; l < L; ++l)
-      DG_CHECK(layer(c, w, l, kv, kv->len + r0, m, true, l > 0, l + 1 < L ? Next::NextLayer : Next::None, ws, s));
+      DG_CHECK(layer(c, w, l, kv, kv->len + r0, m, m, l > 0, l + 1 < L ? Next::NextLayer : Next::None, ws, s));
   }
   return DG_OK;
 }
@@ -497,17 +531,19 @@ int dg_commit_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const 
   return dg_prefill_kv(cfg, w, kv, block_tokens, cfg ? cfg->canvas : 0, ws, ws_bytes, stream);
 }
 
-int dg_generate_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const dg_sampler* sp, uint32_t block,
-                      int32_t* tokens_out, dg_block_status* h_status, void* ws, size_t ws_bytes, void* stream) {
+int dg_generate_block_overlapped(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const dg_sampler* sp,
+                                 uint32_t block, const int32_t* pending, int32_t defer_commit, int32_t* tokens_out,
+                                 dg_block_status* h_status, void* ws, size_t ws_bytes, void* stream) {
   DG_CHECK(check_cfg(cfg));
   DG_CHECK(check_weights(cfg, w, true, true));
   DG_CHECK(check_sampler(cfg, sp));
-  if (!tokens_out || !h_status) return DG_ERR_INVALID;
-  DG_CHECK(check_kv(kv, cfg->canvas));
-  DG_CHECK(check_ws(cfg, cfg->canvas, ws, ws_bytes));
-  hipStream_t s = (hipStream_t)stream;
+  if (!tokens_out || !h_status || (defer_commit != 0 && defer_commit != 1)) return DG_ERR_INVALID;
   const int S = cfg->canvas;
-  Ws wsv = carve(cfg, S, (char*)ws);
+  const int64_t rows = pending ? 2 * (int64_t)S : S;  // the first pass also commits `pending`
+  DG_CHECK(check_kv(kv, rows));
+  DG_CHECK(check_ws(cfg, rows, ws, ws_bytes));
+  hipStream_t s = (hipStream_t)stream;
+  Ws wsv = carve(cfg, rows, (char*)ws);
   const StopParams stp = stop_params(cfg, sp);
   const bool fixed = sp->fixed_steps > 0;
   const int limit = fixed ? sp->fixed_steps : sp->max_steps;
@@ -517,7 +553,13 @@ int dg_generate_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, cons
                                  nullptr, s));
   dg_block_status st{};
   for (int t = 1;; ++t) {
-    DG_CHECK(denoise(cfg, w, kv, wsv.canvas, sp->inv_temperature, wsv.pred, wsv.conf, wsv.ent, nullptr, wsv, s));
+    if (t == 1 && pending) {
+      DG_CHECK(denoise_committing(cfg, w, kv, pending, wsv.canvas, sp->inv_temperature, wsv.pred, wsv.conf, wsv.ent,
+                                  wsv, s));
+      kv->len += S;  // the pending block is committed (in stream order) before every later pass
+    } else {
+      DG_CHECK(denoise(cfg, w, kv, wsv.canvas, sp->inv_temperature, wsv.pred, wsv.conf, wsv.ent, nullptr, wsv, s));
+    }
     DG_LAUNCH(DG_K_STOP_CHECK, s, launch_stop_check(wsv.ent, wsv.pred, wsv.prev_pred, S, t, stp, wsv.status, s));
     bool stop;
     if (fixed) {
@@ -536,11 +578,18 @@ int dg_generate_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, cons
   DG_TRY(hipMemcpyAsync(tokens_out, wsv.pred, (size_t)S * 4, hipMemcpyDeviceToDevice, s));
   // read the status before the commit reuses the workspace
   if (fixed) DG_TRY(hipMemcpyAsync(&st, wsv.status, sizeof(st), hipMemcpyDeviceToHost, s));
-  DG_CHECK(prefill(cfg, w, kv, tokens_out, S, ws, ws_bytes, s));
-  kv->len += S;
+  if (!defer_commit) {
+    DG_CHECK(prefill(cfg, w, kv, tokens_out, S, ws, ws_bytes, s));
+    kv->len += S;
+  }
   DG_TRY(hipStreamSynchronize(s));
   *h_status = st;
   return DG_OK;
+}
+
+int dg_generate_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const dg_sampler* sp, uint32_t block,
+                      int32_t* tokens_out, dg_block_status* h_status, void* ws, size_t ws_bytes, void* stream) {
+  return dg_generate_block_overlapped(cfg, w, kv, sp, block, nullptr, 0, tokens_out, h_status, ws, ws_bytes, stream);
 }
 
 int dg_layer_forward(const dg_config* cfg, const dg_weights* w, int32_t layer_i, const dg_kv* kv, const void* x_in,
@@ -557,7 +606,7 @@ int dg_layer_forward(const dg_config* cfg, const dg_weights* w, int32_t layer_i,
   Ws wsv = carve(cfg, n, (char*)ws);
   const size_t hb = (size_t)n * cfg->d_model * esize(cfg);
   DG_TRY(hipMemcpyAsync(wsv.X, x_in, hb, hipMemcpyDeviceToDevice, s));
-  DG_CHECK(layer(cfg, w, layer_i, kv, kv->len, n, causal != 0, false, Next::None, wsv, s));
+  DG_CHECK(layer(cfg, w, layer_i, kv, kv->len, n, causal != 0 ? n : 0, false, Next::None, wsv, s));
   DG_TRY(hipMemcpyAsync(x_out, wsv.X, hb, hipMemcpyDeviceToDevice, s));
   if (dbg) {
     const size_t rb = (size_t)n * cfg->top_k * 4;

@@ -119,13 +119,15 @@ hipError_t launch_moe_down(const MoeArgs& a, hipStream_t s);
 
 // ---- k_attn.hip
 struct AttnArgs {
-  const void* q;      // [Hq][q_rows][Dh]
+  const void* q;      // [Hq][q_stride][Dh]; this launch's queries are rows [row0, row0 + q_rows) of each head
   const void* kc;     // [Hkv][cap][Dh]
   const void* vc;     // [Hkv][Dh][cap]
   float* o_part;      // [n_split][Hq][q_rows][Dh]
   float* ml_part;     // [n_split][Hq][q_rows][2]  (running max in log2 units, sum)
-  void* o;            // [q_rows][Hq*Dh], fragment-tiled (rows padded to 16)
-  int q_rows;         // M
+  void* o;            // [layer rows][Hq*Dh], fragment-tiled (rows padded to 16); this launch writes rows row0..
+  int q_rows;         // query rows of this launch
+  int q_stride;       // rows per head in q (the layer's rows)
+  int row0;           // first row of this launch in q and in o
   int n_heads, n_kv_heads, head_dim;
   int64_t cap;
   int64_t n_keys;     // keys visible: [0, n_keys)

@@ -165,7 +165,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_attn(AttnArgs a) {
   for (int qt = 0; qt < QT; ++qt) {
     const int mq = q0 + 16 * qt + row16;
     my_pos[qt] = a.q_pos0 + mq;
-    const T* qrow = (const T*)a.q + ((int64_t)h * a.q_rows + min(mq, a.q_rows - 1)) * DH + quad * 8;
+    const T* qrow = (const T*)a.q + ((int64_t)h * a.q_stride + a.row0 + min(mq, a.q_rows - 1)) * DH + quad * 8;
 #pragma unroll
     for (int ks = 0; ks < C::KF; ++ks) qf[qt][ks].load(qrow + 32 * ks);
   }
@@ -378,7 +378,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const float inv = L > 0.f ? 1.0f / L : 0.f;
 #pragma unroll
   for (int t = 0; t < 8; ++t) acc[t] *= inv;
-  Vec8<T>::store((T*)a.o + tiled_offset(m, h * DH + c, a.n_heads * DH), acc);
+  Vec8<T>::store((T*)a.o + tiled_offset(a.row0 + m, h * DH + c, a.n_heads * DH), acc);
 }
 
 // Key splits: enough workgroups to cover the chip (~256), at least two key chunks per split, and then

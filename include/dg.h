@@ -244,6 +244,25 @@ int dg_generate_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, cons
                       uint32_t block, int32_t* tokens_out, dg_block_status* h_status, void* ws,
                       size_t ws_bytes, void* stream);
 
+/* dg_generate_block with each commit overlapped on the next block's first pass.  The commit
+ * and a pass are both a forward of 256 rows through every layer, and the expert and head
+ * weights dominate their cost, so one forward of both row sets streams the weights once.
+ * pending (nullable, device [canvas]): tokens of an earlier block generated with
+ * defer_commit = 1 and not yet committed.  They are committed at kv->len inside this
+ * block's first pass: rows 0 .. canvas-1 of that forward attend causally and their keys and
+ * values become cache rows kv->len ..; then kv->len grows by canvas before the later passes.
+ * defer_commit (0 or 1): with 1 this block's tokens (tokens_out) are not committed; pass them
+ * as `pending` to the next call or commit them with dg_commit_block.  pending may alias
+ * tokens_out (it is read in the first pass, before tokens_out is written).  With pending,
+ * the workspace and the cache must hold 2 * canvas rows (dg_workspace_size(cfg, 2 * canvas,
+ * ...); kv->len + 2 * canvas <= capacity).  The tokens and cache equal those of
+ * dg_generate_block on the same blocks up to the summation order of the attention splits.
+ * Errors as dg_generate_block; DG_ERR_INVALID also for defer_commit not 0 or 1. */
+int dg_generate_block_overlapped(const dg_config* cfg, const dg_weights* w, dg_kv* kv,
+                                 const dg_sampler* sampler, uint32_t block, const int32_t* pending,
+                                 int32_t defer_commit, int32_t* tokens_out, dg_block_status* h_status,
+                                 void* ws, size_t ws_bytes, void* stream);
+
 /* --- finer-grained calls of the same path (each is one stage of dg_denoise_step) --- */
 
 /* One transformer block `layer` over n hidden rows x_in -> x_out ([n, d_model];

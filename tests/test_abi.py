@@ -26,6 +26,7 @@ def _declared():
 def test_header_declares_the_documented_calls():
     names = _declared()
     for n in ("dg_prefill_kv", "dg_denoise_step", "dg_canvas_update", "dg_commit_block", "dg_generate_block",
+              "dg_generate_block_overlapped",
               "dg_workspace_size", "dg_status_string"):
         assert n in names
     assert set(names) == set(dg.EXPORTED)
@@ -165,6 +166,16 @@ def test_calls_validate_before_any_device_work():
     with pytest.raises(dg.DGError) as e:
         dg.dg_generate_block(cfg, w, kv, bad, 0, buf, buf, ws_bytes, 0)
     assert e.value.status == dg.DG_ERR_INVALID
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_generate_block_overlapped(cfg, w, kv, dg.make_sampler(4), 0, None, 2, buf, buf, ws_bytes, 0)
+    assert e.value.status == dg.DG_ERR_INVALID
+    kv_short = dg.KV(buf, buf, capacity=64, length=16)  # 16 + 2 * 32 > 64: a pending block needs two canvases
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_generate_block_overlapped(cfg, w, kv_short, dg.make_sampler(4), 0, buf, 1, buf, buf, ws_bytes, 0)
+    assert e.value.status == dg.DG_ERR_KV_FULL
+    with pytest.raises(dg.DGError) as e:  # the workspace holds one canvas of rows, a pending block needs two
+        dg.dg_generate_block_overlapped(cfg, w, kv, dg.make_sampler(4), 0, buf, 1, buf, buf, ws_bytes, 0)
+    assert e.value.status == dg.DG_ERR_WORKSPACE
     with pytest.raises(dg.DGError) as e:
         dg.dg_stop_check(cfg, dg.make_sampler(4), 0, buf, buf, buf, buf, 0)
     assert e.value.status == dg.DG_ERR_INVALID

@@ -207,6 +207,55 @@ def test_c0_generate_block_equals_step_loop_and_oracle():
     _check_kv(sess2, kv, F32_TOL)
 
 
+def test_c0_overlapped_commits_equal_oracle_blocks():
+    """Three blocks, each block's commit overlapped on the next block's first pass (that forward carries the
+    committed rows causally and the canvas rows bidirectionally); the last block commits at its end.  Same
+    steps, tokens and cache as the oracle's three plain blocks."""
+    d = recipe.C0.dims
+    sess, model, kv = _c0_pair()
+    outs = [sess.i32(d.canvas) for _ in range(3)]
+    pending = None
+    for b in range(3):
+        st = dg.dg_generate_block_overlapped(sess.cfg, sess.weights, sess.kv, dg.make_sampler(recipe.C0.n_new), b,
+                                             pending, 1 if b < 2 else 0, outs[b], sess.ws, sess.ws_bytes)
+        res = osm.generate_block(model, kv, osm.Sampler(n_new=recipe.C0.n_new), block=b)
+        log(f"C0 overlapped block {b}: GPU {st.steps} ({st.reason}), oracle {res.steps} ({res.reason})")
+        assert (res.steps, res.reason) == (st.steps, st.reason)
+        assert np.array_equal(res.tokens, outs[b].cpu().numpy())
+        assert sess.kv.len == recipe.C0.prefix + d.canvas * (b if b < 2 else 3)
+        pending = outs[b]
+    _check_kv(sess, kv, F32_TOL)
+
+
+def test_bf16_overlapped_commits_equal_plain_blocks():
+    """bf16: the overlapped form gives the plain form's tokens (fixed T) and cache up to bf16 rounding."""
+    d = replace(recipe.C0.dims, dtype="bf16")
+    storage = dg_inputs.model_weights_host(d)
+    sp = dg.make_sampler(recipe.C0.n_new, fixed_steps=4)
+    runs = []
+    for overlapped in (False, True):
+        sess, _, _ = _c0_pair(d, storage)
+        outs = [sess.i32(d.canvas) for _ in range(3)]
+        pending = None
+        for b in range(3):
+            if overlapped:
+                dg.dg_generate_block_overlapped(sess.cfg, sess.weights, sess.kv, sp, b, pending, 1 if b < 2 else 0,
+                                                outs[b], sess.ws, sess.ws_bytes)
+                pending = outs[b]
+            else:
+                dg.dg_generate_block(sess.cfg, sess.weights, sess.kv, sp, b, outs[b], sess.ws, sess.ws_bytes)
+        torch.cuda.synchronize()
+        runs.append((sess, [o.cpu().numpy() for o in outs]))
+    (plain, tp), (over, to) = runs
+    for b in range(3):
+        assert np.mean(tp[b] == to[b]) > 0.9, b
+    assert plain.kv.len == over.kv.len
+    for l in range(d.n_layers):
+        for a, c in zip(plain.kv_numpy(l, plain.kv.len), over.kv_numpy(l, over.kv.len)):
+            ok, worst, at = allclose_report(c, a, *BF16_TOL)
+            assert ok, (l, worst, at)
+
+
 def test_c0_fixed_T_block():
     d = recipe.C0.dims
     sess, model, kv = _c0_pair()
