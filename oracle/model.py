@@ -28,6 +28,7 @@ from typing import List, Optional
 import numpy as np
 
 from .numerics import f32, from_storage, rounder
+from .philox import gumbel_noise
 
 
 # ----------------------------------------------------------------------------- building blocks
@@ -245,12 +246,13 @@ class Model:
             traces.append(tr)
         return x, traces
 
-    def head(self, x: np.ndarray, inv_temperature: float = 1.0):
-        return head_stats(x, self.w["final_norm"], self.w["embed"], inv_temperature, self.d.rms_eps, self.rnd)
+    def head(self, x: np.ndarray, inv_temperature: float = 1.0, gumbel=None):
+        return head_stats(x, self.w["final_norm"], self.w["embed"], inv_temperature, self.d.rms_eps, self.rnd,
+                          gumbel=gumbel)
 
 
 def head_stats(x: np.ndarray, g_final: np.ndarray, embed: np.ndarray, inv_temperature: float, eps: float, rnd,
-               chunk: int = 64):
+               chunk: int = 64, gumbel=None):
     """Final norm, tied vocab projection and per-slot softmax statistics.
 
     logits = beta * (rms(x) * g) E^T; pred = argmax (fp32 logits, ties to the lowest
@@ -259,6 +261,12 @@ def head_stats(x: np.ndarray, g_final: np.ndarray, embed: np.ndarray, inv_temper
     works"); ent = -sum_v p ln p in nats, 0 ln 0 = 0 (the entropy the stop rule averages,
     [P2] "How Diffusion Changes the Equation").  Also returns the fp32 top-2 logit
     margin of each slot.
+
+    gumbel = (seed, block, step) samples instead of taking the argmax (the recommended
+    sampler's temperature, [P2] "Architecture Details"): pred = argmax of the fp32
+    perturbed score logits + G, G from oracle.philox.gumbel_noise with row i as slot i
+    (ties to the lowest id); conf = p[pred], the probability of the token drawn; the
+    margin is then the top-2 gap of the perturbed scores.  The entropy is unchanged.
     """
     xf = rnd(rmsnorm(x, g_final, eps))
     n = xf.shape[0]
@@ -268,14 +276,19 @@ def head_stats(x: np.ndarray, g_final: np.ndarray, embed: np.ndarray, inv_temper
     margin = np.empty(n)
     for s0 in range(0, n, chunk):
         lg = inv_temperature * (xf[s0:s0 + chunk] @ embed.T)
-        l32 = f32(lg)
-        pred[s0:s0 + chunk] = np.argmax(l32, axis=1)
+        score = lg
+        if gumbel is not None:
+            seed, block, step = gumbel
+            score = lg + gumbel_noise(seed, block, step, np.arange(s0, s0 + lg.shape[0]), lg.shape[1])
+        l32 = f32(score)
+        choice = np.argmax(l32, axis=1)
+        pred[s0:s0 + chunk] = choice
         top2 = -np.partition(-l32, 1, axis=1)[:, :2]
         margin[s0:s0 + chunk] = top2[:, 0] - top2[:, 1]
         m = lg.max(axis=1, keepdims=True)
         e = np.exp(lg - m)
         p = e / e.sum(axis=1, keepdims=True)
-        conf[s0:s0 + chunk] = p.max(axis=1)
+        conf[s0:s0 + chunk] = p.max(axis=1) if gumbel is None else p[np.arange(p.shape[0]), choice]
         with np.errstate(divide="ignore", invalid="ignore"):
             plogp = np.where(p > 0, p * np.log(p), 0.0)
         ent[s0:s0 + chunk] = -plogp.sum(axis=1)

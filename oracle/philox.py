@@ -55,3 +55,32 @@ def uniform_tokens(seed: int, block: int, step: int, slots, vocab: int) -> np.nd
            np.zeros(n, dtype=np.uint64))
     w0 = philox4x32_10(ctr, key)[0]
     return ((w0 * np.uint64(vocab)) >> np.uint64(32)).astype(np.int64)
+
+
+def gumbel_noise(seed: int, block: int, step: int, slots, vocab: int) -> np.ndarray:
+    """Standard Gumbel noise G[i, v] for slot ``slots[i]`` and token v, float64 [len(slots), vocab].
+
+    The recommended sampler draws each slot's token from the softmax at the pass's
+    temperature ([P2] "Architecture Details": the temperature falls linearly from 0.8
+    to 0.4 over the passes; [P5] "Appendix: Methodology", "Decoding").  This build samples with the Gumbel-max identity
+    (E. J. Gumbel, 1954; argmax_v (l_v + G_v) with i.i.d. standard Gumbel G_v is
+    distributed as softmax(l)), which needs one uniform per (slot, token):
+        w = word (v mod 4) of Philox4x32-10(key = (seed mod 2^32, seed div 2^32),
+                                            counter = (v div 4, slot + 2^16 step, block, 1)),
+        u = (2 floor(w / 2^9) + 1) / 2^24          (exact in fp32, never 0 or 1),
+        G = -ln(-ln u).
+    Counter word 3 is 1 here and 0 for the canvas draws, so the two streams never share
+    a counter.  Slots and steps must stay below 2^16.
+    """
+    slots = np.asarray(slots, dtype=np.uint64)
+    nq = (vocab + 3) // 4
+    n = slots.shape[0]
+    key = (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
+    c0 = np.broadcast_to(np.arange(nq, dtype=np.uint64)[None, :], (n, nq))
+    c1 = np.broadcast_to((slots + (np.uint64(step) << np.uint64(16)))[:, None], (n, nq))
+    c2 = np.full((n, nq), block, dtype=np.uint64)
+    c3 = np.ones((n, nq), dtype=np.uint64)
+    words = philox4x32_10((c0, c1, c2, c3), key)
+    w = np.stack(words, axis=-1).reshape(n, 4 * nq)[:, :vocab]
+    u = (2.0 * (w >> np.uint64(9)).astype(np.float64) + 1.0) / float(1 << 24)
+    return -np.log(-np.log(u))

@@ -18,11 +18,25 @@ by fp32 confidence, descending, ties to the lower slot, NaN last; stability
 compares predictions (not the canvas) and can first fire at t = 2; the
 committed block is the last pass's predictions, written to the cache by a
 causal forward over the block.
+
+Variants of the recommended sampler ([P2] "Architecture Details"; [P5] "Appendix:
+Methodology", "Decoding"), each off by default:
+  * gumbel: each slot's token is drawn from the softmax at the pass's temperature
+    (Gumbel-max, oracle.philox.gumbel_noise) instead of taken as the argmax;
+    confidence is then the probability of the token drawn;
+  * anneal (T_first, T_last): the temperature falls linearly from T_first at pass 1
+    to T_last at the last pass of the budget (fixed_steps when set, else max_steps);
+  * rank_entropy: the keep rule takes the lowest-entropy slots first (fp32 entropy,
+    ascending, ties to the lower slot, NaN last) instead of the most confident;
+  * lock: a kept slot keeps its token for the rest of the block: its prediction is
+    its token, later passes only add slots until k_t are locked;
+  * stop_and: the early stop needs low mean entropy AND two unchanged passes
+    together (the cap still applies); reason STOP_SETTLED.
 """
 from __future__ import annotations
 
 from dataclasses import dataclass, field
-from typing import List, Optional
+from typing import List, Optional, Tuple
 
 import numpy as np
 
@@ -30,7 +44,7 @@ from .model import KVCache, Model
 from .numerics import f32
 from .philox import uniform_tokens
 
-STOP_NONE, STOP_ENTROPY, STOP_STABLE, STOP_CAP, STOP_FIXED = 0, 1, 2, 3, 4
+STOP_NONE, STOP_ENTROPY, STOP_STABLE, STOP_CAP, STOP_FIXED, STOP_SETTLED = 0, 1, 2, 3, 4, 5
 
 
 @dataclass
@@ -41,6 +55,21 @@ class Sampler:
     fixed_steps: int = 0          # >0: run exactly this many passes (timing mode), no early stop
     seed: int = 1
     inv_temperature: float = 1.0
+    gumbel: bool = False
+    anneal: Optional[Tuple[float, float]] = None
+    rank_entropy: bool = False
+    lock: bool = False
+    stop_and: bool = False
+
+
+def pass_inv_temperature(s: Sampler, step: int) -> float:
+    """1 / T of pass ``step`` (1-based): constant, or linear in T over the pass budget."""
+    if s.anneal is None:
+        return float(s.inv_temperature)
+    t_first, t_last = s.anneal
+    n = s.fixed_steps if s.fixed_steps > 0 else s.max_steps
+    frac = 0.0 if n <= 1 else min(1.0, (step - 1) / (n - 1))
+    return 1.0 / (t_first + (t_last - t_first) * frac)
 
 
 def keep_count(step: int, n_new: int, slots: int) -> int:
@@ -58,23 +87,58 @@ def keep_mask(conf, k: int) -> np.ndarray:
     return mask
 
 
+def rank_key(conf, ent, rank_entropy: bool) -> np.ndarray:
+    """Larger ranks first: fp32 confidence, or minus the fp32 entropy."""
+    return -f32(ent) if rank_entropy else f32(conf)
+
+
+def select_keep(key, k: int, locked=None) -> np.ndarray:
+    """Locked slots, then the best unlocked slots by ``key`` (descending, ties to the lower
+    slot, NaN last) until k slots are selected (more if more are locked)."""
+    c = np.asarray(key)
+    key = np.where(np.isnan(c), -np.inf, c)
+    if locked is not None:
+        key = np.where(locked, np.inf, key)
+    order = np.argsort(-key, kind="stable")
+    mask = np.zeros(c.shape[0], dtype=bool)
+    mask[order[:k]] = True
+    if locked is not None:
+        mask |= locked
+    return mask
+
+
 def initial_canvas(seed: int, block: int, slots: int, vocab: int) -> np.ndarray:
     return uniform_tokens(seed, block, 0, np.arange(slots), vocab)
 
 
-def canvas_update(pred, conf, k: int, seed: int, block: int, step: int, vocab: int):
-    """Kept slots take the prediction; every other slot takes a fresh uniform draw."""
-    mask = keep_mask(conf, k)
+def canvas_update(pred, conf, k: int, seed: int, block: int, step: int, vocab: int, ent=None,
+                  rank_entropy: bool = False, locked=None, canvas=None):
+    """Kept slots take the prediction; every other slot takes a fresh uniform draw.
+
+    With ``locked`` (the lock variant) the locked slots stay kept and keep their token
+    ``canvas``; newly kept slots take the prediction."""
+    if rank_entropy or locked is not None:
+        mask = select_keep(rank_key(conf, ent, rank_entropy), k, locked)
+    else:
+        mask = keep_mask(conf, k)
     fresh = uniform_tokens(seed, block, step, np.arange(len(mask)), vocab)
-    return np.where(mask, np.asarray(pred, dtype=np.int64), fresh), mask
+    take = np.asarray(pred, dtype=np.int64)
+    if locked is not None:
+        take = np.where(locked, np.asarray(canvas, dtype=np.int64), take)
+    return np.where(mask, take, fresh), mask
 
 
 def stop_reason(step: int, mean_entropy: float, pred, prev_pred, s: Sampler) -> int:
     if s.fixed_steps > 0:
         return STOP_FIXED if step >= s.fixed_steps else STOP_NONE
-    if mean_entropy < s.entropy_threshold:
+    low = mean_entropy < s.entropy_threshold
+    stable = prev_pred is not None and step >= 2 and np.array_equal(pred, prev_pred)
+    if s.stop_and:
+        if low and stable:
+            return STOP_SETTLED
+    elif low:
         return STOP_ENTROPY
-    if prev_pred is not None and step >= 2 and np.array_equal(pred, prev_pred):
+    elif stable:
         return STOP_STABLE
     if step >= s.max_steps:
         return STOP_CAP
@@ -101,11 +165,13 @@ class BlockResult:
     passes: List[PassRecord]
 
 
-def denoise_pass(model: Model, kv: KVCache, canvas, inv_temperature: float = 1.0, keep_traces: bool = False):
-    """One pass: embed the canvas, run every block bidirectionally over cache + canvas, then the head."""
+def denoise_pass(model: Model, kv: KVCache, canvas, inv_temperature: float = 1.0, keep_traces: bool = False,
+                 gumbel=None):
+    """One pass: embed the canvas, run every block bidirectionally over cache + canvas, then the head
+    (gumbel = (seed, block, step) draws the tokens instead of taking the argmax)."""
     x = model.embed(canvas)
     x, traces = model.body(x, kv, causal=False, append=False)
-    pred, conf, ent, margin = model.head(x, inv_temperature)
+    pred, conf, ent, margin = model.head(x, inv_temperature, gumbel)
     rec = PassRecord(canvas=np.asarray(canvas), pred=pred, conf=conf, ent=ent, margin=margin)
     if keep_traces:
         rec.traces = traces
@@ -127,20 +193,27 @@ def generate_block(model: Model, kv: KVCache, s: Sampler, block: int, keep_trace
     d = model.d
     canvas = initial_canvas(s.seed, block, d.canvas, d.vocab)
     prev = None
+    locked = np.zeros(d.canvas, dtype=bool) if s.lock else None
     passes: List[PassRecord] = []
     step = 0
     reason = STOP_NONE
     mean_ent = float("nan")
     while True:
         step += 1
-        rec, _ = denoise_pass(model, kv, canvas, s.inv_temperature, keep_traces)
+        rec, _ = denoise_pass(model, kv, canvas, pass_inv_temperature(s, step), keep_traces,
+                              (s.seed, block, step) if s.gumbel else None)
+        if locked is not None:  # a locked slot's prediction is its token
+            rec.pred = np.where(locked, canvas, rec.pred)
         passes.append(rec)
         mean_ent = float(np.mean(rec.ent))
         reason = stop_reason(step, mean_ent, rec.pred, prev, s)
         if reason != STOP_NONE:
             break
         k = keep_count(step, s.n_new, d.canvas)
-        canvas, rec.keep = canvas_update(rec.pred, rec.conf, k, s.seed, block, step, d.vocab)
+        canvas, rec.keep = canvas_update(rec.pred, rec.conf, k, s.seed, block, step, d.vocab, rec.ent,
+                                         s.rank_entropy, locked, canvas)
+        if locked is not None:
+            locked = rec.keep.copy()
         prev = rec.pred
     tokens = passes[-1].pred.copy()
     if do_commit:

@@ -449,3 +449,192 @@ def test_model_size_consistent_with_pages():
     total, active = recipe.param_count(recipe.C3.dims)
     assert abs(total / 25.2e9 - 1) < 0.1
     assert abs(active / 3.8e9 - 1) < 0.15
+
+
+# ----------------------------------------------------------------------------- sampler variants
+
+EULER_GAMMA = 0.5772156649015329
+
+
+def test_gumbel_noise_moments_and_range():
+    """Standard Gumbel: mean = Euler's constant, variance = pi^2 / 6; u never 0 or 1."""
+    g = philox.gumbel_noise(7, 2, 3, np.arange(64), 16384).ravel()  # 1M draws
+    assert np.isfinite(g).all()
+    assert abs(g.mean() - EULER_GAMMA) < 6e-3
+    assert abs(g.var() - math.pi ** 2 / 6) < 2.5e-2
+    lo, hi = -math.log(-math.log(2.0 ** -24)), -math.log(-math.log(1 - 2.0 ** -24))
+    assert g.min() >= lo - 1e-12 and g.max() <= hi + 1e-12
+    # the CDF at three points: P(G <= x) = exp(-exp(-x))
+    for x in (-1.0, 0.0, 2.0):
+        assert abs((g <= x).mean() - math.exp(-math.exp(-x))) < 3e-3
+
+
+def test_gumbel_noise_counter_layout():
+    """Token v of slot s takes word v mod 4 of the counter (v div 4, s + 2^16 t, block, 1)."""
+    seed, block, step = (5 << 32) | 11, 9, 4
+    g = philox.gumbel_noise(seed, block, step, np.array([3, 7]), 10)
+    for i, s in enumerate((3, 7)):
+        for v in range(10):
+            w = philox.philox4x32_10((v // 4, s + (step << 16), block, 1), (11, 5))[v % 4]
+            u = (2 * (int(w) >> 9) + 1) / 2.0 ** 24
+            assert g[i, v] == -math.log(-math.log(u))
+    # distinct from the canvas stream and from the neighbouring step / block
+    assert not np.array_equal(g, philox.gumbel_noise(seed, block, step + 1, np.array([3, 7]), 10))
+    assert not np.array_equal(g, philox.gumbel_noise(seed, block + 1, step, np.array([3, 7]), 10))
+
+
+@pytest.mark.parametrize("beta", [1.0, 2.5])
+def test_gumbel_max_draws_from_the_tempered_softmax(beta):
+    """argmax(beta l + G) over 40960 (slot, step) draws: frequencies match softmax(beta l)."""
+    l = np.log(np.array([1.0, 2.0, 3.0, 4.0]))
+    counts = np.zeros(4)
+    for step in range(1, 11):
+        g = philox.gumbel_noise(3, 0, step, np.arange(4096), 4)
+        counts += np.bincount(np.argmax(beta * l + g, axis=1), minlength=4)
+    n = counts.sum()
+    p = np.exp(beta * l) / np.exp(beta * l).sum()
+    sd = np.sqrt(n * p * (1 - p))
+    assert np.all(np.abs(counts - n * p) < 5 * sd), (counts / n, p)
+
+
+def test_head_gumbel_confidence_is_probability_of_the_draw():
+    """Textbook softmax by loops on a tiny vocabulary: conf = p[pred], pred = argmax(beta l + G)."""
+    rng = np.random.default_rng(11)
+    V, d, n, beta = 37, 8, 6, 1.25
+    x = rng.normal(size=(n, d))
+    E = rng.normal(size=(V, d)) * 0.7
+    pred, conf, ent, margin = om.head_stats(x, np.ones(d), E, beta, 0.0, lambda t: t, gumbel=(4, 1, 2))
+    g = philox.gumbel_noise(4, 1, 2, np.arange(n), V)
+    plain = om.head_stats(x, np.ones(d), E, beta, 0.0, lambda t: t)
+    for i in range(n):
+        r = math.sqrt(sum(v * v for v in x[i]) / d)
+        lg = [beta * sum((x[i][c] / r) * E[v][c] for c in range(d)) for v in range(V)]
+        score = [lg[v] + g[i][v] for v in range(V)]
+        best = max(range(V), key=lambda v: (score[v], -v))
+        m = max(lg)
+        z = sum(math.exp(a - m) for a in lg)
+        assert pred[i] == best
+        assert abs(conf[i] - math.exp(lg[best] - m) / z) < 1e-12
+        assert conf[i] <= plain[1][i] + 1e-15
+        assert abs(ent[i] - plain[2][i]) < 1e-12  # the entropy does not depend on the draw
+    assert (pred != plain[0]).any()  # at this temperature some draws leave the argmax
+
+
+def test_head_gumbel_reduces_to_argmax_when_one_logit_dominates():
+    """A logit gap above the Gumbel range (|G| < 17 for u in (0, 1) on the 2^-24 grid) makes the
+    draw the argmax, and conf = max p."""
+    V, d = 512, 2
+    E = np.zeros((V, d))
+    E[77] = [20.0, 20.0]
+    x = np.ones((3, d))
+    pred, conf, _, _ = om.head_stats(x, np.ones(d), E, 1.0, 0.0, lambda t: t, gumbel=(1, 0, 1))
+    ref = om.head_stats(x, np.ones(d), E, 1.0, 0.0, lambda t: t)
+    assert np.all(pred == 77) and np.array_equal(pred, ref[0])
+    np.testing.assert_allclose(conf, ref[1], rtol=1e-14)
+
+
+def test_anneal_schedule_page_values():
+    with open(os.path.join(GOLDEN, "page_constants.json")) as f:
+        pc = json.load(f)
+    t0, t1 = pc["anneal_temperature_first"]["value"], pc["anneal_temperature_last"]["value"]
+    cap = pc["max_denoising_steps"]["value"]
+    s = osm.Sampler(n_new=26, anneal=(t0, t1))
+    temps = [1.0 / osm.pass_inv_temperature(s, t) for t in range(1, cap + 1)]
+    assert abs(temps[0] - 0.8) < 1e-15 and abs(temps[-1] - 0.4) < 1e-15
+    steps = np.diff(temps)
+    np.testing.assert_allclose(steps, -0.4 / 47, rtol=1e-12)  # linear in T, falling
+    s10 = osm.Sampler(n_new=26, anneal=(t0, t1), fixed_steps=pc["timing_steps_T"]["value"])
+    assert abs(1.0 / osm.pass_inv_temperature(s10, 10) - 0.4) < 1e-15
+    assert abs(1.0 / osm.pass_inv_temperature(s10, 1) - 0.8) < 1e-15
+    assert osm.pass_inv_temperature(osm.Sampler(n_new=1, inv_temperature=2.5), 7) == 2.5
+
+
+def test_entropy_rank_equals_confidence_rank_for_two_level_slots():
+    """One boosted token over a uniform rest: entropy falls as the confidence grows, so both
+    keep rules select the same slots; hand cases pin the ties and NaN."""
+    V, d, n = 300, 2, 24
+    rng = np.random.default_rng(5)
+    a = rng.permutation(np.linspace(0.5, 9.0, n))  # the boosted logit of each slot
+    E = np.zeros((V, d))
+    E[5] = [1.0, 0.0]
+    x = np.array([[1.0, 1.0]])  # normalised to itself
+    stats = [om.head_stats(x, np.ones(d), E * ai, 1.0, 0.0, lambda t: t) for ai in a]
+    conf = np.array([st[1][0] for st in stats])
+    ent = np.array([st[2][0] for st in stats])
+    assert np.all(np.argsort(conf) == np.argsort(-ent))
+    for k in (1, 5, 12, 24):
+        assert np.array_equal(osm.select_keep(osm.rank_key(conf, ent, True), k), osm.keep_mask(conf, k))
+    key = osm.rank_key(None, np.array([0.3, np.nan, 0.1, 0.1, 0.2]), True)
+    assert list(np.nonzero(osm.select_keep(key, 3))[0]) == [2, 3, 4]
+    assert list(np.nonzero(osm.select_keep(key, 4))[0]) == [0, 2, 3, 4]
+
+
+def test_lock_update_hand_case():
+    """Locked slots stay kept with their token; new locks fill up to k by the key; the rest redraw."""
+    S, V = 6, 1000
+    pred = np.array([10, 11, 12, 13, 14, 15])
+    conf = np.array([0.9, 0.1, 0.8, 0.7, 0.95, 0.2])
+    canvas = np.array([100, 101, 102, 103, 104, 105])
+    locked = np.array([False, True, False, False, False, True])
+    out, mask = osm.canvas_update(pred, conf, 4, 1, 0, 3, V, None, False, locked, canvas)
+    assert list(np.nonzero(mask)[0]) == [0, 1, 4, 5]
+    assert list(out[[0, 1, 4, 5]]) == [10, 101, 14, 105]
+    fresh = philox.uniform_tokens(1, 0, 3, np.arange(S), V)
+    assert list(out[[2, 3]]) == list(fresh[[2, 3]])
+    # k below the locked count: nothing new locks, nothing unlocks
+    out2, mask2 = osm.canvas_update(pred, conf, 1, 1, 0, 3, V, None, False, locked, canvas)
+    assert np.array_equal(mask2, locked) and list(out2[[1, 5]]) == [101, 105]
+
+
+def test_lock_block_invariants_c0():
+    """The lock variant on the tiny model: k_t slots locked after pass t, a locked token never
+    changes again, and the committed block keeps every locked token."""
+    d = recipe.C0.dims
+    m = oracle_model(d)
+    kv = om.KVCache(d.n_layers, d.n_kv_heads, d.head_dim)
+    osm.prefill(m, kv, dg_inputs.prompt_tokens(recipe.C0.prefix, d.vocab))
+    s = osm.Sampler(n_new=4, fixed_steps=10, lock=True, gumbel=True, anneal=(0.8, 0.4))
+    res = osm.generate_block(m, kv, s, block=0, do_commit=False)
+    assert res.steps == 10 and res.reason == osm.STOP_FIXED
+    locked_tok = {}
+    for t, rec in enumerate(res.passes, start=1):
+        for slot, tok in locked_tok.items():
+            assert rec.canvas[slot] == tok and rec.pred[slot] == tok
+        if rec.keep is not None:
+            assert rec.keep.sum() == min(d.canvas, 4 * t)
+            for slot in np.nonzero(rec.keep)[0]:
+                locked_tok.setdefault(int(slot), int(res.passes[t].canvas[slot]))
+    assert all(res.tokens[s_] == tok for s_, tok in locked_tok.items())
+
+
+def test_stop_and_rule_cases():
+    p = np.arange(4)
+    s_or = osm.Sampler(n_new=26, entropy_threshold=0.005)
+    s_and = osm.Sampler(n_new=26, entropy_threshold=0.005, stop_and=True)
+    assert osm.stop_reason(3, 0.001, p, p + 1, s_or) == osm.STOP_ENTROPY
+    assert osm.stop_reason(3, 0.001, p, p + 1, s_and) == osm.STOP_NONE       # low but unsettled
+    assert osm.stop_reason(3, 2.0, p, p.copy(), s_or) == osm.STOP_STABLE
+    assert osm.stop_reason(3, 2.0, p, p.copy(), s_and) == osm.STOP_NONE      # stable but uncertain
+    assert osm.stop_reason(3, 0.001, p, p.copy(), s_and) == osm.STOP_SETTLED
+    assert osm.stop_reason(1, 0.001, p, None, s_and) == osm.STOP_NONE        # stability needs two passes
+    assert osm.stop_reason(48, 2.0, p, p + 1, s_and) == osm.STOP_CAP
+    s_fix = osm.Sampler(n_new=26, fixed_steps=10, stop_and=True)
+    assert osm.stop_reason(10, 2.0, p, p + 1, s_fix) == osm.STOP_FIXED
+
+
+def test_recommended_sampler_block_c0():
+    """All variants together with the pages' thresholds (0.005 and 0.1): random weights never reach
+    them, so with the AND rule the block runs to the cap or to two settled passes."""
+    d = recipe.C0.dims
+    m = oracle_model(d)
+    for thr in (0.005, 0.1):
+        kv = om.KVCache(d.n_layers, d.n_kv_heads, d.head_dim)
+        osm.prefill(m, kv, dg_inputs.prompt_tokens(recipe.C0.prefix, d.vocab))
+        s = osm.Sampler(n_new=4, entropy_threshold=thr, gumbel=True, anneal=(0.8, 0.4), rank_entropy=True,
+                        lock=True, stop_and=True)
+        res = osm.generate_block(m, kv, s, block=0, do_commit=False)
+        assert res.reason in (osm.STOP_CAP, osm.STOP_SETTLED) and 1 <= res.steps <= 48
+        if res.reason == osm.STOP_CAP:
+            assert res.steps == 48
+        for rec in res.passes:
+            assert np.all(rec.ent >= 0) and np.all(rec.ent <= math.log(d.vocab) + 1e-9)
