@@ -27,10 +27,13 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 DG_OK, DG_ERR_INVALID, DG_ERR_UNSUPPORTED, DG_ERR_KV_FULL, DG_ERR_WORKSPACE, DG_ERR_HIP = 0, -1, -2, -3, -4, -5
 DG_F32, DG_BF16 = 0, 1
-DG_STOP_NONE, DG_STOP_ENTROPY, DG_STOP_STABLE, DG_STOP_CAP, DG_STOP_FIXED = 0, 1, 2, 3, 4
+DG_STOP_NONE, DG_STOP_ENTROPY, DG_STOP_STABLE, DG_STOP_CAP, DG_STOP_FIXED, DG_STOP_SETTLED = 0, 1, 2, 3, 4, 5
 DG_WARN_NUMERIC = 0x1
+# sampler variants (dg_sampler.flags)
+DG_SAMPLE_GUMBEL, DG_SAMPLE_ANNEAL, DG_KEEP_ENTROPY, DG_KEEP_LOCK, DG_STOP_AND = 0x1, 0x2, 0x4, 0x8, 0x10
 EXPORTED = ("dg_workspace_size", "dg_prefill_kv", "dg_denoise_step", "dg_canvas_update", "dg_commit_block",
             "dg_generate_block", "dg_generate_block_overlapped", "dg_layer_forward", "dg_vocab_head", "dg_stop_check", "dg_status_string",
+            "dg_denoise_step_sampler", "dg_canvas_update_sampler", "dg_vocab_head_sampler", "dg_sampler_inv_temperature",
             "dg_last_hip_error", "dg_timing_start", "dg_timing_stop", "dg_packed_elems", "dg_pack_matrix")
 # kernel classes of dg_timing_* (dg_kernel in dg.h), in enum order
 KERNELS = ("embed", "rmsnorm", "gemm_qkv", "attention", "attn_merge", "gemm_o", "route",
@@ -75,7 +78,8 @@ class dg_kv(ctypes.Structure):
 class dg_sampler(ctypes.Structure):
     _fields_ = [("n_new", ctypes.c_int32), ("max_steps", ctypes.c_int32), ("fixed_steps", ctypes.c_int32),
                 ("entropy_threshold", ctypes.c_float), ("inv_temperature", ctypes.c_float),
-                ("flags", ctypes.c_uint32), ("seed", ctypes.c_uint64)]
+                ("flags", ctypes.c_uint32), ("seed", ctypes.c_uint64), ("temperature_first", ctypes.c_float),
+                ("temperature_last", ctypes.c_float)]
 
 
 class dg_block_status(ctypes.Structure):
@@ -105,7 +109,13 @@ _SIGS = {
     "dg_layer_forward": [_P(dg_config), _P(dg_weights), _i32, _P(dg_kv), _vp, _vp, _i64, _i32, _P(dg_debug), _vp,
                          _sz, _vp],
     "dg_vocab_head": [_P(dg_config), _P(dg_weights), _vp, _i64, _f32, _vp, _vp, _vp, _vp, _sz, _vp],
-    "dg_stop_check": [_P(dg_config), _P(dg_sampler), _i32, _vp, _vp, _vp, _vp, _vp],
+    "dg_stop_check": [_P(dg_config), _P(dg_sampler), _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "dg_denoise_step_sampler": [_P(dg_config), _P(dg_weights), _P(dg_kv), _P(dg_sampler), _u32, _i32, _vp, _vp, _vp,
+                                _vp, _vp, _sz, _vp],
+    "dg_canvas_update_sampler": [_P(dg_config), _P(dg_sampler), _u32, _i32, _vp, _vp, _vp, _vp, _vp, _vp],
+    "dg_vocab_head_sampler": [_P(dg_config), _P(dg_weights), _P(dg_sampler), _u32, _i32, _vp, _i64, _vp, _vp, _vp,
+                              _vp, _sz, _vp],
+    "dg_sampler_inv_temperature": [_P(dg_sampler), _i32, _P(ctypes.c_float)],
     "dg_packed_elems": [_i64, _i64, _P(_i64)],
     "dg_pack_matrix": [_vp, _vp, _i64, _i64, _i64, _i32, _vp],
 }
@@ -271,9 +281,40 @@ def dg_vocab_head(cfg, weights, x, n: int, inv_temperature: float, pred, conf, e
                                                _stream(stream)))
 
 
-def dg_stop_check(cfg, sampler: dg_sampler, step: int, entropy, pred, prev_pred, d_status, stream=None) -> None:
+def dg_stop_check(cfg, sampler: dg_sampler, step: int, entropy, pred, prev_pred, d_status, canvas=None,
+                  lock_mask=None, stream=None) -> None:
     _check("dg_stop_check", _lib.dg_stop_check(ctypes.byref(cfg), ctypes.byref(sampler), step, _ptr(entropy),
-                                               _ptr(pred), _ptr(prev_pred), _ptr(d_status), _stream(stream)))
+                                               _ptr(pred), _ptr(prev_pred), _ptr(canvas), _ptr(lock_mask),
+                                               _ptr(d_status), _stream(stream)))
+
+
+def dg_denoise_step_sampler(cfg, weights, kv, sampler: dg_sampler, block: int, step: int, canvas, pred, conf,
+                            entropy, ws, ws_bytes: int, stream=None) -> None:
+    _check("dg_denoise_step_sampler",
+           _lib.dg_denoise_step_sampler(ctypes.byref(cfg), _w(weights), _kv(kv), ctypes.byref(sampler), block, step,
+                                        _ptr(canvas), _ptr(pred), _ptr(conf), _ptr(entropy), _ptr(ws), ws_bytes,
+                                        _stream(stream)))
+
+
+def dg_canvas_update_sampler(cfg, sampler: dg_sampler, block: int, step: int, pred, conf, entropy, canvas,
+                             lock_mask=None, stream=None) -> None:
+    _check("dg_canvas_update_sampler",
+           _lib.dg_canvas_update_sampler(ctypes.byref(cfg), ctypes.byref(sampler), block, step, _ptr(pred),
+                                         _ptr(conf), _ptr(entropy), _ptr(canvas), _ptr(lock_mask), _stream(stream)))
+
+
+def dg_vocab_head_sampler(cfg, weights, sampler: dg_sampler, block: int, step: int, x, n: int, pred, conf, entropy,
+                          ws, ws_bytes: int, stream=None) -> None:
+    _check("dg_vocab_head_sampler",
+           _lib.dg_vocab_head_sampler(ctypes.byref(cfg), _w(weights), ctypes.byref(sampler), block, step, _ptr(x), n,
+                                      _ptr(pred), _ptr(conf), _ptr(entropy), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def dg_sampler_inv_temperature(sampler: dg_sampler, step: int) -> float:
+    out = ctypes.c_float()
+    _check("dg_sampler_inv_temperature", _lib.dg_sampler_inv_temperature(ctypes.byref(sampler), step,
+                                                                         ctypes.byref(out)))
+    return float(out.value)
 
 
 def dg_status_string(status: int) -> str:
@@ -285,9 +326,11 @@ def dg_last_hip_error() -> int:
 
 
 def make_sampler(n_new: int, max_steps: int = 48, fixed_steps: int = 0, entropy_threshold: float = 0.05,
-                 inv_temperature: float = 1.0, seed: int = 1) -> dg_sampler:
+                 inv_temperature: float = 1.0, seed: int = 1, flags: int = 0, temperature_first: float = 0.0,
+                 temperature_last: float = 0.0) -> dg_sampler:
     return dg_sampler(n_new=n_new, max_steps=max_steps, fixed_steps=fixed_steps,
-                      entropy_threshold=entropy_threshold, inv_temperature=inv_temperature, flags=0, seed=seed)
+                      entropy_threshold=entropy_threshold, inv_temperature=inv_temperature, flags=flags, seed=seed,
+                      temperature_first=temperature_first, temperature_last=temperature_last)
 
 
 def dg_timing_start(kernels: Sequence[str]) -> None:

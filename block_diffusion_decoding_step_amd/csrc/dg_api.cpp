@@ -147,12 +147,14 @@ struct Ws {
   void* Hs;
   void* Ys;
   float4* hpart;
+  float2* hpart2;
   dg_block_status* status;
   int32_t* prev_pred;
   int32_t* canvas;
   int32_t* pred;
   float* conf;
   float* ent;
+  uint8_t* lock;
   size_t bytes;
   int64_t rows;
 };
@@ -196,12 +198,14 @@ Ws carve(const dg_config* c, int64_t M, char* base) {
   w.Hs = take(Mp * c->ffn_shared * es);
   w.Ys = take(M * d * es);
   w.hpart = (float4*)take((size_t)head_groups(c->vocab) * M * 16);
+  w.hpart2 = (float2*)take((size_t)head_groups(c->vocab) * M * 8);
   w.status = (dg_block_status*)take(sizeof(dg_block_status));
   w.prev_pred = (int32_t*)take(c->canvas * 4);
   w.canvas = (int32_t*)take(c->canvas * 4);
   w.pred = (int32_t*)take(c->canvas * 4);
   w.conf = (float*)take(c->canvas * 4);
   w.ent = (float*)take(c->canvas * 4);
+  w.lock = (uint8_t*)take(c->canvas);
   w.bytes = off;
   return w;
 }
@@ -381,12 +385,38 @@ int embed(const dg_config* c, const dg_weights* w, const int32_t* tok, int64_t M
   return DG_OK;
 }
 
+// temperature and token choice of one pass: the argmax, or (gumbel) a draw from the tempered softmax
+// keyed by (seed, block, step)
+struct PassParams {
+  float inv_temp;
+  bool gumbel;
+  uint64_t seed;
+  uint32_t block, step;
+};
+PassParams argmax_pass(float inv_temp) { return PassParams{inv_temp, false, 0, 0, 0}; }
+
+// 1 / T of pass `step`: the sampler's constant, or (anneal) T linear from temperature_first at pass 1 to
+// temperature_last at the last pass of the budget
+float pass_inv_temperature(const dg_sampler* sp, int step) {
+  if (!(sp->flags & DG_SAMPLE_ANNEAL)) return sp->inv_temperature;
+  const int n = sp->fixed_steps > 0 ? sp->fixed_steps : sp->max_steps;
+  const double frac = n <= 1 ? 0.0 : std::min(1.0, (double)(step - 1) / (double)(n - 1));
+  const double t = (double)sp->temperature_first + ((double)sp->temperature_last - sp->temperature_first) * frac;
+  return (float)(1.0 / t);
+}
+PassParams sampler_pass(const dg_sampler* sp, uint32_t block, int step) {
+  return PassParams{pass_inv_temperature(sp, step), (sp->flags & DG_SAMPLE_GUMBEL) != 0, sp->seed, block,
+                    (uint32_t)step};
+}
+
 // final norm (unless normed: ws.Xn already holds it) + fused head over rows [row0, row0 + M) of ws.X
-int head(const dg_config* c, const dg_weights* w, int64_t M, float inv_temp, int32_t* pred, float* conf, float* ent,
-         bool normed, const Ws& ws, hipStream_t s, int64_t row0 = 0) {
+int head(const dg_config* c, const dg_weights* w, int64_t M, const PassParams& pp, int32_t* pred, float* conf,
+         float* ent, bool normed, const Ws& ws, hipStream_t s, int64_t row0 = 0) {
   HeadArgs h{};
   h.x = (const char*)ws.Xn + row0 * c->d_model * esize(c); h.E = w->embed; h.part = ws.hpart; h.n = (int)M; h.d = c->d_model; h.V = c->vocab;
-  h.n_groups = head_groups(c->vocab); h.beta_log2e = inv_temp * 1.4426950408889634f;
+  h.n_groups = head_groups(c->vocab); h.beta_log2e = pp.inv_temp * 1.4426950408889634f;
+  h.part2 = ws.hpart2; h.gumbel = pp.gumbel ? 1 : 0;
+  h.k0 = (uint32_t)pp.seed; h.k1 = (uint32_t)(pp.seed >> 32); h.block = pp.block; h.step = pp.step;
   h.pred = pred; h.conf = conf; h.ent = ent;
   if (c->dtype == DG_BF16) {
     if (!normed)
@@ -406,7 +436,7 @@ int head(const dg_config* c, const dg_weights* w, int64_t M, float inv_temp, int
 }
 
 // denoising pass with an already-validated configuration
-int denoise(const dg_config* c, const dg_weights* w, const dg_kv* kv, const int32_t* canvas, float inv_temp,
+int denoise(const dg_config* c, const dg_weights* w, const dg_kv* kv, const int32_t* canvas, const PassParams& pp,
             int32_t* pred, float* conf, float* ent, const dg_debug* dbg, const Ws& ws, hipStream_t s) {
   const int64_t S = c->canvas;
   DG_CHECK(embed(c, w, canvas, S, ws, s));
@@ -425,7 +455,7 @@ int denoise(const dg_config* c, const dg_weights* w, const dg_kv* kv, const int3
         DG_TRY(hipMemcpyAsync((char*)dbg->router_logits + l * lb, ws.rlog, lb, hipMemcpyDeviceToDevice, s));
     }
   }
-  return head(c, w, S, inv_temp, pred, conf, ent, L > 0, ws, s);
+  return head(c, w, S, pp, pred, conf, ent, L > 0, ws, s);
 }
 
 // A pass that also commits the previous block: rows [0, S) are that block's tokens at cache rows
@@ -433,7 +463,7 @@ int denoise(const dg_config* c, const dg_weights* w, const dg_kv* kv, const int3
 // len + S..).  Every weight is streamed once for both; the head runs on the canvas rows only.  The
 // caller advances kv->len by S afterwards.
 int denoise_committing(const dg_config* c, const dg_weights* w, const dg_kv* kv, const int32_t* block_tokens,
-                       const int32_t* canvas, float inv_temp, int32_t* pred, float* conf, float* ent, const Ws& ws,
+                       const int32_t* canvas, const PassParams& pp, int32_t* pred, float* conf, float* ent, const Ws& ws,
                        hipStream_t s) {
   const int64_t S = c->canvas;
   DG_CHECK(embed(c, w, block_tokens, S, ws, s, 0));
@@ -441,7 +471,7 @@ int denoise_committing(const dg_config* c, const dg_weights* w, const dg_kv* kv,
   const int L = c->n_layers;
   for (int l = 0; l < L; ++l)
     DG_CHECK(layer(c, w, l, kv, kv->len, 2 * S, S, l > 0, l + 1 < L ? Next::NextLayer : Next::Head, ws, s));
-  return head(c, w, S, inv_temp, pred, conf, ent, L > 0, ws, s, S);
+  return head(c, w, S, pp, pred, conf, ent, L > 0, ws, s, S);
 }
 
 // causal forward of n tokens at kv->len.., chunked to the workspace; does not change kv->len
@@ -466,13 +496,23 @@ StopParams stop_params(const dg_config* c, const dg_sampler* sp) {
   p.ln_vocab = logf((float)c->vocab);
   p.max_steps = sp->max_steps;
   p.fixed_steps = sp->fixed_steps;
+  p.and_rule = (sp->flags & DG_STOP_AND) ? 1 : 0;
   return p;
 }
 
 int check_sampler(const dg_config* c, const dg_sampler* sp) {
   if (!sp) return DG_ERR_INVALID;
-  if (sp->n_new < 0 || sp->max_steps < 1 || sp->fixed_steps < 0 || sp->flags != 0) return DG_ERR_INVALID;
-  if (!(sp->inv_temperature > 0.f) || std::isnan(sp->entropy_threshold)) return DG_ERR_INVALID;
+  if (sp->n_new < 0 || sp->max_steps < 1 || sp->fixed_steps < 0 || (sp->flags & ~DG_SAMPLER_FLAGS)) return DG_ERR_INVALID;
+  if (std::isnan(sp->entropy_threshold)) return DG_ERR_INVALID;
+  if (sp->flags & DG_SAMPLE_ANNEAL) {
+    if (!(sp->temperature_first > 0.f) || !(sp->temperature_last > 0.f) || std::isinf(sp->temperature_first) ||
+        std::isinf(sp->temperature_last))
+      return DG_ERR_INVALID;
+  } else if (!(sp->inv_temperature > 0.f)) {
+    return DG_ERR_INVALID;
+  }
+  // the draw's Philox counter holds the slot and the pass in 16 bits each
+  if ((sp->flags & DG_SAMPLE_GUMBEL) && (sp->max_steps > 65535 || sp->fixed_steps > 65535)) return DG_ERR_INVALID;
   (void)c;
   return DG_OK;
 }
@@ -512,7 +552,22 @@ int dg_denoise_step(const dg_config* cfg, const dg_weights* w, const dg_kv* kv, 
   DG_CHECK(check_kv(kv, cfg->canvas));
   DG_CHECK(check_ws(cfg, cfg->canvas, ws, ws_bytes));
   Ws wsv = carve(cfg, cfg->canvas, (char*)ws);
-  return denoise(cfg, w, kv, canvas, inv_temperature, pred, conf, entropy, dbg, wsv, (hipStream_t)stream);
+  return denoise(cfg, w, kv, canvas, argmax_pass(inv_temperature), pred, conf, entropy, dbg, wsv,
+                 (hipStream_t)stream);
+}
+
+int dg_denoise_step_sampler(const dg_config* cfg, const dg_weights* w, const dg_kv* kv, const dg_sampler* sampler,
+                            uint32_t block, int32_t step, const int32_t* canvas, int32_t* pred, float* conf,
+                            float* entropy, void* ws, size_t ws_bytes, void* stream) {
+  DG_CHECK(check_cfg(cfg));
+  DG_CHECK(check_weights(cfg, w, true, true));
+  DG_CHECK(check_sampler(cfg, sampler));
+  if (!canvas || !pred || !conf || !entropy || step < 1 || step > 65535) return DG_ERR_INVALID;
+  DG_CHECK(check_kv(kv, cfg->canvas));
+  DG_CHECK(check_ws(cfg, cfg->canvas, ws, ws_bytes));
+  Ws wsv = carve(cfg, cfg->canvas, (char*)ws);
+  return denoise(cfg, w, kv, canvas, sampler_pass(sampler, block, step), pred, conf, entropy, nullptr, wsv,
+                 (hipStream_t)stream);
 }
 
 int dg_canvas_update(const dg_config* cfg, const int32_t* pred, const float* conf, int32_t keep_count, uint64_t seed,
@@ -520,9 +575,25 @@ int dg_canvas_update(const dg_config* cfg, const int32_t* pred, const float* con
   DG_CHECK(check_cfg(cfg));
   if (!canvas_out || keep_count < 0 || keep_count > cfg->canvas) return DG_ERR_INVALID;
   if (keep_count > 0 && (!pred || !conf)) return DG_ERR_INVALID;
-  DG_LAUNCH(DG_K_CANVAS_UPDATE, (hipStream_t)stream,
-            launch_canvas_update(pred, conf, cfg->canvas, keep_count, seed, block, step, (uint32_t)cfg->vocab,
-                                 canvas_out, keep_mask, (hipStream_t)stream));
+  CanvasArgs ca{pred, conf, nullptr, 0, nullptr, cfg->canvas, keep_count, seed, block, step, (uint32_t)cfg->vocab,
+                canvas_out, keep_mask};
+  DG_LAUNCH(DG_K_CANVAS_UPDATE, (hipStream_t)stream, launch_canvas_update(ca, (hipStream_t)stream));
+  return DG_OK;
+}
+
+int dg_canvas_update_sampler(const dg_config* cfg, const dg_sampler* sampler, uint32_t block, int32_t step,
+                             const int32_t* pred, const float* conf, const float* entropy, int32_t* canvas,
+                             uint8_t* lock_mask, void* stream) {
+  DG_CHECK(check_cfg(cfg));
+  DG_CHECK(check_sampler(cfg, sampler));
+  if (step < 0 || !canvas) return DG_ERR_INVALID;
+  const int keep = (int)std::min<int64_t>(cfg->canvas, (int64_t)step * sampler->n_new);
+  const bool lock = (sampler->flags & DG_KEEP_LOCK) != 0, by_ent = (sampler->flags & DG_KEEP_ENTROPY) != 0;
+  if (keep > 0 && (!pred || (by_ent ? !entropy : !conf))) return DG_ERR_INVALID;
+  if (lock && !lock_mask) return DG_ERR_INVALID;
+  CanvasArgs ca{pred, conf, entropy, by_ent ? 1 : 0, (lock && step > 0) ? lock_mask : nullptr, cfg->canvas, keep,
+                sampler->seed, block, (uint32_t)step, (uint32_t)cfg->vocab, canvas, lock_mask};
+  DG_LAUNCH(DG_K_CANVAS_UPDATE, (hipStream_t)stream, launch_canvas_update(ca, (hipStream_t)stream));
   return DG_OK;
 }
 
@@ -547,20 +618,23 @@ int dg_generate_block_overlapped(const dg_config* cfg, const dg_weights* w, dg_k
   const StopParams stp = stop_params(cfg, sp);
   const bool fixed = sp->fixed_steps > 0;
   const int limit = fixed ? sp->fixed_steps : sp->max_steps;
+  const bool lock = (sp->flags & DG_KEEP_LOCK) != 0;
+  uint8_t* lock_mask = lock ? wsv.lock : nullptr;  // the locked slots; cleared by the initial draw
 
-  DG_LAUNCH(DG_K_CANVAS_UPDATE, s,
-            launch_canvas_update(nullptr, nullptr, S, 0, sp->seed, block, 0, (uint32_t)cfg->vocab, wsv.canvas,
-                                 nullptr, s));
+  CanvasArgs ca{nullptr, nullptr, nullptr, 0, nullptr, S, 0, sp->seed, block, 0, (uint32_t)cfg->vocab, wsv.canvas,
+                lock_mask};
+  DG_LAUNCH(DG_K_CANVAS_UPDATE, s, launch_canvas_update(ca, s));
   dg_block_status st{};
   for (int t = 1;; ++t) {
+    const PassParams pp = sampler_pass(sp, block, t);
     if (t == 1 && pending) {
-      DG_CHECK(denoise_committing(cfg, w, kv, pending, wsv.canvas, sp->inv_temperature, wsv.pred, wsv.conf, wsv.ent,
-                                  wsv, s));
+      DG_CHECK(denoise_committing(cfg, w, kv, pending, wsv.canvas, pp, wsv.pred, wsv.conf, wsv.ent, wsv, s));
       kv->len += S;  // the pending block is committed (in stream order) before every later pass
     } else {
-      DG_CHECK(denoise(cfg, w, kv, wsv.canvas, sp->inv_temperature, wsv.pred, wsv.conf, wsv.ent, nullptr, wsv, s));
+      DG_CHECK(denoise(cfg, w, kv, wsv.canvas, pp, wsv.pred, wsv.conf, wsv.ent, nullptr, wsv, s));
     }
-    DG_LAUNCH(DG_K_STOP_CHECK, s, launch_stop_check(wsv.ent, wsv.pred, wsv.prev_pred, S, t, stp, wsv.status, s));
+    DG_LAUNCH(DG_K_STOP_CHECK, s,
+              launch_stop_check(wsv.ent, wsv.pred, wsv.prev_pred, wsv.canvas, lock_mask, S, t, stp, wsv.status, s));
     bool stop;
     if (fixed) {
       stop = t >= limit;
@@ -570,10 +644,10 @@ int dg_generate_block_overlapped(const dg_config* cfg, const dg_weights* w, dg_k
       stop = st.reason != DG_STOP_NONE;
     }
     if (stop) break;
-    const int keep = (int)std::min<int64_t>(S, (int64_t)t * sp->n_new);
-    DG_LAUNCH(DG_K_CANVAS_UPDATE, s,
-              launch_canvas_update(wsv.pred, wsv.conf, S, keep, sp->seed, block, (uint32_t)t, (uint32_t)cfg->vocab,
-                                   wsv.canvas, nullptr, s));
+    ca = CanvasArgs{wsv.pred, wsv.conf, wsv.ent, (sp->flags & DG_KEEP_ENTROPY) ? 1 : 0, lock_mask, S,
+                    (int)std::min<int64_t>(S, (int64_t)t * sp->n_new), sp->seed, block, (uint32_t)t,
+                    (uint32_t)cfg->vocab, wsv.canvas, lock_mask};
+    DG_LAUNCH(DG_K_CANVAS_UPDATE, s, launch_canvas_update(ca, s));
   }
   DG_TRY(hipMemcpyAsync(tokens_out, wsv.pred, (size_t)S * 4, hipMemcpyDeviceToDevice, s));
   // read the status before the commit reuses the workspace
@@ -630,17 +704,45 @@ int dg_vocab_head(const dg_config* cfg, const dg_weights* w, const void* x, int6
   hipStream_t s = (hipStream_t)stream;
   Ws wsv = carve(cfg, n, (char*)ws);
   DG_TRY(hipMemcpyAsync(wsv.X, x, (size_t)n * cfg->d_model * esize(cfg), hipMemcpyDeviceToDevice, s));
-  return head(cfg, w, n, inv_temperature, pred, conf, entropy, false, wsv, s);
+  return head(cfg, w, n, argmax_pass(inv_temperature), pred, conf, entropy, false, wsv, s);
 }
 
-int dg_stop_check(const dg_config* cfg, const dg_sampler* sampler, int32_t step, const float* entropy,
-                  const int32_t* pred, int32_t* prev_pred, dg_block_status* d_status, void* stream) {
+int dg_vocab_head_sampler(const dg_config* cfg, const dg_weights* w, const dg_sampler* sampler, uint32_t block,
+                          int32_t step, const void* x, int64_t n, int32_t* pred, float* conf, float* entropy,
+                          void* ws, size_t ws_bytes, void* stream) {
+  DG_CHECK(check_cfg(cfg));
+  DG_CHECK(check_weights(cfg, w, false, true));
+  DG_CHECK(check_sampler(cfg, sampler));
+  if (!aligned16(x) || !pred || !conf || !entropy || n < 1 || n > moe_max_rows(cfg->n_experts) || step < 1 ||
+      step > 65535)
+    return DG_ERR_INVALID;
+  DG_CHECK(check_ws(cfg, n, ws, ws_bytes));
+  hipStream_t s = (hipStream_t)stream;
+  Ws wsv = carve(cfg, n, (char*)ws);
+  DG_TRY(hipMemcpyAsync(wsv.X, x, (size_t)n * cfg->d_model * esize(cfg), hipMemcpyDeviceToDevice, s));
+  return head(cfg, w, n, sampler_pass(sampler, block, step), pred, conf, entropy, false, wsv, s);
+}
+
+int dg_sampler_inv_temperature(const dg_sampler* sampler, int32_t step, float* h_inv_temperature) {
+  if (!h_inv_temperature) return DG_ERR_INVALID;
+  *h_inv_temperature = 0.f;
+  DG_CHECK(check_sampler(nullptr, sampler));
+  if (step < 1) return DG_ERR_INVALID;
+  *h_inv_temperature = pass_inv_temperature(sampler, step);
+  return DG_OK;
+}
+
+int dg_stop_check(const dg_config* cfg, const dg_sampler* sampler, int32_t step, const float* entropy, int32_t* pred,
+                  int32_t* prev_pred, const int32_t* canvas, const uint8_t* lock_mask, dg_block_status* d_status,
+                  void* stream) {
   DG_CHECK(check_cfg(cfg));
   DG_CHECK(check_sampler(cfg, sampler));
   if (step < 1 || !entropy || !pred || !prev_pred || !d_status) return DG_ERR_INVALID;
+  const bool lock = (sampler->flags & DG_KEEP_LOCK) != 0;
+  if (lock && (!canvas || !lock_mask)) return DG_ERR_INVALID;
   DG_LAUNCH(DG_K_STOP_CHECK, (hipStream_t)stream,
-            launch_stop_check(entropy, pred, prev_pred, cfg->canvas, step, stop_params(cfg, sampler), d_status,
-                              (hipStream_t)stream));
+            launch_stop_check(entropy, pred, prev_pred, lock ? canvas : nullptr, lock ? lock_mask : nullptr,
+                              cfg->canvas, step, stop_params(cfg, sampler), d_status, (hipStream_t)stream));
   return DG_OK;
 }
 

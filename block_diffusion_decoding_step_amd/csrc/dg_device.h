@@ -122,6 +122,28 @@ struct Vec8<float> {
   }
 };
 
+// ---------------------------------------------------------------- Philox4x32-10
+// Counter-based generator of Salmon, Moraes, Dror and Shaw ("Parallel Random Numbers: As Easy
+// as 1, 2, 3", SC'11): ten rounds; each round forms the 64-bit products of counter words 0 and 2
+// with two fixed multipliers, moves their low halves to words 3 and 1 and xors their high halves
+// with words 1 / 3 and the key; the key advances by two Weyl constants between rounds.
+__device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                               uint32_t k1) {
+  const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u, W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) { k0 += W0; k1 += W1; }
+    const uint64_t p0 = (uint64_t)M0 * c0;
+    const uint64_t p1 = (uint64_t)M1 * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+  }
+  return uint4{c0, c1, c2, c3};
+}
+
 // 64-bit integer min / max as plain compares (the generic min/max overloads may go through double)
 __device__ __forceinline__ int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
 __device__ __forceinline__ int64_t imax64(int64_t a, int64_t b) { return a > b ? a : b; }

@@ -35,6 +35,22 @@ struct StopParams {
   float ln_vocab;
   int max_steps;
   int fixed_steps;
+  int and_rule;  // early stop needs low entropy and two unchanged passes together
+};
+
+// keep the best `keep` slots (confidence, or lowest entropy with rank_entropy; locked slots first
+// and always), kept slots take pred (locked ones keep their canvas token), the rest a Philox draw
+struct CanvasArgs {
+  const int32_t* pred;
+  const float* conf;
+  const float* ent;       // read with rank_entropy
+  int rank_entropy;
+  const uint8_t* lock;    // null, or the locked slots (may alias keep_mask)
+  int S, keep;
+  uint64_t seed;
+  uint32_t block, step, V;
+  int32_t* canvas;        // in/out (read at locked slots)
+  uint8_t* keep_mask;     // optional output
 };
 
 // ---- k_misc.hip
@@ -72,11 +88,11 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 template <typename T>
 hipError_t launch_moe_combine(T* X, const T* Ys, const T* Yp, const int32_t* pos, const float* w, int M, int d,
                               int k, const T* g, T* Yn, int yn_tiled, float eps, hipStream_t s);
-hipError_t launch_stop_check(const float* ent, const int32_t* pred, int32_t* prev, int S, int step, StopParams sp,
-                             dg_block_status* out, hipStream_t s);
-hipError_t launch_canvas_update(const int32_t* pred, const float* conf, int S, int keep, uint64_t seed,
-                                uint32_t block, uint32_t step, uint32_t V, int32_t* canvas, uint8_t* keep_mask,
-                                hipStream_t s);
+// with lock (non-null) the locked slots' predictions are replaced by their canvas tokens first
+hipError_t launch_stop_check(const float* ent, int32_t* pred, int32_t* prev, const int32_t* canvas,
+                             const uint8_t* lock, int S, int step, StopParams sp, dg_block_status* out,
+                             hipStream_t s);
+hipError_t launch_canvas_update(const CanvasArgs& a, hipStream_t s);
 
 // ---- k_gemm.hip
 enum class GemmEpi { Store, Resid, QKV, SwiGLU };
@@ -146,10 +162,15 @@ int attention_splits(int64_t n_keys, int q_rows, int n_heads, int n_kv_heads, in
 struct HeadArgs {
   const void* x;      // normalised hidden [n, d]
   const void* E;      // [V, d]
-  float4* part;       // [n_groups][n] partials (max, argmax bits, Z, S1), natural units
+  float4* part;       // [n_groups][n] partials (max, argmax or drawn token bits, Z, S1), natural units
+  float2* part2;      // gumbel: [n_groups][n] (best perturbed score, scaled logit of the drawn token)
   int n, d, V;
   int n_groups;
   float beta_log2e;   // inv_temperature * log2(e)
+  // gumbel: draw token v of row r with the Gumbel noise of Philox counter (v / 4, r + 65536 * step,
+  // block, 1) under key (k0, k1) instead of taking the argmax; conf = probability of the draw
+  int gumbel;
+  uint32_t k0, k1, block, step;
   int32_t* pred;
   float* conf;
   float* ent;

@@ -26,7 +26,17 @@
 // four quads of a wave and the four token waves of a slot are merged in fixed
 // order into one partial per (workgroup, slot).  A merge kernel combines the
 // workgroups in fixed order (deterministic).
+//
+// Sampling variant (gumbel): the recommended sampler draws each slot's token from
+// the softmax at the pass's temperature ([P2] "Architecture Details").  By the
+// Gumbel-max identity the token argmax_v (beta l_v + G_v), with independent
+// standard Gumbel G_v, is such a draw, so the fold also keeps the best perturbed
+// score, its token and its scaled logit; conf becomes the probability of the drawn
+// token, e^(beta l_a - m) / Z.  G_v = -ln(-ln u), u = (2 floor(w / 2^9) + 1) / 2^24
+// (exact in fp32, never 0 or 1), w = word v mod 4 of Philox4x32-10 at counter
+// (v / 4, row + 2^16 step, block, 1): one generator call serves four tokens.
 #include <type_traits>
+#include <utility>
 
 #include "dg_device.h"
 #include "dg_kernels.h"
@@ -59,6 +69,54 @@ __device__ __forceinline__ void stat_merge(Stat& x, const Stat& y) {
   x.s1 = s1;
 }
 
+// the draw of the sampling variant: best perturbed score g, its scaled logit l, its token a
+struct Draw {
+  float g, l;
+  int a;
+};
+__device__ __forceinline__ void draw_merge(Draw& x, const Draw& y) {
+  if (y.g > x.g || (y.g == x.g && y.a < x.a)) x = y;
+}
+__device__ __forceinline__ Draw draw_shfl(const Draw& x, int o) {
+  return Draw{__shfl_xor(x.g, o, 64), __shfl_xor(x.l, o, 64), __shfl_xor(x.a, o, 64)};
+}
+constexpr Draw kNoDraw{-INFINITY, 0.f, 0x7fffffff};
+
+// Gumbel noise of tokens 4q .. 4q+3 of row `row`.  -ln u is taken from the Mercator series of
+// -ln(1 - e), e = 1 - u (exact), when u > 15/16, where a log of u itself would lose the small
+// result to cancellation; eight terms leave a relative error below 1e-10 there.  The logs are the
+// hardware log2 (normal inputs only: u >= 2^-24, -ln u >= 2^-24).
+__device__ __forceinline__ float gumbel_of(uint32_t w) {
+  constexpr float kLn2 = 0.6931471805599453f;
+  const uint32_t k = w >> 9;                                     // u = (2k + 1) / 2^24
+  const float u = (float)(2u * k + 1u) * 0x1p-24f;
+  const float e = (float)((1u << 24) - 2u * k - 1u) * 0x1p-24f;  // 1 - u
+  float sr = 1.f / 8.f;
+#pragma unroll
+  for (int n = 7; n >= 1; --n) sr = fmaf(e, sr, 1.f / (float)n);
+  const float far = -kLn2 * __builtin_amdgcn_logf(u);
+  const float inner = e < 0.0625f ? e * sr : far;
+  return -kLn2 * __builtin_amdgcn_logf(inner);
+}
+__device__ __forceinline__ void gumbel4(const HeadArgs& a, uint32_t q, uint32_t row, float (&g)[4]) {
+  const uint4 w = philox4x32_10(q, row + (a.step << 16), a.block, 1u, a.k0, a.k1);
+  g[0] = gumbel_of(w.x);
+  g[1] = gumbel_of(w.y);
+  g[2] = gumbel_of(w.z);
+  g[3] = gumbel_of(w.w);
+}
+
+// calls f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>) in order: a loop that is always
+// fully unrolled (register arrays indexed by the counter stay in registers at any body size)
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 template <typename T>
 struct HeadCfg {
   static constexpr int KC = sizeof(T) == 2 ? 2 : 1;   // K steps per stage
@@ -73,7 +131,7 @@ constexpr int kHeadTokens = 256;   // vocabulary rows per tile
 constexpr int kHeadMaxGroups = 256;
 
 // grid = (n_groups, ceil(n / 256)); block = 512
-template <typename T>
+template <typename T, bool DRAW>
 __global__ __launch_bounds__(512, 1) void k_vocab_head(HeadArgs a) {
   using C = HeadCfg<T>;
   static_assert(C::LOADS == 8, "stage layout");
@@ -129,8 +187,12 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head(HeadArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = zero4();
   Stat st[8];
+  Draw dr[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) st[j] = Stat{-INFINITY, 0.f, 0.f, 0x7fffffff};
+  for (int j = 0; j < 8; ++j) {
+    st[j] = Stat{-INFINITY, 0.f, 0.f, 0x7fffffff};
+    dr[j] = kNoDraw;
+  }
 
   uint4 r[C::LOADS];
   if (total > 0) {
@@ -169,8 +231,8 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head(HeadArgs a) {
       // tile finished: lane holds, for slot slot_base + 128*wsl + 16*j + row16,
       // tokens v0 + 16*i + 4*quad + rr
       const int v0 = ((int)blockIdx.x + (q / nch) * G) * kHeadTokens + 64 * wv;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      static_for<8>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value;
         Stat loc{-INFINITY, 0.f, 0.f, 0x7fffffff};
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -195,9 +257,23 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head(HeadArgs a) {
             }
         }
         stat_merge(st[j], loc);
+        if constexpr (DRAW) {
+          const uint32_t row = (uint32_t)(slot_base + 128 * wsl + 16 * j + row16);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float gn[4];
+            gumbel4(a, (uint32_t)(v0 + 16 * i + 4 * quad) >> 2, row, gn);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const int v = v0 + 16 * i + 4 * quad + rr;
+              const float l = acc[i][j][rr] * beta;
+              if (v < a.V && l + gn[rr] > dr[j].g) dr[j] = Draw{l + gn[rr], l, v};
+            }
+          }
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i][j] = zero4();
-      }
+      });
     }
     if (q + 1 < total) commit((q + 1) & 1, r);
     __syncthreads();
@@ -213,14 +289,18 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head(HeadArgs a) {
       y.s1 = __shfl_xor(st[j].s1, o, 64);
       y.a = __shfl_xor(st[j].a, o, 64);
       stat_merge(st[j], y);
+      if constexpr (DRAW) draw_merge(dr[j], draw_shfl(dr[j], o));
     }
   }
   float4* red = reinterpret_cast<float4*>(lds);  // [4 token waves][256 slots]; stages are no longer read
+  float4* redd = red + 4 * kHeadSlots;          // the draws, same layout
   if (quad == 0) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      red[wv * kHeadSlots + 128 * wsl + 16 * j + row16] =
-          make_float4(st[j].m, __int_as_float(st[j].a), st[j].z, st[j].s1);
+    for (int j = 0; j < 8; ++j) {
+      const int o = wv * kHeadSlots + 128 * wsl + 16 * j + row16;
+      red[o] = make_float4(st[j].m, __int_as_float(st[j].a), st[j].z, st[j].s1);
+      if constexpr (DRAW) redd[o] = make_float4(dr[j].g, dr[j].l, __int_as_float(dr[j].a), 0.f);
+    }
   }
   __syncthreads();
   if (t < kHeadSlots && slot_base + t < a.n) {
@@ -231,7 +311,18 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head(HeadArgs a) {
       p = red[k * kHeadSlots + t];
       stat_merge(x, Stat{p.x, p.z, p.w, __float_as_int(p.y)});
     }
-    a.part[(int64_t)blockIdx.x * a.n + slot_base + t] = make_float4(x.m, __int_as_float(x.a), x.z, x.s1);
+    const int64_t o = (int64_t)blockIdx.x * a.n + slot_base + t;
+    if constexpr (DRAW) {
+      Draw y = kNoDraw;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float4 q = redd[k * kHeadSlots + t];
+        draw_merge(y, Draw{q.x, q.y, __float_as_int(q.z)});
+      }
+      x.a = y.a;
+      a.part2[o] = make_float2(y.g, y.l);
+    }
+    a.part[o] = make_float4(x.m, __int_as_float(x.a), x.z, x.s1);
   }
 }
 
@@ -244,23 +335,27 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head(HeadArgs a) {
 // stage of matrix work is shorter than their round trip while the vocabulary stream loads the memory
 // system.  The running per-slot states live in LDS and the eight token waves of a slot merge in wave
 // order.
-constexpr int kHeadKC = 2;      // K steps per X stage
-constexpr int kHeadEDepth = 4;  // K steps of E fragments in flight per wave: the two stages of a loop turn
-static_assert(kHeadEDepth == 2 * kHeadKC, "the ring slot of a K step is 2 * (stage parity) + its index in the stage");
+constexpr int kHeadKC = 2;  // K steps per X stage; the E ring holds the K steps of two stages (a loop turn):
+                            // the ring slot of a K step is KC * (stage parity) + its index in the stage
 
+template <bool DRAW>
 __global__ __launch_bounds__(512, 1) void k_vocab_head_bf16(HeadArgs a) {
   using T = bf16;
-  constexpr int STAGE = kHeadKC * 16 * kFragElems * 2;  // X fragments of kHeadKC steps: 32 KB
+  // the draw's generator needs registers: it runs with one K step per stage (a two-step E ring)
+  constexpr int KC = DRAW ? 1 : kHeadKC;
+  constexpr int EDEPTH = 2 * KC;
+  constexpr int STAGE = KC * 16 * kFragElems * 2;  // X fragments of KC steps: 32 KB at KC = 2
   constexpr int LOADS = STAGE / 16 / 512;                // 16-byte units per thread per stage
   static_assert(LOADS * 16 * 512 == STAGE, "stage layout");
   __shared__ uint4 lds[2 * STAGE / 16];
   __shared__ float4 run[8][kHeadSlots];  // running (max, argmax bits, Z, S1) per token wave and slot
+  __shared__ float4 rund[DRAW ? 8 : 1][kHeadSlots];  // gumbel: running draw (g, l, token bits, -)
   const int t = threadIdx.x, lane = lane_id(), w = wave_id();
   const int quad = lane >> 4;
   const int row16 = lane & 15;
   const int slot_base = blockIdx.y * kHeadSlots;
   const int ks = a.d / 32;
-  const int nch = (ks + kHeadKC - 1) / kHeadKC;
+  const int nch = (ks + KC - 1) / KC;
   const int n_tiles = (a.V + kHeadTokens - 1) / kHeadTokens;
   const int G = gridDim.x;
   const int my_tiles = (n_tiles - (int)blockIdx.x + G - 1) / G;
@@ -278,7 +373,7 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head_bf16(HeadArgs a) {
     for (int j = 0; j < LOADS; ++j) {
       const int u = j * 512 + t;
       const int g = u >> 6, fl = u & 63;
-      const int s = c * kHeadKC + (g >> 4);
+      const int s = c * KC + (g >> 4);
       const int row = min(slot_base + 16 * (g & 15) + (fl & 15), a.n - 1);
       const T* src = X + (int64_t)row * a.d + 32 * min(s, ks - 1) + 8 * (fl >> 4);
       r[j] = s < ks ? *reinterpret_cast<const uint4*>(src) : uint4{0u, 0u, 0u, 0u};
@@ -289,10 +384,10 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head_bf16(HeadArgs a) {
     for (int j = 0; j < LOADS; ++j) lds[buf * (STAGE / 16) + j * 512 + t] = r[j];
   };
   // E fragments of flat K step f (over this workgroup's tiles); steps past the end reload the last one
-  const int nsteps = total * kHeadKC;
+  const int nsteps = total * KC;
   auto e_load = [&](int f, Frag<T> (&e)[2]) __attribute__((always_inline)) {
     f = min(f, nsteps - 1);
-    const int tl = f / (nch * kHeadKC), s = f % (nch * kHeadKC);
+    const int tl = f / (nch * KC), s = f % (nch * KC);
     const int tile = (int)blockIdx.x + tl * G;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -306,13 +401,16 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head_bf16(HeadArgs a) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[i][j] = zero4();
-  for (int i = lane; i < kHeadSlots; i += 64) run[w][i] = make_float4(-INFINITY, __int_as_float(0x7fffffff), 0.f, 0.f);
+  for (int i = lane; i < kHeadSlots; i += 64) {
+    run[w][i] = make_float4(-INFINITY, __int_as_float(0x7fffffff), 0.f, 0.f);
+    if constexpr (DRAW) rund[w][i] = make_float4(-INFINITY, 0.f, __int_as_float(0x7fffffff), 0.f);
+  }
 
   // tile finished: lane holds, for slot slot_base + 16*j + row16, tokens v0 + 16*i + 4*quad + rr
   auto fold_tile = [&](int q) __attribute__((always_inline)) {
     const int v0 = ((int)blockIdx.x + (q / nch) * G) * kHeadTokens + 32 * w;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    static_for<16>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int j = decltype(jc)::value;
       Stat loc{-INFINITY, 0.f, 0.f, 0x7fffffff};
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -346,20 +444,43 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head_bf16(HeadArgs a) {
         y.a = __shfl_xor(loc.a, o, 64);
         stat_merge(loc, y);
       }
+      Draw dl = kNoDraw;
+      if constexpr (DRAW) {
+        const uint32_t row = (uint32_t)(slot_base + 16 * j + row16);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          float gn[4];
+          gumbel4(a, (uint32_t)(v0 + 16 * i + 4 * quad) >> 2, row, gn);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int v = v0 + 16 * i + 4 * quad + rr;
+            const float l = acc[i][j][rr] * beta;
+            if (v < a.V && l + gn[rr] > dl.g) dl = Draw{l + gn[rr], l, v};
+          }
+        }
+#pragma unroll
+        for (int o = 16; o <= 32; o <<= 1) draw_merge(dl, draw_shfl(dl, o));
+      }
       if (quad == 0) {
         const float4 p = run[w][16 * j + row16];
         Stat x{p.x, p.z, p.w, __float_as_int(p.y)};
         stat_merge(x, loc);
         run[w][16 * j + row16] = make_float4(x.m, __int_as_float(x.a), x.z, x.s1);
+        if constexpr (DRAW) {
+          const float4 q = rund[w][16 * j + row16];
+          Draw y{q.x, q.y, __float_as_int(q.z)};
+          draw_merge(y, dl);
+          rund[w][16 * j + row16] = make_float4(y.g, y.l, __int_as_float(y.a), 0.f);
+        }
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) acc[i][j] = zero4();
-    }
+    });
   };
 
-  Frag<T> ering[kHeadEDepth][2];
+  Frag<T> ering[EDEPTH][2];
 #pragma unroll
-  for (int dd = 0; dd < kHeadEDepth; ++dd) e_load(dd, ering[dd]);
+  for (int dd = 0; dd < EDEPTH; ++dd) e_load(dd, ering[dd]);
   // X loads run two stages ahead of their LDS stage: stage q's data is requested at the start of stage
   // q - 2 into register set q & 1 and written to LDS buffer q & 1 at the end of stage q - 1
   uint4 r[2][LOADS];
@@ -375,8 +496,8 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head_bf16(HeadArgs a) {
     if (q + 2 < total) issue(q + 2, r[B]);
     const T* base = reinterpret_cast<const T*>(lds) + B * (STAGE / 2) + lane * 8;
 #pragma unroll
-    for (int kk = 0; kk < kHeadKC; ++kk) {
-      Frag<T>(&ea)[2] = ering[2 * B + kk];
+    for (int kk = 0; kk < KC; ++kk) {
+      Frag<T>(&ea)[2] = ering[KC * B + kk];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         Frag<T> fb[8];
@@ -387,7 +508,7 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head_bf16(HeadArgs a) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) mma(acc[i][8 * half + j], ea[i], fb[j]);
       }
-      e_load(q * kHeadKC + kk + kHeadEDepth, ering[2 * B + kk]);
+      e_load(q * KC + kk + EDEPTH, ering[KC * B + kk]);
     }
     if (q % nch == nch - 1) fold_tile(q);
     if (q + 1 < total) commit(1 - B, r[1 - B]);
@@ -405,19 +526,38 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head_bf16(HeadArgs a) {
       p = run[k2][t];
       stat_merge(x, Stat{p.x, p.z, p.w, __float_as_int(p.y)});
     }
-    a.part[(int64_t)blockIdx.x * a.n + slot_base + t] = make_float4(x.m, __int_as_float(x.a), x.z, x.s1);
+    const int64_t o = (int64_t)blockIdx.x * a.n + slot_base + t;
+    if constexpr (DRAW) {
+      Draw y = kNoDraw;
+#pragma unroll
+      for (int k2 = 0; k2 < 8; ++k2) {
+        const float4 q = rund[k2][t];
+        draw_merge(y, Draw{q.x, q.y, __float_as_int(q.z)});
+      }
+      x.a = y.a;
+      a.part2[o] = make_float2(y.g, y.l);
+    }
+    a.part[o] = make_float4(x.m, __int_as_float(x.a), x.z, x.s1);
   }
 }
 
 // One wave per slot: lane i merges groups i, i+64, ... in order, then a fixed
 // butterfly merges the lanes.
+template <bool DRAW>
 __global__ __launch_bounds__(256) void k_head_merge(HeadArgs a) {
   const int slot = blockIdx.x * 4 + wave_id();
   if (slot >= a.n) return;
   const int lane = lane_id();
   Stat st{-INFINITY, 0.f, 0.f, 0x7fffffff};
+  Draw dr = kNoDraw;
   for (int gi = lane; gi < a.n_groups; gi += 64) {
-    float4 p = a.part[(int64_t)gi * a.n + slot];
+    const int64_t o = (int64_t)gi * a.n + slot;
+    float4 p = a.part[o];
+    if constexpr (DRAW) {
+      const float2 q = a.part2[o];
+      draw_merge(dr, Draw{q.x, q.y, __float_as_int(p.y)});
+      p.y = __int_as_float(0x7fffffff);  // the slot's argmax is not needed
+    }
     Stat y{p.x, p.z, p.w, __float_as_int(p.y)};
     stat_merge(st, y);
   }
@@ -429,10 +569,16 @@ __global__ __launch_bounds__(256) void k_head_merge(HeadArgs a) {
     y.s1 = __shfl_xor(st.s1, o, 64);
     y.a = __shfl_xor(st.a, o, 64);
     stat_merge(st, y);
+    if constexpr (DRAW) draw_merge(dr, draw_shfl(dr, o));
   }
   if (lane == 0) {
-    a.pred[slot] = st.a;
-    a.conf[slot] = 1.0f / st.z;
+    if constexpr (DRAW) {
+      a.pred[slot] = dr.a;
+      a.conf[slot] = exp2f((dr.l - st.m) * 1.4426950408889634f) / st.z;
+    } else {
+      a.pred[slot] = st.a;
+      a.conf[slot] = 1.0f / st.z;
+    }
     a.ent[slot] = logf(st.z) - st.s1 / st.z;
   }
 }
@@ -445,15 +591,25 @@ int head_groups(int V) {
 template <typename T>
 hipError_t launch_vocab_head(const HeadArgs& a, hipStream_t s) {
   dim3 grid(a.n_groups, (a.n + kHeadSlots - 1) / kHeadSlots);
-  if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL(k_vocab_head_bf16, grid, dim3(512), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_vocab_head<T>, grid, dim3(512), 0, s, a);
+  if constexpr (sizeof(T) == 2) {
+    if (a.gumbel)
+      hipLaunchKernelGGL(k_vocab_head_bf16<true>, grid, dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL(k_vocab_head_bf16<false>, grid, dim3(512), 0, s, a);
+  } else {
+    if (a.gumbel)
+      hipLaunchKernelGGL((k_vocab_head<T, true>), grid, dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_vocab_head<T, false>), grid, dim3(512), 0, s, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_head_merge(const HeadArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_head_merge, dim3((a.n + 3) / 4), dim3(256), 0, s, a);
+  if (a.gumbel)
+    hipLaunchKernelGGL(k_head_merge<true>, dim3((a.n + 3) / 4), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_head_merge<false>, dim3((a.n + 3) / 4), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

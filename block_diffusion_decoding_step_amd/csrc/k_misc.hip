@@ -417,9 +417,12 @@ __global__ __launch_bounds__(1024) void k_moe_combine(T* __restrict__ X, const T
 // [P2] "How Diffusion Changes the Equation": stop when the mean canvas entropy is
 // under a threshold or when predictions are unchanged over two consecutive
 // passes, at most 48 passes; [P5] "How block diffusion works": the mean covers
-// every slot.  One workgroup; S <= 1024.
-__global__ __launch_bounds__(1024) void k_stop_check(const float* __restrict__ ent, const int32_t* __restrict__ pred,
-                                                     int32_t* __restrict__ prev, int S, int step,
+// every slot.  With and_rule the early stop needs both at once ([P2] "Architecture
+// Details": the recommended sampler).  With lock, a locked slot's prediction is
+// replaced by its canvas token first (pred is rewritten).  One workgroup; S <= 1024.
+__global__ __launch_bounds__(1024) void k_stop_check(const float* __restrict__ ent, int32_t* __restrict__ pred,
+                                                     int32_t* __restrict__ prev, const int32_t* __restrict__ canvas,
+                                                     const uint8_t* __restrict__ lock, int S, int step,
                                                      StopParams sp, dg_block_status* __restrict__ out) {
   __shared__ float part[1024];
   __shared__ int diff, bad;
@@ -427,10 +430,16 @@ __global__ __launch_bounds__(1024) void k_stop_check(const float* __restrict__ e
   if (i == 0) { diff = 0; bad = 0; }
   __syncthreads();
   float e = 0.f;
+  int32_t p = 0;
   if (i < S) {
     e = ent[i];
     if (!(e >= 0.f && e <= sp.ln_vocab * 1.0001f + 1e-5f)) atomicOr(&bad, 1);
-    if (pred[i] != prev[i]) atomicOr(&diff, 1);
+    p = pred[i];
+    if (lock && lock[i]) {
+      p = canvas[i];
+      pred[i] = p;
+    }
+    if (p != prev[i]) atomicOr(&diff, 1);
   }
   part[i] = e;
   __syncthreads();
@@ -438,18 +447,19 @@ __global__ __launch_bounds__(1024) void k_stop_check(const float* __restrict__ e
     if (i < s) part[i] += part[i + s];
     __syncthreads();
   }
-  if (i < S) prev[i] = pred[i];
+  if (i < S) prev[i] = p;
   if (i == 0) {
     float mean = part[0] / (float)S;
+    const bool low = mean < sp.threshold, stable = step >= 2 && !diff;
     int reason = 0;
     if (sp.fixed_steps > 0) {
-      reason = step >= sp.fixed_steps ? 4 : 0;
-    } else if (mean < sp.threshold) {
-      reason = 1;
-    } else if (step >= 2 && !diff) {
-      reason = 2;
+      reason = step >= sp.fixed_steps ? DG_STOP_FIXED : 0;
+    } else if (sp.and_rule ? (low && stable) : low) {
+      reason = sp.and_rule ? DG_STOP_SETTLED : DG_STOP_ENTROPY;
+    } else if (!sp.and_rule && stable) {
+      reason = DG_STOP_STABLE;
     } else if (step >= sp.max_steps) {
-      reason = 3;
+      reason = DG_STOP_CAP;
     }
     out->steps = step;
     out->reason = reason;
@@ -459,40 +469,26 @@ __global__ __launch_bounds__(1024) void k_stop_check(const float* __restrict__ e
 }
 
 // ============================================================== canvas update (Philox)
-// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds; each round takes
-// the 64-bit products of counter words 0 and 2 with two fixed multipliers, swaps
-// in their low halves and xors their high halves with words 1/3 and the key;
-// the key advances by two Weyl constants between rounds.
-__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
-                                                 uint32_t k1) {
-  const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u, W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
-#pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    if (r) { k0 += W0; k1 += W1; }
-    uint64_t p0 = (uint64_t)M0 * c0;
-    uint64_t p1 = (uint64_t)M1 * c2;
-    uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
-    uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
-    uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
-    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
-  }
-  return c0;
-}
-
 // [P5] "How block diffusion works": each pass keeps the slots the model is most
 // confident about and re-randomises the rest; the canvas starts as random tokens.
-// One workgroup of S threads (S <= 1024).  rank_i counts slots that precede slot i
-// in (conf descending, slot ascending) order; NaN ranks as -inf.
+// The key is the confidence, or minus the entropy (rank_entropy: lowest entropy
+// first, [P2] "Architecture Details"); NaN ranks as -inf.  With lock (non-null),
+// locked slots rank first, stay kept and keep their canvas token.  One workgroup
+// of S threads (S <= 1024); rank_i counts slots that precede slot i in (key
+// descending, slot ascending) order.  lock and keep_mask may alias (each thread
+// reads its own entry before the barrier and writes it after).
 __global__ __launch_bounds__(1024) void k_canvas_update(const int32_t* __restrict__ pred,
-                                                        const float* __restrict__ conf, int S, int keep,
+                                                        const float* __restrict__ conf, const float* ent,
+                                                        int rank_entropy, const uint8_t* lock, int S, int keep,
                                                         uint32_t k0, uint32_t k1, uint32_t block, uint32_t step,
-                                                        uint32_t V, int32_t* __restrict__ canvas,
-                                                        uint8_t* __restrict__ keep_mask) {
+                                                        uint32_t V, int32_t* __restrict__ canvas, uint8_t* keep_mask) {
   __shared__ float key[1024];
   int i = threadIdx.x;
+  const bool locked = lock && i < S && lock[i];
   if (keep > 0 && i < S) {
-    float c = conf[i];
-    key[i] = (c != c) ? -INFINITY : c;
+    float c = rank_entropy ? -ent[i] : conf[i];
+    c = (c != c) ? -INFINITY : c;
+    key[i] = locked ? INFINITY : c;
   }
   __syncthreads();
   if (i >= S) return;
@@ -508,11 +504,14 @@ __global__ __launch_bounds__(1024) void k_canvas_update(const int32_t* __restric
     }
     kept = rank < keep;
   }
+  kept = kept || locked;
   int32_t out;
-  if (kept) {
+  if (locked) {
+    out = canvas[i];
+  } else if (kept) {
     out = pred[i];
   } else {
-    uint32_t w0 = philox_word0((uint32_t)i, step, block, 0u, k0, k1);
+    const uint32_t w0 = philox4x32_10((uint32_t)i, step, block, 0u, k0, k1).x;
     out = (int32_t)(((uint64_t)w0 * V) >> 32);
   }
   canvas[i] = out;
@@ -567,17 +566,17 @@ hipError_t launch_moe_combine(T* X, const T* Ys, const T* Yp, const int32_t* pos
                      yn_tiled, eps);
   return hipGetLastError();
 }
-hipError_t launch_stop_check(const float* ent, const int32_t* pred, int32_t* prev, int S, int step, StopParams sp,
-                             dg_block_status* out, hipStream_t s) {
-  hipLaunchKernelGGL(k_stop_check, dim3(1), dim3(1024), 0, s, ent, pred, prev, S, step, sp, out);
+hipError_t launch_stop_check(const float* ent, int32_t* pred, int32_t* prev, const int32_t* canvas,
+                             const uint8_t* lock, int S, int step, StopParams sp, dg_block_status* out,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(k_stop_check, dim3(1), dim3(1024), 0, s, ent, pred, prev, canvas, lock, S, step, sp, out);
   return hipGetLastError();
 }
-hipError_t launch_canvas_update(const int32_t* pred, const float* conf, int S, int keep, uint64_t seed,
-                                uint32_t block, uint32_t step, uint32_t V, int32_t* canvas, uint8_t* keep_mask,
-                                hipStream_t s) {
-  int threads = ((S + 63) / 64) * 64;
-  hipLaunchKernelGGL(k_canvas_update, dim3(1), dim3(threads), 0, s, pred, conf, S, keep, (uint32_t)seed,
-                     (uint32_t)(seed >> 32), block, step, V, canvas, keep_mask);
+hipError_t launch_canvas_update(const CanvasArgs& a, hipStream_t s) {
+  int threads = ((a.S + 63) / 64) * 64;
+  hipLaunchKernelGGL(k_canvas_update, dim3(1), dim3(threads), 0, s, a.pred, a.conf, a.ent, a.rank_entropy, a.lock,
+                     a.S, a.keep, (uint32_t)a.seed, (uint32_t)(a.seed >> 32), a.block, a.step, a.V, a.canvas,
+                     a.keep_mask);
   return hipGetLastError();
 }
 

@@ -76,13 +76,15 @@ typedef enum dg_dtype { DG_F32 = 0, DG_BF16 = 1 } dg_dtype;
 
 /* Why a block stopped ([P2] "How Diffusion Changes the Equation": entropy below a
  * threshold, or predictions unchanged over two consecutive passes, or 48 passes;
- * the three are OR-ed).  FIXED = a fixed pass count requested by the caller. */
+ * the three are OR-ed).  FIXED = a fixed pass count requested by the caller.
+ * SETTLED = low entropy and two unchanged passes together (DG_STOP_AND). */
 typedef enum dg_stop {
   DG_STOP_NONE = 0,
   DG_STOP_ENTROPY = 1,
   DG_STOP_STABLE = 2,
   DG_STOP_CAP = 3,
-  DG_STOP_FIXED = 4
+  DG_STOP_FIXED = 4,
+  DG_STOP_SETTLED = 5
 } dg_stop;
 
 /* Model dimensions.  The pages give a 128-expert MoE with 8 routed + 1 shared
@@ -135,21 +137,51 @@ typedef struct dg_kv {
   int64_t capacity;
 } dg_kv;
 
+/* Sampler variants (dg_sampler.flags), each off by default.  Together they give the
+ * recommended sampler of [P2] "Architecture Details" (temperature falling linearly
+ * from 0.8 to 0.4 over the passes, lowest-entropy tokens locked first, stop when
+ * the mean entropy is below 0.005 and the top tokens are stable over two passes);
+ * [P5] "Appendix: Methodology", "Decoding" runs it with a bound of 0.1.
+ *   DG_SAMPLE_GUMBEL: each slot's token is drawn from the softmax at the pass's
+ *     temperature (Gumbel-max: argmax_v of beta l_v + G_v, G_v = -ln(-ln u),
+ *     u = (2 floor(w / 2^9) + 1) / 2^24, w = word v mod 4 of Philox4x32-10 with key
+ *     (seed low, seed high) and counter (v / 4, slot + 65536 * pass, block, 1));
+ *     conf is then the probability of the drawn token.  Passes and slots < 65536.
+ *   DG_SAMPLE_ANNEAL: the temperature of pass t is temperature_first + (temperature_last
+ *     - temperature_first) (t - 1) / (N - 1), N = fixed_steps if > 0 else max_steps
+ *     (temperature_first when N = 1); inv_temperature is then ignored.
+ *   DG_KEEP_ENTROPY: the keep rule ranks by entropy, lowest first (ties to the lower
+ *     slot, NaN last), instead of by confidence.
+ *   DG_KEEP_LOCK: a kept slot keeps its token for the rest of the block: its
+ *     prediction is replaced by that token (so stability and the committed block see
+ *     it), later updates keep it and add unlocked slots until k_t are locked.
+ *   DG_STOP_AND: the early stop needs mean entropy < entropy_threshold and two
+ *     unchanged passes together (reason SETTLED); fixed_steps and max_steps as before. */
+#define DG_SAMPLE_GUMBEL 0x1u
+#define DG_SAMPLE_ANNEAL 0x2u
+#define DG_KEEP_ENTROPY 0x4u
+#define DG_KEEP_LOCK 0x8u
+#define DG_STOP_AND 0x10u
+#define DG_SAMPLER_FLAGS 0x1Fu
+
 /* Sampler of dg_generate_block.
  *   keep count after pass t: k_t = min(canvas, t * n_new) ([P5] "How block diffusion
  *   works": keep the most confident slots, re-randomise the rest);
  *   fixed_steps > 0: run exactly that many passes (timing mode, reason FIXED);
  *   otherwise stop on mean entropy < entropy_threshold, on two equal consecutive
  *   predictions, or at max_steps (<= 48 by default, any value >= 1 accepted).
- *   seed keys the Philox canvas draws; inv_temperature scales the logits. */
+ *   seed keys the Philox canvas draws; inv_temperature scales the logits.
+ *   flags: DG_SAMPLE_* / DG_KEEP_* / DG_STOP_AND bits (above); other bits are invalid. */
 typedef struct dg_sampler {
   int32_t n_new;
   int32_t max_steps;
   int32_t fixed_steps;
   float entropy_threshold;
   float inv_temperature;
-  uint32_t flags;       /* reserved, must be 0 */
+  uint32_t flags;
   uint64_t seed;
+  float temperature_first;  /* DG_SAMPLE_ANNEAL: temperature of pass 1 (> 0) */
+  float temperature_last;   /* DG_SAMPLE_ANNEAL: temperature of the last pass of the budget (> 0) */
 } dg_sampler;
 
 /* Block status (host struct for dg_generate_block; device struct for dg_stop_check). */
@@ -215,6 +247,15 @@ int dg_denoise_step(const dg_config* cfg, const dg_weights* w, const dg_kv* kv, 
                     float inv_temperature, int32_t* pred, float* conf, float* entropy, const dg_debug* dbg,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* Pass `step` (1-based, < 65536) of block `block` as dg_generate_block runs it under
+ * `sampler` ([P2] "Architecture Details"): dg_denoise_step at that pass's temperature,
+ * and with DG_SAMPLE_GUMBEL pred is the drawn token and conf its probability.  The
+ * lock of DG_KEEP_LOCK is applied by dg_stop_check, not here.  Errors as
+ * dg_denoise_step; DG_ERR_INVALID also for an invalid sampler or step. */
+int dg_denoise_step_sampler(const dg_config* cfg, const dg_weights* w, const dg_kv* kv, const dg_sampler* sampler,
+                            uint32_t block, int32_t step, const int32_t* canvas, int32_t* pred, float* conf,
+                            float* entropy, void* ws, size_t ws_bytes, void* stream);
+
 /* Canvas update ([P5] "How block diffusion works": keep the most confident slots,
  * re-randomise the others; any slot may change on a later pass).  The keep_count
  * slots of highest conf (ties to the lower slot, NaN last) take pred; every other
@@ -226,6 +267,18 @@ int dg_denoise_step(const dg_config* cfg, const dg_weights* w, const dg_kv* kv, 
 int dg_canvas_update(const dg_config* cfg, const int32_t* pred, const float* conf, int32_t keep_count,
                      uint64_t seed, uint32_t block, uint32_t step, int32_t* canvas_out, uint8_t* keep_mask,
                      void* stream);
+
+/* The canvas update after pass `step` as dg_generate_block runs it under `sampler`: keep
+ * count k_step = min(canvas, step * n_new), ranked by conf or (DG_KEEP_ENTROPY) by
+ * entropy; redraws as dg_canvas_update with the sampler's seed.  step = 0 gives the
+ * initial canvas.  DG_KEEP_LOCK: lock_mask (device uint8 [canvas], required) holds the
+ * locked slots on entry (ignored at step 0) and on return; locked slots keep their
+ * token in `canvas` (in/out) and count toward k_step.  Without it lock_mask (may be
+ * NULL) receives the keep mask.  pred and the ranking input may be NULL when nothing
+ * is kept.  DG_ERR_INVALID for a NULL canvas, a missing input or step < 0. */
+int dg_canvas_update_sampler(const dg_config* cfg, const dg_sampler* sampler, uint32_t block, int32_t step,
+                             const int32_t* pred, const float* conf, const float* entropy, int32_t* canvas,
+                             uint8_t* lock_mask, void* stream);
 
 /* Commit a finished block ([P2] "How Diffusion Changes the Equation": each 256-token
  * block is committed to the KV cache before the next; [P3] "How diffusion text
@@ -283,13 +336,28 @@ int dg_layer_forward(const dg_config* cfg, const dg_weights* w, int32_t layer, c
 int dg_vocab_head(const dg_config* cfg, const dg_weights* w, const void* x, int64_t n, float inv_temperature,
                   int32_t* pred, float* conf, float* entropy, void* ws, size_t ws_bytes, void* stream);
 
+/* dg_vocab_head at pass `step` (1..65535) of `block` under `sampler`: that pass's
+ * temperature and, with DG_SAMPLE_GUMBEL, the draw of dg_denoise_step_sampler (row i
+ * is slot i of the draw's counter). */
+int dg_vocab_head_sampler(const dg_config* cfg, const dg_weights* w, const dg_sampler* sampler, uint32_t block,
+                          int32_t step, const void* x, int64_t n, int32_t* pred, float* conf, float* entropy,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* Host only: 1 / temperature of pass `step` (>= 1) under `sampler` (inv_temperature, or the
+ * DG_SAMPLE_ANNEAL schedule), as the passes above use it.  0 is written on error. */
+int dg_sampler_inv_temperature(const dg_sampler* sampler, int32_t step, float* h_inv_temperature);
+
 /* Stop check after pass `step` (1-based): writes a dg_block_status to d_status
  * (device) with reason ENTROPY if mean(entropy) < threshold, else STABLE if
  * step >= 2 and pred equals prev_pred on every slot, else CAP if step >= max_steps,
- * else NONE (fixed_steps > 0: FIXED when step >= fixed_steps, else NONE).  Then
- * copies pred into prev_pred.  Uses cfg->canvas slots. */
-int dg_stop_check(const dg_config* cfg, const dg_sampler* sampler, int32_t step, const float* entropy,
-                  const int32_t* pred, int32_t* prev_pred, dg_block_status* d_status, void* stream);
+ * else NONE (fixed_steps > 0: FIXED when step >= fixed_steps, else NONE).  With
+ * DG_STOP_AND the early stop needs both conditions (reason SETTLED).  Then copies pred
+ * into prev_pred.  With DG_KEEP_LOCK, pred (in/out) first takes the canvas token
+ * (`canvas`, the pass's input) at every slot set in lock_mask; canvas and lock_mask are
+ * required then and ignored otherwise (may be NULL).  Uses cfg->canvas slots. */
+int dg_stop_check(const dg_config* cfg, const dg_sampler* sampler, int32_t step, const float* entropy, int32_t* pred,
+                  int32_t* prev_pred, const int32_t* canvas, const uint8_t* lock_mask, dg_block_status* d_status,
+                  void* stream);
 
 /* --- measurement support: HIP-event timing of kernel classes --------------------- */
 

@@ -252,7 +252,7 @@ class Model:
 
 
 def head_stats(x: np.ndarray, g_final: np.ndarray, embed: np.ndarray, inv_temperature: float, eps: float, rnd,
-               chunk: int = 64, gumbel=None):
+               chunk: int = 64, gumbel=None, slots=None):
     """Final norm, tied vocab projection and per-slot softmax statistics.
 
     logits = beta * (rms(x) * g) E^T; pred = argmax (fp32 logits, ties to the lowest
@@ -265,7 +265,7 @@ def head_stats(x: np.ndarray, g_final: np.ndarray, embed: np.ndarray, inv_temper
     gumbel = (seed, block, step) samples instead of taking the argmax (the recommended
     sampler's temperature, [P2] "Architecture Details"): pred = argmax of the fp32
     perturbed score logits + G, G from oracle.philox.gumbel_noise with row i as slot i
-    (ties to the lowest id); conf = p[pred], the probability of the token drawn; the
+    (or as slot slots[i]; ties to the lowest id); conf = p[pred], the probability of the token drawn; the
     margin is then the top-2 gap of the perturbed scores.  The entropy is unchanged.
     """
     xf = rnd(rmsnorm(x, g_final, eps))
@@ -279,7 +279,8 @@ def head_stats(x: np.ndarray, g_final: np.ndarray, embed: np.ndarray, inv_temper
         score = lg
         if gumbel is not None:
             seed, block, step = gumbel
-            score = lg + gumbel_noise(seed, block, step, np.arange(s0, s0 + lg.shape[0]), lg.shape[1])
+            rows = np.arange(s0, s0 + lg.shape[0]) if slots is None else np.asarray(slots)[s0:s0 + lg.shape[0]]
+            score = lg + gumbel_noise(seed, block, step, rows, lg.shape[1])
         l32 = f32(score)
         choice = np.argmax(l32, axis=1)
         pred[s0:s0 + chunk] = choice

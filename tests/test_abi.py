@@ -26,7 +26,8 @@ def _declared():
 def test_header_declares_the_documented_calls():
     names = _declared()
     for n in ("dg_prefill_kv", "dg_denoise_step", "dg_canvas_update", "dg_commit_block", "dg_generate_block",
-              "dg_generate_block_overlapped",
+              "dg_generate_block_overlapped", "dg_denoise_step_sampler", "dg_canvas_update_sampler",
+              "dg_vocab_head_sampler", "dg_sampler_inv_temperature",
               "dg_workspace_size", "dg_status_string"):
         assert n in names
     assert set(names) == set(dg.EXPORTED)
@@ -177,7 +178,7 @@ def test_calls_validate_before_any_device_work():
         dg.dg_generate_block_overlapped(cfg, w, kv, dg.make_sampler(4), 0, buf, 1, buf, buf, ws_bytes, 0)
     assert e.value.status == dg.DG_ERR_WORKSPACE
     with pytest.raises(dg.DGError) as e:
-        dg.dg_stop_check(cfg, dg.make_sampler(4), 0, buf, buf, buf, buf, 0)
+        dg.dg_stop_check(cfg, dg.make_sampler(4), 0, buf, buf, buf, buf, stream=0)
     assert e.value.status == dg.DG_ERR_INVALID
     with pytest.raises(dg.DGError) as e:
         dg.dg_canvas_update(cfg, buf, buf, cfg.canvas + 1, 1, 0, 1, buf, None, 0)
@@ -211,3 +212,69 @@ def test_pack_rejects_overlap_and_bad_dtype():
         dg.dg_pack_matrix(a, _Fake(0x100000 + 64), 1, 16, 32, dg.DG_BF16, 0)
     with pytest.raises(dg.DGError):
         dg.dg_pack_matrix(a, _Fake(0x900000), 1, 16, 32, 7, 0)
+
+
+# ----------------------------------------------------------------------------- sampler variants
+
+def test_sampler_flag_values_match_header():
+    text = open(HEADER).read()
+    for name in ("DG_SAMPLE_GUMBEL", "DG_SAMPLE_ANNEAL", "DG_KEEP_ENTROPY", "DG_KEEP_LOCK", "DG_STOP_AND"):
+        m = re.search(r"#define %s (0x[0-9A-Fa-f]+)u" % name, text)
+        assert m and int(m.group(1), 16) == getattr(dg, name), name
+    assert "DG_STOP_SETTLED = 5" in text and dg.DG_STOP_SETTLED == 5
+
+
+def test_anneal_schedule_equals_oracle():
+    """The host schedule of the passes' temperatures against the oracle's (fp32 rounding of 1/T)."""
+    from oracle import sampler as osm
+    for fixed, cap in ((0, 48), (10, 48), (1, 48), (0, 1)):
+        sp = dg.make_sampler(26, max_steps=cap, fixed_steps=fixed, flags=dg.DG_SAMPLE_ANNEAL, temperature_first=0.8,
+                             temperature_last=0.4)
+        ref = osm.Sampler(n_new=26, max_steps=cap, fixed_steps=fixed, anneal=(float(ctypes.c_float(0.8).value),
+                                                                              float(ctypes.c_float(0.4).value)))
+        for t in range(1, (fixed or cap) + 1):
+            got = dg.dg_sampler_inv_temperature(sp, t)
+            assert got == float(ctypes.c_float(osm.pass_inv_temperature(ref, t)).value), (fixed, cap, t)
+    sp = dg.make_sampler(4, inv_temperature=2.5)
+    assert dg.dg_sampler_inv_temperature(sp, 7) == 2.5
+
+
+def test_sampler_variants_validate():
+    cfg = _cfg()
+    w = _fake_weights(cfg.n_layers)
+    buf = _Fake(0x20000)
+    ws_bytes = dg.dg_workspace_size(cfg, cfg.canvas)
+    kv = dg.KV(buf, buf, capacity=128, length=0)
+    bad = [dg.make_sampler(4, flags=0x20),                                                # unknown bit
+           dg.make_sampler(4, flags=dg.DG_SAMPLE_ANNEAL, temperature_first=0.8),            # last = 0
+           dg.make_sampler(4, flags=dg.DG_SAMPLE_ANNEAL, temperature_first=float("inf"), temperature_last=0.4),
+           dg.make_sampler(4, inv_temperature=0.0),
+           dg.make_sampler(4, max_steps=70000, flags=dg.DG_SAMPLE_GUMBEL)]                 # pass beyond 16 bits
+    for sp in bad:
+        with pytest.raises(dg.DGError) as e:
+            dg.dg_sampler_inv_temperature(sp, 1)
+        assert e.value.status == dg.DG_ERR_INVALID
+        with pytest.raises(dg.DGError) as e:
+            dg.dg_generate_block(cfg, w, kv, sp, 0, buf, buf, ws_bytes, 0)
+        assert e.value.status == dg.DG_ERR_INVALID
+    ok = dg.make_sampler(4, flags=dg.DG_SAMPLE_ANNEAL | dg.DG_SAMPLE_GUMBEL, inv_temperature=0.0,
+                         temperature_first=0.8, temperature_last=0.4)
+    assert abs(dg.dg_sampler_inv_temperature(ok, 1) - 1.25) < 1e-6   # inv_temperature is ignored under anneal
+    lock = dg.make_sampler(4, flags=dg.DG_KEEP_LOCK)
+    cases = [
+        lambda: dg.dg_stop_check(cfg, lock, 1, buf, buf, buf, buf, None, buf, 0),            # lock without canvas
+        lambda: dg.dg_stop_check(cfg, lock, 1, buf, buf, buf, buf, buf, None, 0),            # lock without mask
+        lambda: dg.dg_canvas_update_sampler(cfg, lock, 0, 2, buf, buf, buf, buf, None, 0),   # lock without mask
+        lambda: dg.dg_canvas_update_sampler(cfg, dg.make_sampler(4), 0, -1, buf, buf, buf, buf, None, 0),
+        lambda: dg.dg_canvas_update_sampler(cfg, dg.make_sampler(4, flags=dg.DG_KEEP_ENTROPY), 0, 2, buf, buf, None,
+                                            buf, None, 0),                                 # entropy ranking, no entropy
+        lambda: dg.dg_canvas_update_sampler(cfg, dg.make_sampler(4), 0, 1, buf, buf, buf, None, None, 0),
+        lambda: dg.dg_denoise_step_sampler(cfg, w, kv, dg.make_sampler(4), 0, 0, buf, buf, buf, buf, buf, ws_bytes,
+                                           0),                                             # passes count from 1
+        lambda: dg.dg_vocab_head_sampler(cfg, w, dg.make_sampler(4), 0, 70000, buf, 4, buf, buf, buf, buf, ws_bytes,
+                                         0),
+    ]
+    for i, c in enumerate(cases):
+        with pytest.raises(dg.DGError) as e:
+            c()
+        assert e.value.status == dg.DG_ERR_INVALID, i

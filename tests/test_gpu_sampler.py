@@ -1,0 +1,250 @@
+"""GPU parity of the sampler variants (Gumbel-max draws at an annealed temperature, entropy-ranked keep,
+locking, the AND stop rule) against the oracle, through the C ABI.
+
+Same bars as the other parity tests: bit-exact for integer work (tokens, keep and lock masks, step counts,
+stop reasons; a draw is compared where the oracle's top-2 gap of the perturbed scores exceeds 1e-2 in bf16),
+1e-4 relative in fp32 and 2e-2 in bf16 for the floating-point statistics.
+"""
+from __future__ import annotations
+
+import math
+import sys
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import block_diffusion_decoding_step_amd as dg  # noqa: E402
+import dg_inputs  # noqa: E402
+from dg_inputs import device as gdev  # noqa: E402
+from dg_inputs import recipe  # noqa: E402
+from oracle import model as om  # noqa: E402
+from oracle import numerics  # noqa: E402
+from oracle import sampler as osm  # noqa: E402
+from tests._gpu import Session, allclose_report, to_f64  # noqa: E402
+from tests._helpers import oracle_model  # noqa: E402
+
+F32_TOL = (1e-4, 1e-4)
+BF16_TOL = (2e-2, 2e-2)
+MARGIN = 1e-2
+ALL = dg.DG_SAMPLE_GUMBEL | dg.DG_SAMPLE_ANNEAL | dg.DG_KEEP_ENTROPY | dg.DG_KEEP_LOCK | dg.DG_STOP_AND
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _f32(x):
+    return float(np.float32(x))
+
+
+def _pair(flags, **kw):
+    """GPU and oracle samplers with the same settings (temperatures as the fp32 values the GPU reads)."""
+    anneal = (_f32(0.8), _f32(0.4)) if flags & dg.DG_SAMPLE_ANNEAL else None
+    args = dict(n_new=recipe.C0.n_new, **kw)
+    sp = dg.make_sampler(**args, flags=flags, temperature_first=0.8, temperature_last=0.4)
+    ref = osm.Sampler(**args, gumbel=bool(flags & dg.DG_SAMPLE_GUMBEL), anneal=anneal,
+                      rank_entropy=bool(flags & dg.DG_KEEP_ENTROPY), lock=bool(flags & dg.DG_KEEP_LOCK),
+                      stop_and=bool(flags & dg.DG_STOP_AND))
+    return sp, ref
+
+
+def _c0_session():
+    d = recipe.C0.dims
+    storage = dg_inputs.model_weights_host(d)
+    sess = Session(d, capacity=recipe.C0.prefix + 4 * d.canvas, max_tokens=max(d.canvas, 64),
+                   weights=gdev.from_host(storage, d.dtype))
+    model = oracle_model(d, storage)
+    kv = om.KVCache(d.n_layers, d.n_kv_heads, d.head_dim)
+    prompt = dg_inputs.prompt_tokens(recipe.C0.prefix, d.vocab)
+    sess.prefill(prompt)
+    osm.prefill(model, kv, prompt)
+    return sess, model, kv
+
+
+CASES = [
+    ("gumbel_fixed", dg.DG_SAMPLE_GUMBEL, dict(fixed_steps=10, inv_temperature=1.25)),
+    ("gumbel_anneal_adaptive", dg.DG_SAMPLE_GUMBEL | dg.DG_SAMPLE_ANNEAL, dict()),
+    ("entropy_rank_adaptive", dg.DG_KEEP_ENTROPY, dict()),
+    ("lock_gumbel_fixed", dg.DG_KEEP_LOCK | dg.DG_SAMPLE_GUMBEL | dg.DG_SAMPLE_ANNEAL, dict(fixed_steps=10)),
+    ("recommended_0.005", ALL, dict(entropy_threshold=0.005)),
+    ("recommended_0.1", ALL, dict(entropy_threshold=0.1, seed=(5 << 32) | 9)),
+]
+
+
+@pytest.mark.parametrize("name,flags,kw", CASES, ids=[c[0] for c in CASES])
+def test_c0_variant_blocks_equal_oracle(name, flags, kw):
+    """Two consecutive blocks of the tiny fp32 model under each variant: tokens, passes and stop reasons equal
+    the oracle's, and the committed cache matches."""
+    d = recipe.C0.dims
+    sess, model, kv = _c0_session()
+    sp, ref = _pair(flags, **kw)
+    for block in (0, 1):
+        log(f"{name}: block {block}")
+        out = sess.i32(d.canvas)
+        st = dg.dg_generate_block(sess.cfg, sess.weights, sess.kv, sp, block, out, sess.ws, sess.ws_bytes)
+        res = osm.generate_block(model, kv, ref, block=block)
+        log(f"{name} block {block}: GPU {st.steps} passes reason {st.reason}; oracle {res.steps} reason {res.reason}")
+        assert (st.steps, st.reason) == (res.steps, res.reason)
+        assert np.array_equal(out.cpu().numpy(), res.tokens)
+        assert abs(st.mean_entropy - res.mean_entropy) <= 1e-4 * abs(res.mean_entropy) + 1e-6
+        torch.cuda.synchronize()
+        assert sess.kv.len == kv.length
+        for l in range(d.n_layers):
+            gk, gv = sess.kv_numpy(l, kv.length)
+            assert allclose_report(gk, kv.k[l], *F32_TOL)[0] and allclose_report(gv, kv.v[l], *F32_TOL)[0]
+
+
+def test_c0_step_calls_equal_generate_block():
+    """dg_denoise_step_sampler -> dg_stop_check -> dg_canvas_update_sampler, called pass by pass with every
+    variant on, reproduce dg_generate_block: each pass's canvas, lock mask and statistics equal the oracle's."""
+    d = recipe.C0.dims
+    S = d.canvas
+    sp, ref = _pair(ALL, entropy_threshold=0.1)
+    sess, model, kv = _c0_session()
+    canvas, lock = sess.i32(S), torch.zeros(S, dtype=torch.uint8, device="cuda")
+    dg.dg_canvas_update_sampler(sess.cfg, sp, 0, 0, None, None, None, canvas, lock)
+    prev = torch.zeros(S, dtype=torch.int32, device="cuda")
+    st = torch.zeros(4, dtype=torch.int32, device="cuda")
+    pred, conf, ent = sess.i32(S), sess.f32(S), sess.f32(S)
+    res = osm.generate_block(model, kv, ref, block=0, do_commit=False)
+    t = 0
+    while True:
+        t += 1
+        o = res.passes[t - 1]
+        assert np.array_equal(canvas.cpu().numpy(), o.canvas), f"canvas at pass {t}"
+        dg.dg_denoise_step_sampler(sess.cfg, sess.weights, sess.kv, sp, 0, t, canvas, pred, conf, ent, sess.ws,
+                                   sess.ws_bytes)
+        dg.dg_stop_check(sess.cfg, sp, t, ent, pred, prev, st, canvas, lock)
+        torch.cuda.synchronize()
+        assert np.array_equal(pred.cpu().numpy(), o.pred), f"pred at pass {t}"
+        assert allclose_report(to_f64(ent), o.ent, *F32_TOL)[0], f"entropy at pass {t}"
+        assert allclose_report(to_f64(conf), o.conf, 1e-7, F32_TOL[1])[0], f"confidence at pass {t}"
+        a = st.cpu().numpy()
+        if a[1] != dg.DG_STOP_NONE:
+            break
+        dg.dg_canvas_update_sampler(sess.cfg, sp, 0, t, pred, conf, ent, canvas, lock)
+        torch.cuda.synchronize()
+        assert np.array_equal(lock.cpu().numpy().astype(bool), o.keep), f"lock mask after pass {t}"
+    assert (t, int(a[1])) == (res.steps, res.reason)
+    out = sess.i32(S)
+    sess2, _, _ = _c0_session()
+    st2 = dg.dg_generate_block(sess2.cfg, sess2.weights, sess2.kv, sp, 0, out, sess2.ws, sess2.ws_bytes)
+    assert (st2.steps, st2.reason) == (t, int(a[1]))
+    assert np.array_equal(out.cpu().numpy(), pred.cpu().numpy())
+
+
+@pytest.mark.parametrize("S,V", [(32, 4096), (256, 262144), (200, 1000)])
+def test_canvas_update_variants_bit_exact(S, V):
+    """Entropy ranking and locking against the oracle on tied, NaN and ragged inputs."""
+    d = replace(recipe.C0.dims, canvas=S, vocab=V)
+    cfg = dg.make_config(d)
+    pred_h = dg_inputs.uniform_int(S, 3, 21, V)
+    conf_h = (dg_inputs.uniform_int(S, 3, 22, 16).astype(np.float32) / 16.0).astype(np.float32)
+    ent_h = (dg_inputs.uniform_int(S, 3, 23, 8).astype(np.float32) / 4.0).astype(np.float32)
+    ent_h[S // 5] = np.nan
+    conf_h[S // 3] = np.nan
+    pred, conf, ent = (torch.from_numpy(a).cuda() for a in (pred_h, conf_h, ent_h))
+    for flags in (dg.DG_KEEP_ENTROPY, dg.DG_KEEP_LOCK, dg.DG_KEEP_LOCK | dg.DG_KEEP_ENTROPY):
+        sp = dg.make_sampler(max(1, S // 10), seed=(3 << 32) | 1, flags=flags)
+        canvas = torch.empty(S, dtype=torch.int32, device="cuda")
+        lock = torch.zeros(S, dtype=torch.uint8, device="cuda")
+        dg.dg_canvas_update_sampler(cfg, sp, 4, 0, None, None, None, canvas, lock)
+        ref_canvas = osm.initial_canvas(sp.seed, 4, S, V)
+        locked = np.zeros(S, dtype=bool) if flags & dg.DG_KEEP_LOCK else None
+        for step in (1, 2, 5, 9, 10, 11):
+            # new predictions each pass (a permutation of the base arrays) so locked tokens are visible
+            perm = np.roll(np.arange(S), 7 * step)
+            p_h, c_h, e_h = pred_h[perm], conf_h[perm], ent_h[perm]
+            pred.copy_(torch.from_numpy(p_h)), conf.copy_(torch.from_numpy(c_h)), ent.copy_(torch.from_numpy(e_h))
+            dg.dg_canvas_update_sampler(cfg, sp, 4, step, pred, conf, ent, canvas, lock)
+            torch.cuda.synchronize()
+            k = osm.keep_count(step, sp.n_new, S)
+            ref_canvas, mask = osm.canvas_update(p_h, c_h.astype(np.float64), k, sp.seed, 4, step, V,
+                                                 e_h.astype(np.float64), bool(flags & dg.DG_KEEP_ENTROPY), locked,
+                                                 ref_canvas)
+            if locked is not None:
+                locked = mask.copy()
+            assert np.array_equal(canvas.cpu().numpy(), ref_canvas), (flags, S, step)
+            assert np.array_equal(lock.cpu().numpy().astype(bool), mask), (flags, S, step)
+
+
+def test_stop_check_and_rule_and_lock():
+    d = recipe.C0.dims
+    cfg = dg.make_config(d)
+    S = d.canvas
+    st = torch.zeros(4, dtype=torch.int32, device="cuda")
+    prev = torch.zeros(S, dtype=torch.int32, device="cuda")
+    base = torch.arange(S, dtype=torch.int32, device="cuda")
+    low = torch.full((S,), 0.001, device="cuda")
+    high = torch.full((S,), 3.0, device="cuda")
+    s_and = dg.make_sampler(4, entropy_threshold=0.005, flags=dg.DG_STOP_AND)
+
+    def run(step, ent, p, sampler, canvas=None, lock=None):
+        q = p.clone()
+        dg.dg_stop_check(cfg, sampler, step, ent, q, prev, st, canvas, lock)
+        torch.cuda.synchronize()
+        return int(st.cpu().numpy()[1]), q.cpu().numpy()
+
+    assert run(1, low, base, s_and)[0] == dg.DG_STOP_NONE        # low entropy alone does not stop
+    assert run(2, high, base, s_and)[0] == dg.DG_STOP_NONE       # stable alone does not stop
+    assert run(3, low, base, s_and)[0] == dg.DG_STOP_SETTLED     # both
+    assert run(4, low, base + 1, s_and)[0] == dg.DG_STOP_NONE
+    assert run(48, high, base, s_and)[0] == dg.DG_STOP_CAP
+    # lock: locked slots report their canvas token, so a pass whose model predictions moved only there is stable
+    s_lock = dg.make_sampler(4, flags=dg.DG_KEEP_LOCK)
+    canvas = base + 1000
+    lock = torch.zeros(S, dtype=torch.uint8, device="cuda")
+    lock[::3] = 1
+    expect = np.where(lock.cpu().numpy().astype(bool), canvas.cpu().numpy(), base.cpu().numpy())
+    r1, q1 = run(5, high, base, s_lock, canvas, lock)
+    assert np.array_equal(q1, expect) and r1 == dg.DG_STOP_NONE
+    moved = base.clone()
+    moved[::3] += 77                                              # only locked slots change
+    r2, q2 = run(6, high, moved, s_lock, canvas, lock)
+    assert np.array_equal(q2, expect) and r2 == dg.DG_STOP_STABLE
+
+
+def test_head_c2_bf16_gumbel_sampled_slots():
+    """Full vocabulary (256 x 262144 x 2816, bf16) with the draw at T = 0.8: sampled slots against the oracle
+    (draws where the perturbed top-2 gap exceeds 1e-2, conf and entropy within the bf16 bar); every slot by
+    invariants."""
+    d = recipe.C2.dims
+    w = {"embed": gdev.normal_tensor((d.vocab, d.d_model), 0, recipe.STREAM_EMBED, 0.02, d.dtype),
+         "final_norm": torch.ones(d.d_model, dtype=gdev.torch_dtype(d.dtype), device="cuda"), "layers": []}
+    sess = Session(replace(d, n_layers=0), capacity=32, weights=w)
+    x_host = dg_inputs.hidden((d.canvas, d.d_model), "bf16")
+    x_dev = torch.from_numpy(x_host.view(np.int16)).cuda().view(torch.bfloat16)
+    sp = dg.make_sampler(26, seed=11, flags=dg.DG_SAMPLE_GUMBEL, inv_temperature=1.25)
+    n = d.canvas
+    pred, conf, ent = sess.i32(n), sess.f32(n), sess.f32(n)
+    dg.dg_vocab_head_sampler(sess.cfg, sess.weights, sp, 3, 2, x_dev, n, pred, conf, ent, sess.ws, sess.ws_bytes)
+    p0, c0, e0 = sess.i32(n), sess.f32(n), sess.f32(n)
+    dg.dg_vocab_head(sess.cfg, sess.weights, x_dev, n, 1.25, p0, c0, e0, sess.ws, sess.ws_bytes)
+    torch.cuda.synchronize()
+    pred, conf, ent = pred.cpu().numpy(), to_f64(conf), to_f64(ent)
+    c_max, e_plain = to_f64(c0), to_f64(e0)
+    assert np.all((pred >= 0) & (pred < d.vocab))
+    assert np.all((conf > 0) & (conf <= c_max * (1 + 1e-5)))      # a draw is never more probable than the mode
+    assert np.array_equal(ent, e_plain)                             # the entropy does not depend on the draw
+    assert (pred != p0.cpu().numpy()).mean() > 0.5                  # at this temperature most draws leave the mode
+    log("gumbel head C2: generating E on host for the oracle")
+    E64 = numerics.from_storage(dg_inputs.embed_host(d), "bf16")
+    rows = np.array([0, 1, 37, 100, 128, 200, 254, 255])
+    xs = numerics.from_storage(x_host[rows], d.dtype)
+    opred, oconf, oent, margin = om.head_stats(xs, np.ones(d.d_model), E64, 1.25, d.rms_eps,
+                                               numerics.rounder(d.dtype), gumbel=(11, 3, 2), slots=rows)
+    sel = margin > MARGIN
+    log(f"gumbel head C2: {int(sel.sum())}/{len(rows)} draws compared")
+    assert sel.sum() >= len(rows) // 2
+    assert np.array_equal(pred[rows][sel], opred[sel])
+    same = pred[rows] == opred
+    assert allclose_report(conf[rows][same], oconf[same], 1e-7, BF16_TOL[1])[0]
+    assert allclose_report(ent[rows], oent, *BF16_TOL)[0]
