@@ -14,7 +14,10 @@ carries one commit, of the block before it (the cache length is reset to the
 prompt before each step, so every step does identical work).  With --workload
 long_context_bf16 the prompt is 131072 tokens and one step is 4 consecutive
 blocks.  Reported value: canvas tokens per second = 256 * blocks / (step
-time); also ms per denoising pass.
+time); also ms per denoising pass.  --sampler recommended runs the same
+workload under the recommended sampler's variants (Gumbel-max draws at a
+temperature annealed from 0.8 to 0.4, entropy-ranked locking keep, AND stop
+rule; still a fixed T).
 
 Extra objects on the JSON line:
   roofline     — the dominant kernel (routed-expert gate/up projection, HBM
@@ -169,6 +172,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="full_loop_bf16", choices=["full_loop_bf16", "long_context_bf16"])
+    ap.add_argument("--sampler", default="plain", choices=["plain", "recommended"],
+                    help="plain: argmax and confidence-ranked keep; recommended: Gumbel-max draws at a temperature "
+                         "annealed 0.8 -> 0.4, entropy-ranked locking keep, AND stop rule (fixed T either way)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (reference for HBM byte counters)")
@@ -209,7 +215,17 @@ def main() -> int:
     torch.cuda.synchronize()
     t_prefill = time.perf_counter() - t0
     P = kv.len
-    sampler = dg.make_sampler(wl.n_new, fixed_steps=T, seed=recipe.INPUT_SEED)
+    flags = 0
+    if args.sampler == "recommended":
+        flags = dg.DG_SAMPLE_GUMBEL | dg.DG_SAMPLE_ANNEAL | dg.DG_KEEP_ENTROPY | dg.DG_KEEP_LOCK | dg.DG_STOP_AND
+    sampler = dg.make_sampler(wl.n_new, fixed_steps=T, seed=recipe.INPUT_SEED, entropy_threshold=0.005, flags=flags,
+                              temperature_first=0.8, temperature_last=0.4)
+
+    def one_pass(dbg=None, t=1):
+        if flags == 0 or dbg is not None:
+            dg.dg_denoise_step(cfg, weights, kv, canvas, 1.0, pred, conf, ent, dbg, ws, ws_bytes)
+        else:
+            dg.dg_denoise_step_sampler(cfg, weights, kv, sampler, 0, t, canvas, pred, conf, ent, ws, ws_bytes)
     toks = [torch.empty(d.canvas, dtype=torch.int32, device="cuda") for _ in range(2)]
     pending = [None]
 
@@ -262,15 +278,15 @@ def main() -> int:
     dg.dg_timing_start([dom])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(n_pass):
-        dg.dg_denoise_step(cfg, weights, kv, canvas, 1.0, pred, conf, ent, None, ws, ws_bytes)
+    for i in range(n_pass):
+        one_pass(t=i % T + 1)
     torch.cuda.synchronize()
     pass_ms = (time.perf_counter() - t0) / n_pass * 1e3
     tim = dg.dg_timing_stop()
 
     # routing of one pass: experts hit per layer (for the algorithmic bytes)
     ridx = torch.empty((d.n_layers, d.canvas, d.top_k), dtype=torch.int32, device="cuda")
-    dg.dg_denoise_step(cfg, weights, kv, canvas, 1.0, pred, conf, ent, {"route_idx": ridx}, ws, ws_bytes)
+    one_pass({"route_idx": ridx})
     torch.cuda.synchronize()
     ri = ridx.cpu().numpy()
     experts_hit = float(np.mean([len(np.unique(ri[l])) for l in range(d.n_layers)]))
@@ -289,7 +305,7 @@ def main() -> int:
     # per-kernel breakdown from one extra instrumented denoising pass (outside the timed region)
     kv.len = P
     dg.dg_timing_start(list(dg.KERNELS))
-    dg.dg_denoise_step(cfg, weights, kv, canvas, 1.0, pred, conf, ent, None, ws, ws_bytes)
+    one_pass()
     torch.cuda.synchronize()
     breakdown = dg.dg_timing_stop()
 
@@ -345,6 +361,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": wl.name, "description": wl.description,
                    "canvas": d.canvas, "prefix": wl.prefix, "T": T, "batch": 1, "blocks_per_step": blocks,
+                   "sampler": args.sampler,
                    "step": (f"{blocks} block(s), each: {T} passes + stop checks + {T - 1} keep/re-randomise updates "
                             f"+ one commit (of the previous block, inside the first pass)"),
                    "canvas_tokens_per_s_without_commit": round(d.canvas / (T * pass_ms * 1e-3), 2),
