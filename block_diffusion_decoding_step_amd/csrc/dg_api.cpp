@@ -116,7 +116,8 @@ int side_for(hipStream_t main, Side** out) {
     DG_TRY(expr);                 \
   } while (0)
 
-constexpr int64_t kPartialRows = 4096;  // attention split partials hold n_split * rows <= max(this, rows)
+constexpr int64_t kPartialRows = 4096;
+constexpr int kMaxSeq = 8;  // sequences of one batched call  // attention split partials hold n_split * rows <= max(this, rows)
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline size_t esize(const dg_config* c) { return c->dtype == DG_BF16 ? 2 : 4; }
@@ -148,6 +149,8 @@ struct Ws {
   void* Ys;
   float4* hpart;
   float2* hpart2;
+  void* kst;  // staging of a batched call's new keys   [Hkv][M][Dh]
+  void* vst;  // staging of a batched call's new values [Hkv][Dh][M]
   dg_block_status* status;
   int32_t* prev_pred;
   int32_t* canvas;
@@ -199,13 +202,17 @@ Ws carve(const dg_config* c, int64_t M, char* base) {
   w.Ys = take(M * d * es);
   w.hpart = (float4*)take((size_t)head_groups(c->vocab) * M * 16);
   w.hpart2 = (float2*)take((size_t)head_groups(c->vocab) * M * 8);
-  w.status = (dg_block_status*)take(sizeof(dg_block_status));
-  w.prev_pred = (int32_t*)take(c->canvas * 4);
-  w.canvas = (int32_t*)take(c->canvas * 4);
-  w.pred = (int32_t*)take(c->canvas * 4);
-  w.conf = (float*)take(c->canvas * 4);
-  w.ent = (float*)take(c->canvas * 4);
-  w.lock = (uint8_t*)take(c->canvas);
+  w.kst = take((size_t)c->n_kv_heads * M * c->head_dim * es);
+  w.vst = take((size_t)c->n_kv_heads * c->head_dim * M * es);
+  // per-slot state of up to M / canvas canvases (at least one)
+  const int64_t slots = std::max<int64_t>(M, c->canvas);
+  w.status = (dg_block_status*)take(sizeof(dg_block_status) * kMaxSeq);
+  w.prev_pred = (int32_t*)take(slots * 4);
+  w.canvas = (int32_t*)take(slots * 4);
+  w.pred = (int32_t*)take(slots * 4);
+  w.conf = (float*)take(slots * 4);
+  w.ent = (float*)take(slots * 4);
+  w.lock = (uint8_t*)take(slots);
   w.bytes = off;
   return w;
 }
@@ -279,18 +286,35 @@ int64_t rows_supported(const dg_config* c, size_t ws_bytes, int64_t limit) {
 // (fragment-tiled, so that layer skips its own RMSNorm), or the final-normalised rows for the head.
 enum class Next { None, NextLayer, Head };
 
-// One layer over M rows at cache positions pos0.. : rows [0, n_causal) attend causally (a prompt chunk
-// or a committed block), rows [n_causal, M) attend to every key [0, pos0 + M) (the canvas).
+// The rows of one layer call, by sequence: segment i holds rows [row0, row0 + rows) of the call, at
+// positions pos0.. of its own cache; its first n_causal rows attend causally (a prompt chunk or a
+// committed block), the rest to every key [0, pos0 + rows) (a canvas).
+struct Seg {
+  const dg_kv* kv;
+  int64_t pos0, row0, rows, n_causal;
+};
+struct Segs {
+  int n;
+  Seg seg[kMaxSeq];
+};
+Segs one_seq(const dg_kv* kv, int64_t pos0, int64_t M, int64_t n_causal) {
+  Segs g{};
+  g.n = 1;
+  g.seg[0] = Seg{kv, pos0, 0, M, n_causal};
+  return g;
+}
+
+// One layer over M rows (the segments' rows).
 template <typename T>
-int layer_t(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int64_t pos0, int64_t M,
-            int64_t n_causal, bool normed_in, Next next, const Ws& ws, hipStream_t s) {
+int layer_t(const dg_config* c, const dg_weights* w, int l, const Segs& sg, int64_t M, bool normed_in, Next next,
+            const Ws& ws, hipStream_t s) {
   const dg_layer_weights& L = w->h_layers[l];
   const int d = c->d_model, hq = c->n_heads, hkv = c->n_kv_heads, dh = c->head_dim;
   const int E = c->n_experts, k = c->top_k;
   const int Mi = (int)M;
   const size_t es = sizeof(T);
-  char* kbase = (char*)kv->k + (size_t)l * hkv * kv->capacity * dh * es;
-  char* vbase = (char*)kv->v + (size_t)l * hkv * dh * kv->capacity * es;
+  auto kbase = [&](const dg_kv* kv) { return (char*)kv->k + (size_t)l * hkv * kv->capacity * dh * es; };
+  auto vbase = [&](const dg_kv* kv) { return (char*)kv->v + (size_t)l * hkv * dh * kv->capacity * es; };
 
   // attention half (normed_in: the previous layer's combine already wrote attn_norm(X) to ws.Xt)
   if (!normed_in)
@@ -298,18 +322,30 @@ int layer_t(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int
                                                   c->rms_eps, s));
   GemmArgs g{};
   g.A = ws.Xt; g.a_tiled = 1; g.B = L.wqkv; g.M = Mi; g.N = (hq + 2 * hkv) * dh; g.K = d; g.lda = d; g.ldb = d;
-  g.q = ws.Q; g.kc = kbase; g.vc = vbase; g.n_heads = hq; g.n_kv_heads = hkv; g.head_dim = dh; g.q_rows = Mi;
-  g.cap = kv->capacity; g.pos0 = pos0;
+  g.q = ws.Q; g.n_heads = hq; g.n_kv_heads = hkv; g.head_dim = dh; g.q_rows = Mi;
+  if (sg.n == 1) {  // keys and values go straight into the cache
+    g.kc = kbase(sg.seg[0].kv); g.vc = vbase(sg.seg[0].kv); g.cap = sg.seg[0].kv->capacity; g.pos0 = sg.seg[0].pos0;
+  } else {          // several caches: staged, then copied into each sequence's cache
+    g.kc = ws.kst; g.vc = ws.vst; g.cap = M; g.pos0 = 0;
+  }
   DG_LAUNCH(DG_K_GEMM_QKV, s, launch_gemm<T>(GemmEpi::QKV, g, s));
+  if (sg.n > 1) {
+    for (int i = 0; i < sg.n; ++i) {
+      const Seg& q = sg.seg[i];
+      KvScatterArgs ka{ws.kst, ws.vst, Mi, hkv, dh, kbase(q.kv), vbase(q.kv), q.kv->capacity, q.pos0, (int)q.row0,
+                       (int)q.rows};
+      DG_LAUNCH(DG_K_GEMM_QKV, s, launch_kv_scatter<T>(ka, s));
+    }
+  }
 
-  // attention: one launch (and merge) per row range of one mask
-  auto attend = [&](int64_t row0, int64_t rows, bool causal) -> int {
+  // attention: one launch (and merge) per row range of one sequence and one mask
+  auto attend = [&](const Seg& q, int64_t off, int64_t rows, bool causal) -> int {
     AttnArgs at{};
-    at.q = ws.Q; at.kc = kbase; at.vc = vbase; at.o_part = ws.opart; at.ml_part = ws.mlpart; at.o = ws.O;
-    at.q_rows = (int)rows; at.q_stride = Mi; at.row0 = (int)row0; at.n_heads = hq; at.n_kv_heads = hkv;
-    at.head_dim = dh; at.cap = kv->capacity;
-    at.n_keys = causal ? pos0 + row0 + rows : pos0 + M;
-    at.q_pos0 = pos0 + row0; at.causal = causal ? 1 : 0;
+    at.q = ws.Q; at.kc = kbase(q.kv); at.vc = vbase(q.kv); at.o_part = ws.opart; at.ml_part = ws.mlpart;
+    at.o = ws.O; at.q_rows = (int)rows; at.q_stride = Mi; at.row0 = (int)(q.row0 + off); at.n_heads = hq;
+    at.n_kv_heads = hkv; at.head_dim = dh; at.cap = q.kv->capacity;
+    at.n_keys = causal ? q.pos0 + off + rows : q.pos0 + q.rows;
+    at.q_pos0 = q.pos0 + off; at.causal = causal ? 1 : 0;
     const int max_split =
         (int)std::min<int64_t>(kAttnMaxSplit, std::max<int64_t>(1, std::max(kPartialRows, M) / rows));
     at.n_split = attention_splits(at.n_keys, (int)rows, hq, hkv, at.causal, max_split);
@@ -317,8 +353,11 @@ int layer_t(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int
     DG_LAUNCH(DG_K_ATTN_MERGE, s, launch_attention_merge<T>(at, s));
     return DG_OK;
   };
-  if (n_causal > 0) DG_CHECK(attend(0, n_causal, true));
-  if (n_causal < M) DG_CHECK(attend(n_causal, M - n_causal, false));
+  for (int i = 0; i < sg.n; ++i) {
+    const Seg& q = sg.seg[i];
+    if (q.n_causal > 0) DG_CHECK(attend(q, 0, q.n_causal, true));
+    if (q.n_causal < q.rows) DG_CHECK(attend(q, q.n_causal, q.rows - q.n_causal, false));
+  }
 
   g = GemmArgs{};
   g.A = ws.O; g.a_tiled = 1; g.B = L.wo; g.C = ws.X; g.M = Mi; g.N = d; g.K = hq * dh; g.lda = hq * dh; g.ldb = hq * dh; g.ldc = d;
@@ -366,10 +405,14 @@ int layer_t(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int
   return DG_OK;
 }
 
+int layer(const dg_config* c, const dg_weights* w, int l, const Segs& sg, int64_t M, bool normed_in, Next next,
+          const Ws& ws, hipStream_t s) {
+  if (c->dtype == DG_BF16) return layer_t<bf16>(c, w, l, sg, M, normed_in, next, ws, s);
+  return layer_t<float>(c, w, l, sg, M, normed_in, next, ws, s);
+}
 int layer(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int64_t pos0, int64_t M, int64_t n_causal,
           bool normed_in, Next next, const Ws& ws, hipStream_t s) {
-  if (c->dtype == DG_BF16) return layer_t<bf16>(c, w, l, kv, pos0, M, n_causal, normed_in, next, ws, s);
-  return layer_t<float>(c, w, l, kv, pos0, M, n_causal, normed_in, next, ws, s);
+  return layer(c, w, l, one_seq(kv, pos0, M, n_causal), M, normed_in, next, ws, s);
 }
 
 // rows [row0, row0 + M) of ws.X = embeddings of tok[0, M)
@@ -664,6 +707,102 @@ int dg_generate_block_overlapped(const dg_config* cfg, const dg_weights* w, dg_k
 int dg_generate_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const dg_sampler* sp, uint32_t block,
                       int32_t* tokens_out, dg_block_status* h_status, void* ws, size_t ws_bytes, void* stream) {
   return dg_generate_block_overlapped(cfg, w, kv, sp, block, nullptr, 0, tokens_out, h_status, ws, ws_bytes, stream);
+}
+
+int dg_generate_blocks(const dg_config* cfg, const dg_weights* w, dg_kv* kvs, int32_t n_seq, const dg_sampler* sp,
+                       const uint32_t* h_blocks, int32_t* tokens_out, dg_block_status* h_status, void* ws,
+                       size_t ws_bytes, void* stream) {
+  DG_CHECK(check_cfg(cfg));
+  DG_CHECK(check_weights(cfg, w, true, true));
+  DG_CHECK(check_sampler(cfg, sp));
+  if (!kvs || !h_blocks || !tokens_out || !h_status || n_seq < 1 || n_seq > kMaxSeq) return DG_ERR_INVALID;
+  const int S = cfg->canvas;
+  const int64_t M = (int64_t)n_seq * S;
+  if (M > moe_max_rows(cfg->n_experts)) return DG_ERR_INVALID;
+  for (int b = 0; b < n_seq; ++b) {
+    DG_CHECK(check_kv(&kvs[b], S));
+    for (int b2 = 0; b2 < b; ++b2)
+      if (kvs[b2].k == kvs[b].k || kvs[b2].v == kvs[b].v) return DG_ERR_INVALID;  // each sequence its own cache
+  }
+  DG_CHECK(check_ws(cfg, M, ws, ws_bytes));
+  hipStream_t s = (hipStream_t)stream;
+  Ws wsv = carve(cfg, M, (char*)ws);
+  const StopParams stp = stop_params(cfg, sp);
+  const bool fixed = sp->fixed_steps > 0, lock = (sp->flags & DG_KEEP_LOCK) != 0;
+  const bool by_ent = (sp->flags & DG_KEEP_ENTROPY) != 0, draw = (sp->flags & DG_SAMPLE_GUMBEL) != 0;
+  const int L = cfg->n_layers;
+  const uint32_t V = (uint32_t)cfg->vocab;
+  Segs sg{};
+  sg.n = n_seq;
+  for (int b = 0; b < n_seq; ++b) sg.seg[b] = Seg{&kvs[b], kvs[b].len, (int64_t)b * S, S, 0};
+  auto lock_of = [&](int b) { return lock ? wsv.lock + (size_t)b * S : nullptr; };
+
+  for (int b = 0; b < n_seq; ++b) {
+    CanvasArgs ca{nullptr, nullptr, nullptr, 0, nullptr, S, 0, sp->seed, h_blocks[b], 0, V, wsv.canvas + (size_t)b * S,
+                  lock_of(b)};
+    DG_LAUNCH(DG_K_CANVAS_UPDATE, s, launch_canvas_update(ca, s));
+  }
+  bool done[kMaxSeq] = {};
+  int n_done = 0;
+  dg_block_status st[kMaxSeq] = {};
+  for (int t = 1; n_done < n_seq; ++t) {
+    // one pass over every canvas; a finished canvas still runs (its rows are ignored from then on)
+    DG_CHECK(embed(cfg, w, wsv.canvas, M, wsv, s));
+    for (int l = 0; l < L; ++l)
+      DG_CHECK(layer(cfg, w, l, sg, M, l > 0, l + 1 < L ? Next::NextLayer : Next::Head, wsv, s));
+    if (!draw) {
+      DG_CHECK(head(cfg, w, M, sampler_pass(sp, 0, t), wsv.pred, wsv.conf, wsv.ent, L > 0, wsv, s));
+    } else {  // each canvas draws with its own block's counters
+      for (int b = 0; b < n_seq; ++b)
+        if (!done[b])
+          DG_CHECK(head(cfg, w, S, sampler_pass(sp, h_blocks[b], t), wsv.pred + (size_t)b * S,
+                        wsv.conf + (size_t)b * S, wsv.ent + (size_t)b * S, L > 0, wsv, s, (int64_t)b * S));
+    }
+    for (int b = 0; b < n_seq; ++b) {
+      if (done[b]) continue;
+      const size_t o = (size_t)b * S;
+      DG_LAUNCH(DG_K_STOP_CHECK, s,
+                launch_stop_check(wsv.ent + o, wsv.pred + o, wsv.prev_pred + o, wsv.canvas + o, lock_of(b), S, t,
+                                  stp, wsv.status + b, s));
+    }
+    bool stop[kMaxSeq] = {};
+    if (fixed) {
+      for (int b = 0; b < n_seq; ++b) stop[b] = t >= sp->fixed_steps;
+    } else {
+      DG_TRY(hipMemcpyAsync(st, wsv.status, sizeof(dg_block_status) * n_seq, hipMemcpyDeviceToHost, s));
+      DG_TRY(hipStreamSynchronize(s));
+      for (int b = 0; b < n_seq; ++b) stop[b] = !done[b] && st[b].reason != DG_STOP_NONE;
+    }
+    for (int b = 0; b < n_seq; ++b) {
+      if (done[b] || !stop[b]) continue;
+      DG_TRY(hipMemcpyAsync(tokens_out + (size_t)b * S, wsv.pred + (size_t)b * S, (size_t)S * 4,
+                            hipMemcpyDeviceToDevice, s));
+      done[b] = true;
+      ++n_done;
+    }
+    if (n_done == n_seq) break;
+    const int keep = (int)std::min<int64_t>(S, (int64_t)t * sp->n_new);
+    for (int b = 0; b < n_seq; ++b) {
+      if (done[b]) continue;
+      const size_t o = (size_t)b * S;
+      CanvasArgs ca{wsv.pred + o, wsv.conf + o, wsv.ent + o, by_ent ? 1 : 0, lock_of(b), S, keep, sp->seed,
+                    h_blocks[b], (uint32_t)t, V, wsv.canvas + o, lock_of(b)};
+      DG_LAUNCH(DG_K_CANVAS_UPDATE, s, launch_canvas_update(ca, s));
+    }
+  }
+  if (fixed) DG_TRY(hipMemcpyAsync(st, wsv.status, sizeof(dg_block_status) * n_seq, hipMemcpyDeviceToHost, s));
+  // commit every block in one causal forward: each sequence's rows attend causally within its own cache
+  DG_CHECK(embed(cfg, w, tokens_out, M, wsv, s));
+  Segs cg = sg;
+  for (int b = 0; b < n_seq; ++b) cg.seg[b].n_causal = S;
+  for (int l = 0; l < L; ++l)
+    DG_CHECK(layer(cfg, w, l, cg, M, l > 0, l + 1 < L ? Next::NextLayer : Next::None, wsv, s));
+  DG_TRY(hipStreamSynchronize(s));
+  for (int b = 0; b < n_seq; ++b) {
+    kvs[b].len += S;
+    h_status[b] = st[b];
+  }
+  return DG_OK;
 }
 
 int dg_layer_forward(const dg_config* cfg, const dg_weights* w, int32_t layer_i, const dg_kv* kv, const void* x_in,

@@ -94,6 +94,20 @@ hipError_t launch_stop_check(const float* ent, int32_t* pred, int32_t* prev, con
                              hipStream_t s);
 hipError_t launch_canvas_update(const CanvasArgs& a, hipStream_t s);
 
+// keys and values of one sequence's rows of a batched call: from the call's staging buffers (QKV epilogue
+// with cap = M, pos0 = 0) to positions pos0.. of the sequence's cache
+struct KvScatterArgs {
+  const void* ks;  // [Hkv][M][Dh]
+  const void* vs;  // [Hkv][Dh][M]
+  int M, n_kv_heads, head_dim;
+  void* kc;        // the layer's key cache   [Hkv][cap][Dh]
+  void* vc;        // the layer's value cache [Hkv][Dh][cap]
+  int64_t cap, pos0;
+  int row0, rows;  // the sequence's rows of the call
+};
+template <typename T>
+hipError_t launch_kv_scatter(const KvScatterArgs& a, hipStream_t s);
+
 // ---- k_gemm.hip
 enum class GemmEpi { Store, Resid, QKV, SwiGLU };
 

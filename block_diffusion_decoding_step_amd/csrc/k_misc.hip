@@ -7,6 +7,8 @@
 // and Gemma 4".
 #include <hip/hip_ext.h>
 
+#include <algorithm>
+
 #include "dg_device.h"
 #include "dg_kernels.h"
 #include "dg_wave_gemm.h"
@@ -518,7 +520,39 @@ __global__ __launch_bounds__(1024) void k_canvas_update(const int32_t* __restric
   if (keep_mask) keep_mask[i] = kept ? 1 : 0;
 }
 
+// ============================================================== batched calls: cache scatter
+// One thread per element; keys [h][pos][dh] and values [h][dh][pos], so both copies walk their
+// innermost index fastest.
+template <typename T>
+__global__ __launch_bounds__(256) void k_kv_scatter(KvScatterArgs a) {
+  const int dh = a.head_dim;
+  const int64_t n = (int64_t)a.n_kv_heads * a.rows * dh;
+  const T* ks = (const T*)a.ks;
+  const T* vs = (const T*)a.vs;
+  T* kd = (T*)a.kc;
+  T* vd = (T*)a.vc;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(i % dh);
+    const int64_t hr = i / dh;
+    const int r = (int)(hr % a.rows), h = (int)(hr / a.rows);
+    kd[((int64_t)h * a.cap + a.pos0 + r) * dh + c] = ks[((int64_t)h * a.M + a.row0 + r) * dh + c];
+    const int r2 = (int)(i % a.rows);
+    const int64_t hc = i / a.rows;  // h * dh + column
+    vd[hc * a.cap + a.pos0 + r2] = vs[hc * a.M + a.row0 + r2];
+  }
+}
+
 // ============================================================== launchers
+template <typename T>
+hipError_t launch_kv_scatter(const KvScatterArgs& a, hipStream_t s) {
+  const int64_t n = (int64_t)a.n_kv_heads * a.rows * a.head_dim;
+  if (n <= 0) return hipSuccess;
+  const int64_t g = std::min<int64_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_kv_scatter<T>, dim3((unsigned)g), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+template hipError_t launch_kv_scatter<float>(const KvScatterArgs&, hipStream_t);
+template hipError_t launch_kv_scatter<bf16>(const KvScatterArgs&, hipStream_t);
 template <typename T>
 hipError_t launch_embed(const int32_t* tok, const T* E, T* X, int M, int d, int V, hipStream_t s) {
   hipLaunchKernelGGL(k_embed<T>, dim3(M), dim3(256), 0, s, tok, E, X, M, d, V);

@@ -316,6 +316,22 @@ int dg_generate_block_overlapped(const dg_config* cfg, const dg_weights* w, dg_k
                                  int32_t defer_commit, int32_t* tokens_out, dg_block_status* h_status,
                                  void* ws, size_t ws_bytes, void* stream);
 
+/* Blocks of n_seq independent sequences at once (batch > 1 canvases; [P2] "Benchmark Numbers"
+ * runs batch 4).  Sequence b has its own cache kvs[b] (host array of n_seq caches, no two sharing
+ * memory), block id h_blocks[b] (host) for its Philox draws, and output tokens_out[b * canvas ..]
+ * (device [n_seq][canvas]); h_status[b] (host) receives its status.  Each sequence's result equals
+ * dg_generate_block on its own (up to the summation order of attention splits): the passes run
+ * over all n_seq canvases together (every weight read serves all of them), each canvas attends to
+ * its own cache, and its stop check and update are its own.  In adaptive mode a finished canvas is
+ * carried along unchanged until every canvas has stopped.  The blocks are committed together at
+ * the end (kvs[b].len += canvas).  1 <= n_seq <= 8, n_seq * canvas <= the routing row limit
+ * (2048 for 128 experts); the workspace must hold n_seq * canvas rows and each cache canvas more
+ * rows.  DG_ERR_INVALID for a bad count, aliasing caches or NULL arrays; others as
+ * dg_generate_block. */
+int dg_generate_blocks(const dg_config* cfg, const dg_weights* w, dg_kv* kvs, int32_t n_seq,
+                       const dg_sampler* sampler, const uint32_t* h_blocks, int32_t* tokens_out,
+                       dg_block_status* h_status, void* ws, size_t ws_bytes, void* stream);
+
 /* --- finer-grained calls of the same path (each is one stage of dg_denoise_step) --- */
 
 /* One transformer block `layer` over n hidden rows x_in -> x_out ([n, d_model];

@@ -278,3 +278,27 @@ def test_sampler_variants_validate():
         with pytest.raises(dg.DGError) as e:
             c()
         assert e.value.status == dg.DG_ERR_INVALID, i
+
+
+def test_generate_blocks_validate():
+    cfg = _cfg()
+    w = _fake_weights(cfg.n_layers)
+    buf = _Fake(0x20000)
+    ws1 = dg.dg_workspace_size(cfg, cfg.canvas)
+    ws3 = dg.dg_workspace_size(cfg, 3 * cfg.canvas)
+    sp = dg.make_sampler(4)
+    kvs = [dg.KV(_Fake(0x100000 * (i + 1)), _Fake(0x100000 * (i + 1) + 0x80000), capacity=128, length=0)
+           for i in range(9)]
+    cases = [
+        (lambda: dg.dg_generate_blocks(cfg, w, [], sp, [], buf, buf, ws1, 0), dg.DG_ERR_INVALID),        # no sequence
+        (lambda: dg.dg_generate_blocks(cfg, w, kvs, sp, list(range(9)), buf, buf, ws3, 0), dg.DG_ERR_INVALID),  # > 8
+        (lambda: dg.dg_generate_blocks(cfg, w, [kvs[0], kvs[0]], sp, [0, 1], buf, buf, ws3, 0), dg.DG_ERR_INVALID),
+        (lambda: dg.dg_generate_blocks(cfg, w, kvs[:3], sp, [0, 1, 2], buf, buf, ws1, 0), dg.DG_ERR_WORKSPACE),
+        (lambda: dg.dg_generate_blocks(cfg, w, kvs[:2] + [dg.KV(buf, buf, capacity=96, length=80)], sp, [0, 1, 2],
+                                       buf, buf, ws3, 0), dg.DG_ERR_KV_FULL),
+    ]
+    for i, (c, status) in enumerate(cases):
+        with pytest.raises(dg.DGError) as e:
+            c()
+        assert e.value.status == status, i
+    assert [kv.len for kv in kvs] == [0] * 9

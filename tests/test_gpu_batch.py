@@ -1,0 +1,125 @@
+"""GPU parity of batched blocks (dg_generate_blocks: several independent sequences' canvases in one pass)
+against the oracle run sequence by sequence, and against single-sequence blocks on the GPU.
+
+Bars as elsewhere: tokens, passes and stop reasons bit-exact in fp32; caches within 1e-4 (fp32) or 2e-2
+(bf16) of the reference; bf16 tokens compared by agreement with single-sequence runs.
+"""
+from __future__ import annotations
+
+import sys
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+import block_diffusion_decoding_step_amd as dg  # noqa: E402
+import dg_inputs  # noqa: E402
+from dg_inputs import device as gdev  # noqa: E402
+from dg_inputs import recipe  # noqa: E402
+from oracle import model as om  # noqa: E402
+from oracle import sampler as osm  # noqa: E402
+from tests._gpu import Session, allclose_report  # noqa: E402
+from tests._helpers import oracle_model  # noqa: E402
+
+F32_TOL = (1e-4, 1e-4)
+BF16_TOL = (2e-2, 2e-2)
+ALL = dg.DG_SAMPLE_GUMBEL | dg.DG_SAMPLE_ANNEAL | dg.DG_KEEP_ENTROPY | dg.DG_KEEP_LOCK | dg.DG_STOP_AND
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _sessions(d, prefixes, weights=None, packed=False):
+    """One session (cache) per sequence over shared device weights (the first session's packed copy); sequence
+    b's prompt is drawn with seed b + 1."""
+    out = []
+    for b, p in enumerate(prefixes):
+        if out:
+            s = Session(d, capacity=p + 3 * d.canvas, weights=out[0].w, packed=True)
+        else:
+            s = Session(d, capacity=p + 3 * d.canvas, weights=weights, packed=packed)
+        if p:
+            s.prefill(dg_inputs.prompt_tokens(p, d.vocab, seed=b + 1))
+        out.append(s)
+    return out
+
+
+def _batch(sessions, sp, blocks):
+    d = sessions[0].d
+    n = len(sessions)
+    ws_bytes = dg.dg_workspace_size(sessions[0].cfg, n * d.canvas)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty((n, d.canvas), dtype=torch.int32, device="cuda")
+    st = dg.dg_generate_blocks(sessions[0].cfg, sessions[0].weights, [s.kv for s in sessions], sp, blocks, out, ws,
+                               ws_bytes)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), st
+
+
+@pytest.mark.parametrize("flags,kw", [(0, dict()), (ALL, dict(entropy_threshold=0.1))], ids=["plain", "recommended"])
+def test_c0_batch_equals_oracle_per_sequence(flags, kw):
+    """Three sequences with different prompts and lengths (64, 40 and 0 tokens) and block ids: each one's
+    tokens, passes, stop reason and committed cache equal the oracle's single-sequence block."""
+    d = recipe.C0.dims
+    storage = dg_inputs.model_weights_host(d)
+    prefixes, blocks = [64, 40, 0], [0, 5, 2]
+    sessions = _sessions(d, prefixes, weights=gdev.from_host(storage, d.dtype))
+    anneal = (float(np.float32(0.8)), float(np.float32(0.4))) if flags & dg.DG_SAMPLE_ANNEAL else None
+    sp = dg.make_sampler(recipe.C0.n_new, flags=flags, temperature_first=0.8, temperature_last=0.4, **kw)
+    ref = osm.Sampler(n_new=recipe.C0.n_new, gumbel=bool(flags & dg.DG_SAMPLE_GUMBEL), anneal=anneal,
+                      rank_entropy=bool(flags & dg.DG_KEEP_ENTROPY), lock=bool(flags & dg.DG_KEEP_LOCK),
+                      stop_and=bool(flags & dg.DG_STOP_AND), **kw)
+    toks, st = _batch(sessions, sp, blocks)
+    model = oracle_model(d, storage)
+    for b, (p, blk) in enumerate(zip(prefixes, blocks)):
+        kv = om.KVCache(d.n_layers, d.n_kv_heads, d.head_dim)
+        if p:
+            osm.prefill(model, kv, dg_inputs.prompt_tokens(p, d.vocab, seed=b + 1))
+        res = osm.generate_block(model, kv, ref, block=blk)
+        log(f"seq {b}: GPU {st[b].steps} passes reason {st[b].reason}; oracle {res.steps} reason {res.reason}")
+        assert (st[b].steps, st[b].reason) == (res.steps, res.reason), b
+        assert np.array_equal(toks[b], res.tokens), b
+        s = sessions[b]
+        assert s.kv.len == kv.length == p + d.canvas
+        for l in range(d.n_layers):
+            gk, gv = s.kv_numpy(l, kv.length)
+            assert allclose_report(gk, kv.k[l], *F32_TOL)[0] and allclose_report(gv, kv.v[l], *F32_TOL)[0], (b, l)
+
+
+@pytest.mark.parametrize("dims", ["c0_bf16", "c3_two_layers"])
+def test_bf16_batch_equals_single_sequence_blocks(dims):
+    """bf16 at fixed T: four sequences in one batched call against the same four blocks run one at a time
+    (tokens by agreement, caches within the bf16 bar).  c3_two_layers has the benchmark's shapes (d 2816, 128
+    experts top-8, 262144 vocabulary, canvas 256) with two layers: 1024 rows per pass."""
+    if dims == "c0_bf16":
+        d, prefixes, T = replace(recipe.C0.dims, dtype="bf16"), [64, 40, 17, 96], 4
+    else:
+        d, prefixes, T = replace(recipe.C3.dims, n_layers=2), [512, 300, 64, 700], 3
+    n_new = -(-d.canvas // T)
+    sp = dg.make_sampler(n_new, fixed_steps=T)
+    blocks = [3, 1, 4, 1]
+    log(f"{dims}: building weights")
+    batch = _sessions(d, prefixes)
+    toks, st = _batch(batch, sp, blocks)
+    assert all(s.steps == T and s.reason == dg.DG_STOP_FIXED for s in st)
+    single = _sessions(d, prefixes, weights=batch[0].w, packed=True)
+    for b, s in enumerate(single):
+        out = s.i32(d.canvas)
+        stb = dg.dg_generate_block(s.cfg, s.weights, s.kv, sp, blocks[b], out, s.ws, s.ws_bytes)
+        assert (stb.steps, stb.reason) == (st[b].steps, st[b].reason)
+        same = float(np.mean(out.cpu().numpy() == toks[b]))
+        log(f"{dims} seq {b}: token agreement with the single-sequence block {same:.4f}")
+        assert same > 0.9, b
+        assert s.kv.len == batch[b].kv.len == prefixes[b] + d.canvas
+        for l in range(d.n_layers):
+            for a, c in zip(s.kv_numpy(l, s.kv.len), batch[b].kv_numpy(l, s.kv.len)):
+                ok, worst, at = allclose_report(c, a, *BF16_TOL)
+                assert ok, (b, l, worst, at)
