@@ -166,6 +166,104 @@ def cpu_baseline(wl, log_fn) -> dict:
             "ms_per_denoising_step": t_pass * 1e3}
 
 
+def run_batch(args, wl) -> int:
+    """--batch B: one step is B independent sequences' blocks in one dg_generate_blocks call (each sequence has
+    its own 4096-token prompt and cache; T passes over all B canvases, then one causal forward committing all B
+    blocks).  value = B * 256 / step time.  The roofline kernel is the gate/up projection over the B * 256 rows,
+    timed with HIP events over the timed steps (passes and commits have the same row count); at 8 * B * 256
+    routed pairs every expert is hit (a given expert is missed with probability (1 - 8/128)^(8 B 256))."""
+    import numpy as np
+    import torch
+
+    import block_diffusion_decoding_step_amd as dg
+    from dg_inputs import device as gdev
+    from dg_inputs import recipe
+
+    d, T, B = wl.dims, wl.fixed_steps, args.batch
+    if B * d.canvas > 2048 or B > 8:
+        print(f"--batch {B}: at most 8 canvases and 2048 rows per pass", file=sys.stderr)
+        return 2
+    log(f"bench: {wl.name} batch {B}; generating weights on the device")
+    w = gdev.packed_model_weights_device(d)
+    weights = dg.Weights(w["embed"], w["final_norm"], w["layers"])
+    cfg = dg.make_config(d)
+    cap = ((wl.prefix + wl.blocks * d.canvas + 31) // 32) * 32
+    ws_bytes = dg.dg_workspace_size(cfg, max(B * d.canvas, 2048))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    kvs, keep = [], []
+    t0 = time.perf_counter()
+    for b in range(B):
+        k, v = gdev.kv_tensors(d, cap)
+        kv = dg.KV(k, v, cap, 0)
+        prompt = gdev.uniform_tensor(wl.prefix, recipe.INPUT_SEED + b, recipe.STREAM_PROMPT, d.vocab)
+        dg.dg_prefill_kv(cfg, weights, kv, prompt, wl.prefix, ws, ws_bytes)
+        kvs.append(kv)
+        keep.append((k, v))
+    torch.cuda.synchronize()
+    t_prefill = time.perf_counter() - t0
+    P = [kv.len for kv in kvs]
+    sampler = dg.make_sampler(wl.n_new, fixed_steps=T, seed=recipe.INPUT_SEED)
+    toks = torch.empty((B, d.canvas), dtype=torch.int32, device="cuda")
+
+    def step(i):
+        out = []
+        for j in range(wl.blocks):
+            if j == 0:
+                for kv, p in zip(kvs, P):
+                    kv.len = p
+            out += dg.dg_generate_blocks(cfg, weights, kvs, sampler, [(i * wl.blocks + j) * B + b for b in range(B)],
+                                         toks, ws, ws_bytes)
+        return out
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    dg.dg_timing_start(["moe_gate_up"])
+    t0 = time.perf_counter()
+    statuses = [st for i in range(args.steps) for st in step(i)]
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t0
+    tim = dg.dg_timing_stop()
+    assert all(s.steps == T and s.reason == dg.DG_STOP_FIXED for s in statuses)
+    block_ms = t_total / args.steps * 1e3
+    value = B * d.canvas * wl.blocks * args.steps / t_total
+    g_ms, g_n = tim["moe_gate_up"]
+    g_avg = g_ms / g_n
+    M = B * d.canvas
+    g_work = gate_up_bytes(d, d.n_experts, M * d.top_k)
+    achieved = g_work / (g_avg * 1e-3) / 1e9
+    out = {
+        "metric": METRIC.replace("at batch 1", f"at batch {B}"),
+        "value": round(value, 2),
+        "unit": "canvas tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(block_ms, 4),
+        "ms_per_denoising_step": None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name + f"_batch{B}", "description": wl.description, "canvas": d.canvas,
+                   "prefix": wl.prefix, "T": T, "batch": B, "blocks_per_step": wl.blocks,
+                   "step": (f"{wl.blocks} x (B = {B} blocks in one dg_generate_blocks call: {T} passes over all "
+                            f"{M} canvas rows + stop checks + updates, then one causal forward committing all "
+                            f"{B} blocks)"),
+                   "ms_per_denoising_step_note": "passes run inside dg_generate_blocks and are not timed alone",
+                   "prefill_s": round(t_prefill, 3)},
+        "roofline": {"kernel": "k_moe_gate_up", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": g_work, "avg_launch_ms": round(g_avg, 5),
+                     "launches": g_n, "rows_per_launch": M},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, log)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -175,6 +273,8 @@ def main() -> int:
     ap.add_argument("--sampler", default="plain", choices=["plain", "recommended"],
                     help="plain: argmax and confidence-ranked keep; recommended: Gumbel-max draws at a temperature "
                          "annealed 0.8 -> 0.4, entropy-ranked locking keep, AND stop rule (fixed T either way)")
+    ap.add_argument("--batch", type=int, default=1,
+                    help="canvases per pass (independent sequences, dg_generate_blocks); 1 is the batch-1 workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (reference for HBM byte counters)")
@@ -197,6 +297,8 @@ def main() -> int:
     d = wl.dims
     T = wl.fixed_steps
     torch.cuda.set_device(0)
+    if args.batch > 1:
+        return run_batch(args, wl)
     stream = torch.cuda.current_stream()
     log(f"bench: {wl.name} on {torch.cuda.get_device_name(0)}; generating weights on the device")
     w = gdev.packed_model_weights_device(d)
