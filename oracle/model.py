@@ -158,6 +158,11 @@ class KVCache:
         self.k[layer] = np.concatenate([self.k[layer], k_new], axis=1)
         self.v[layer] = np.concatenate([self.v[layer], v_new], axis=1)
 
+    def truncate(self, length: int) -> None:
+        """Keep rows [0, length) of every layer."""
+        self.k = [k[:, :length] for k in self.k]
+        self.v = [v[:, :length] for v in self.v]
+
 
 def weights_to_f64(storage: dict, dtype: str) -> dict:
     """Convert a storage-form weight dict (as produced by the input generator) to float64 values."""

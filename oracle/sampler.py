@@ -219,3 +219,32 @@ def generate_block(model: Model, kv: KVCache, s: Sampler, block: int, keep_trace
     if do_commit:
         commit(model, kv, tokens)
     return BlockResult(tokens=tokens, steps=step, reason=reason, mean_entropy=mean_ent, passes=passes)
+
+
+@dataclass
+class VerifyResult:
+    accepted: int          # draft tokens accepted (>= 1)
+    ar_pred: np.ndarray    # greedy prediction of the causal pass at each draft row (for the position after it)
+    next_token: int        # ar_pred[accepted - 1]: the causal pass's token for the first position not accepted
+    margin: np.ndarray     # fp32 top-2 logit margin of each row's prediction
+
+
+def verify_block(model: Model, kv: KVCache, draft) -> VerifyResult:
+    """Self-speculative verify ([P1] "The result that complicates 'faster, not smarter'": one set of weights
+    drafts a block bidirectionally and verifies it causally over the same KV cache).
+
+    Reading: a causal forward of the draft after the committed cache (the commit's forward) gives, at each row i,
+    the greedy next-token prediction a_i.  Token d_0 is taken as drafted (its causal prediction would need the
+    previous row's hidden state, which the cache does not keep); token d_i (i >= 1) is accepted while every
+    earlier one was and a_(i-1) == d_i.  The accepted rows stay in the cache; a_(accepted - 1) is the causal
+    pass's token for the next position, for the caller to use."""
+    draft = np.asarray(draft, dtype=np.int64)
+    base = kv.length
+    x = model.embed(draft)
+    x, _ = model.body(x, kv, causal=True, append=True)
+    pred, _, _, margin = model.head(x)
+    n = 1
+    while n < len(draft) and pred[n - 1] == draft[n]:
+        n += 1
+    kv.truncate(base + n)
+    return VerifyResult(accepted=n, ar_pred=pred, next_token=int(pred[n - 1]), margin=margin)

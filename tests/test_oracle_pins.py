@@ -638,3 +638,63 @@ def test_recommended_sampler_block_c0():
             assert res.steps == 48
         for rec in res.passes:
             assert np.all(rec.ent >= 0) and np.all(rec.ent <= math.log(d.vocab) + 1e-9)
+
+
+
+# ----------------------------------------------------------------------------- self-speculative verify
+
+def _self_retrieval_model():
+    """Attention and expert outputs zeroed: each row's hidden state is its own embedding, so the greedy causal
+    prediction of a row is its own token (a copy model)."""
+    d = _c0_like()
+    st = dg_inputs.model_weights_host(d)
+    for layer in st["layers"]:
+        layer["wo"] = np.zeros_like(layer["wo"])
+        layer["w_down"] = np.zeros_like(layer["w_down"])
+        layer["ws_down"] = np.zeros_like(layer["ws_down"])
+    st["final_norm"] = dg_inputs.const(st["final_norm"].shape, 10.0, d.dtype)
+    return d, oracle_model(d, st)
+
+
+def test_verify_copy_model_accepts_runs():
+    """With a copy model a_i = d_i, so d_i is accepted while it repeats its predecessor: the accepted count is the
+    length of the leading run, and the next token repeats the run's token."""
+    d, m = _self_retrieval_model()
+    S = d.canvas
+    for draft, n_expect in [([5] * S, S), ([5, 5, 5, 7] + [7] * (S - 4), 3), ([9, 8] + [8] * (S - 2), 1)]:
+        kv = om.KVCache(d.n_layers, d.n_kv_heads, d.head_dim)
+        osm.prefill(m, kv, dg_inputs.prompt_tokens(6, d.vocab))
+        r = osm.verify_block(m, kv, draft)
+        assert np.array_equal(r.ar_pred, draft)
+        assert r.accepted == n_expect and r.next_token == draft[n_expect - 1]
+        assert kv.length == 6 + n_expect
+
+
+def test_verify_rows_equal_commit_rows():
+    """The verify pass is the commit's causal forward: its kept cache rows equal a commit of the accepted tokens,
+    and a draft made of the causal pass's own greedy continuation is accepted whole."""
+    d = recipe.C0.dims
+    m = oracle_model(d)
+    prompt = dg_inputs.prompt_tokens(recipe.C0.prefix, d.vocab)
+    kv = om.KVCache(d.n_layers, d.n_kv_heads, d.head_dim)
+    osm.prefill(m, kv, prompt)
+    # greedy continuation of the prompt, one causal step at a time
+    x = m.embed(prompt)
+    kv_g = om.KVCache(d.n_layers, d.n_kv_heads, d.head_dim)
+    h, _ = m.body(x, kv_g, causal=True, append=True)
+    tok = int(m.head(h[-1:])[0][0])
+    greedy = []
+    for _ in range(8):
+        greedy.append(tok)
+        h, _ = m.body(m.embed([tok]), kv_g, causal=True, append=True)
+        tok = int(m.head(h)[0][0])
+    draft = np.array(greedy + list(dg_inputs.prompt_tokens(d.canvas - 8, d.vocab, seed=9)))
+    r = osm.verify_block(m, kv, draft)
+    assert r.accepted >= 8 and np.array_equal(r.ar_pred[:7], draft[1:8])
+    assert r.next_token == r.ar_pred[r.accepted - 1]
+    kv_c = om.KVCache(d.n_layers, d.n_kv_heads, d.head_dim)
+    osm.prefill(m, kv_c, prompt)
+    osm.commit(m, kv_c, draft[:r.accepted])
+    for l in range(d.n_layers):
+        np.testing.assert_allclose(kv.k[l], kv_c.k[l], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(kv.v[l], kv_c.v[l], rtol=1e-12, atol=1e-12)
