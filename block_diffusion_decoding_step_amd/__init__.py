@@ -33,7 +33,7 @@ DG_WARN_NUMERIC = 0x1
 DG_SAMPLE_GUMBEL, DG_SAMPLE_ANNEAL, DG_KEEP_ENTROPY, DG_KEEP_LOCK, DG_STOP_AND = 0x1, 0x2, 0x4, 0x8, 0x10
 EXPORTED = ("dg_workspace_size", "dg_prefill_kv", "dg_denoise_step", "dg_canvas_update", "dg_commit_block",
             "dg_generate_block", "dg_generate_block_overlapped", "dg_layer_forward", "dg_vocab_head", "dg_stop_check", "dg_status_string",
-            "dg_generate_blocks", "dg_denoise_step_sampler", "dg_canvas_update_sampler", "dg_vocab_head_sampler", "dg_sampler_inv_temperature",
+            "dg_generate_blocks", "dg_verify_block", "dg_denoise_step_sampler", "dg_canvas_update_sampler", "dg_vocab_head_sampler", "dg_sampler_inv_temperature",
             "dg_last_hip_error", "dg_timing_start", "dg_timing_stop", "dg_packed_elems", "dg_pack_matrix")
 # kernel classes of dg_timing_* (dg_kernel in dg.h), in enum order
 KERNELS = ("embed", "rmsnorm", "gemm_qkv", "attention", "attn_merge", "gemm_o", "route",
@@ -108,6 +108,7 @@ _SIGS = {
                                      _P(dg_block_status), _vp, _sz, _vp],
     "dg_generate_blocks": [_P(dg_config), _P(dg_weights), _P(dg_kv), _i32, _P(dg_sampler), _P(_u32), _vp,
                            _P(dg_block_status), _vp, _sz, _vp],
+    "dg_verify_block": [_P(dg_config), _P(dg_weights), _P(dg_kv), _vp, _vp, _P(_i32), _P(_i32), _vp, _sz, _vp],
     "dg_layer_forward": [_P(dg_config), _P(dg_weights), _i32, _P(dg_kv), _vp, _vp, _i64, _i32, _P(dg_debug), _vp,
                          _sz, _vp],
     "dg_vocab_head": [_P(dg_config), _P(dg_weights), _vp, _i64, _f32, _vp, _vp, _vp, _vp, _sz, _vp],
@@ -275,6 +276,15 @@ def dg_generate_blocks(cfg, weights, kvs, sampler: dg_sampler, blocks, tokens_ou
     for kv, a in zip(kvs, arr):
         kv.len = int(a.len)
     return list(st)
+
+
+def dg_verify_block(cfg, weights, kv, draft, ar_pred, ws, ws_bytes: int, stream=None) -> tuple:
+    """Self-speculative verify; returns (accepted, next_token); kv.len grows by accepted."""
+    n, nxt = _i32(0), _i32(0)
+    _check("dg_verify_block", _lib.dg_verify_block(ctypes.byref(cfg), _w(weights), _kv(kv), _ptr(draft),
+                                                   _ptr(ar_pred), ctypes.byref(n), ctypes.byref(nxt), _ptr(ws),
+                                                   ws_bytes, _stream(stream)))
+    return int(n.value), int(nxt.value)
 
 
 def _dbg(dbg):

@@ -805,6 +805,34 @@ int dg_generate_blocks(const dg_config* cfg, const dg_weights* w, dg_kv* kvs, in
   return DG_OK;
 }
 
+int dg_verify_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const int32_t* draft, int32_t* ar_pred,
+                    int32_t* h_accepted, int32_t* h_next_token, void* ws, size_t ws_bytes, void* stream) {
+  DG_CHECK(check_cfg(cfg));
+  DG_CHECK(check_weights(cfg, w, true, true));
+  if (!draft || !ar_pred || !h_accepted || !h_next_token) return DG_ERR_INVALID;
+  const int S = cfg->canvas;
+  DG_CHECK(check_kv(kv, S));
+  DG_CHECK(check_ws(cfg, S, ws, ws_bytes));
+  hipStream_t s = (hipStream_t)stream;
+  Ws wsv = carve(cfg, S, (char*)ws);
+  // the commit's causal forward over the draft, then the greedy prediction of every row
+  DG_CHECK(embed(cfg, w, draft, S, wsv, s));
+  const int L = cfg->n_layers;
+  for (int l = 0; l < L; ++l)
+    DG_CHECK(layer(cfg, w, l, kv, kv->len, S, S, l > 0, l + 1 < L ? Next::NextLayer : Next::Head, wsv, s));
+  DG_CHECK(head(cfg, w, S, argmax_pass(1.0f), ar_pred, wsv.conf, wsv.ent, L > 0, wsv, s));
+  std::vector<int32_t> hp(S), hd(S);
+  DG_TRY(hipMemcpyAsync(hp.data(), ar_pred, (size_t)S * 4, hipMemcpyDeviceToHost, s));
+  DG_TRY(hipMemcpyAsync(hd.data(), draft, (size_t)S * 4, hipMemcpyDeviceToHost, s));
+  DG_TRY(hipStreamSynchronize(s));
+  int n = 1;
+  while (n < S && hp[n - 1] == hd[n]) ++n;
+  *h_accepted = n;
+  *h_next_token = hp[n - 1];
+  kv->len += n;
+  return DG_OK;
+}
+
 int dg_layer_forward(const dg_config* cfg, const dg_weights* w, int32_t layer_i, const dg_kv* kv, const void* x_in,
                      void* x_out, int64_t n, int32_t causal, const dg_debug* dbg, void* ws, size_t ws_bytes,
                      void* stream) {

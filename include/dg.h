@@ -332,6 +332,19 @@ int dg_generate_blocks(const dg_config* cfg, const dg_weights* w, dg_kv* kvs, in
                        const dg_sampler* sampler, const uint32_t* h_blocks, int32_t* tokens_out,
                        dg_block_status* h_status, void* ws, size_t ws_bytes, void* stream);
 
+/* Self-speculative verify of a drafted block ([P1] "The result that complicates 'faster, not
+ * smarter'": one set of weights drafts a block bidirectionally and verifies it causally over the
+ * same KV cache).  The commit's causal forward over draft (device [canvas], e.g. dg_generate_block
+ * output with the commit deferred) at positions kv->len.. writes their keys and values and the
+ * greedy prediction of each row, the token the causal pass gives the position after it, to
+ * ar_pred (device [canvas]).  draft[0] is taken as drafted; draft[i] (i >= 1) is accepted while
+ * every earlier one was and ar_pred[i - 1] == draft[i].  h_accepted (host) receives the count
+ * (1 .. canvas) and h_next_token (host) ar_pred[count - 1], the causal pass's token for the first
+ * position not accepted.  kv->len grows by the count; the cache rows past it are scratch.  Needs
+ * kv->len + canvas <= capacity and a workspace of canvas rows; synchronises `stream` once. */
+int dg_verify_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const int32_t* draft, int32_t* ar_pred,
+                    int32_t* h_accepted, int32_t* h_next_token, void* ws, size_t ws_bytes, void* stream);
+
 /* --- finer-grained calls of the same path (each is one stage of dg_denoise_step) --- */
 
 /* One transformer block `layer` over n hidden rows x_in -> x_out ([n, d_model];

@@ -27,7 +27,7 @@ def test_header_declares_the_documented_calls():
     names = _declared()
     for n in ("dg_prefill_kv", "dg_denoise_step", "dg_canvas_update", "dg_commit_block", "dg_generate_block",
               "dg_generate_block_overlapped", "dg_denoise_step_sampler", "dg_canvas_update_sampler",
-              "dg_vocab_head_sampler", "dg_sampler_inv_temperature",
+              "dg_vocab_head_sampler", "dg_sampler_inv_temperature", "dg_generate_blocks", "dg_verify_block",
               "dg_workspace_size", "dg_status_string"):
         assert n in names
     assert set(names) == set(dg.EXPORTED)
@@ -302,3 +302,22 @@ def test_generate_blocks_validate():
             c()
         assert e.value.status == status, i
     assert [kv.len for kv in kvs] == [0] * 9
+
+
+def test_verify_block_validates():
+    cfg = _cfg()
+    w = _fake_weights(cfg.n_layers)
+    buf = _Fake(0x20000)
+    ws_bytes = dg.dg_workspace_size(cfg, cfg.canvas)
+    kv = dg.KV(buf, buf, capacity=96, length=80)   # 80 + 32 > 96
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_verify_block(cfg, w, kv, buf, buf, buf, ws_bytes, 0)
+    assert e.value.status == dg.DG_ERR_KV_FULL
+    kv = dg.KV(buf, buf, capacity=128, length=0)
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_verify_block(cfg, w, kv, None, buf, buf, ws_bytes, 0)
+    assert e.value.status == dg.DG_ERR_INVALID
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_verify_block(cfg, w, kv, buf, buf, buf, ws_bytes - 256, 0)
+    assert e.value.status == dg.DG_ERR_WORKSPACE
+    assert kv.len == 0
