@@ -123,3 +123,27 @@ def test_bf16_batch_equals_single_sequence_blocks(dims):
             for a, c in zip(s.kv_numpy(l, s.kv.len), batch[b].kv_numpy(l, s.kv.len)):
                 ok, worst, at = allclose_report(c, a, *BF16_TOL)
                 assert ok, (b, l, worst, at)
+
+
+@pytest.mark.parametrize("canvas,prefixes", [(71, [33, 0, 70]), (32, [5, 64, 1, 17, 40, 2, 0, 9])],
+                         ids=["ragged_canvas", "eight_sequences"])
+def test_c0_batch_edges_equal_oracle(canvas, prefixes):
+    """A ragged canvas (71 slots: segment boundaries off the 16-row fragments) and the most sequences per call
+    (8): each sequence equals the oracle's single-sequence block at a fixed T."""
+    d = replace(recipe.C0.dims, canvas=canvas)
+    storage = dg_inputs.model_weights_host(d)
+    sessions = _sessions(d, prefixes, weights=gdev.from_host(storage, d.dtype))
+    blocks = list(range(7, 7 + len(prefixes)))
+    sp = dg.make_sampler(-(-canvas // 4), fixed_steps=4)
+    toks, st = _batch(sessions, sp, blocks)
+    model = oracle_model(d, storage)
+    for b, (p, blk) in enumerate(zip(prefixes, blocks)):
+        kv = om.KVCache(d.n_layers, d.n_kv_heads, d.head_dim)
+        if p:
+            osm.prefill(model, kv, dg_inputs.prompt_tokens(p, d.vocab, seed=b + 1))
+        res = osm.generate_block(model, kv, osm.Sampler(n_new=-(-canvas // 4), fixed_steps=4), block=blk)
+        assert (st[b].steps, st[b].reason) == (res.steps, res.reason), b
+        assert np.array_equal(toks[b], res.tokens), b
+        for l in range(d.n_layers):
+            gk, gv = sessions[b].kv_numpy(l, kv.length)
+            assert allclose_report(gk, kv.k[l], *F32_TOL)[0] and allclose_report(gv, kv.v[l], *F32_TOL)[0], (b, l)

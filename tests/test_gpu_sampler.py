@@ -248,3 +248,24 @@ def test_head_c2_bf16_gumbel_sampled_slots():
     same = pred[rows] == opred
     assert allclose_report(conf[rows][same], oconf[same], 1e-7, BF16_TOL[1])[0]
     assert allclose_report(ent[rows], oent, *BF16_TOL)[0]
+
+
+def test_c0_ragged_canvas_recommended_sampler():
+    """71 slots (not a multiple of the 16-row fragments or of the head's slot tiles) under every variant."""
+    d = replace(recipe.C0.dims, canvas=71)
+    storage = dg_inputs.model_weights_host(d)
+    sess = Session(d, capacity=recipe.C0.prefix + 2 * d.canvas, weights=gdev.from_host(storage, d.dtype))
+    model = oracle_model(d, storage)
+    kv = om.KVCache(d.n_layers, d.n_kv_heads, d.head_dim)
+    prompt = dg_inputs.prompt_tokens(recipe.C0.prefix, d.vocab)
+    sess.prefill(prompt)
+    osm.prefill(model, kv, prompt)
+    sp = dg.make_sampler(9, entropy_threshold=0.1, flags=ALL, temperature_first=0.8, temperature_last=0.4)
+    ref = osm.Sampler(n_new=9, entropy_threshold=0.1, gumbel=True, anneal=(_f32(0.8), _f32(0.4)), rank_entropy=True,
+                      lock=True, stop_and=True)
+    out = sess.i32(d.canvas)
+    st = dg.dg_generate_block(sess.cfg, sess.weights, sess.kv, sp, 2, out, sess.ws, sess.ws_bytes)
+    res = osm.generate_block(model, kv, ref, block=2)
+    log(f"ragged recommended: GPU {st.steps} ({st.reason}), oracle {res.steps} ({res.reason})")
+    assert (st.steps, st.reason) == (res.steps, res.reason)
+    assert np.array_equal(out.cpu().numpy(), res.tokens)

@@ -131,3 +131,16 @@ def test_bf16_verify_rule_and_cache():
         gk, gv = sess.kv_numpy(l, recipe.C0.prefix + keep)
         assert allclose_report(gk, kv.k[l][:, :recipe.C0.prefix + keep], *BF16_TOL)[0]
         assert allclose_report(gv, kv.v[l][:, :recipe.C0.prefix + keep], *BF16_TOL)[0]
+
+
+def test_c0_ragged_canvas_verify():
+    d = replace(recipe.C0.dims, canvas=71)
+    storage = dg_inputs.model_weights_host(d)
+    sess, model, kv, prompt = _pair(d, storage, 45)
+    draft = np.array(_greedy(model, prompt, 5) + list(dg_inputs.prompt_tokens(d.canvas - 5, d.vocab, seed=3)))
+    n, nxt, ar = _verify(sess, draft)
+    ref = osm.verify_block(model, kv, draft)
+    assert np.array_equal(ar, ref.ar_pred) and (n, nxt) == (ref.accepted, ref.next_token) and n >= 5
+    for l in range(d.n_layers):
+        gk, gv = sess.kv_numpy(l, kv.length)
+        assert allclose_report(gk, kv.k[l], *F32_TOL)[0] and allclose_report(gv, kv.v[l], *F32_TOL)[0], l
