@@ -385,10 +385,12 @@ int layer_t(const dg_config* c, const dg_weights* w, int l, const Segs& sg, int6
   ra.Xt = ws.Xt; ra.Wr = L.w_router; ra.logits = ws.rlog; ra.cand_v = ws.cand_v; ra.cand_e = ws.cand_e;
   ra.idx = ws.ridx; ra.w = ws.rw; ra.counts = ws.counts; ra.offsets = ws.offsets; ra.perm = ws.perm;
   ra.pos = ws.pos; ra.tiles = ws.tiles; ra.n_tiles = ws.n_tiles; ra.M = Mi; ra.d = d; ra.E = E; ra.k = k;
+  ra.tile_rows = moe_tile_rows(Mi, E, k);
   DG_LAUNCH(DG_K_ROUTE, s, launch_route<T>(ra, s));
 
   MoeArgs ma{};
   ma.tiles = ws.tiles; ma.n_tiles = ws.n_tiles; ma.max_tiles = moe_max_tiles(Mi, E, k); ma.perm = ws.perm;
+  ma.tile_rows = ra.tile_rows;
   ma.X = ws.Xn; ma.W = L.w_gate_up; ma.out = ws.Hp; ma.d = d; ma.F = c->ffn_expert;
   DG_LAUNCH(DG_K_MOE_GATE_UP, s, launch_moe_gate_up<T>(ma, s));
   ma.X = ws.Hp; ma.W = L.w_down; ma.out = ws.Yp;

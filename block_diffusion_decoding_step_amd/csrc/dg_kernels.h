@@ -18,7 +18,10 @@ constexpr int kRouteMasks = 4096;
 // rows per routed-expert work tile, and the bound on the number of tiles.  A tile is the int4
 // (expert, first pair, rows, packed) with packed = tiles of that expert | (index of this tile among
 // them) << 8 | (rows of the expert's last tile) << 16; an expert holds at most 2048 pairs (64 tiles).
+// Calls with many rows per expert (stacked canvases, prompt chunks) use tiles of kMoeWideRows.
 constexpr int kMoeTileRows = 32;
+constexpr int kMoeWideRows = 64;
+inline int moe_tile_rows(int M, int E, int k) { return M * k >= 48 * E ? kMoeWideRows : kMoeTileRows; }
 __host__ __device__ inline int moe_pack_tile_w(int tiles_of_expert, int index, int last_rows) {
   return tiles_of_expert | (index << 8) | (last_rows << 16);
 }
@@ -80,6 +83,7 @@ struct RouteArgs {
   int4* tiles;        // work tiles (expert, first pair, rows, packed as moe_pack_tile_w)
   int32_t* n_tiles;
   int M, d, E, k;
+  int tile_rows;      // kMoeTileRows or kMoeWideRows
 };
 constexpr int kRouteSlices = 2;  // expert slices of the router (candidate lists per row)
 template <typename T>
@@ -141,6 +145,7 @@ struct MoeArgs {
   const void* W;          // gate_up: [E][2F][d]; down: [E][d][F]
   void* out;              // gate_up: H [pairs, F]; down: Yp [pairs, d]
   int d, F;
+  int tile_rows;          // as the routing's
 };
 template <typename T>
 hipError_t launch_moe_gate_up(const MoeArgs& a, hipStream_t s);

@@ -31,12 +31,14 @@ struct Depth<bf16> {
   static constexpr int v = 2;     // dense tiles (4 A + 4 B fragments per step)
   static constexpr int moe1 = 4;  // routed experts, one 16-row M-tile
   static constexpr int moe2 = 3;  // routed experts, two 16-row M-tiles
+  static constexpr int moe4 = 2;  // routed experts, three or four 16-row M-tiles (wide tiles)
 };
 template <>
 struct Depth<float> {
   static constexpr int v = 1;
   static constexpr int moe1 = 1;
   static constexpr int moe2 = 1;
+  static constexpr int moe4 = 1;
 };
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
@@ -230,7 +232,7 @@ __device__ __forceinline__ void moe_gate_up_body(const MoeArgs& a, f32x4 (*red)[
   const T* X = (const T*)a.X;
   const T* W = (const T*)a.W + (int64_t)e * 2 * a.F * a.d;
   // the weight loads need only the tile: they are issued before the row gather's indices arrive
-  constexpr int D = MT == 1 ? Depth<T>::moe1 : Depth<T>::moe2;
+  constexpr int D = MT == 1 ? Depth<T>::moe1 : MT == 2 ? Depth<T>::moe2 : Depth<T>::moe4;
   const T* bp[NT];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -294,7 +296,7 @@ __device__ __forceinline__ bool moe_unit(const MoeArgs& a, int ncols, int n_tile
   const int r = u - ncols * (u / ncols - j);  // unit index within the expert's ncols * te units
   const int jj = r % te;
   col = r / te;
-  tile = make_int4(t.x, t.y + (jj - j) * kMoeTileRows, jj == te - 1 ? last : kMoeTileRows, te);
+  tile = make_int4(t.x, t.y + (jj - j) * a.tile_rows, jj == te - 1 ? last : a.tile_rows, te);
   return true;
 }
 static inline int moe_grid(int max_tiles, int ncols) { return 8 * ((max_tiles + 7) / 8) * ncols; }
@@ -311,6 +313,25 @@ __global__ __launch_bounds__(256, 2) void k_moe_gate_up(MoeArgs a) {
     else moe_gate_up_body<T, 1, false>(a, red, tile.x, tile.y, tile.z, c0);
   } else {  // weights read once: streamed (non-temporal)
     if (tile.z > 16) moe_gate_up_body<T, 2, true>(a, red, tile.x, tile.y, tile.z, c0);
+    else moe_gate_up_body<T, 1, true>(a, red, tile.x, tile.y, tile.z, c0);
+  }
+}
+
+// wide tiles (up to 64 rows): a separate kernel, so that the 32-row kernel keeps its register budget
+template <typename T>
+__global__ __launch_bounds__(256, 2) void k_moe_gate_up_wide(MoeArgs a) {
+  __shared__ f32x4 red[4][8][64];
+  int4 tile;
+  int col;
+  if (!moe_unit(a, (a.F + 63) / 64, min(*a.n_tiles, a.max_tiles), tile, col)) return;
+  const int c0 = col * 64;
+  if (tile.w > 1) {
+    if (tile.z > 32) moe_gate_up_body<T, 4, false>(a, red, tile.x, tile.y, tile.z, c0);
+    else if (tile.z > 16) moe_gate_up_body<T, 2, false>(a, red, tile.x, tile.y, tile.z, c0);
+    else moe_gate_up_body<T, 1, false>(a, red, tile.x, tile.y, tile.z, c0);
+  } else {
+    if (tile.z > 32) moe_gate_up_body<T, 4, true>(a, red, tile.x, tile.y, tile.z, c0);
+    else if (tile.z > 16) moe_gate_up_body<T, 2, true>(a, red, tile.x, tile.y, tile.z, c0);
     else moe_gate_up_body<T, 1, true>(a, red, tile.x, tile.y, tile.z, c0);
   }
 }
@@ -373,14 +394,41 @@ __global__ __launch_bounds__(256) void k_moe_down(MoeArgs a) {
   }
 }
 
+// wide tiles; held to two waves per SIMD (the four-fragment path would otherwise take the register file)
+template <typename T>
+__global__ __launch_bounds__(256, 2) void k_moe_down_wide(MoeArgs a) {
+  int4 tile;
+  int col;
+  if (!moe_unit(a, (a.d + 255) / 256, min(*a.n_tiles, a.max_tiles), tile, col)) return;
+  const int c0 = col * 256 + wave_id() * 64;
+  if (c0 >= a.d) return;
+  if (tile.w > 1) {
+    if (tile.z > 32) moe_down_body<T, 4, false>(a, tile.x, tile.y, tile.z, c0);
+    else if (tile.z > 16) moe_down_body<T, 2, false>(a, tile.x, tile.y, tile.z, c0);
+    else moe_down_body<T, 1, false>(a, tile.x, tile.y, tile.z, c0);
+  } else {
+    if (tile.z > 32) moe_down_body<T, 4, true>(a, tile.x, tile.y, tile.z, c0);
+    else if (tile.z > 16) moe_down_body<T, 2, true>(a, tile.x, tile.y, tile.z, c0);
+    else moe_down_body<T, 1, true>(a, tile.x, tile.y, tile.z, c0);
+  }
+}
+
 template <typename T>
 hipError_t launch_moe_gate_up(const MoeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_moe_gate_up<T>, dim3(moe_grid(a.max_tiles, (a.F + 63) / 64)), dim3(256), 0, s, a);
+  const dim3 grid(moe_grid(a.max_tiles, (a.F + 63) / 64));
+  if (a.tile_rows > kMoeTileRows)
+    hipLaunchKernelGGL(k_moe_gate_up_wide<T>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_moe_gate_up<T>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 template <typename T>
 hipError_t launch_moe_down(const MoeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_moe_down<T>, dim3(moe_grid(a.max_tiles, (a.d + 255) / 256)), dim3(256), 0, s, a);
+  const dim3 grid(moe_grid(a.max_tiles, (a.d + 255) / 256));
+  if (a.tile_rows > kMoeTileRows)
+    hipLaunchKernelGGL(k_moe_down_wide<T>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_moe_down<T>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -328,7 +328,8 @@ __global__ __launch_bounds__(1024) void k_route_order(RouteArgs a) {
     }
     a.counts[tid] = n_e;
   }
-  const int t_e = (n_e + kMoeTileRows - 1) / kMoeTileRows;
+  const int tr = a.tile_rows;
+  const int t_e = (n_e + tr - 1) / tr;
   int inc_n = n_e, inc_t = t_e;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -344,8 +345,7 @@ __global__ __launch_bounds__(1024) void k_route_order(RouteArgs a) {
     off_s[tid] = off;
     a.offsets[tid] = off;
     for (int i = 0; i < t_e; ++i)
-      a.tiles[toff + i] = make_int4(tid, off + i * kMoeTileRows, min(kMoeTileRows, n_e - i * kMoeTileRows),
-                                    moe_pack_tile_w(t_e, i, n_e - (t_e - 1) * kMoeTileRows));
+      a.tiles[toff + i] = make_int4(tid, off + i * tr, min(tr, n_e - i * tr), moe_pack_tile_w(t_e, i, n_e - (t_e - 1) * tr));
     if (tid == E - 1) {
       a.offsets[E] = off + n_e;
       *a.n_tiles = toff + t_e;
