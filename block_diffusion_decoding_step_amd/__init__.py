@@ -38,7 +38,7 @@ EXPORTED = ("dg_workspace_size", "dg_prefill_kv", "dg_denoise_step", "dg_canvas_
 # kernel classes of dg_timing_* (dg_kernel in dg.h), in enum order
 KERNELS = ("embed", "rmsnorm", "gemm_qkv", "attention", "attn_merge", "gemm_o", "route",
            "moe_gate_up", "moe_down", "shared_gate_up", "shared_down", "moe_combine", "vocab_head",
-           "head_merge", "stop_check", "canvas_update")
+           "head_merge", "stop_check", "canvas_update", "kv_scatter")
 
 
 class DGError(RuntimeError):

@@ -334,7 +334,7 @@ int layer_t(const dg_config* c, const dg_weights* w, int l, const Segs& sg, int6
       const Seg& q = sg.seg[i];
       KvScatterArgs ka{ws.kst, ws.vst, Mi, hkv, dh, kbase(q.kv), vbase(q.kv), q.kv->capacity, q.pos0, (int)q.row0,
                        (int)q.rows};
-      DG_LAUNCH(DG_K_GEMM_QKV, s, launch_kv_scatter<T>(ka, s));
+      DG_LAUNCH(DG_K_KV_SCATTER, s, launch_kv_scatter<T>(ka, s));
     }
   }
 

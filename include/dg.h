@@ -409,6 +409,7 @@ typedef enum dg_kernel {
   DG_K_HEAD_MERGE,
   DG_K_STOP_CHECK,
   DG_K_CANVAS_UPDATE,
+  DG_K_KV_SCATTER,     /* batched calls: new keys/values into each sequence's cache */
   DG_K_COUNT
 } dg_kernel;
 
