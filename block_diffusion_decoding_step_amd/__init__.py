@@ -33,7 +33,7 @@ DG_WARN_NUMERIC = 0x1
 DG_SAMPLE_GUMBEL, DG_SAMPLE_ANNEAL, DG_KEEP_ENTROPY, DG_KEEP_LOCK, DG_STOP_AND = 0x1, 0x2, 0x4, 0x8, 0x10
 EXPORTED = ("dg_workspace_size", "dg_prefill_kv", "dg_denoise_step", "dg_canvas_update", "dg_commit_block",
             "dg_generate_block", "dg_generate_block_overlapped", "dg_layer_forward", "dg_vocab_head", "dg_stop_check", "dg_status_string",
-            "dg_generate_blocks", "dg_verify_block", "dg_denoise_step_sampler", "dg_canvas_update_sampler", "dg_vocab_head_sampler", "dg_sampler_inv_temperature",
+            "dg_generate_blocks", "dg_generate_blocks_overlapped", "dg_verify_block", "dg_denoise_step_sampler", "dg_canvas_update_sampler", "dg_vocab_head_sampler", "dg_sampler_inv_temperature",
             "dg_last_hip_error", "dg_timing_start", "dg_timing_stop", "dg_packed_elems", "dg_pack_matrix")
 # kernel classes of dg_timing_* (dg_kernel in dg.h), in enum order
 KERNELS = ("embed", "rmsnorm", "gemm_qkv", "attention", "attn_merge", "gemm_o", "route",
@@ -108,6 +108,8 @@ _SIGS = {
                                      _P(dg_block_status), _vp, _sz, _vp],
     "dg_generate_blocks": [_P(dg_config), _P(dg_weights), _P(dg_kv), _i32, _P(dg_sampler), _P(_u32), _vp,
                            _P(dg_block_status), _vp, _sz, _vp],
+    "dg_generate_blocks_overlapped": [_P(dg_config), _P(dg_weights), _P(dg_kv), _i32, _P(dg_sampler), _P(_u32), _vp,
+                                      _i32, _vp, _P(dg_block_status), _vp, _sz, _vp],
     "dg_verify_block": [_P(dg_config), _P(dg_weights), _P(dg_kv), _vp, _vp, _P(_i32), _P(_i32), _vp, _sz, _vp],
     "dg_layer_forward": [_P(dg_config), _P(dg_weights), _i32, _P(dg_kv), _vp, _vp, _i64, _i32, _P(dg_debug), _vp,
                          _sz, _vp],
@@ -273,6 +275,22 @@ def dg_generate_blocks(cfg, weights, kvs, sampler: dg_sampler, blocks, tokens_ou
     rc = _lib.dg_generate_blocks(ctypes.byref(cfg), _w(weights), arr, n, ctypes.byref(sampler), ids,
                                  _ptr(tokens_out), st, _ptr(ws), ws_bytes, _stream(stream))
     _check("dg_generate_blocks", rc)
+    for kv, a in zip(kvs, arr):
+        kv.len = int(a.len)
+    return list(st)
+
+
+def dg_generate_blocks_overlapped(cfg, weights, kvs, sampler: dg_sampler, blocks, pending, defer_commit: int,
+                                  tokens_out, ws, ws_bytes: int, stream=None) -> list:
+    """dg_generate_blocks with the pending blocks committed inside the first pass (see include/dg.h)."""
+    n = len(kvs)
+    arr = (dg_kv * n)(*[kv.struct for kv in kvs])
+    ids = (ctypes.c_uint32 * n)(*[int(b) for b in blocks])
+    st = (dg_block_status * n)()
+    rc = _lib.dg_generate_blocks_overlapped(ctypes.byref(cfg), _w(weights), arr, n, ctypes.byref(sampler), ids,
+                                            _ptr(pending), defer_commit, _ptr(tokens_out), st, _ptr(ws), ws_bytes,
+                                            _stream(stream))
+    _check("dg_generate_blocks_overlapped", rc)
     for kv, a in zip(kvs, arr):
         kv.len = int(a.len)
     return list(st)

@@ -711,24 +711,27 @@ int dg_generate_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, cons
   return dg_generate_block_overlapped(cfg, w, kv, sp, block, nullptr, 0, tokens_out, h_status, ws, ws_bytes, stream);
 }
 
-int dg_generate_blocks(const dg_config* cfg, const dg_weights* w, dg_kv* kvs, int32_t n_seq, const dg_sampler* sp,
-                       const uint32_t* h_blocks, int32_t* tokens_out, dg_block_status* h_status, void* ws,
-                       size_t ws_bytes, void* stream) {
+int dg_generate_blocks_overlapped(const dg_config* cfg, const dg_weights* w, dg_kv* kvs, int32_t n_seq,
+                                  const dg_sampler* sp, const uint32_t* h_blocks, const int32_t* pending,
+                                  int32_t defer_commit, int32_t* tokens_out, dg_block_status* h_status, void* ws,
+                                  size_t ws_bytes, void* stream) {
   DG_CHECK(check_cfg(cfg));
   DG_CHECK(check_weights(cfg, w, true, true));
   DG_CHECK(check_sampler(cfg, sp));
   if (!kvs || !h_blocks || !tokens_out || !h_status || n_seq < 1 || n_seq > kMaxSeq) return DG_ERR_INVALID;
+  if (defer_commit != 0 && defer_commit != 1) return DG_ERR_INVALID;
   const int S = cfg->canvas;
   const int64_t M = (int64_t)n_seq * S;
-  if (M > moe_max_rows(cfg->n_experts)) return DG_ERR_INVALID;
+  const int64_t rows = pending ? 2 * M : M;  // the first pass also commits the pending blocks
+  if (rows > moe_max_rows(cfg->n_experts)) return DG_ERR_INVALID;
   for (int b = 0; b < n_seq; ++b) {
-    DG_CHECK(check_kv(&kvs[b], S));
+    DG_CHECK(check_kv(&kvs[b], pending ? 2 * S : S));
     for (int b2 = 0; b2 < b; ++b2)
       if (kvs[b2].k == kvs[b].k || kvs[b2].v == kvs[b].v) return DG_ERR_INVALID;  // each sequence its own cache
   }
-  DG_CHECK(check_ws(cfg, M, ws, ws_bytes));
+  DG_CHECK(check_ws(cfg, rows, ws, ws_bytes));
   hipStream_t s = (hipStream_t)stream;
-  Ws wsv = carve(cfg, M, (char*)ws);
+  Ws wsv = carve(cfg, rows, (char*)ws);
   const StopParams stp = stop_params(cfg, sp);
   const bool fixed = sp->fixed_steps > 0, lock = (sp->flags & DG_KEEP_LOCK) != 0;
   const bool by_ent = (sp->flags & DG_KEEP_ENTROPY) != 0, draw = (sp->flags & DG_SAMPLE_GUMBEL) != 0;
@@ -748,17 +751,38 @@ int dg_generate_blocks(const dg_config* cfg, const dg_weights* w, dg_kv* kvs, in
   int n_done = 0;
   dg_block_status st[kMaxSeq] = {};
   for (int t = 1; n_done < n_seq; ++t) {
-    // one pass over every canvas; a finished canvas still runs (its rows are ignored from then on)
-    DG_CHECK(embed(cfg, w, wsv.canvas, M, wsv, s));
-    for (int l = 0; l < L; ++l)
-      DG_CHECK(layer(cfg, w, l, sg, M, l > 0, l + 1 < L ? Next::NextLayer : Next::Head, wsv, s));
-    if (!draw) {
-      DG_CHECK(head(cfg, w, M, sampler_pass(sp, 0, t), wsv.pred, wsv.conf, wsv.ent, L > 0, wsv, s));
-    } else {  // each canvas draws with its own block's counters
+    if (t == 1 && pending) {
+      // sequence b's rows [2bS, 2bS + S) are its pending block (causal, committed at its cache's end), rows
+      // [2bS + S, 2(b+1)S) its canvas, which sees the committed block
+      Segs pg{};
+      pg.n = n_seq;
+      for (int b = 0; b < n_seq; ++b) {
+        pg.seg[b] = Seg{&kvs[b], kvs[b].len, 2 * (int64_t)b * S, 2 * (int64_t)S, S};
+        DG_CHECK(embed(cfg, w, pending + (size_t)b * S, S, wsv, s, 2 * (int64_t)b * S));
+        DG_CHECK(embed(cfg, w, wsv.canvas + (size_t)b * S, S, wsv, s, (2 * (int64_t)b + 1) * S));
+      }
+      for (int l = 0; l < L; ++l)
+        DG_CHECK(layer(cfg, w, l, pg, rows, l > 0, l + 1 < L ? Next::NextLayer : Next::Head, wsv, s));
       for (int b = 0; b < n_seq; ++b)
-        if (!done[b])
-          DG_CHECK(head(cfg, w, S, sampler_pass(sp, h_blocks[b], t), wsv.pred + (size_t)b * S,
-                        wsv.conf + (size_t)b * S, wsv.ent + (size_t)b * S, L > 0, wsv, s, (int64_t)b * S));
+        DG_CHECK(head(cfg, w, S, sampler_pass(sp, h_blocks[b], t), wsv.pred + (size_t)b * S, wsv.conf + (size_t)b * S,
+                      wsv.ent + (size_t)b * S, L > 0, wsv, s, (2 * (int64_t)b + 1) * S));
+      for (int b = 0; b < n_seq; ++b) {  // committed (in stream order) before every later pass
+        kvs[b].len += S;
+        sg.seg[b].pos0 = kvs[b].len;
+      }
+    } else {
+      // one pass over every canvas; a finished canvas still runs (its rows are ignored from then on)
+      DG_CHECK(embed(cfg, w, wsv.canvas, M, wsv, s));
+      for (int l = 0; l < L; ++l)
+        DG_CHECK(layer(cfg, w, l, sg, M, l > 0, l + 1 < L ? Next::NextLayer : Next::Head, wsv, s));
+      if (!draw) {
+        DG_CHECK(head(cfg, w, M, sampler_pass(sp, 0, t), wsv.pred, wsv.conf, wsv.ent, L > 0, wsv, s));
+      } else {  // each canvas draws with its own block's counters
+        for (int b = 0; b < n_seq; ++b)
+          if (!done[b])
+            DG_CHECK(head(cfg, w, S, sampler_pass(sp, h_blocks[b], t), wsv.pred + (size_t)b * S,
+                          wsv.conf + (size_t)b * S, wsv.ent + (size_t)b * S, L > 0, wsv, s, (int64_t)b * S));
+      }
     }
     for (int b = 0; b < n_seq; ++b) {
       if (done[b]) continue;
@@ -793,18 +817,27 @@ int dg_generate_blocks(const dg_config* cfg, const dg_weights* w, dg_kv* kvs, in
     }
   }
   if (fixed) DG_TRY(hipMemcpyAsync(st, wsv.status, sizeof(dg_block_status) * n_seq, hipMemcpyDeviceToHost, s));
-  // commit every block in one causal forward: each sequence's rows attend causally within its own cache
-  DG_CHECK(embed(cfg, w, tokens_out, M, wsv, s));
-  Segs cg = sg;
-  for (int b = 0; b < n_seq; ++b) cg.seg[b].n_causal = S;
-  for (int l = 0; l < L; ++l)
-    DG_CHECK(layer(cfg, w, l, cg, M, l > 0, l + 1 < L ? Next::NextLayer : Next::None, wsv, s));
+  if (!defer_commit) {
+    // commit every block in one causal forward: each sequence's rows attend causally within its own cache
+    DG_CHECK(embed(cfg, w, tokens_out, M, wsv, s));
+    Segs cg = sg;
+    for (int b = 0; b < n_seq; ++b) cg.seg[b].n_causal = S;
+    for (int l = 0; l < L; ++l)
+      DG_CHECK(layer(cfg, w, l, cg, M, l > 0, l + 1 < L ? Next::NextLayer : Next::None, wsv, s));
+  }
   DG_TRY(hipStreamSynchronize(s));
   for (int b = 0; b < n_seq; ++b) {
-    kvs[b].len += S;
+    if (!defer_commit) kvs[b].len += S;
     h_status[b] = st[b];
   }
   return DG_OK;
+}
+
+int dg_generate_blocks(const dg_config* cfg, const dg_weights* w, dg_kv* kvs, int32_t n_seq, const dg_sampler* sp,
+                       const uint32_t* h_blocks, int32_t* tokens_out, dg_block_status* h_status, void* ws,
+                       size_t ws_bytes, void* stream) {
+  return dg_generate_blocks_overlapped(cfg, w, kvs, n_seq, sp, h_blocks, nullptr, 0, tokens_out, h_status, ws,
+                                       ws_bytes, stream);
 }
 
 int dg_verify_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const int32_t* draft, int32_t* ar_pred,

@@ -332,6 +332,20 @@ int dg_generate_blocks(const dg_config* cfg, const dg_weights* w, dg_kv* kvs, in
                        const dg_sampler* sampler, const uint32_t* h_blocks, int32_t* tokens_out,
                        dg_block_status* h_status, void* ws, size_t ws_bytes, void* stream);
 
+/* dg_generate_blocks with each sequence's commit carried by the next call's first pass, as
+ * dg_generate_block_overlapped does for one sequence.  pending (nullable, device [n_seq][canvas]):
+ * blocks of an earlier call made with defer_commit = 1; sequence b's pending block is committed at
+ * kvs[b].len inside this call's first pass (its rows attend causally, the canvas rows see them),
+ * then kvs[b].len grows by canvas.  defer_commit (0 or 1): with 1 this call's blocks are not
+ * committed.  pending may alias tokens_out.  With pending the pass holds 2 * n_seq * canvas rows
+ * (<= the routing row limit: 4 canvases of 256 for 128 experts), the workspace must hold them and
+ * each cache 2 * canvas more rows.  Errors as dg_generate_blocks; DG_ERR_INVALID also for
+ * defer_commit not 0 or 1. */
+int dg_generate_blocks_overlapped(const dg_config* cfg, const dg_weights* w, dg_kv* kvs, int32_t n_seq,
+                                  const dg_sampler* sampler, const uint32_t* h_blocks, const int32_t* pending,
+                                  int32_t defer_commit, int32_t* tokens_out, dg_block_status* h_status,
+                                  void* ws, size_t ws_bytes, void* stream);
+
 /* Self-speculative verify of a drafted block ([P1] "The result that complicates 'faster, not
  * smarter'": one set of weights drafts a block bidirectionally and verifies it causally over the
  * same KV cache).  The commit's causal forward over draft (device [canvas], e.g. dg_generate_block

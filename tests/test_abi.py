@@ -28,6 +28,7 @@ def test_header_declares_the_documented_calls():
     for n in ("dg_prefill_kv", "dg_denoise_step", "dg_canvas_update", "dg_commit_block", "dg_generate_block",
               "dg_generate_block_overlapped", "dg_denoise_step_sampler", "dg_canvas_update_sampler",
               "dg_vocab_head_sampler", "dg_sampler_inv_temperature", "dg_generate_blocks", "dg_verify_block",
+              "dg_generate_blocks_overlapped",
               "dg_workspace_size", "dg_status_string"):
         assert n in names
     assert set(names) == set(dg.EXPORTED)
@@ -302,6 +303,12 @@ def test_generate_blocks_validate():
             c()
         assert e.value.status == status, i
     assert [kv.len for kv in kvs] == [0] * 9
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_generate_blocks_overlapped(cfg, w, kvs[:2], sp, [0, 1], None, 2, buf, buf, ws3, 0)
+    assert e.value.status == dg.DG_ERR_INVALID
+    with pytest.raises(dg.DGError) as e:  # a pending block doubles the rows of the first pass
+        dg.dg_generate_blocks_overlapped(cfg, w, kvs[:3], sp, [0, 1, 2], buf, 1, buf, buf, ws3, 0)
+    assert e.value.status == dg.DG_ERR_WORKSPACE
 
 
 def test_verify_block_validates():

@@ -147,3 +147,46 @@ def test_c0_batch_edges_equal_oracle(canvas, prefixes):
         for l in range(d.n_layers):
             gk, gv = sessions[b].kv_numpy(l, kv.length)
             assert allclose_report(gk, kv.k[l], *F32_TOL)[0] and allclose_report(gv, kv.v[l], *F32_TOL)[0], (b, l)
+
+
+def test_c0_batch_overlapped_commits_equal_oracle():
+    """Three consecutive batched calls of three sequences, each call's blocks committed inside the next call's
+    first pass (the last call commits its own): every block and the final caches equal the oracle's blocks
+    generated and committed one after another."""
+    d = recipe.C0.dims
+    storage = dg_inputs.model_weights_host(d)
+    prefixes = [64, 40, 0]
+    sessions = []
+    w = gdev.from_host(storage, d.dtype)
+    for b, p in enumerate(prefixes):
+        s = Session(d, capacity=p + 5 * d.canvas, weights=w if not sessions else sessions[0].w,
+                    packed=bool(sessions))
+        if p:
+            s.prefill(dg_inputs.prompt_tokens(p, d.vocab, seed=b + 1))
+        sessions.append(s)
+    n = len(sessions)
+    ws_bytes = dg.dg_workspace_size(sessions[0].cfg, 2 * n * d.canvas)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    sp = dg.make_sampler(recipe.C0.n_new)
+    outs = [torch.empty((n, d.canvas), dtype=torch.int32, device="cuda") for _ in range(3)]
+    gpu = []
+    for c in range(3):
+        st = dg.dg_generate_blocks_overlapped(sessions[0].cfg, sessions[0].weights, [s.kv for s in sessions], sp,
+                                              [10 * c + b for b in range(n)], outs[c - 1] if c else None,
+                                              1 if c < 2 else 0, outs[c], ws, ws_bytes)
+        torch.cuda.synchronize()
+        gpu.append((outs[c].cpu().numpy(), [(x.steps, x.reason) for x in st]))
+    model = oracle_model(d, storage)
+    for b, p in enumerate(prefixes):
+        kv = om.KVCache(d.n_layers, d.n_kv_heads, d.head_dim)
+        if p:
+            osm.prefill(model, kv, dg_inputs.prompt_tokens(p, d.vocab, seed=b + 1))
+        for c in range(3):
+            res = osm.generate_block(model, kv, osm.Sampler(n_new=recipe.C0.n_new), block=10 * c + b)
+            assert gpu[c][1][b] == (res.steps, res.reason), (b, c)
+            assert np.array_equal(gpu[c][0][b], res.tokens), (b, c)
+        s = sessions[b]
+        assert s.kv.len == kv.length == p + 3 * d.canvas
+        for l in range(d.n_layers):
+            gk, gv = s.kv_numpy(l, kv.length)
+            assert allclose_report(gk, kv.k[l], *F32_TOL)[0] and allclose_report(gv, kv.v[l], *F32_TOL)[0], (b, l)
