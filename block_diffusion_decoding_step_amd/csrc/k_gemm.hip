@@ -32,6 +32,7 @@ struct Depth<bf16> {
   static constexpr int moe1 = 4;  // routed experts, one 16-row M-tile
   static constexpr int moe2 = 3;  // routed experts, two 16-row M-tiles
   static constexpr int moe4 = 2;  // routed experts, three or four 16-row M-tiles (wide tiles)
+  static constexpr int down = 6;  // routed down projection (K = ffn width, short), one or two M-tiles
 };
 template <>
 struct Depth<float> {
@@ -39,6 +40,7 @@ struct Depth<float> {
   static constexpr int moe1 = 1;
   static constexpr int moe2 = 1;
   static constexpr int moe4 = 1;
+  static constexpr int down = 1;
 };
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
@@ -360,7 +362,7 @@ __device__ __forceinline__ void moe_down_body(const MoeArgs& a, int e, int p0, i
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = zero4();
-  wave_gemm<T, MT, NT, Depth<T>::moe1, false, NTL>(acc, ap, bp, ks, 32, kFragElems);
+  wave_gemm<T, MT, NT, (MT <= 2 ? Depth<T>::down : Depth<T>::moe1), false, NTL>(acc, ap, bp, ks, 32, kFragElems);
   T* Y = (T*)a.out;
   const int rq = (lane >> 4) * 4;
 #pragma unroll
