@@ -297,7 +297,7 @@ def main() -> int:
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one MI355X only: this build runs the whole denoising step on a single GPU "
+        print(f"bench.py measures one MI355X only: the library runs the whole denoising step on a single GPU "
               f"with no collectives (asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         return 2
 

@@ -62,7 +62,7 @@ def gumbel_noise(seed: int, block: int, step: int, slots, vocab: int) -> np.ndar
 
     The recommended sampler draws each slot's token from the softmax at the pass's
     temperature ([P2] "Architecture Details": the temperature falls linearly from 0.8
-    to 0.4 over the passes; [P5] "Appendix: Methodology", "Decoding").  This build samples with the Gumbel-max identity
+    to 0.4 over the passes; [P5] "Appendix: Methodology", "Decoding").  The draw uses the Gumbel-max identity
     (E. J. Gumbel, 1954; argmax_v (l_v + G_v) with i.i.d. standard Gumbel G_v is
     distributed as softmax(l)), which needs one uniform per (slot, token):
         w = word (v mod 4) of Philox4x32-10(key = (seed mod 2^32, seed div 2^32),

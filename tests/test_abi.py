@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 from dataclasses import replace
 
 import pytest
@@ -328,3 +329,9 @@ def test_verify_block_validates():
         dg.dg_verify_block(cfg, w, kv, buf, buf, buf, ws_bytes - 256, 0)
     assert e.value.status == dg.DG_ERR_WORKSPACE
     assert kv.len == 0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2 and "one MI355X" in r.stderr and r.stdout == ""
