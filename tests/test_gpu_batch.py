@@ -78,6 +78,8 @@ def test_c0_batch_equals_oracle_per_sequence(flags, kw):
                       rank_entropy=bool(flags & dg.DG_KEEP_ENTROPY), lock=bool(flags & dg.DG_KEEP_LOCK),
                       stop_and=bool(flags & dg.DG_STOP_AND), **kw)
     toks, st = _batch(sessions, sp, blocks)
+    if flags == 0:  # the sequences stop at different passes (9, 9 and 15): finished canvases ride along
+        assert len({x.steps for x in st}) > 1
     model = oracle_model(d, storage)
     for b, (p, blk) in enumerate(zip(prefixes, blocks)):
         kv = om.KVCache(d.n_layers, d.n_kv_heads, d.head_dim)
