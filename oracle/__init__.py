@@ -42,6 +42,13 @@ Pins (tests/test_oracle_*.py, all run without a GPU):
     E2 (self-retrieval -> entropy stop at step 1), fixed-T stop, 48-step cap
   * bf16 rounding: exhaustive agreement with the fp32 route on all bf16
     neighbours and ties
+  * layer wiring (tests/test_oracle_wiring.py): closed forms for weights that
+    make the block solvable by hand (W_o = 0 with routed experts equal to the
+    shared one; W_q = 0 with zero down projections; both), computed with plain
+    loops and distinct attention / FFN norm gains
+  * canvas token mapping: the all-zero Philox counter's published word 0
+    mapped by the multiply-shift (104607 of 262144, 1634 of 4096)
+  * SiLU: silu(1), silu(-1), silu(0) and the large-|z| limits
 Parity unpinned: none of the functions above is left without a pin; the
 whole-model forward has no golden values on the pages and is pinned only
 through its parts.
