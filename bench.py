@@ -184,6 +184,7 @@ def run_batch(args, wl) -> int:
         print(f"--batch {B}: at most 8 canvases and 2048 rows per pass", file=sys.stderr)
         return 2
     log(f"bench: {wl.name} batch {B}; generating weights on the device")
+    side = dg.Side()  # the shared expert's stream and events, owned here
     w = gdev.packed_model_weights_device(d)
     weights = dg.Weights(w["embed"], w["final_norm"], w["layers"])
     cfg = dg.make_config(d)
@@ -196,7 +197,7 @@ def run_batch(args, wl) -> int:
         k, v = gdev.kv_tensors(d, cap)
         kv = dg.KV(k, v, cap, 0)
         prompt = gdev.uniform_tensor(wl.prefix, recipe.INPUT_SEED + b, recipe.STREAM_PROMPT, d.vocab)
-        dg.dg_prefill_kv(cfg, weights, kv, prompt, wl.prefix, ws, ws_bytes)
+        dg.dg_prefill_kv(cfg, weights, kv, prompt, wl.prefix, ws, ws_bytes, side=side)
         kvs.append(kv)
         keep.append((k, v))
     torch.cuda.synchronize()
@@ -220,10 +221,10 @@ def run_batch(args, wl) -> int:
             if overlap:
                 q = (i * wl.blocks + j) % 2
                 out += dg.dg_generate_blocks_overlapped(cfg, weights, kvs, sampler, ids, pending[0], 1, toks2[q], ws,
-                                                        ws_bytes)
+                                                        ws_bytes, side=side)
                 pending[0] = toks2[q]
             else:
-                out += dg.dg_generate_blocks(cfg, weights, kvs, sampler, ids, toks, ws, ws_bytes)
+                out += dg.dg_generate_blocks(cfg, weights, kvs, sampler, ids, toks, ws, ws_bytes, side=side)
         return out
 
     for i in range(args.warmup):
@@ -317,6 +318,7 @@ def main() -> int:
         return run_batch(args, wl)
     stream = torch.cuda.current_stream()
     log(f"bench: {wl.name} on {torch.cuda.get_device_name(0)}; generating weights on the device")
+    side = dg.Side()  # the shared expert's stream and events, owned here
     w = gdev.packed_model_weights_device(d)
     weights = dg.Weights(w["embed"], w["final_norm"], w["layers"])
     cfg = dg.make_config(d)
@@ -329,7 +331,7 @@ def main() -> int:
     prompt = gdev.uniform_tensor(wl.prefix, recipe.INPUT_SEED, recipe.STREAM_PROMPT, d.vocab)
     log(f"bench: prefill {wl.prefix} tokens")
     t0 = time.perf_counter()
-    dg.dg_prefill_kv(cfg, weights, kv, prompt, wl.prefix, ws, ws_bytes)
+    dg.dg_prefill_kv(cfg, weights, kv, prompt, wl.prefix, ws, ws_bytes, side=side)
     torch.cuda.synchronize()
     t_prefill = time.perf_counter() - t0
     P = kv.len
@@ -341,9 +343,9 @@ def main() -> int:
 
     def one_pass(dbg=None, t=1):
         if flags == 0 or dbg is not None:
-            dg.dg_denoise_step(cfg, weights, kv, canvas, 1.0, pred, conf, ent, dbg, ws, ws_bytes)
+            dg.dg_denoise_step(cfg, weights, kv, canvas, 1.0, pred, conf, ent, dbg, ws, ws_bytes, side=side)
         else:
-            dg.dg_denoise_step_sampler(cfg, weights, kv, sampler, 0, t, canvas, pred, conf, ent, ws, ws_bytes)
+            dg.dg_denoise_step_sampler(cfg, weights, kv, sampler, 0, t, canvas, pred, conf, ent, ws, ws_bytes, side=side)
     toks = [torch.empty(d.canvas, dtype=torch.int32, device="cuda") for _ in range(2)]
     pending = [None]
 
@@ -359,7 +361,7 @@ def main() -> int:
         for b in range(blocks):
             j = i * blocks + b
             out.append(dg.dg_generate_block_overlapped(cfg, weights, kv, sampler, j, pending[0], 1, toks[j % 2], ws,
-                                                       ws_bytes))
+                                                       ws_bytes, side=side))
             pending[0] = toks[j % 2]
         return out
 
@@ -368,7 +370,7 @@ def main() -> int:
         step(i)
     if pending[0] is None:  # no warmup: one untimed block leaves the pending commit the first timed step carries
         kv.len = P
-        dg.dg_generate_block_overlapped(cfg, weights, kv, sampler, 0, None, 1, toks[1], ws, ws_bytes)
+        dg.dg_generate_block_overlapped(cfg, weights, kv, sampler, 0, None, 1, toks[1], ws, ws_bytes, side=side)
         pending[0] = toks[1]
     torch.cuda.synchronize()
 

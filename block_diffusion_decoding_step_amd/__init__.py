@@ -34,7 +34,8 @@ DG_SAMPLE_GUMBEL, DG_SAMPLE_ANNEAL, DG_KEEP_ENTROPY, DG_KEEP_LOCK, DG_STOP_AND =
 EXPORTED = ("dg_workspace_size", "dg_prefill_kv", "dg_denoise_step", "dg_canvas_update", "dg_commit_block",
             "dg_generate_block", "dg_generate_block_overlapped", "dg_layer_forward", "dg_vocab_head", "dg_stop_check", "dg_status_string",
             "dg_generate_blocks", "dg_generate_blocks_overlapped", "dg_verify_block", "dg_denoise_step_sampler", "dg_canvas_update_sampler", "dg_vocab_head_sampler", "dg_sampler_inv_temperature",
-            "dg_last_hip_error", "dg_timing_start", "dg_timing_stop", "dg_packed_elems", "dg_pack_matrix")
+            "dg_last_hip_error", "dg_timing_start", "dg_timing_stop", "dg_packed_elems", "dg_pack_matrix",
+            "dg_side_create", "dg_side_destroy")
 # kernel classes of dg_timing_* (dg_kernel in dg.h), in enum order
 KERNELS = ("embed", "rmsnorm", "gemm_qkv", "attention", "attn_merge", "gemm_o", "route",
            "moe_gate_up", "moe_down", "shared_gate_up", "shared_down", "moe_combine", "vocab_head",
@@ -87,6 +88,10 @@ class dg_block_status(ctypes.Structure):
                 ("flags", ctypes.c_uint32)]
 
 
+class dg_side(ctypes.Structure):
+    _fields_ = [("stream", ctypes.c_void_p), ("fork", ctypes.c_void_p), ("join", ctypes.c_void_p)]
+
+
 class dg_debug(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_void_p), ("route_idx", ctypes.c_void_p), ("route_w", ctypes.c_void_p),
                 ("router_logits", ctypes.c_void_p)]
@@ -97,32 +102,34 @@ _vp, _i32, _i64, _u32, _u64, _f32, _sz = (ctypes.c_void_p, ctypes.c_int32, ctype
                                           ctypes.c_uint64, ctypes.c_float, ctypes.c_size_t)
 _SIGS = {
     "dg_workspace_size": [_P(dg_config), _i64, _P(_sz)],
-    "dg_prefill_kv": [_P(dg_config), _P(dg_weights), _P(dg_kv), _vp, _i64, _vp, _sz, _vp],
+    "dg_prefill_kv": [_P(dg_config), _P(dg_weights), _P(dg_kv), _vp, _i64, _vp, _sz, _P(dg_side), _vp],
     "dg_denoise_step": [_P(dg_config), _P(dg_weights), _P(dg_kv), _vp, _f32, _vp, _vp, _vp, _P(dg_debug), _vp, _sz,
-                        _vp],
+                        _P(dg_side), _vp],
     "dg_canvas_update": [_P(dg_config), _vp, _vp, _i32, _u64, _u32, _u32, _vp, _vp, _vp],
-    "dg_commit_block": [_P(dg_config), _P(dg_weights), _P(dg_kv), _vp, _vp, _sz, _vp],
+    "dg_commit_block": [_P(dg_config), _P(dg_weights), _P(dg_kv), _vp, _vp, _sz, _P(dg_side), _vp],
     "dg_generate_block": [_P(dg_config), _P(dg_weights), _P(dg_kv), _P(dg_sampler), _u32, _vp, _P(dg_block_status),
-                          _vp, _sz, _vp],
+                          _vp, _sz, _P(dg_side), _vp],
     "dg_generate_block_overlapped": [_P(dg_config), _P(dg_weights), _P(dg_kv), _P(dg_sampler), _u32, _vp, _i32, _vp,
-                                     _P(dg_block_status), _vp, _sz, _vp],
+                                     _P(dg_block_status), _vp, _sz, _P(dg_side), _vp],
     "dg_generate_blocks": [_P(dg_config), _P(dg_weights), _P(dg_kv), _i32, _P(dg_sampler), _P(_u32), _vp,
-                           _P(dg_block_status), _vp, _sz, _vp],
+                           _P(dg_block_status), _vp, _sz, _P(dg_side), _vp],
     "dg_generate_blocks_overlapped": [_P(dg_config), _P(dg_weights), _P(dg_kv), _i32, _P(dg_sampler), _P(_u32), _vp,
-                                      _i32, _vp, _P(dg_block_status), _vp, _sz, _vp],
-    "dg_verify_block": [_P(dg_config), _P(dg_weights), _P(dg_kv), _vp, _vp, _P(_i32), _P(_i32), _vp, _sz, _vp],
+                                      _i32, _vp, _P(dg_block_status), _vp, _sz, _P(dg_side), _vp],
+    "dg_verify_block": [_P(dg_config), _P(dg_weights), _P(dg_kv), _vp, _vp, _P(_i32), _P(_i32), _vp, _sz, _P(dg_side), _vp],
     "dg_layer_forward": [_P(dg_config), _P(dg_weights), _i32, _P(dg_kv), _vp, _vp, _i64, _i32, _P(dg_debug), _vp,
-                         _sz, _vp],
+                         _sz, _P(dg_side), _vp],
     "dg_vocab_head": [_P(dg_config), _P(dg_weights), _vp, _i64, _f32, _vp, _vp, _vp, _vp, _sz, _vp],
     "dg_stop_check": [_P(dg_config), _P(dg_sampler), _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "dg_denoise_step_sampler": [_P(dg_config), _P(dg_weights), _P(dg_kv), _P(dg_sampler), _u32, _i32, _vp, _vp, _vp,
-                                _vp, _vp, _sz, _vp],
+                                _vp, _vp, _sz, _P(dg_side), _vp],
     "dg_canvas_update_sampler": [_P(dg_config), _P(dg_sampler), _u32, _i32, _vp, _vp, _vp, _vp, _vp, _vp],
     "dg_vocab_head_sampler": [_P(dg_config), _P(dg_weights), _P(dg_sampler), _u32, _i32, _vp, _i64, _vp, _vp, _vp,
                               _vp, _sz, _vp],
     "dg_sampler_inv_temperature": [_P(dg_sampler), _i32, _P(ctypes.c_float)],
     "dg_packed_elems": [_i64, _i64, _P(_i64)],
     "dg_pack_matrix": [_vp, _vp, _i64, _i64, _i64, _i32, _vp],
+    "dg_side_create": [_P(dg_side)],
+    "dg_side_destroy": [_P(dg_side)],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -155,6 +162,31 @@ def _stream(stream) -> Optional[int]:
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
+
+
+def _side(side):
+    if side is None:
+        return None
+    return ctypes.byref(side.struct if isinstance(side, Side) else side)
+
+
+class Side:
+    """A caller-owned dg_side: the side stream and fork/join events of the shared expert, made by
+    dg_side_create and destroyed by close() (or when the object is collected)."""
+
+    def __init__(self):
+        self.struct = dg_side()
+        _check("dg_side_create", _lib.dg_side_create(ctypes.byref(self.struct)))
+
+    def close(self) -> None:
+        if self.struct.stream:
+            _check("dg_side_destroy", _lib.dg_side_destroy(ctypes.byref(self.struct)))
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # pragma: no cover - interpreter shutdown
+            pass
 
 
 def _check(fn: str, rc: int) -> None:
@@ -221,17 +253,17 @@ def dg_workspace_size(cfg: dg_config, max_tokens: int) -> int:
     return int(out.value)
 
 
-def dg_prefill_kv(cfg, weights, kv, tokens, n: int, ws, ws_bytes: int, stream=None) -> None:
+def dg_prefill_kv(cfg, weights, kv, tokens, n: int, ws, ws_bytes: int, side=None, stream=None) -> None:
     _check("dg_prefill_kv", _lib.dg_prefill_kv(ctypes.byref(cfg), _w(weights), _kv(kv), _ptr(tokens), n, _ptr(ws),
-                                               ws_bytes, _stream(stream)))
+                                               ws_bytes, _side(side), _stream(stream)))
 
 
 def dg_denoise_step(cfg, weights, kv, canvas, inv_temperature: float, pred, conf, entropy, dbg=None, ws=None,
-                    ws_bytes: int = 0, stream=None) -> None:
+                    ws_bytes: int = 0, side=None, stream=None) -> None:
     d = _dbg(dbg)
     _check("dg_denoise_step", _lib.dg_denoise_step(ctypes.byref(cfg), _w(weights), _kv(kv), _ptr(canvas),
                                                    inv_temperature, _ptr(pred), _ptr(conf), _ptr(entropy), d,
-                                                   _ptr(ws), ws_bytes, _stream(stream)))
+                                                   _ptr(ws), ws_bytes, _side(side), _stream(stream)))
 
 
 def dg_canvas_update(cfg, pred, conf, keep_count: int, seed: int, block: int, step: int, canvas_out,
@@ -241,39 +273,39 @@ def dg_canvas_update(cfg, pred, conf, keep_count: int, seed: int, block: int, st
                                                      _stream(stream)))
 
 
-def dg_commit_block(cfg, weights, kv, block_tokens, ws, ws_bytes: int, stream=None) -> None:
+def dg_commit_block(cfg, weights, kv, block_tokens, ws, ws_bytes: int, side=None, stream=None) -> None:
     _check("dg_commit_block", _lib.dg_commit_block(ctypes.byref(cfg), _w(weights), _kv(kv), _ptr(block_tokens),
-                                                   _ptr(ws), ws_bytes, _stream(stream)))
+                                                   _ptr(ws), ws_bytes, _side(side), _stream(stream)))
 
 
 def dg_generate_block(cfg, weights, kv, sampler: dg_sampler, block: int, tokens_out, ws, ws_bytes: int,
-                      stream=None) -> dg_block_status:
+                      side=None, stream=None) -> dg_block_status:
     st = dg_block_status()
     _check("dg_generate_block", _lib.dg_generate_block(ctypes.byref(cfg), _w(weights), _kv(kv),
                                                        ctypes.byref(sampler), block, _ptr(tokens_out),
-                                                       ctypes.byref(st), _ptr(ws), ws_bytes, _stream(stream)))
+                                                       ctypes.byref(st), _ptr(ws), ws_bytes, _side(side), _stream(stream)))
     return st
 
 
 def dg_generate_block_overlapped(cfg, weights, kv, sampler: dg_sampler, block: int, pending, defer_commit: int,
-                                 tokens_out, ws, ws_bytes: int, stream=None) -> dg_block_status:
+                                 tokens_out, ws, ws_bytes: int, side=None, stream=None) -> dg_block_status:
     st = dg_block_status()
     _check("dg_generate_block_overlapped",
            _lib.dg_generate_block_overlapped(ctypes.byref(cfg), _w(weights), _kv(kv), ctypes.byref(sampler), block,
                                              _ptr(pending), defer_commit, _ptr(tokens_out), ctypes.byref(st),
-                                             _ptr(ws), ws_bytes, _stream(stream)))
+                                             _ptr(ws), ws_bytes, _side(side), _stream(stream)))
     return st
 
 
 def dg_generate_blocks(cfg, weights, kvs, sampler: dg_sampler, blocks, tokens_out, ws, ws_bytes: int,
-                       stream=None) -> list:
+                       side=None, stream=None) -> list:
     """Blocks of len(kvs) sequences at once; tokens_out is [n_seq, canvas]; each KV's len grows on success."""
     n = len(kvs)
     arr = (dg_kv * n)(*[kv.struct for kv in kvs])
     ids = (ctypes.c_uint32 * n)(*[int(b) for b in blocks])
     st = (dg_block_status * n)()
     rc = _lib.dg_generate_blocks(ctypes.byref(cfg), _w(weights), arr, n, ctypes.byref(sampler), ids,
-                                 _ptr(tokens_out), st, _ptr(ws), ws_bytes, _stream(stream))
+                                 _ptr(tokens_out), st, _ptr(ws), ws_bytes, _side(side), _stream(stream))
     _check("dg_generate_blocks", rc)
     for kv, a in zip(kvs, arr):
         kv.len = int(a.len)
@@ -281,7 +313,7 @@ def dg_generate_blocks(cfg, weights, kvs, sampler: dg_sampler, blocks, tokens_ou
 
 
 def dg_generate_blocks_overlapped(cfg, weights, kvs, sampler: dg_sampler, blocks, pending, defer_commit: int,
-                                  tokens_out, ws, ws_bytes: int, stream=None) -> list:
+                                  tokens_out, ws, ws_bytes: int, side=None, stream=None) -> list:
     """dg_generate_blocks with the pending blocks committed inside the first pass (see include/dg.h)."""
     n = len(kvs)
     arr = (dg_kv * n)(*[kv.struct for kv in kvs])
@@ -289,19 +321,19 @@ def dg_generate_blocks_overlapped(cfg, weights, kvs, sampler: dg_sampler, blocks
     st = (dg_block_status * n)()
     rc = _lib.dg_generate_blocks_overlapped(ctypes.byref(cfg), _w(weights), arr, n, ctypes.byref(sampler), ids,
                                             _ptr(pending), defer_commit, _ptr(tokens_out), st, _ptr(ws), ws_bytes,
-                                            _stream(stream))
+                                            _side(side), _stream(stream))
     _check("dg_generate_blocks_overlapped", rc)
     for kv, a in zip(kvs, arr):
         kv.len = int(a.len)
     return list(st)
 
 
-def dg_verify_block(cfg, weights, kv, draft, ar_pred, ws, ws_bytes: int, stream=None) -> tuple:
+def dg_verify_block(cfg, weights, kv, draft, ar_pred, ws, ws_bytes: int, side=None, stream=None) -> tuple:
     """Self-speculative verify; returns (accepted, next_token); kv.len grows by accepted."""
     n, nxt = _i32(0), _i32(0)
     _check("dg_verify_block", _lib.dg_verify_block(ctypes.byref(cfg), _w(weights), _kv(kv), _ptr(draft),
                                                    _ptr(ar_pred), ctypes.byref(n), ctypes.byref(nxt), _ptr(ws),
-                                                   ws_bytes, _stream(stream)))
+                                                   ws_bytes, _side(side), _stream(stream)))
     return int(n.value), int(nxt.value)
 
 
@@ -313,10 +345,10 @@ def _dbg(dbg):
 
 
 def dg_layer_forward(cfg, weights, layer: int, kv, x_in, x_out, n: int, causal: int, dbg=None, ws=None,
-                     ws_bytes: int = 0, stream=None) -> None:
+                     ws_bytes: int = 0, side=None, stream=None) -> None:
     _check("dg_layer_forward", _lib.dg_layer_forward(ctypes.byref(cfg), _w(weights), layer, _kv(kv), _ptr(x_in),
                                                      _ptr(x_out), n, causal, _dbg(dbg), _ptr(ws), ws_bytes,
-                                                     _stream(stream)))
+                                                     _side(side), _stream(stream)))
 
 
 def dg_vocab_head(cfg, weights, x, n: int, inv_temperature: float, pred, conf, entropy, ws, ws_bytes: int,
@@ -334,11 +366,11 @@ def dg_stop_check(cfg, sampler: dg_sampler, step: int, entropy, pred, prev_pred,
 
 
 def dg_denoise_step_sampler(cfg, weights, kv, sampler: dg_sampler, block: int, step: int, canvas, pred, conf,
-                            entropy, ws, ws_bytes: int, stream=None) -> None:
+                            entropy, ws, ws_bytes: int, side=None, stream=None) -> None:
     _check("dg_denoise_step_sampler",
            _lib.dg_denoise_step_sampler(ctypes.byref(cfg), _w(weights), _kv(kv), ctypes.byref(sampler), block, step,
                                         _ptr(canvas), _ptr(pred), _ptr(conf), _ptr(entropy), _ptr(ws), ws_bytes,
-                                        _stream(stream)))
+                                        _side(side), _stream(stream)))
 
 
 def dg_canvas_update_sampler(cfg, sampler: dg_sampler, block: int, step: int, pred, conf, entropy, canvas,

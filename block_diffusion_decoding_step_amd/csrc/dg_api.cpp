@@ -10,9 +10,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
-#include <map>
 #include <mutex>
-#include <utility>
 #include <vector>
 
 #include "../../include/dg.h"
@@ -82,31 +80,20 @@ struct TimeScope {
 };
 
 // ------------------------------------------------------------------ side stream
-// The shared expert depends only on the FFN-normalised rows, so it runs on a side stream while the
-// caller's stream does the routing and the routed experts; the two join before the combine.  One side
-// stream (default priority, non-blocking) and a fork/join event pair per (device, caller stream),
-// created on first use and kept for the life of the process.
-struct Side {
+// The shared expert depends only on the FFN-normalised rows.  With a caller-owned dg_side it runs on the
+// side stream while the caller's stream does the routing and the routed experts, and the two join before
+// the combine; without one it runs on the caller's stream.  The library creates and keeps nothing.
+struct SideRef {
   hipStream_t s;
   hipEvent_t fork, join;
 };
-std::mutex g_side_mu;
-std::map<std::pair<int, hipStream_t>, Side> g_side;
-
-int side_for(hipStream_t main, Side** out) {
-  int dev = 0;
-  DG_TRY(hipGetDevice(&dev));
-  std::lock_guard<std::mutex> lk(g_side_mu);
-  const auto key = std::make_pair(dev, main);
-  auto it = g_side.find(key);
-  if (it == g_side.end()) {
-    Side sd{};
-    DG_TRY(hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking));
-    DG_TRY(hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming));
-    DG_TRY(hipEventCreateWithFlags(&sd.join, hipEventDisableTiming));
-    it = g_side.emplace(key, sd).first;
-  }
-  *out = &it->second;
+bool side_of(const dg_side* side, SideRef* out) {
+  if (!side || !side->stream) return false;
+  *out = SideRef{(hipStream_t)side->stream, (hipEvent_t)side->fork, (hipEvent_t)side->join};
+  return true;
+}
+int check_side(const dg_side* side) {
+  if (side && side->stream && (!side->fork || !side->join || side->fork == side->join)) return DG_ERR_INVALID;
   return DG_OK;
 }
 
@@ -307,7 +294,7 @@ Segs one_seq(const dg_kv* kv, int64_t pos0, int64_t M, int64_t n_causal) {
 // One layer over M rows (the segments' rows).
 template <typename T>
 int layer_t(const dg_config* c, const dg_weights* w, int l, const Segs& sg, int64_t M, bool normed_in, Next next,
-            const Ws& ws, hipStream_t s) {
+            const Ws& ws, const dg_side* side, hipStream_t s) {
   const dg_layer_weights& L = w->h_layers[l];
   const int d = c->d_model, hq = c->n_heads, hkv = c->n_kv_heads, dh = c->head_dim;
   const int E = c->n_experts, k = c->top_k;
@@ -364,21 +351,23 @@ int layer_t(const dg_config* c, const dg_weights* w, int l, const Segs& sg, int6
   DG_LAUNCH(DG_K_GEMM_O, s, launch_gemm<T>(GemmEpi::Resid, g, s));
 
   // MoE half ([P2] "Architecture Details": 8 routed experts of 128, plus 1 shared)
-  // shared expert on the side stream, concurrent with the routing and the routed experts; the fork and
-  // join events complete with the norm and the shared down projection themselves
-  Side* sd = nullptr;
-  DG_CHECK(side_for(s, &sd));
+  // shared expert: on the caller's side stream when there is one, concurrent with the routing and the routed
+  // experts (the fork and join events complete with the norm and the shared down projection themselves);
+  // otherwise on the caller's stream
+  SideRef sd{};
+  const bool fork = side_of(side, &sd);
+  const hipStream_t ss = fork ? sd.s : s;
   DG_LAUNCH(DG_K_RMSNORM, s, launch_rmsnorm<T>((const T*)ws.X, (const T*)L.ffn_norm, (T*)ws.Xn, (T*)ws.Xt, Mi, d,
-                                                c->rms_eps, s, sd->fork));
-  DG_TRY(hipStreamWaitEvent(sd->s, sd->fork, 0));
+                                                c->rms_eps, s, fork ? sd.fork : nullptr));
+  if (fork) DG_TRY(hipStreamWaitEvent(ss, sd.fork, 0));
   g = GemmArgs{};
   g.A = ws.Xt; g.a_tiled = 1; g.B = L.ws_gate_up; g.C = ws.Hs; g.M = Mi; g.N = c->ffn_shared; g.K = d; g.lda = d;
   g.ldb = d; g.ldc = c->ffn_shared;
-  DG_LAUNCH(DG_K_SHARED_GATE_UP, sd->s, launch_gemm<T>(GemmEpi::SwiGLU, g, sd->s));
+  DG_LAUNCH(DG_K_SHARED_GATE_UP, ss, launch_gemm<T>(GemmEpi::SwiGLU, g, ss));
   g = GemmArgs{};
   g.A = ws.Hs; g.a_tiled = 1; g.B = L.ws_down; g.C = ws.Ys; g.M = Mi; g.N = d; g.K = c->ffn_shared;
   g.lda = c->ffn_shared; g.ldb = c->ffn_shared; g.ldc = d;
-  DG_LAUNCH(DG_K_SHARED_DOWN, sd->s, launch_gemm<T>(GemmEpi::Store, g, sd->s, sd->join));
+  DG_LAUNCH(DG_K_SHARED_DOWN, ss, launch_gemm<T>(GemmEpi::Store, g, ss, fork ? sd.join : nullptr));
 
   // router logits, top-k, softmax weights and the token->expert order
   RouteArgs ra{};
@@ -396,7 +385,7 @@ int layer_t(const dg_config* c, const dg_weights* w, int l, const Segs& sg, int6
   ma.X = ws.Hp; ma.W = L.w_down; ma.out = ws.Yp;
   DG_LAUNCH(DG_K_MOE_DOWN, s, launch_moe_down<T>(ma, s));
 
-  DG_TRY(hipStreamWaitEvent(s, sd->join, 0));  // join: the combine reads the shared expert's output
+  if (fork) DG_TRY(hipStreamWaitEvent(s, sd.join, 0));  // join: the combine reads the shared expert's output
   const T* g_next = next == Next::NextLayer ? (const T*)w->h_layers[l + 1].attn_norm
                     : next == Next::Head      ? (const T*)w->final_norm
                                               : nullptr;
@@ -408,13 +397,13 @@ int layer_t(const dg_config* c, const dg_weights* w, int l, const Segs& sg, int6
 }
 
 int layer(const dg_config* c, const dg_weights* w, int l, const Segs& sg, int64_t M, bool normed_in, Next next,
-          const Ws& ws, hipStream_t s) {
-  if (c->dtype == DG_BF16) return layer_t<bf16>(c, w, l, sg, M, normed_in, next, ws, s);
-  return layer_t<float>(c, w, l, sg, M, normed_in, next, ws, s);
+          const Ws& ws, const dg_side* side, hipStream_t s) {
+  if (c->dtype == DG_BF16) return layer_t<bf16>(c, w, l, sg, M, normed_in, next, ws, side, s);
+  return layer_t<float>(c, w, l, sg, M, normed_in, next, ws, side, s);
 }
 int layer(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int64_t pos0, int64_t M, int64_t n_causal,
-          bool normed_in, Next next, const Ws& ws, hipStream_t s) {
-  return layer(c, w, l, one_seq(kv, pos0, M, n_causal), M, normed_in, next, ws, s);
+          bool normed_in, Next next, const Ws& ws, const dg_side* side, hipStream_t s) {
+  return layer(c, w, l, one_seq(kv, pos0, M, n_causal), M, normed_in, next, ws, side, s);
 }
 
 // rows [row0, row0 + M) of ws.X = embeddings of tok[0, M)
@@ -482,12 +471,13 @@ int head(const dg_config* c, const dg_weights* w, int64_t M, const PassParams& p
 
 // denoising pass with an already-validated configuration
 int denoise(const dg_config* c, const dg_weights* w, const dg_kv* kv, const int32_t* canvas, const PassParams& pp,
-            int32_t* pred, float* conf, float* ent, const dg_debug* dbg, const Ws& ws, hipStream_t s) {
+            int32_t* pred, float* conf, float* ent, const dg_debug* dbg, const Ws& ws, const dg_side* side,
+            hipStream_t s) {
   const int64_t S = c->canvas;
   DG_CHECK(embed(c, w, canvas, S, ws, s));
   const int L = c->n_layers;
   for (int l = 0; l < L; ++l) {
-    DG_CHECK(layer(c, w, l, kv, kv->len, S, 0, l > 0, l + 1 < L ? Next::NextLayer : Next::Head, ws, s));
+    DG_CHECK(layer(c, w, l, kv, kv->len, S, 0, l > 0, l + 1 < L ? Next::NextLayer : Next::Head, ws, side, s));
     if (dbg) {
       const size_t hb = (size_t)S * c->d_model * esize(c);
       if (dbg->hidden) DG_TRY(hipMemcpyAsync((char*)dbg->hidden + l * hb, ws.X, hb, hipMemcpyDeviceToDevice, s));
@@ -509,19 +499,19 @@ int denoise(const dg_config* c, const dg_weights* w, const dg_kv* kv, const int3
 // caller advances kv->len by S afterwards.
 int denoise_committing(const dg_config* c, const dg_weights* w, const dg_kv* kv, const int32_t* block_tokens,
                        const int32_t* canvas, const PassParams& pp, int32_t* pred, float* conf, float* ent, const Ws& ws,
-                       hipStream_t s) {
+                       const dg_side* side, hipStream_t s) {
   const int64_t S = c->canvas;
   DG_CHECK(embed(c, w, block_tokens, S, ws, s, 0));
   DG_CHECK(embed(c, w, canvas, S, ws, s, S));
   const int L = c->n_layers;
   for (int l = 0; l < L; ++l)
-    DG_CHECK(layer(c, w, l, kv, kv->len, 2 * S, S, l > 0, l + 1 < L ? Next::NextLayer : Next::Head, ws, s));
+    DG_CHECK(layer(c, w, l, kv, kv->len, 2 * S, S, l > 0, l + 1 < L ? Next::NextLayer : Next::Head, ws, side, s));
   return head(c, w, S, pp, pred, conf, ent, L > 0, ws, s, S);
 }
 
 // causal forward of n tokens at kv->len.., chunked to the workspace; does not change kv->len
 int prefill(const dg_config* c, const dg_weights* w, const dg_kv* kv, const int32_t* tokens, int64_t n, void* wsp,
-            size_t ws_bytes, hipStream_t s) {
+            size_t ws_bytes, const dg_side* side, hipStream_t s) {
   const int64_t chunk = rows_supported(c, ws_bytes, moe_max_rows(c->n_experts));
   if (chunk < 1) return DG_ERR_WORKSPACE;
   for (int64_t r0 = 0; r0 < n; r0 += chunk) {
@@ -530,7 +520,7 @@ int prefill(const dg_config* c, const dg_weights* w, const dg_kv* kv, const int3
     DG_CHECK(embed(c, w, tokens + r0, m, ws, s));
     const int L = c->n_layers;
     for (int l = 0; l < L; ++l)
-      DG_CHECK(layer(c, w, l, kv, kv->len + r0, m, m, l > 0, l + 1 < L ? Next::NextLayer : Next::None, ws, s));
+      DG_CHECK(layer(c, w, l, kv, kv->len + r0, m, m, l > 0, l + 1 < L ? Next::NextLayer : Next::None, ws, side, s));
   }
   return DG_OK;
 }
@@ -575,43 +565,46 @@ int dg_workspace_size(const dg_config* cfg, int64_t max_tokens, size_t* h_bytes)
 }
 
 int dg_prefill_kv(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const int32_t* tokens, int64_t n, void* ws,
-                  size_t ws_bytes, void* stream) {
+                  size_t ws_bytes, const dg_side* side, void* stream) {
   DG_CHECK(check_cfg(cfg));
+  DG_CHECK(check_side(side));
   DG_CHECK(check_weights(cfg, w, true, false));
   if (n < 0 || (n > 0 && !tokens)) return DG_ERR_INVALID;
   DG_CHECK(check_kv(kv, n));
   if (n == 0) return DG_OK;
   if (!ws || ((uintptr_t)ws & 255u) || rows_supported(cfg, ws_bytes, 1) < 1) return DG_ERR_WORKSPACE;
-  DG_CHECK(prefill(cfg, w, kv, tokens, n, ws, ws_bytes, (hipStream_t)stream));
+  DG_CHECK(prefill(cfg, w, kv, tokens, n, ws, ws_bytes, side, (hipStream_t)stream));
   kv->len += n;
   return DG_OK;
 }
 
 int dg_denoise_step(const dg_config* cfg, const dg_weights* w, const dg_kv* kv, const int32_t* canvas,
                     float inv_temperature, int32_t* pred, float* conf, float* entropy, const dg_debug* dbg, void* ws,
-                    size_t ws_bytes, void* stream) {
+                    size_t ws_bytes, const dg_side* side, void* stream) {
   DG_CHECK(check_cfg(cfg));
+  DG_CHECK(check_side(side));
   DG_CHECK(check_weights(cfg, w, true, true));
   if (!canvas || !pred || !conf || !entropy) return DG_ERR_INVALID;
   if (!(inv_temperature > 0.f)) return DG_ERR_INVALID;
   DG_CHECK(check_kv(kv, cfg->canvas));
   DG_CHECK(check_ws(cfg, cfg->canvas, ws, ws_bytes));
   Ws wsv = carve(cfg, cfg->canvas, (char*)ws);
-  return denoise(cfg, w, kv, canvas, argmax_pass(inv_temperature), pred, conf, entropy, dbg, wsv,
+  return denoise(cfg, w, kv, canvas, argmax_pass(inv_temperature), pred, conf, entropy, dbg, wsv, side,
                  (hipStream_t)stream);
 }
 
 int dg_denoise_step_sampler(const dg_config* cfg, const dg_weights* w, const dg_kv* kv, const dg_sampler* sampler,
                             uint32_t block, int32_t step, const int32_t* canvas, int32_t* pred, float* conf,
-                            float* entropy, void* ws, size_t ws_bytes, void* stream) {
+                            float* entropy, void* ws, size_t ws_bytes, const dg_side* side, void* stream) {
   DG_CHECK(check_cfg(cfg));
+  DG_CHECK(check_side(side));
   DG_CHECK(check_weights(cfg, w, true, true));
   DG_CHECK(check_sampler(cfg, sampler));
   if (!canvas || !pred || !conf || !entropy || step < 1 || step > 65535) return DG_ERR_INVALID;
   DG_CHECK(check_kv(kv, cfg->canvas));
   DG_CHECK(check_ws(cfg, cfg->canvas, ws, ws_bytes));
   Ws wsv = carve(cfg, cfg->canvas, (char*)ws);
-  return denoise(cfg, w, kv, canvas, sampler_pass(sampler, block, step), pred, conf, entropy, nullptr, wsv,
+  return denoise(cfg, w, kv, canvas, sampler_pass(sampler, block, step), pred, conf, entropy, nullptr, wsv, side,
                  (hipStream_t)stream);
 }
 
@@ -643,19 +636,21 @@ int dg_canvas_update_sampler(const dg_config* cfg, const dg_sampler* sampler, ui
 }
 
 int dg_commit_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const int32_t* block_tokens, void* ws,
-                    size_t ws_bytes, void* stream) {
-  return dg_prefill_kv(cfg, w, kv, block_tokens, cfg ? cfg->canvas : 0, ws, ws_bytes, stream);
+                    size_t ws_bytes, const dg_side* side, void* stream) {
+  return dg_prefill_kv(cfg, w, kv, block_tokens, cfg ? cfg->canvas : 0, ws, ws_bytes, side, stream);
 }
 
 int dg_generate_block_overlapped(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const dg_sampler* sp,
                                  uint32_t block, const int32_t* pending, int32_t defer_commit, int32_t* tokens_out,
-                                 dg_block_status* h_status, void* ws, size_t ws_bytes, void* stream) {
+                                 dg_block_status* h_status, void* ws, size_t ws_bytes, const dg_side* side, void* stream) {
   DG_CHECK(check_cfg(cfg));
+  DG_CHECK(check_side(side));
   DG_CHECK(check_weights(cfg, w, true, true));
   DG_CHECK(check_sampler(cfg, sp));
   if (!tokens_out || !h_status || (defer_commit != 0 && defer_commit != 1)) return DG_ERR_INVALID;
   const int S = cfg->canvas;
   const int64_t rows = pending ? 2 * (int64_t)S : S;  // the first pass also commits `pending`
+  if (rows > moe_max_rows(cfg->n_experts)) return DG_ERR_INVALID;  // rows one routing step orders
   DG_CHECK(check_kv(kv, rows));
   DG_CHECK(check_ws(cfg, rows, ws, ws_bytes));
   hipStream_t s = (hipStream_t)stream;
@@ -673,10 +668,10 @@ int dg_generate_block_overlapped(const dg_config* cfg, const dg_weights* w, dg_k
   for (int t = 1;; ++t) {
     const PassParams pp = sampler_pass(sp, block, t);
     if (t == 1 && pending) {
-      DG_CHECK(denoise_committing(cfg, w, kv, pending, wsv.canvas, pp, wsv.pred, wsv.conf, wsv.ent, wsv, s));
+      DG_CHECK(denoise_committing(cfg, w, kv, pending, wsv.canvas, pp, wsv.pred, wsv.conf, wsv.ent, wsv, side, s));
       kv->len += S;  // the pending block is committed (in stream order) before every later pass
     } else {
-      DG_CHECK(denoise(cfg, w, kv, wsv.canvas, pp, wsv.pred, wsv.conf, wsv.ent, nullptr, wsv, s));
+      DG_CHECK(denoise(cfg, w, kv, wsv.canvas, pp, wsv.pred, wsv.conf, wsv.ent, nullptr, wsv, side, s));
     }
     DG_LAUNCH(DG_K_STOP_CHECK, s,
               launch_stop_check(wsv.ent, wsv.pred, wsv.prev_pred, wsv.canvas, lock_mask, S, t, stp, wsv.status, s));
@@ -698,7 +693,7 @@ int dg_generate_block_overlapped(const dg_config* cfg, const dg_weights* w, dg_k
   // read the status before the commit reuses the workspace
   if (fixed) DG_TRY(hipMemcpyAsync(&st, wsv.status, sizeof(st), hipMemcpyDeviceToHost, s));
   if (!defer_commit) {
-    DG_CHECK(prefill(cfg, w, kv, tokens_out, S, ws, ws_bytes, s));
+    DG_CHECK(prefill(cfg, w, kv, tokens_out, S, ws, ws_bytes, side, s));
     kv->len += S;
   }
   DG_TRY(hipStreamSynchronize(s));
@@ -707,15 +702,17 @@ int dg_generate_block_overlapped(const dg_config* cfg, const dg_weights* w, dg_k
 }
 
 int dg_generate_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const dg_sampler* sp, uint32_t block,
-                      int32_t* tokens_out, dg_block_status* h_status, void* ws, size_t ws_bytes, void* stream) {
-  return dg_generate_block_overlapped(cfg, w, kv, sp, block, nullptr, 0, tokens_out, h_status, ws, ws_bytes, stream);
+                      int32_t* tokens_out, dg_block_status* h_status, void* ws, size_t ws_bytes, const dg_side* side, void* stream) {
+  return dg_generate_block_overlapped(cfg, w, kv, sp, block, nullptr, 0, tokens_out, h_status, ws, ws_bytes, side,
+                                      stream);
 }
 
 int dg_generate_blocks_overlapped(const dg_config* cfg, const dg_weights* w, dg_kv* kvs, int32_t n_seq,
                                   const dg_sampler* sp, const uint32_t* h_blocks, const int32_t* pending,
                                   int32_t defer_commit, int32_t* tokens_out, dg_block_status* h_status, void* ws,
-                                  size_t ws_bytes, void* stream) {
+                                  size_t ws_bytes, const dg_side* side, void* stream) {
   DG_CHECK(check_cfg(cfg));
+  DG_CHECK(check_side(side));
   DG_CHECK(check_weights(cfg, w, true, true));
   DG_CHECK(check_sampler(cfg, sp));
   if (!kvs || !h_blocks || !tokens_out || !h_status || n_seq < 1 || n_seq > kMaxSeq) return DG_ERR_INVALID;
@@ -762,7 +759,7 @@ int dg_generate_blocks_overlapped(const dg_config* cfg, const dg_weights* w, dg_
         DG_CHECK(embed(cfg, w, wsv.canvas + (size_t)b * S, S, wsv, s, (2 * (int64_t)b + 1) * S));
       }
       for (int l = 0; l < L; ++l)
-        DG_CHECK(layer(cfg, w, l, pg, rows, l > 0, l + 1 < L ? Next::NextLayer : Next::Head, wsv, s));
+        DG_CHECK(layer(cfg, w, l, pg, rows, l > 0, l + 1 < L ? Next::NextLayer : Next::Head, wsv, side, s));
       for (int b = 0; b < n_seq; ++b)
         DG_CHECK(head(cfg, w, S, sampler_pass(sp, h_blocks[b], t), wsv.pred + (size_t)b * S, wsv.conf + (size_t)b * S,
                       wsv.ent + (size_t)b * S, L > 0, wsv, s, (2 * (int64_t)b + 1) * S));
@@ -774,7 +771,7 @@ int dg_generate_blocks_overlapped(const dg_config* cfg, const dg_weights* w, dg_
       // one pass over every canvas; a finished canvas still runs (its rows are ignored from then on)
       DG_CHECK(embed(cfg, w, wsv.canvas, M, wsv, s));
       for (int l = 0; l < L; ++l)
-        DG_CHECK(layer(cfg, w, l, sg, M, l > 0, l + 1 < L ? Next::NextLayer : Next::Head, wsv, s));
+        DG_CHECK(layer(cfg, w, l, sg, M, l > 0, l + 1 < L ? Next::NextLayer : Next::Head, wsv, side, s));
       if (!draw) {
         DG_CHECK(head(cfg, w, M, sampler_pass(sp, 0, t), wsv.pred, wsv.conf, wsv.ent, L > 0, wsv, s));
       } else {  // each canvas draws with its own block's counters
@@ -823,7 +820,7 @@ int dg_generate_blocks_overlapped(const dg_config* cfg, const dg_weights* w, dg_
     Segs cg = sg;
     for (int b = 0; b < n_seq; ++b) cg.seg[b].n_causal = S;
     for (int l = 0; l < L; ++l)
-      DG_CHECK(layer(cfg, w, l, cg, M, l > 0, l + 1 < L ? Next::NextLayer : Next::None, wsv, s));
+      DG_CHECK(layer(cfg, w, l, cg, M, l > 0, l + 1 < L ? Next::NextLayer : Next::None, wsv, side, s));
   }
   DG_TRY(hipStreamSynchronize(s));
   for (int b = 0; b < n_seq; ++b) {
@@ -835,14 +832,15 @@ int dg_generate_blocks_overlapped(const dg_config* cfg, const dg_weights* w, dg_
 
 int dg_generate_blocks(const dg_config* cfg, const dg_weights* w, dg_kv* kvs, int32_t n_seq, const dg_sampler* sp,
                        const uint32_t* h_blocks, int32_t* tokens_out, dg_block_status* h_status, void* ws,
-                       size_t ws_bytes, void* stream) {
+                       size_t ws_bytes, const dg_side* side, void* stream) {
   return dg_generate_blocks_overlapped(cfg, w, kvs, n_seq, sp, h_blocks, nullptr, 0, tokens_out, h_status, ws,
-                                       ws_bytes, stream);
+                                       ws_bytes, side, stream);
 }
 
 int dg_verify_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const int32_t* draft, int32_t* ar_pred,
-                    int32_t* h_accepted, int32_t* h_next_token, void* ws, size_t ws_bytes, void* stream) {
+                    int32_t* h_accepted, int32_t* h_next_token, void* ws, size_t ws_bytes, const dg_side* side, void* stream) {
   DG_CHECK(check_cfg(cfg));
+  DG_CHECK(check_side(side));
   DG_CHECK(check_weights(cfg, w, true, true));
   if (!draft || !ar_pred || !h_accepted || !h_next_token) return DG_ERR_INVALID;
   const int S = cfg->canvas;
@@ -854,7 +852,7 @@ int dg_verify_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const 
   DG_CHECK(embed(cfg, w, draft, S, wsv, s));
   const int L = cfg->n_layers;
   for (int l = 0; l < L; ++l)
-    DG_CHECK(layer(cfg, w, l, kv, kv->len, S, S, l > 0, l + 1 < L ? Next::NextLayer : Next::Head, wsv, s));
+    DG_CHECK(layer(cfg, w, l, kv, kv->len, S, S, l > 0, l + 1 < L ? Next::NextLayer : Next::Head, wsv, side, s));
   DG_CHECK(head(cfg, w, S, argmax_pass(1.0f), ar_pred, wsv.conf, wsv.ent, L > 0, wsv, s));
   std::vector<int32_t> hp(S), hd(S);
   DG_TRY(hipMemcpyAsync(hp.data(), ar_pred, (size_t)S * 4, hipMemcpyDeviceToHost, s));
@@ -870,8 +868,9 @@ int dg_verify_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const 
 
 int dg_layer_forward(const dg_config* cfg, const dg_weights* w, int32_t layer_i, const dg_kv* kv, const void* x_in,
                      void* x_out, int64_t n, int32_t causal, const dg_debug* dbg, void* ws, size_t ws_bytes,
-                     void* stream) {
+                     const dg_side* side, void* stream) {
   DG_CHECK(check_cfg(cfg));
+  DG_CHECK(check_side(side));
   if (!w || !w->h_layers || layer_i < 0 || layer_i >= cfg->n_layers) return DG_ERR_INVALID;
   DG_CHECK(check_layer_weights(w->h_layers[layer_i]));
   if (!aligned16(x_in) || !aligned16(x_out) || n < 1 || n > moe_max_rows(cfg->n_experts)) return DG_ERR_INVALID;
@@ -882,7 +881,7 @@ int dg_layer_forward(const dg_config* cfg, const dg_weights* w, int32_t layer_i,
   Ws wsv = carve(cfg, n, (char*)ws);
   const size_t hb = (size_t)n * cfg->d_model * esize(cfg);
   DG_TRY(hipMemcpyAsync(wsv.X, x_in, hb, hipMemcpyDeviceToDevice, s));
-  DG_CHECK(layer(cfg, w, layer_i, kv, kv->len, n, causal != 0 ? n : 0, false, Next::None, wsv, s));
+  DG_CHECK(layer(cfg, w, layer_i, kv, kv->len, n, causal != 0 ? n : 0, false, Next::None, wsv, side, s));
   DG_TRY(hipMemcpyAsync(x_out, wsv.X, hb, hipMemcpyDeviceToDevice, s));
   if (dbg) {
     const size_t rb = (size_t)n * cfg->top_k * 4;
@@ -945,6 +944,40 @@ int dg_stop_check(const dg_config* cfg, const dg_sampler* sampler, int32_t step,
   DG_LAUNCH(DG_K_STOP_CHECK, (hipStream_t)stream,
             launch_stop_check(entropy, pred, prev_pred, lock ? canvas : nullptr, lock ? lock_mask : nullptr,
                               cfg->canvas, step, stop_params(cfg, sampler), d_status, (hipStream_t)stream));
+  return DG_OK;
+}
+
+int dg_side_create(dg_side* h_side) {
+  if (!h_side) return DG_ERR_INVALID;
+  *h_side = dg_side{nullptr, nullptr, nullptr};
+  hipStream_t st = nullptr;
+  hipEvent_t f = nullptr, j = nullptr;
+  hipError_t e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);  // default priority
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&f, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&j, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    if (j) (void)hipEventDestroy(j);
+    if (f) (void)hipEventDestroy(f);
+    if (st) (void)hipStreamDestroy(st);
+    g_hip_error = (int)e;
+    return DG_ERR_HIP;
+  }
+  *h_side = dg_side{st, f, j};
+  return DG_OK;
+}
+
+int dg_side_destroy(dg_side* h_side) {
+  if (!h_side) return DG_ERR_INVALID;
+  hipError_t e = hipSuccess, r;
+  if (h_side->stream && (r = hipStreamSynchronize((hipStream_t)h_side->stream)) != hipSuccess) e = r;
+  if (h_side->join && (r = hipEventDestroy((hipEvent_t)h_side->join)) != hipSuccess) e = r;
+  if (h_side->fork && (r = hipEventDestroy((hipEvent_t)h_side->fork)) != hipSuccess) e = r;
+  if (h_side->stream && (r = hipStreamDestroy((hipStream_t)h_side->stream)) != hipSuccess) e = r;
+  *h_side = dg_side{nullptr, nullptr, nullptr};
+  if (e != hipSuccess) {
+    g_hip_error = (int)e;
+    return DG_ERR_HIP;
+  }
   return DG_OK;
 }
 

@@ -581,6 +581,9 @@ hipError_t launch_rmsnorm(const T* X, const T* g, T* Y, T* Yt, int M, int d, flo
 template <typename T>
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.M <= 0) return hipSuccess;
+  // the ordering workgroup's LDS holds kRouteMaxRows rows and one mask per (expert, 64-token chunk)
+  if (a.M > kRouteMaxRows || a.E * ((a.M + 63) / 64) > kRouteMasks || a.E > 256 || a.k > 16)
+    return hipErrorInvalidValue;
   const int nt = route_tiles(a.E), slices = (a.E + 16 * nt - 1) / (16 * nt);
   const dim3 grid(((a.M + 15) / 16) * slices), block(64 * kRouteWaves);
   if (nt == 4)

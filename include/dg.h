@@ -11,11 +11,11 @@
  *
  * Conventions for every call
  *   - Pointers are DEVICE pointers unless the name starts with h_.
- *   - The caller owns all memory (weights, KV cache, inputs, outputs, workspace);
- *     the library never allocates device memory.  Its only state is, per (device,
- *     caller stream), one side stream and two events, created on first use and kept
- *     for the life of the process: each layer's shared expert runs on the side
- *     stream, concurrent with the routed experts, and joins before the combine.
+ *   - The caller owns all memory (weights, KV cache, inputs, outputs, workspace)
+ *     and every stream and event; the library never allocates device memory and
+ *     keeps no device state beyond its loaded code objects.  Calls that run layers
+ *     take an optional caller-owned dg_side (below) for the shared expert's
+ *     concurrency.
  *     Calls on one caller stream must be issued from one host thread at a time.
  *   - Calls are stream-ordered and return after enqueueing on `stream` (a
  *     hipStream_t passed as void*; NULL = the default stream).  Exceptions:
@@ -137,6 +137,32 @@ typedef struct dg_kv {
   int64_t capacity;
 } dg_kv;
 
+/* Caller-owned concurrency for the shared expert.  Each layer's shared expert reads only
+ * the FFN-normalised rows ([P2] "Architecture Details": one shared expert beside the 8
+ * routed ones), so it can run on a second stream while the caller's stream does the
+ * routing and the routed experts; the two join before the combine.  stream: a hipStream_t
+ * other than the caller's; fork, join: two distinct hipEvent_t (timing may be disabled).
+ * Every call that runs layers takes a `const dg_side* side` before its stream: NULL (or a
+ * NULL side->stream) runs the shared expert on the caller's stream, with the same results
+ * bit for bit.  One dg_side serves one caller stream at a time.  The library keeps no
+ * reference to it after a call returns; the caller destroys it once the work that used it
+ * has completed.  DG_ERR_INVALID when side->stream is set and an event is NULL or the two
+ * events are the same. */
+typedef struct dg_side {
+  void* stream;
+  void* fork;
+  void* join;
+} dg_side;
+
+/* Convenience for callers: create a non-blocking stream of default priority and two events
+ * with timing disabled on the current device into *h_side (all NULL on failure,
+ * DG_ERR_HIP).  The caller owns them. */
+int dg_side_create(dg_side* h_side);
+
+/* Wait for h_side->stream, destroy the stream and events and clear *h_side.  Also accepts
+ * a side made by the caller's own HIP calls. */
+int dg_side_destroy(dg_side* h_side);
+
 /* Sampler variants (dg_sampler.flags), each off by default.  Together they give the
  * recommended sampler of [P2] "Architecture Details" (temperature falling linearly
  * from 0.8 to 0.4 over the passes, lowest-entropy tokens locked first, stop when
@@ -232,7 +258,7 @@ int dg_workspace_size(const dg_config* cfg, int64_t max_tokens, size_t* h_bytes)
  * autoregressive pass caches the prompt context).  Query i sees cache rows
  * 0 .. kv->len + i.  Tokens outside [0, vocab) are clamped into range. */
 int dg_prefill_kv(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const int32_t* tokens, int64_t n,
-                  void* ws, size_t ws_bytes, void* stream);
+                  void* ws, size_t ws_bytes, const dg_side* side, void* stream);
 
 /* One denoising pass over the canvas ([P2] "How Diffusion Changes the Equation":
  * bidirectional attention over the whole block; [P5] "How block diffusion works"):
@@ -245,7 +271,7 @@ int dg_prefill_kv(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const in
  * kv->len + canvas <= capacity.  inv_temperature multiplies the logits. */
 int dg_denoise_step(const dg_config* cfg, const dg_weights* w, const dg_kv* kv, const int32_t* canvas,
                     float inv_temperature, int32_t* pred, float* conf, float* entropy, const dg_debug* dbg,
-                    void* ws, size_t ws_bytes, void* stream);
+                    void* ws, size_t ws_bytes, const dg_side* side, void* stream);
 
 /* Pass `step` (1-based, < 65536) of block `block` as dg_generate_block runs it under
  * `sampler` ([P2] "Architecture Details"): dg_denoise_step at that pass's temperature,
@@ -254,7 +280,7 @@ int dg_denoise_step(const dg_config* cfg, const dg_weights* w, const dg_kv* kv, 
  * dg_denoise_step; DG_ERR_INVALID also for an invalid sampler or step. */
 int dg_denoise_step_sampler(const dg_config* cfg, const dg_weights* w, const dg_kv* kv, const dg_sampler* sampler,
                             uint32_t block, int32_t step, const int32_t* canvas, int32_t* pred, float* conf,
-                            float* entropy, void* ws, size_t ws_bytes, void* stream);
+                            float* entropy, void* ws, size_t ws_bytes, const dg_side* side, void* stream);
 
 /* Canvas update ([P5] "How block diffusion works": keep the most confident slots,
  * re-randomise the others; any slot may change on a later pass).  The keep_count
@@ -285,7 +311,7 @@ int dg_canvas_update_sampler(const dg_config* cfg, const dg_sampler* sampler, ui
  * generation differs").  Same as dg_prefill_kv of the canvas tokens: a causal
  * forward at positions kv->len .. kv->len+canvas-1; on success kv->len += canvas. */
 int dg_commit_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const int32_t* block_tokens,
-                    void* ws, size_t ws_bytes, void* stream);
+                    void* ws, size_t ws_bytes, const dg_side* side, void* stream);
 
 /* One whole block: initial random canvas, passes t = 1, 2, ... each followed by
  * the stop check and, if not stopping, the canvas update with k_t; then the last
@@ -295,7 +321,7 @@ int dg_commit_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const 
  * fixed mode (sampler->fixed_steps > 0) synchronises once at the end. */
 int dg_generate_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const dg_sampler* sampler,
                       uint32_t block, int32_t* tokens_out, dg_block_status* h_status, void* ws,
-                      size_t ws_bytes, void* stream);
+                      size_t ws_bytes, const dg_side* side, void* stream);
 
 /* dg_generate_block with each commit overlapped on the next block's first pass.  The commit
  * and a pass are both a forward of 256 rows through every layer, and the expert and head
@@ -308,13 +334,14 @@ int dg_generate_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, cons
  * as `pending` to the next call or commit them with dg_commit_block.  pending may alias
  * tokens_out (it is read in the first pass, before tokens_out is written).  With pending,
  * the workspace and the cache must hold 2 * canvas rows (dg_workspace_size(cfg, 2 * canvas,
- * ...); kv->len + 2 * canvas <= capacity).  The tokens and cache equal those of
+ * ...); kv->len + 2 * canvas <= capacity), and 2 * canvas must not exceed the rows one
+ * routing step orders, min(2048, 64 * (4096 / n_experts)) (else DG_ERR_INVALID).  The tokens and cache equal those of
  * dg_generate_block on the same blocks up to the summation order of the attention splits.
  * Errors as dg_generate_block; DG_ERR_INVALID also for defer_commit not 0 or 1. */
 int dg_generate_block_overlapped(const dg_config* cfg, const dg_weights* w, dg_kv* kv,
                                  const dg_sampler* sampler, uint32_t block, const int32_t* pending,
                                  int32_t defer_commit, int32_t* tokens_out, dg_block_status* h_status,
-                                 void* ws, size_t ws_bytes, void* stream);
+                                 void* ws, size_t ws_bytes, const dg_side* side, void* stream);
 
 /* Blocks of n_seq independent sequences at once (batch > 1 canvases; [P2] "Benchmark Numbers"
  * runs batch 4).  Sequence b has its own cache kvs[b] (host array of n_seq caches, no two sharing
@@ -330,7 +357,7 @@ int dg_generate_block_overlapped(const dg_config* cfg, const dg_weights* w, dg_k
  * dg_generate_block. */
 int dg_generate_blocks(const dg_config* cfg, const dg_weights* w, dg_kv* kvs, int32_t n_seq,
                        const dg_sampler* sampler, const uint32_t* h_blocks, int32_t* tokens_out,
-                       dg_block_status* h_status, void* ws, size_t ws_bytes, void* stream);
+                       dg_block_status* h_status, void* ws, size_t ws_bytes, const dg_side* side, void* stream);
 
 /* dg_generate_blocks with each sequence's commit carried by the next call's first pass, as
  * dg_generate_block_overlapped does for one sequence.  pending (nullable, device [n_seq][canvas]):
@@ -344,7 +371,7 @@ int dg_generate_blocks(const dg_config* cfg, const dg_weights* w, dg_kv* kvs, in
 int dg_generate_blocks_overlapped(const dg_config* cfg, const dg_weights* w, dg_kv* kvs, int32_t n_seq,
                                   const dg_sampler* sampler, const uint32_t* h_blocks, const int32_t* pending,
                                   int32_t defer_commit, int32_t* tokens_out, dg_block_status* h_status,
-                                  void* ws, size_t ws_bytes, void* stream);
+                                  void* ws, size_t ws_bytes, const dg_side* side, void* stream);
 
 /* Self-speculative verify of a drafted block ([P1] "The result that complicates 'faster, not
  * smarter'": one set of weights drafts a block bidirectionally and verifies it causally over the
@@ -357,7 +384,7 @@ int dg_generate_blocks_overlapped(const dg_config* cfg, const dg_weights* w, dg_
  * position not accepted.  kv->len grows by the count; the cache rows past it are scratch.  Needs
  * kv->len + canvas <= capacity and a workspace of canvas rows; synchronises `stream` once. */
 int dg_verify_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const int32_t* draft, int32_t* ar_pred,
-                    int32_t* h_accepted, int32_t* h_next_token, void* ws, size_t ws_bytes, void* stream);
+                    int32_t* h_accepted, int32_t* h_next_token, void* ws, size_t ws_bytes, const dg_side* side, void* stream);
 
 /* --- finer-grained calls of the same path (each is one stage of dg_denoise_step) --- */
 
@@ -371,7 +398,7 @@ int dg_verify_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const 
  * (x_out already holds the result). */
 int dg_layer_forward(const dg_config* cfg, const dg_weights* w, int32_t layer, const dg_kv* kv,
                      const void* x_in, void* x_out, int64_t n, int32_t causal, const dg_debug* dbg, void* ws,
-                     size_t ws_bytes, void* stream);
+                     size_t ws_bytes, const dg_side* side, void* stream);
 
 /* Final RMSNorm + tied vocab projection fused with the per-slot softmax
  * statistics: for each of n rows, pred/conf/entropy as in dg_denoise_step.  The

@@ -31,6 +31,9 @@ class Session:
         self.ws_bytes = dg.dg_workspace_size(self.cfg, mt)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
         self.S = d.canvas
+        # the shared expert's side stream and events (caller-owned); passes and prefills made through the session
+        # run the shared expert concurrently, as the benchmark does
+        self.side = dg.Side()
 
     def i32(self, n):
         return torch.empty(n, dtype=torch.int32, device="cuda")
@@ -40,13 +43,13 @@ class Session:
 
     def prefill(self, tokens: np.ndarray):
         t = torch.from_numpy(np.asarray(tokens, dtype=np.int32)).cuda()
-        dg.dg_prefill_kv(self.cfg, self.weights, self.kv, t, len(tokens), self.ws, self.ws_bytes)
+        dg.dg_prefill_kv(self.cfg, self.weights, self.kv, t, len(tokens), self.ws, self.ws_bytes, side=self.side)
 
     def denoise(self, canvas, dbg=None, inv_temperature=1.0):
         c = canvas if torch.is_tensor(canvas) else torch.from_numpy(np.asarray(canvas, dtype=np.int32)).cuda()
         pred, conf, ent = self.i32(self.S), self.f32(self.S), self.f32(self.S)
         dg.dg_denoise_step(self.cfg, self.weights, self.kv, c, inv_temperature, pred, conf, ent, dbg, self.ws,
-                           self.ws_bytes)
+                           self.ws_bytes, side=self.side)
         return pred, conf, ent
 
     def kv_numpy(self, layer: int, length: int):
@@ -102,3 +105,40 @@ def compare_routing(g_idx: np.ndarray, g_w: np.ndarray, g_logits: np.ndarray, o_
         full[np.nonzero(rows)[0]] = same
         return full
     return same
+
+
+# ----------------------------------------------------------------------------- teacher-forced oracle checks
+
+def gpu_cache_as_oracle(sess: Session, n_rows: int):
+    """The GPU's first n_rows cache rows of every layer as an oracle KVCache (the teacher-forced context)."""
+    from oracle import model as om
+    kv = om.KVCache(sess.d.n_layers, sess.d.n_kv_heads, sess.d.head_dim)
+    for l in range(sess.d.n_layers):
+        kv.k[l], kv.v[l] = sess.kv_numpy(l, n_rows)
+    return kv
+
+
+def check_pass_on_gpu_cache(model, kv, canvas, tokens, mean_entropy, tol, margin=1e-2) -> int:
+    """The oracle's pass over `canvas` with the cache `kv` against a GPU pass's tokens (compared where the
+    oracle's top-2 margin exceeds `margin`) and mean entropy (within tol).  Returns the slots compared."""
+    from oracle import sampler as osm
+    rec, _ = osm.denoise_pass(model, kv, canvas)
+    sel = rec.margin > margin
+    bad = np.nonzero(sel & (np.asarray(tokens) != rec.pred))[0]
+    assert bad.size == 0, f"tokens differ away from a near-tie at slots {bad[:10]}"
+    ref = float(np.mean(rec.ent))
+    assert abs(mean_entropy - ref) <= tol[0] + tol[1] * abs(ref), (mean_entropy, ref)
+    return int(sel.sum())
+
+
+def check_commit_on_gpu_cache(model, kv, tokens, sess: Session, tol):
+    """Commit `tokens` in the oracle after the cache `kv` (the GPU's rows before them) and compare the rows it
+    appends with the GPU's cache rows at the same positions, every layer."""
+    from oracle import sampler as osm
+    r0 = kv.length
+    osm.commit(model, kv, np.asarray(tokens, dtype=np.int64))
+    for l in range(sess.d.n_layers):
+        gk, gv = sess.kv_numpy(l, kv.length)
+        rk = allclose_report(gk[:, r0:], kv.k[l][:, r0:], *tol)
+        rv = allclose_report(gv[:, r0:], kv.v[l][:, r0:], *tol)
+        assert rk[0] and rv[0], (l, rk, rv)

@@ -55,7 +55,7 @@ def test_struct_layouts_match_header():
     src = ('#include <stdio.h>\n#include <stddef.h>\n#include "dg.h"\n'
            'int main(void){printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(dg_config), sizeof(dg_layer_weights),'
            ' sizeof(dg_weights), sizeof(dg_kv), sizeof(dg_sampler), offsetof(dg_sampler, seed),'
-           ' sizeof(dg_block_status), sizeof(dg_debug)); return 0;}\n')
+           ' sizeof(dg_block_status), sizeof(dg_debug)); printf("%zu\\n", sizeof(dg_side)); return 0;}\n')
     exe = "/tmp/dg_layout_probe"
     r = subprocess.run(["gcc", "-I", os.path.dirname(HEADER), "-x", "c", "-", "-o", exe], input=src,
                        capture_output=True, text=True)
@@ -63,7 +63,7 @@ def test_struct_layouts_match_header():
     got = [int(x) for x in subprocess.run([exe], capture_output=True, text=True).stdout.split()]
     exp = [ctypes.sizeof(dg.dg_config), ctypes.sizeof(dg.dg_layer_weights), ctypes.sizeof(dg.dg_weights),
            ctypes.sizeof(dg.dg_kv), ctypes.sizeof(dg.dg_sampler), dg.dg_sampler.seed.offset,
-           ctypes.sizeof(dg.dg_block_status), ctypes.sizeof(dg.dg_debug)]
+           ctypes.sizeof(dg.dg_block_status), ctypes.sizeof(dg.dg_debug), ctypes.sizeof(dg.dg_side)]
     assert got == exp
 
 
@@ -135,49 +135,49 @@ def test_calls_validate_before_any_device_work():
     ws_bytes = dg.dg_workspace_size(cfg, cfg.canvas)
     kv = dg.KV(buf, buf, capacity=96, length=80)  # 80 + 32 > 96
     with pytest.raises(dg.DGError) as e:
-        dg.dg_denoise_step(cfg, w, kv, buf, 1.0, buf, buf, buf, None, buf, ws_bytes, 0)
+        dg.dg_denoise_step(cfg, w, kv, buf, 1.0, buf, buf, buf, None, buf, ws_bytes, stream=0)
     assert e.value.status == dg.DG_ERR_KV_FULL
     kv = dg.KV(buf, buf, capacity=100, length=0)  # capacity not a multiple of 32
     with pytest.raises(dg.DGError) as e:
-        dg.dg_denoise_step(cfg, w, kv, buf, 1.0, buf, buf, buf, None, buf, ws_bytes, 0)
+        dg.dg_denoise_step(cfg, w, kv, buf, 1.0, buf, buf, buf, None, buf, ws_bytes, stream=0)
     assert e.value.status == dg.DG_ERR_INVALID
     kv = dg.KV(buf, buf, capacity=128, length=0)
     with pytest.raises(dg.DGError) as e:
-        dg.dg_denoise_step(cfg, w, kv, buf, 1.0, buf, buf, buf, None, buf, ws_bytes - 256, 0)
+        dg.dg_denoise_step(cfg, w, kv, buf, 1.0, buf, buf, buf, None, buf, ws_bytes - 256, stream=0)
     assert e.value.status == dg.DG_ERR_WORKSPACE
     with pytest.raises(dg.DGError) as e:
-        dg.dg_denoise_step(cfg, w, kv, None, 1.0, buf, buf, buf, None, buf, ws_bytes, 0)
+        dg.dg_denoise_step(cfg, w, kv, None, 1.0, buf, buf, buf, None, buf, ws_bytes, stream=0)
     assert e.value.status == dg.DG_ERR_INVALID
     with pytest.raises(dg.DGError) as e:
-        dg.dg_denoise_step(cfg, w, kv, buf, 0.0, buf, buf, buf, None, buf, ws_bytes, 0)
+        dg.dg_denoise_step(cfg, w, kv, buf, 0.0, buf, buf, buf, None, buf, ws_bytes, stream=0)
     assert e.value.status == dg.DG_ERR_INVALID
     with pytest.raises(dg.DGError) as e:   # misaligned weight pointer
         dg.dg_denoise_step(cfg, _fake_weights_misaligned(cfg.n_layers), kv, buf, 1.0, buf, buf, buf, None, buf,
-                           ws_bytes, 0)
+                           ws_bytes, stream=0)
     assert e.value.status == dg.DG_ERR_INVALID
     with pytest.raises(dg.DGError) as e:
-        dg.dg_prefill_kv(cfg, w, kv, buf, 200, buf, ws_bytes, 0)
+        dg.dg_prefill_kv(cfg, w, kv, buf, 200, buf, ws_bytes, stream=0)
     assert e.value.status == dg.DG_ERR_KV_FULL
     with pytest.raises(dg.DGError) as e:
-        dg.dg_layer_forward(cfg, w, 5, kv, buf, buf, 32, 0, None, buf, ws_bytes, 0)
+        dg.dg_layer_forward(cfg, w, 5, kv, buf, buf, 32, 0, None, buf, ws_bytes, stream=0)
     assert e.value.status == dg.DG_ERR_INVALID
     with pytest.raises(dg.DGError) as e:
-        dg.dg_layer_forward(cfg, w, 0, kv, buf, buf, 32, 2, None, buf, ws_bytes, 0)
+        dg.dg_layer_forward(cfg, w, 0, kv, buf, buf, 32, 2, None, buf, ws_bytes, stream=0)
     assert e.value.status == dg.DG_ERR_INVALID
     bad = dg.make_sampler(4)
     bad.max_steps = 0
     with pytest.raises(dg.DGError) as e:
-        dg.dg_generate_block(cfg, w, kv, bad, 0, buf, buf, ws_bytes, 0)
+        dg.dg_generate_block(cfg, w, kv, bad, 0, buf, buf, ws_bytes, stream=0)
     assert e.value.status == dg.DG_ERR_INVALID
     with pytest.raises(dg.DGError) as e:
-        dg.dg_generate_block_overlapped(cfg, w, kv, dg.make_sampler(4), 0, None, 2, buf, buf, ws_bytes, 0)
+        dg.dg_generate_block_overlapped(cfg, w, kv, dg.make_sampler(4), 0, None, 2, buf, buf, ws_bytes, stream=0)
     assert e.value.status == dg.DG_ERR_INVALID
     kv_short = dg.KV(buf, buf, capacity=64, length=16)  # 16 + 2 * 32 > 64: a pending block needs two canvases
     with pytest.raises(dg.DGError) as e:
-        dg.dg_generate_block_overlapped(cfg, w, kv_short, dg.make_sampler(4), 0, buf, 1, buf, buf, ws_bytes, 0)
+        dg.dg_generate_block_overlapped(cfg, w, kv_short, dg.make_sampler(4), 0, buf, 1, buf, buf, ws_bytes, stream=0)
     assert e.value.status == dg.DG_ERR_KV_FULL
     with pytest.raises(dg.DGError) as e:  # the workspace holds one canvas of rows, a pending block needs two
-        dg.dg_generate_block_overlapped(cfg, w, kv, dg.make_sampler(4), 0, buf, 1, buf, buf, ws_bytes, 0)
+        dg.dg_generate_block_overlapped(cfg, w, kv, dg.make_sampler(4), 0, buf, 1, buf, buf, ws_bytes, stream=0)
     assert e.value.status == dg.DG_ERR_WORKSPACE
     with pytest.raises(dg.DGError) as e:
         dg.dg_stop_check(cfg, dg.make_sampler(4), 0, buf, buf, buf, buf, stream=0)
@@ -257,7 +257,7 @@ def test_sampler_variants_validate():
             dg.dg_sampler_inv_temperature(sp, 1)
         assert e.value.status == dg.DG_ERR_INVALID
         with pytest.raises(dg.DGError) as e:
-            dg.dg_generate_block(cfg, w, kv, sp, 0, buf, buf, ws_bytes, 0)
+            dg.dg_generate_block(cfg, w, kv, sp, 0, buf, buf, ws_bytes, stream=0)
         assert e.value.status == dg.DG_ERR_INVALID
     ok = dg.make_sampler(4, flags=dg.DG_SAMPLE_ANNEAL | dg.DG_SAMPLE_GUMBEL, inv_temperature=0.0,
                          temperature_first=0.8, temperature_last=0.4)
@@ -272,7 +272,7 @@ def test_sampler_variants_validate():
                                             buf, None, 0),                                 # entropy ranking, no entropy
         lambda: dg.dg_canvas_update_sampler(cfg, dg.make_sampler(4), 0, 1, buf, buf, buf, None, None, 0),
         lambda: dg.dg_denoise_step_sampler(cfg, w, kv, dg.make_sampler(4), 0, 0, buf, buf, buf, buf, buf, ws_bytes,
-                                           0),                                             # passes count from 1
+                                           stream=0),                                             # passes count from 1
         lambda: dg.dg_vocab_head_sampler(cfg, w, dg.make_sampler(4), 0, 70000, buf, 4, buf, buf, buf, buf, ws_bytes,
                                          0),
     ]
@@ -292,12 +292,12 @@ def test_generate_blocks_validate():
     kvs = [dg.KV(_Fake(0x100000 * (i + 1)), _Fake(0x100000 * (i + 1) + 0x80000), capacity=128, length=0)
            for i in range(9)]
     cases = [
-        (lambda: dg.dg_generate_blocks(cfg, w, [], sp, [], buf, buf, ws1, 0), dg.DG_ERR_INVALID),        # no sequence
-        (lambda: dg.dg_generate_blocks(cfg, w, kvs, sp, list(range(9)), buf, buf, ws3, 0), dg.DG_ERR_INVALID),  # > 8
-        (lambda: dg.dg_generate_blocks(cfg, w, [kvs[0], kvs[0]], sp, [0, 1], buf, buf, ws3, 0), dg.DG_ERR_INVALID),
-        (lambda: dg.dg_generate_blocks(cfg, w, kvs[:3], sp, [0, 1, 2], buf, buf, ws1, 0), dg.DG_ERR_WORKSPACE),
+        (lambda: dg.dg_generate_blocks(cfg, w, [], sp, [], buf, buf, ws1, stream=0), dg.DG_ERR_INVALID),        # no sequence
+        (lambda: dg.dg_generate_blocks(cfg, w, kvs, sp, list(range(9)), buf, buf, ws3, stream=0), dg.DG_ERR_INVALID),  # > 8
+        (lambda: dg.dg_generate_blocks(cfg, w, [kvs[0], kvs[0]], sp, [0, 1], buf, buf, ws3, stream=0), dg.DG_ERR_INVALID),
+        (lambda: dg.dg_generate_blocks(cfg, w, kvs[:3], sp, [0, 1, 2], buf, buf, ws1, stream=0), dg.DG_ERR_WORKSPACE),
         (lambda: dg.dg_generate_blocks(cfg, w, kvs[:2] + [dg.KV(buf, buf, capacity=96, length=80)], sp, [0, 1, 2],
-                                       buf, buf, ws3, 0), dg.DG_ERR_KV_FULL),
+                                       buf, buf, ws3, stream=0), dg.DG_ERR_KV_FULL),
     ]
     for i, (c, status) in enumerate(cases):
         with pytest.raises(dg.DGError) as e:
@@ -305,11 +305,53 @@ def test_generate_blocks_validate():
         assert e.value.status == status, i
     assert [kv.len for kv in kvs] == [0] * 9
     with pytest.raises(dg.DGError) as e:
-        dg.dg_generate_blocks_overlapped(cfg, w, kvs[:2], sp, [0, 1], None, 2, buf, buf, ws3, 0)
+        dg.dg_generate_blocks_overlapped(cfg, w, kvs[:2], sp, [0, 1], None, 2, buf, buf, ws3, stream=0)
     assert e.value.status == dg.DG_ERR_INVALID
     with pytest.raises(dg.DGError) as e:  # a pending block doubles the rows of the first pass
-        dg.dg_generate_blocks_overlapped(cfg, w, kvs[:3], sp, [0, 1, 2], buf, 1, buf, buf, ws3, 0)
+        dg.dg_generate_blocks_overlapped(cfg, w, kvs[:3], sp, [0, 1, 2], buf, 1, buf, buf, ws3, stream=0)
     assert e.value.status == dg.DG_ERR_WORKSPACE
+
+
+def test_overlapped_pending_rows_within_routing_limit():
+    """A pending block doubles the first pass's rows; with 256 experts and a 1024-slot canvas that is 2048 rows,
+    beyond the 1024 one routing step orders for 256 experts: rejected before any device work, however large the
+    workspace."""
+    cfg = _cfg(n_experts=256, top_k=8, canvas=1024)
+    w = _fake_weights(cfg.n_layers)
+    buf = _Fake(0x20000)
+    kv = dg.KV(buf, buf, capacity=4096, length=0)
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_generate_block_overlapped(cfg, w, kv, dg.make_sampler(4), 0, buf, 1, buf, buf, 1 << 40, stream=0)
+    assert e.value.status == dg.DG_ERR_INVALID
+    assert kv.len == 0
+
+
+def test_side_validates():
+    """A dg_side with a stream needs two distinct events; an all-NULL side (or none) is accepted and means the
+    shared expert runs on the caller's stream."""
+    cfg = _cfg()
+    w = _fake_weights(cfg.n_layers)
+    buf = _Fake(0x20000)
+    ws_bytes = dg.dg_workspace_size(cfg, cfg.canvas)
+    kv = dg.KV(buf, buf, capacity=96, length=80)  # 80 + 32 > 96: a valid side gets as far as the cache check
+    for bad in (dg.dg_side(0x1000, None, 0x3000), dg.dg_side(0x1000, 0x2000, None), dg.dg_side(0x1000, 0x2000, 0x2000)):
+        with pytest.raises(dg.DGError) as e:
+            dg.dg_denoise_step(cfg, w, kv, buf, 1.0, buf, buf, buf, None, buf, ws_bytes, bad, stream=0)
+        assert e.value.status == dg.DG_ERR_INVALID
+    for ok in (None, dg.dg_side(None, None, None), dg.dg_side(0x1000, 0x2000, 0x3000)):
+        with pytest.raises(dg.DGError) as e:
+            dg.dg_denoise_step(cfg, w, kv, buf, 1.0, buf, buf, buf, None, buf, ws_bytes, ok, stream=0)
+        assert e.value.status == dg.DG_ERR_KV_FULL
+
+
+def test_side_create_and_destroy_validate():
+    lib = ctypes.CDLL(dg.LIB_PATH)
+    lib.dg_side_create.argtypes = [ctypes.c_void_p]
+    lib.dg_side_destroy.argtypes = [ctypes.c_void_p]
+    assert lib.dg_side_create(None) == dg.DG_ERR_INVALID
+    assert lib.dg_side_destroy(None) == dg.DG_ERR_INVALID
+    empty = dg.dg_side(None, None, None)   # nothing to destroy: a no-op
+    assert lib.dg_side_destroy(ctypes.byref(empty)) == dg.DG_OK
 
 
 def test_verify_block_validates():
@@ -319,14 +361,14 @@ def test_verify_block_validates():
     ws_bytes = dg.dg_workspace_size(cfg, cfg.canvas)
     kv = dg.KV(buf, buf, capacity=96, length=80)   # 80 + 32 > 96
     with pytest.raises(dg.DGError) as e:
-        dg.dg_verify_block(cfg, w, kv, buf, buf, buf, ws_bytes, 0)
+        dg.dg_verify_block(cfg, w, kv, buf, buf, buf, ws_bytes, stream=0)
     assert e.value.status == dg.DG_ERR_KV_FULL
     kv = dg.KV(buf, buf, capacity=128, length=0)
     with pytest.raises(dg.DGError) as e:
-        dg.dg_verify_block(cfg, w, kv, None, buf, buf, ws_bytes, 0)
+        dg.dg_verify_block(cfg, w, kv, None, buf, buf, ws_bytes, stream=0)
     assert e.value.status == dg.DG_ERR_INVALID
     with pytest.raises(dg.DGError) as e:
-        dg.dg_verify_block(cfg, w, kv, buf, buf, buf, ws_bytes - 256, 0)
+        dg.dg_verify_block(cfg, w, kv, buf, buf, buf, ws_bytes - 256, stream=0)
     assert e.value.status == dg.DG_ERR_WORKSPACE
     assert kv.len == 0
 

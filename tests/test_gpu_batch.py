@@ -1,8 +1,9 @@
 """GPU parity of batched blocks (dg_generate_blocks: several independent sequences' canvases in one pass)
-against the oracle run sequence by sequence, and against single-sequence blocks on the GPU.
+against the oracle run sequence by sequence.
 
 Bars as elsewhere: tokens, passes and stop reasons bit-exact in fp32; caches within 1e-4 (fp32) or 2e-2
-(bf16) of the reference; bf16 tokens compared by agreement with single-sequence runs.
+(bf16) of the oracle; bf16 tokens equal to the oracle's on the GPU's context wherever the oracle's top-2
+margin exceeds 1e-2.
 """
 from __future__ import annotations
 
@@ -96,35 +97,55 @@ def test_c0_batch_equals_oracle_per_sequence(flags, kw):
             assert allclose_report(gk, kv.k[l], *F32_TOL)[0] and allclose_report(gv, kv.v[l], *F32_TOL)[0], (b, l)
 
 
-@pytest.mark.parametrize("dims", ["c0_bf16", "c3_two_layers"])
-def test_bf16_batch_equals_single_sequence_blocks(dims):
-    """bf16 at fixed T: four sequences in one batched call against the same four blocks run one at a time
-    (tokens by agreement, caches within the bf16 bar).  c3_two_layers has the benchmark's shapes (d 2816, 128
-    experts top-8, 262144 vocabulary, canvas 256) with two layers: 1024 rows per pass."""
-    if dims == "c0_bf16":
-        d, prefixes, T = replace(recipe.C0.dims, dtype="bf16"), [64, 40, 17, 96], 4
-    else:
-        d, prefixes, T = replace(recipe.C3.dims, n_layers=2), [512, 300, 64, 700], 3
-    n_new = -(-d.canvas // T)
-    sp = dg.make_sampler(n_new, fixed_steps=T)
-    blocks = [3, 1, 4, 1]
-    log(f"{dims}: building weights")
-    batch = _sessions(d, prefixes)
-    toks, st = _batch(batch, sp, blocks)
-    assert all(s.steps == T and s.reason == dg.DG_STOP_FIXED for s in st)
-    single = _sessions(d, prefixes, weights=batch[0].w, packed=True)
-    for b, s in enumerate(single):
-        out = s.i32(d.canvas)
-        stb = dg.dg_generate_block(s.cfg, s.weights, s.kv, sp, blocks[b], out, s.ws, s.ws_bytes)
-        assert (stb.steps, stb.reason) == (st[b].steps, st[b].reason)
-        same = float(np.mean(out.cpu().numpy() == toks[b]))
-        log(f"{dims} seq {b}: token agreement with the single-sequence block {same:.4f}")
-        assert same > 0.9, b
-        assert s.kv.len == batch[b].kv.len == prefixes[b] + d.canvas
+@pytest.mark.parametrize("overlapped", [False, True], ids=["commit_at_end", "commit_in_next_pass"])
+def test_c3_two_layers_batch_against_oracle(overlapped):
+    """bf16 at the benchmark's widths (d 2816, 128 experts top-8, 262144 vocabulary, canvas 256) with two layers
+    and four sequences per call: 1024 canvas rows per pass (the 64-row expert tiles).  Each call runs one pass;
+    with overlapped=True the second call's first pass also carries the first call's four blocks (2048 rows).
+    Every sequence is checked against the oracle on the GPU's context (teacher-forced): its tokens where the
+    oracle's top-2 margin exceeds 1e-2, its mean entropy, and each committed block's cache rows, every layer,
+    at the bf16 bar; the prompt caches are checked free-running."""
+    from tests._gpu import check_commit_on_gpu_cache, check_pass_on_gpu_cache, gpu_cache_as_oracle
+    d = replace(recipe.C3.dims, n_layers=2)
+    S = d.canvas
+    prefixes, calls = [512, 300, 64, 700], ([[3, 1, 4, 1], [5, 9, 2, 6]] if overlapped else [[3, 1, 4, 1]])
+    log("c3_two_layers: building weights and prompts")
+    sessions = _sessions(d, prefixes)
+    model = oracle_model(d)
+    for b, (s, p) in enumerate(zip(sessions, prefixes)):  # prompt caches, free-running
+        kv = om.KVCache(d.n_layers, d.n_kv_heads, d.head_dim)
+        osm.prefill(model, kv, dg_inputs.prompt_tokens(p, d.vocab, seed=b + 1))
         for l in range(d.n_layers):
-            for a, c in zip(s.kv_numpy(l, s.kv.len), batch[b].kv_numpy(l, s.kv.len)):
-                ok, worst, at = allclose_report(c, a, *BF16_TOL)
-                assert ok, (b, l, worst, at)
+            gk, gv = s.kv_numpy(l, p)
+            assert allclose_report(gk, kv.k[l], *BF16_TOL)[0] and allclose_report(gv, kv.v[l], *BF16_TOL)[0], (b, l)
+    n = len(sessions)
+    ws_bytes = dg.dg_workspace_size(sessions[0].cfg, (2 if overlapped else 1) * n * S)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    sp = dg.make_sampler(26, fixed_steps=1)
+    outs = [torch.empty((n, S), dtype=torch.int32, device="cuda") for _ in calls]
+    side = sessions[0].side
+    for c, blocks in enumerate(calls):
+        if overlapped:
+            st = dg.dg_generate_blocks_overlapped(sessions[0].cfg, sessions[0].weights, [s.kv for s in sessions], sp,
+                                                  blocks, outs[c - 1] if c else None, 1 if c + 1 < len(calls) else 0,
+                                                  outs[c], ws, ws_bytes, side=side)
+        else:
+            st = dg.dg_generate_blocks(sessions[0].cfg, sessions[0].weights, [s.kv for s in sessions], sp, blocks,
+                                       outs[c], ws, ws_bytes, side=side)
+        torch.cuda.synchronize()
+        assert all((x.steps, x.reason) == (1, dg.DG_STOP_FIXED) for x in st)
+        for b, (s, p) in enumerate(zip(sessions, prefixes)):
+            if overlapped and c > 0:  # the previous call's block, committed inside this call's first pass
+                check_commit_on_gpu_cache(model, gpu_cache_as_oracle(s, p + (c - 1) * S), outs[c - 1][b].cpu().numpy(),
+                                          s, BF16_TOL)
+            m = check_pass_on_gpu_cache(model, gpu_cache_as_oracle(s, p + c * S),
+                                        osm.initial_canvas(sp.seed, blocks[b], S, d.vocab), outs[c][b].cpu().numpy(),
+                                        st[b].mean_entropy, BF16_TOL)
+            log(f"call {c} seq {b}: {m}/{S} tokens compared, mean entropy {st[b].mean_entropy:.4f}")
+    for b, (s, p) in enumerate(zip(sessions, prefixes)):  # each call's own commit at its end
+        assert s.kv.len == p + len(calls) * S
+        check_commit_on_gpu_cache(model, gpu_cache_as_oracle(s, p + (len(calls) - 1) * S), outs[-1][b].cpu().numpy(),
+                                  s, BF16_TOL)
 
 
 @pytest.mark.parametrize("canvas,prefixes", [(71, [33, 0, 70]), (32, [5, 64, 1, 17, 40, 2, 0, 9])],
