@@ -18,7 +18,8 @@ block loop, written from the pages' description:
        (Medium repost)
 
 Modules:
-  numerics — bf16 round-to-nearest-even from float64, decision-precision helpers
+  numerics — bf16 round-to-nearest-even from float64, decision-precision helpers,
+             OCP E4M3 decoding, rounding and per-channel quantisation
   philox   — Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) and the
              uniform token draw U(seed, block, step, slot)
   model    — RMSNorm, bidirectional/causal attention, router, MoE, vocab head
@@ -49,6 +50,11 @@ Pins (tests/test_oracle_*.py, all run without a GPU):
   * canvas token mapping: the all-zero Philox counter's published word 0
     mapped by the multiply-shift (104607 of 262144, 1634 of 4096)
   * SiLU: silu(1), silu(-1), silu(0) and the large-|z| limits
+  * FP8 (OCP E4M3) weights (tests/test_oracle_fp8.py): every code decoded and
+    every tie rounded as torch's float8_e4m3fn conversion does, the format's
+    fixed points (448, 2^-6, 2^-9, NaN codes), saturation, per-channel
+    quantisation closed forms and error bound, scaled experts equal to the
+    dequantised FFN
 Parity unpinned: none of the functions above is left without a pin; the
 whole-model forward has no golden values on the pages and is pinned only
 through its parts.

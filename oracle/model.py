@@ -27,7 +27,9 @@ from typing import List, Optional
 
 import numpy as np
 
+from .numerics import e4m3_decode as e4m3_values
 from .numerics import f32, from_storage, rounder
+from .numerics import quantize_e4m3_rows as e4m3_quantize
 from .philox import gumbel_noise
 
 
@@ -94,22 +96,34 @@ def route(xn: np.ndarray, w_router: np.ndarray, top_k: int):
     return idx, w, r, gap
 
 
-def swiglu_ffn(x: np.ndarray, w_gate_up: np.ndarray, w_down: np.ndarray, rnd) -> np.ndarray:
-    """(silu(x Wg^T) * (x Wu^T)) Wd^T with the hidden product stored (rounded) before the down projection."""
+def swiglu_ffn(x: np.ndarray, w_gate_up: np.ndarray, w_down: np.ndarray, rnd, s_gate_up=None,
+               s_down=None) -> np.ndarray:
+    """(silu(x Wg^T) * (x Wu^T)) Wd^T with the hidden product stored (rounded) before the down projection.
+
+    With per-output-channel scales (FP8 weights: the matrices hold the E4M3 code values and row r of a matrix
+    stands for s[r] times that row) each projection is multiplied by its channel's scale after the dot
+    products: gate/up = (x Q^T) * s_gate_up, down = (h Q_d^T) * s_down."""
     f = w_gate_up.shape[0] // 2
     gu = x @ w_gate_up.T
+    if s_gate_up is not None:
+        gu = gu * s_gate_up
     h = rnd(silu(gu[:, :f]) * gu[:, f:])
-    return rnd(h @ w_down.T)
+    y = h @ w_down.T
+    if s_down is not None:
+        y = y * s_down
+    return rnd(y)
 
 
 def moe_routed(xn: np.ndarray, idx: np.ndarray, w: np.ndarray, w_gate_up: np.ndarray, w_down: np.ndarray,
-               rnd) -> np.ndarray:
-    """Sum over each token's k chosen experts of weight * expert output (expert output stored, then weighted)."""
+               rnd, s_gate_up=None, s_down=None) -> np.ndarray:
+    """Sum over each token's k chosen experts of weight * expert output (expert output stored, then weighted).
+    s_gate_up [E, 2F] / s_down [E, d]: per-output-channel scales of FP8 expert weights (None: plain weights)."""
     n, k = idx.shape
     out = np.zeros((n, w_down.shape[1]))
     for e in np.unique(idx):
         tok, slot = np.nonzero(idx == e)
-        y = swiglu_ffn(xn[tok], w_gate_up[e], w_down[e], rnd)
+        y = swiglu_ffn(xn[tok], w_gate_up[e], w_down[e], rnd, None if s_gate_up is None else s_gate_up[e],
+                       None if s_down is None else s_down[e])
         np.add.at(out, tok, w[tok, slot][:, None] * y)
     return out
 
@@ -175,6 +189,21 @@ def weights_to_f64(storage: dict, dtype: str) -> dict:
     return out
 
 
+EXPERT_MATRICES = ("w_gate_up", "w_down")
+
+
+def fp8_expert_layer(layer: dict) -> dict:
+    """A float64 layer dict with its routed experts' matrices quantised to E4M3 with per-output-channel scales:
+    w_gate_up / w_down become the code values and w_gate_up_scale [E, 2F] / w_down_scale [E, d] their scales
+    (numerics.quantize_e4m3_rows; the other tensors are unchanged)."""
+    out = dict(layer)
+    for n in EXPERT_MATRICES:
+        codes, scales = e4m3_quantize(layer[n])
+        out[n] = e4m3_values(codes)
+        out[n + "_scale"] = scales.astype(np.float64)
+    return out
+
+
 class Model:
     """The denoiser: embedding, n_layers MoE blocks, final norm, tied vocab head."""
 
@@ -206,7 +235,8 @@ class Model:
         x = rnd(x + o @ w["wo"].T)
         xn2 = rnd(rmsnorm(x, w["ffn_norm"], d.rms_eps))
         idx, rw, rlog, gap = route(xn2, w["w_router"], d.top_k)
-        y = moe_routed(xn2, idx, rw, w["w_gate_up"], w["w_down"], rnd)
+        y = moe_routed(xn2, idx, rw, w["w_gate_up"], w["w_down"], rnd, w.get("w_gate_up_scale"),
+                       w.get("w_down_scale"))
         ys = swiglu_ffn(xn2, w["ws_gate_up"], w["ws_down"], rnd)
         x = rnd(x + ys + y)
         if append:
@@ -236,7 +266,8 @@ class Model:
         xr = rnd(x[rows] + o @ w["wo"].T)
         xn2 = rnd(rmsnorm(xr, w["ffn_norm"], d.rms_eps))
         idx, rw, rlog, gap = route(xn2, w["w_router"], d.top_k)
-        y = moe_routed(xn2, idx, rw, w["w_gate_up"], w["w_down"], rnd)
+        y = moe_routed(xn2, idx, rw, w["w_gate_up"], w["w_down"], rnd, w.get("w_gate_up_scale"),
+                       w.get("w_down_scale"))
         ys = swiglu_ffn(xn2, w["ws_gate_up"], w["ws_down"], rnd)
         xr = rnd(xr + ys + y)
         return xr, LayerTrace(idx=idx, w=rw, router_logits=rlog, gap=gap, hidden=xr)
