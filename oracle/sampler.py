@@ -248,3 +248,52 @@ def verify_block(model: Model, kv: KVCache, draft) -> VerifyResult:
         n += 1
     kv.truncate(base + n)
     return VerifyResult(accepted=n, ar_pred=pred, next_token=int(pred[n - 1]), margin=margin)
+
+
+@dataclass
+class SpeculativeResult:
+    tokens: np.ndarray          # the n_tokens output tokens (positions len0 .. len0 + n_tokens - 1)
+    accepted: List[int]         # tokens accepted by each verify
+    drafts: List[np.ndarray]    # each verify's draft (slot 0 replaced by the token carried in)
+
+
+def generate_speculative(model: Model, kv: KVCache, s: Sampler, block0: int, first_token: int,
+                         n_tokens: int) -> SpeculativeResult:
+    """Self-speculative decoding ([P1] "The result that complicates 'faster, not smarter'": the same weights draft a
+    block by diffusion and check it autoregressively over one shared KV cache).
+
+    Reading: the token at the cache's next position is known (``first_token``, e.g. the causal prediction after
+    the prompt).  Each round drafts a block by diffusion at the cache's end (generate_block with the commit
+    deferred, block id block0 + round), puts the known token in slot 0 of the draft, and verifies the draft
+    (verify_block): the accepted prefix is committed and output, and the causal pass's prediction for the first
+    position not accepted becomes the next round's known token.  The rounds stop once n_tokens are out (the
+    last round's surplus is dropped; its rows stay in the cache).  Every output token after the first is the
+    causal model's greedy prediction after the ones before it, so the output equals greedy autoregressive
+    decoding from ``first_token``; the drafts decide only how many tokens each causal pass confirms."""
+    out: List[int] = []
+    accepted: List[int] = []
+    drafts: List[np.ndarray] = []
+    nxt = int(first_token)
+    r = 0
+    while len(out) < n_tokens:
+        res = generate_block(model, kv, s, block=block0 + r, do_commit=False)
+        draft = res.tokens.copy()
+        draft[0] = nxt
+        v = verify_block(model, kv, draft)
+        out.extend(int(t) for t in draft[:v.accepted])
+        accepted.append(v.accepted)
+        drafts.append(draft)
+        nxt = v.next_token
+        r += 1
+    return SpeculativeResult(tokens=np.asarray(out[:n_tokens], dtype=np.int64), accepted=accepted, drafts=drafts)
+
+
+def greedy_autoregressive(model: Model, kv: KVCache, first_token: int, n_tokens: int) -> np.ndarray:
+    """Plain greedy decoding, one causal step per token: the first output is ``first_token`` at the cache's next
+    position; each later one is the argmax of the head after the previous token's causal step."""
+    out = [int(first_token)]
+    while len(out) < n_tokens:
+        x = model.embed([out[-1]])
+        x, _ = model.body(x, kv, causal=True, append=True)
+        out.append(int(model.head(x)[0][0]))
+    return np.asarray(out, dtype=np.int64)

@@ -6,6 +6,7 @@ mistake it would catch.
 from __future__ import annotations
 
 import itertools
+from dataclasses import replace
 import json
 import math
 import os
@@ -698,3 +699,56 @@ def test_verify_rows_equal_commit_rows():
     for l in range(d.n_layers):
         np.testing.assert_allclose(kv.k[l], kv_c.k[l], rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(kv.v[l], kv_c.v[l], rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- self-speculative decoding loop
+
+def test_speculative_equals_greedy_autoregressive_decoding():
+    """The speculative loop outputs exactly greedy autoregressive decoding from the known first token (computed
+    here one causal step at a time, a different route through the same model): the drafts only decide how many
+    tokens each verify confirms.  Catches: emitting an unverified draft token, a wrong next-token carry, a cache
+    that keeps rejected rows."""
+    d, m = _speculative_model()
+    prompt = dg_inputs.prompt_tokens(16, d.vocab)
+    kv = om.KVCache(d.n_layers, d.n_kv_heads, d.head_dim)
+    osm.prefill(m, kv, prompt)
+    kv_ar = om.KVCache(d.n_layers, d.n_kv_heads, d.head_dim)
+    osm.prefill(m, kv_ar, prompt)
+    first = 7
+    res = osm.generate_speculative(m, kv, osm.Sampler(n_new=2, fixed_steps=3), block0=0, first_token=first,
+                                   n_tokens=16)
+    ar = osm.greedy_autoregressive(m, kv_ar, first, 16)
+    assert np.array_equal(res.tokens, ar)
+    assert len(set(ar.tolist())) > 3          # a chain that moves, so a wrong carry or token shows
+    assert max(res.accepted) > 1              # and some draft tokens were confirmed
+    assert sum(res.accepted) >= 16 and all(a >= 1 for a in res.accepted)
+    assert kv.length == 16 + sum(res.accepted)
+    for l in range(d.n_layers):   # the kept cache rows are the autoregressive ones
+        np.testing.assert_allclose(kv.k[l][:, :16 + 15], kv_ar.k[l][:, :16 + 15], rtol=1e-12, atol=1e-12)
+
+
+def _speculative_model():
+    """A one-layer fp32 model whose output projections are scaled up 30 times, so that the layer, not the
+    embedding, decides the head's argmax: its greedy chain moves from token to token (at the seeded random init
+    the tied head mostly returns a row's own token) and some diffusion drafts agree with it."""
+    d = replace(recipe.C0.dims, canvas=8, n_layers=1, vocab=64)
+    st = dg_inputs.model_weights_host(d)
+    for layer in st["layers"]:
+        for n in ("wo", "w_down", "ws_down"):
+            layer[n] = (layer[n] * 30.0).astype(np.float32)
+    return d, oracle_model(d, st)
+
+
+def test_speculative_uniform_model_accepts_whole_blocks():
+    """Zero embeddings give uniform logits, so diffusion and causal passes both predict token 0 everywhere: every
+    verify accepts the whole draft (the known token, then S - 1 zeros) and the output is [t, 0, 0, ...]."""
+    d = replace(recipe.C0.dims, canvas=8, n_layers=1)
+    st = dg_inputs.model_weights_host(d)
+    st["embed"] = np.zeros_like(st["embed"])
+    m = oracle_model(d, st)
+    kv = om.KVCache(d.n_layers, d.n_kv_heads, d.head_dim)
+    osm.prefill(m, kv, dg_inputs.prompt_tokens(5, d.vocab))
+    res = osm.generate_speculative(m, kv, osm.Sampler(n_new=2, fixed_steps=2), block0=3, first_token=9, n_tokens=20)
+    assert res.accepted == [8, 8, 8]
+    assert list(res.tokens) == [9] + [0] * 19
+    assert kv.length == 5 + 24
