@@ -105,13 +105,15 @@ def e4m3_round(x) -> np.ndarray:
 
 
 def e4m3_encode(values) -> np.ndarray:
-    """E4M3-representable float64 values (finite) -> their uint8 codes (the positive zero for 0)."""
+    """E4M3-representable float64 values (finite) -> their uint8 codes.  A zero keeps its sign: +0 is code 0x00,
+    -0 code 0x80 (a negative value that rounds to zero rounds to -0, as in IEEE arithmetic)."""
     v = np.asarray(values, dtype=np.float64)
     table = e4m3_decode(np.arange(256))
-    finite = np.nonzero(~np.isnan(table) & ~((np.arange(256) == 0x80)))[0]   # drop the negative zero
+    finite = np.nonzero(~np.isnan(table) & ~((np.arange(256) == 0x80)))[0]   # the negative zero is added below
     order = np.argsort(table[finite])
     codes = finite[order][np.searchsorted(table[finite][order], v)]
     assert np.array_equal(table[codes], v), "value not representable in E4M3"
+    codes = np.where((v == 0) & np.signbit(v), 0x80, codes)
     return codes.astype(np.uint8)
 
 

@@ -81,7 +81,19 @@ def test_round_random_and_saturation():
 def test_encode_inverts_decode():
     pos = numerics.e4m3_decode(CODES[:0x7F])
     assert np.array_equal(numerics.e4m3_encode(pos), CODES[:0x7F].astype(np.uint8))
-    assert np.array_equal(numerics.e4m3_encode(-pos[1:]), (CODES[1:0x7F] | 0x80).astype(np.uint8))
+    assert np.array_equal(numerics.e4m3_encode(-pos), (CODES[:0x7F] | 0x80).astype(np.uint8))
+
+
+def test_codes_equal_torch_codes_including_signed_zero():
+    """Codes of rounded values, byte for byte against torch's float8_e4m3fn cast, on every tie, the codes, small
+    negative values that round to -0 (code 0x80) and zeros of both signs."""
+    pos = numerics.e4m3_decode(CODES[:0x7F])
+    mids = (pos[:-1] + pos[1:]) / 2
+    x = np.concatenate([mids, -mids, pos, -pos, [-0.0, 0.0, -2.0 ** -10, -1e-5, 2.0 ** -11]]).astype(np.float32)
+    got = numerics.e4m3_encode(numerics.e4m3_round(x))
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, ref)
+    assert got[-5] == 0x80 and got[-4] == 0x00 and got[-3] == 0x80 and got[-2] == 0x80
 
 
 def test_quantize_rows_closed_forms():
