@@ -66,11 +66,16 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def gate_up_bytes(d, experts_hit: float, pairs: int) -> float:
-    """Algorithmic bytes of one routed gate/up launch: each hit expert's [2*fe, d] weights once, the
-    normalised canvas rows once, the SwiGLU products written once."""
-    w = experts_hit * 2 * d.ffn_expert * d.d_model * 2
-    x = d.canvas * d.d_model * 2
+def expert_weight_bytes(d) -> float:
+    """Bytes per routed-expert weight: 2 (bf16) or 1 (FP8 E4M3 codes; their float scales are counted apart)."""
+    return 1.0 if d.expert_dtype == "e4m3" else 2.0
+
+
+def gate_up_bytes(d, experts_hit: float, pairs: int, rows: int = None) -> float:
+    """Algorithmic bytes of one routed gate/up launch: each hit expert's [2*fe, d] weights once (plus, for FP8
+    weights, their 2*fe float scales), the normalised rows once, the SwiGLU products written once."""
+    w = experts_hit * 2 * d.ffn_expert * (d.d_model * expert_weight_bytes(d) + (4 if d.expert_dtype == "e4m3" else 0))
+    x = (d.canvas if rows is None else rows) * d.d_model * 2
     h = pairs * d.ffn_expert * 2
     return w + x + h
 
@@ -158,12 +163,27 @@ def cpu_baseline(wl, log_fn) -> dict:
     t_head, n_head, _ = repeat(lambda: model.head(xo[:head_rows]), 4.0)
     t_pass = d.n_layers * t_layer + (d.canvas / head_rows) * t_head
     t_block = wl.fixed_steps * t_pass + d.n_layers * t_layer
+    single = None
+    try:  # the same single-layer and head samples on one BLAS thread
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t1_layer, _, _ = repeat(lambda: model.layer(0, x, kv, causal=False, append=False), 2.0)
+            t1_head, _, _ = repeat(lambda: model.head(xo[:head_rows]), 2.0)
+        single = {"cores": 1, "ms_per_moe_layer_pass": round(t1_layer * 1e3, 1),
+                  "ms_per_head_pass": round(t1_head * d.canvas / head_rows * 1e3, 1),
+                  "note": (f"one bidirectional MoE layer of the full widths over a {wl.prefix}-key cache and the "
+                           f"vocab head over {d.canvas} slots (extrapolated from {head_rows}), one BLAS thread")}
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        single = None
     return {"value": d.canvas / t_block, "unit": "canvas tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": (f"{n_layer} runs of one bidirectional layer over a {wl.prefix}-key cache "
                        f"({t_layer:.2f} s each) and {n_head} runs of the vocab head on {head_rows} slots "
                        f"({t_head:.2f} s each), float64 numpy; extrapolated to {wl.fixed_steps} passes x "
                        f"{d.n_layers} layers x {d.canvas} head slots + a {d.n_layers}-layer commit"),
-            "ms_per_denoising_step": t_pass * 1e3}
+            "ms_per_denoising_step": t_pass * 1e3,
+            "ms_per_moe_layer_pass": round(t_layer * 1e3, 1),
+            "ms_per_head_pass": round(t_head * d.canvas / head_rows * 1e3, 1),
+            "single_thread": single}
 
 
 def run_batch(args, wl) -> int:
@@ -246,7 +266,7 @@ def run_batch(args, wl) -> int:
     M = B * d.canvas
     # launches per call: T passes of M rows and the commit's M rows (as a pass of its own, or inside the first
     # pass of the next call, which then has 2 M rows): every launch averages (T + 1) M / T rows when overlapped
-    g_work = gate_up_bytes(d, d.n_experts, M * d.top_k * ((T + 1) / T if overlap else 1))
+    g_work = gate_up_bytes(d, d.n_experts, M * d.top_k * ((T + 1) / T if overlap else 1), M)
     achieved = g_work / (g_avg * 1e-3) / 1e9
     out = {
         "metric": METRIC.replace("at batch 1", f"at batch {B}"),
@@ -260,7 +280,7 @@ def run_batch(args, wl) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if d.expert_dtype != "e4m3" else "bf16+e4m3",
         "data": "synthetic",
         "config": {"workload": wl.name + f"_batch{B}", "description": wl.description, "canvas": d.canvas,
                    "prefix": wl.prefix, "T": T, "batch": B, "blocks_per_step": wl.blocks,
@@ -281,17 +301,75 @@ def run_batch(args, wl) -> int:
     return 0
 
 
+def run_speculative(args, wl) -> int:
+    """--speculative N: self-speculative decoding (dg_generate_speculative) of N output tokens after the prompt:
+    each round drafts a 256-slot block by diffusion (T passes, the commit deferred) and verifies it with one causal
+    forward; value = output tokens per second.  With random-init weights the drafts are random tokens, so a verify
+    confirms about one token (the known one carried in): the line measures the loop's cost per round and reports
+    the accepted tokens per verify; it says nothing about trained weights."""
+    import torch
+
+    import block_diffusion_decoding_step_amd as dg
+    from dg_inputs import device as gdev
+    from dg_inputs import recipe
+
+    d, T, N = wl.dims, wl.fixed_steps, args.speculative
+    side = dg.Side()
+    log(f"bench: {wl.name} speculative {N} tokens; generating weights on the device")
+    w = gdev.packed_model_weights_device(d)
+    weights = dg.Weights(w["embed"], w["final_norm"], w["layers"])
+    cfg = dg.make_config(d)
+    cap = ((wl.prefix + 2 * (N + d.canvas) + 31) // 32) * 32
+    k, v = gdev.kv_tensors(d, cap)
+    kv = dg.KV(k, v, cap, 0)
+    ws_bytes = dg.dg_workspace_size(cfg, 2048)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    prompt = gdev.uniform_tensor(wl.prefix, recipe.INPUT_SEED, recipe.STREAM_PROMPT, d.vocab)
+    dg.dg_prefill_kv(cfg, weights, kv, prompt, wl.prefix, ws, ws_bytes, side=side)
+    P = kv.len
+    sampler = dg.make_sampler(wl.n_new, fixed_steps=T, seed=recipe.INPUT_SEED)
+    out = torch.empty(N, dtype=torch.int32, device="cuda")
+    first = int(prompt[-1].item())
+    for _ in range(args.warmup):
+        kv.len = P
+        dg.dg_generate_speculative(cfg, weights, kv, sampler, 0, first, N, out, ws, ws_bytes, side=side)
+    torch.cuda.synchronize()
+    stats, t0 = [], time.perf_counter()
+    for i in range(args.steps):
+        kv.len = P
+        stats.append(dg.dg_generate_speculative(cfg, weights, kv, sampler, 1000 * i, first, N, out, ws, ws_bytes,
+                                                side=side))
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t0
+    rounds = sum(st.rounds for st, _ in stats)
+    accepted = sum(st.accepted for st, _ in stats)
+    res = {"metric": "output tokens/sec, self-speculative decoding at batch 1 (diffusion drafts of 256 slots, "
+                     "T=10, verified causally)",
+           "value": round(N * args.steps / t_total, 3), "unit": "output tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(t_total / args.steps * 1e3, 3), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": wl.name + "_speculative", "prefix": wl.prefix, "canvas": d.canvas, "T": T,
+                      "tokens_per_step": N, "step": f"dg_generate_speculative of {N} tokens after the prompt"},
+           "accepted_per_verify": round(accepted / rounds, 4), "verifies_per_step": rounds / args.steps,
+           "ms_per_round": round(t_total / rounds * 1e3, 3)}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="full_loop_bf16", choices=["full_loop_bf16", "long_context_bf16"])
+    ap.add_argument("--workload", default="full_loop_bf16", choices=["full_loop_bf16", "long_context_bf16",
+                                                                     "full_loop_fp8"])
     ap.add_argument("--sampler", default="plain", choices=["plain", "recommended"],
                     help="plain: argmax and confidence-ranked keep; recommended: Gumbel-max draws at a temperature "
                          "annealed 0.8 -> 0.4, entropy-ranked locking keep, AND stop rule (fixed T either way)")
     ap.add_argument("--batch", type=int, default=1,
                     help="canvases per pass (independent sequences, dg_generate_blocks); 1 is the batch-1 workload")
+    ap.add_argument("--speculative", type=int, default=0,
+                    help="tokens of self-speculative decoding per step (dg_generate_speculative); 0: the block workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (reference for HBM byte counters)")
@@ -316,6 +394,8 @@ def main() -> int:
     torch.cuda.set_device(0)
     if args.batch > 1:
         return run_batch(args, wl)
+    if args.speculative > 0:
+        return run_speculative(args, wl)
     stream = torch.cuda.current_stream()
     log(f"bench: {wl.name} on {torch.cuda.get_device_name(0)}; generating weights on the device")
     side = dg.Side()  # the shared expert's stream and events, owned here
@@ -443,7 +523,9 @@ def main() -> int:
         if ks == SIDE_KERNELS:
             mfma[name]["note"] = SIDE_NOTE
     ex_ms = sum(breakdown.get(k, (0.0, 0))[0] for k in ("moe_gate_up", "moe_down"))
-    ex_bytes = d.n_layers * experts_hit * 3 * d.ffn_expert * d.d_model * 2
+    ex_bytes = d.n_layers * experts_hit * 3 * d.ffn_expert * d.d_model * expert_weight_bytes(d)
+    if d.expert_dtype == "e4m3":  # the scales: 2*fe (gate/up) + d (down) floats per hit expert
+        ex_bytes += d.n_layers * experts_hit * (2 * d.ffn_expert + d.d_model) * 4
     hbm = {"experts": {"gbs": round(ex_bytes / (ex_ms * 1e-3) / 1e9, 1),
                        "frac": round(ex_bytes / (ex_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                        "bytes_per_pass": ex_bytes, "kernels": ["moe_gate_up", "moe_down"]}}
@@ -477,7 +559,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if d.expert_dtype != "e4m3" else "bf16+e4m3",
         "data": "synthetic",
         "config": {"workload": wl.name, "description": wl.description,
                    "canvas": d.canvas, "prefix": wl.prefix, "T": T, "batch": 1, "blocks_per_step": blocks,

@@ -14,7 +14,8 @@ import os
 from typing import Dict, List, Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdg.so")
+# DG_LIBRARY selects another build of the same library (the host-sanitizer build the CPU tests of the C ABI use)
+LIB_PATH = os.environ.get("DG_LIBRARY") or os.path.join(_HERE, "libdg.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() (hipcc, gfx950) first")
@@ -26,7 +27,7 @@ import torch  # noqa: E402,F401
 _lib = ctypes.CDLL(LIB_PATH)
 
 DG_OK, DG_ERR_INVALID, DG_ERR_UNSUPPORTED, DG_ERR_KV_FULL, DG_ERR_WORKSPACE, DG_ERR_HIP = 0, -1, -2, -3, -4, -5
-DG_F32, DG_BF16 = 0, 1
+DG_F32, DG_BF16, DG_E4M3 = 0, 1, 2
 DG_STOP_NONE, DG_STOP_ENTROPY, DG_STOP_STABLE, DG_STOP_CAP, DG_STOP_FIXED, DG_STOP_SETTLED = 0, 1, 2, 3, 4, 5
 DG_WARN_NUMERIC = 0x1
 # sampler variants (dg_sampler.flags)
@@ -35,7 +36,7 @@ EXPORTED = ("dg_workspace_size", "dg_prefill_kv", "dg_denoise_step", "dg_canvas_
             "dg_generate_block", "dg_generate_block_overlapped", "dg_layer_forward", "dg_vocab_head", "dg_stop_check", "dg_status_string",
             "dg_generate_blocks", "dg_generate_blocks_overlapped", "dg_verify_block", "dg_denoise_step_sampler", "dg_canvas_update_sampler", "dg_vocab_head_sampler", "dg_sampler_inv_temperature",
             "dg_last_hip_error", "dg_timing_start", "dg_timing_stop", "dg_packed_elems", "dg_pack_matrix",
-            "dg_side_create", "dg_side_destroy")
+            "dg_side_create", "dg_side_destroy", "dg_generate_speculative", "dg_packed_bytes_e4m3", "dg_quantize_e4m3")
 # kernel classes of dg_timing_* (dg_kernel in dg.h), in enum order
 KERNELS = ("embed", "rmsnorm", "gemm_qkv", "attention", "attn_merge", "gemm_o", "route",
            "moe_gate_up", "moe_down", "shared_gate_up", "shared_down", "moe_combine", "vocab_head",
@@ -58,12 +59,13 @@ class dg_config(ctypes.Structure):
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("ffn_expert", ctypes.c_int32), ("ffn_shared", ctypes.c_int32),
                 ("vocab", ctypes.c_int32), ("canvas", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float)]
+                ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float), ("expert_dtype", ctypes.c_int32)]
 
 
 class dg_layer_weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("attn_norm", "wqkv", "wo", "ffn_norm", "w_router", "w_gate_up",
-                                               "w_down", "ws_gate_up", "ws_down")]
+                                               "w_down", "ws_gate_up", "ws_down", "w_gate_up_scale",
+                                               "w_down_scale")]
 
 
 class dg_weights(ctypes.Structure):
@@ -90,6 +92,11 @@ class dg_block_status(ctypes.Structure):
 
 class dg_side(ctypes.Structure):
     _fields_ = [("stream", ctypes.c_void_p), ("fork", ctypes.c_void_p), ("join", ctypes.c_void_p)]
+
+
+class dg_spec_status(ctypes.Structure):
+    _fields_ = [("rounds", ctypes.c_int32), ("tokens", ctypes.c_int32), ("accepted", ctypes.c_int32),
+                ("next_token", ctypes.c_int32)]
 
 
 class dg_debug(ctypes.Structure):
@@ -129,6 +136,10 @@ _SIGS = {
     "dg_packed_elems": [_i64, _i64, _P(_i64)],
     "dg_pack_matrix": [_vp, _vp, _i64, _i64, _i64, _i32, _vp],
     "dg_side_create": [_P(dg_side)],
+    "dg_generate_speculative": [_P(dg_config), _P(dg_weights), _P(dg_kv), _P(dg_sampler), _u32, _i32, _i32, _vp,
+                                _P(_i32), _P(dg_spec_status), _vp, _sz, _P(dg_side), _vp],
+    "dg_packed_bytes_e4m3": [_i64, _i64, _P(_i64)],
+    "dg_quantize_e4m3": [_vp, _vp, _vp, _i64, _i64, _i64, _vp],
     "dg_side_destroy": [_P(dg_side)],
 }
 for _name, _args in _SIGS.items():
@@ -201,14 +212,15 @@ def make_config(dims, dtype: Optional[str] = None, rms_eps: float = 1e-6) -> dg_
                      n_kv_heads=dims.n_kv_heads, head_dim=dims.head_dim, n_experts=dims.n_experts,
                      top_k=dims.top_k, ffn_expert=dims.ffn_expert, ffn_shared=dims.ffn_shared, vocab=dims.vocab,
                      canvas=dims.canvas, dtype=DG_BF16 if dt == "bf16" else DG_F32,
-                     rms_eps=getattr(dims, "rms_eps", rms_eps), rope_theta=0.0)
+                     rms_eps=getattr(dims, "rms_eps", rms_eps), rope_theta=0.0,
+                     expert_dtype=DG_E4M3 if getattr(dims, "expert_dtype", "") == "e4m3" else 0)
 
 
 class Weights:
     """dg_weights built from device tensors; keeps the tensors alive."""
 
     LAYER_FIELDS = ("attn_norm", "wqkv", "wo", "ffn_norm", "w_router", "w_gate_up", "w_down", "ws_gate_up",
-                    "ws_down")
+                    "ws_down", "w_gate_up_scale", "w_down_scale")
 
     def __init__(self, embed, final_norm, layers: Sequence[Dict[str, object]]):
         self._keep = [embed, final_norm, list(layers)]
@@ -216,7 +228,7 @@ class Weights:
         self._layers = (dg_layer_weights * max(n, 1))()
         for i, lw in enumerate(layers):
             for f in self.LAYER_FIELDS:
-                setattr(self._layers[i], f, _ptr(lw[f]))
+                setattr(self._layers[i], f, _ptr(lw.get(f)))
         self.struct = dg_weights(embed=_ptr(embed), final_norm=_ptr(final_norm),
                                  h_layers=ctypes.cast(self._layers, _P(dg_layer_weights)))
 
@@ -337,6 +349,18 @@ def dg_verify_block(cfg, weights, kv, draft, ar_pred, ws, ws_bytes: int, side=No
     return int(n.value), int(nxt.value)
 
 
+def dg_generate_speculative(cfg, weights, kv, sampler: dg_sampler, block0: int, first_token: int, n_tokens: int,
+                            tokens_out, ws, ws_bytes: int, side=None, stream=None) -> tuple:
+    """Self-speculative decoding; returns (dg_spec_status, accepted count of each round); kv.len grows."""
+    st = dg_spec_status()
+    acc = (ctypes.c_int32 * max(n_tokens, 1))()
+    _check("dg_generate_speculative",
+           _lib.dg_generate_speculative(ctypes.byref(cfg), _w(weights), _kv(kv), ctypes.byref(sampler), block0,
+                                        first_token, n_tokens, _ptr(tokens_out), acc, ctypes.byref(st), _ptr(ws),
+                                        ws_bytes, _side(side), _stream(stream)))
+    return st, [int(acc[i]) for i in range(st.rounds)]
+
+
 def _dbg(dbg):
     if dbg is None:
         return None
@@ -437,7 +461,31 @@ def dg_pack_matrix(src, dst, batch: int, rows: int, cols: int, dtype: int, strea
     _check("dg_pack_matrix", _lib.dg_pack_matrix(_ptr(src), _ptr(dst), batch, rows, cols, dtype, _stream(stream)))
 
 
+def dg_packed_bytes_e4m3(rows: int, cols: int) -> int:
+    out = ctypes.c_int64(0)
+    _check("dg_packed_bytes_e4m3", _lib.dg_packed_bytes_e4m3(rows, cols, ctypes.byref(out)))
+    return int(out.value)
+
+
+def dg_quantize_e4m3(src, dst, scale, batch: int, rows: int, cols: int, stream=None) -> None:
+    _check("dg_quantize_e4m3", _lib.dg_quantize_e4m3(_ptr(src), _ptr(dst), _ptr(scale), batch, rows, cols,
+                                                     _stream(stream)))
+
+
+def quantize_tensor_e4m3(t):
+    """A 2-D [rows, cols] or 3-D [batch, rows, cols] row-major bf16 device tensor -> (E4M3 codes in the FP8
+    pair-tiled layout, uint8 1-D; per-row float32 scales [batch * rows])."""
+    import torch
+    rows, cols = int(t.shape[-2]), int(t.shape[-1])
+    batch = int(t.shape[0]) if t.dim() == 3 else 1
+    codes = torch.empty(batch * dg_packed_bytes_e4m3(rows, cols), dtype=torch.uint8, device=t.device)
+    scale = torch.empty(batch * rows, dtype=torch.float32, device=t.device)
+    dg_quantize_e4m3(t.contiguous(), codes, scale, batch, rows, cols)
+    return codes, scale
+
+
 MATRIX_FIELDS = ("wqkv", "wo", "w_router", "w_gate_up", "w_down", "ws_gate_up", "ws_down")
+EXPERT_FIELDS = ("w_gate_up", "w_down")
 
 
 def pack_tensor(t):
@@ -451,13 +499,22 @@ def pack_tensor(t):
     return out
 
 
-def pack_layer(layer: Dict[str, object]) -> Dict[str, object]:
-    """One layer's weights with every matrix converted to the library's layout (norm gains unchanged)."""
-    return {k: (pack_tensor(v) if k in MATRIX_FIELDS else v) for k, v in layer.items()}
+def pack_layer(layer: Dict[str, object], expert_dtype: str = "") -> Dict[str, object]:
+    """One layer's weights with every matrix converted to the library's layout (norm gains unchanged); with
+    expert_dtype "e4m3" the routed experts' matrices are quantised (codes + "<name>_scale")."""
+    out = {}
+    for k, v in layer.items():
+        if expert_dtype == "e4m3" and k in EXPERT_FIELDS:
+            out[k], out[k + "_scale"] = quantize_tensor_e4m3(v)
+        elif k in MATRIX_FIELDS:
+            out[k] = pack_tensor(v)
+        else:
+            out[k] = v
+    return out
 
 
-def pack_weights(natural: dict) -> dict:
+def pack_weights(natural: dict, expert_dtype: str = "") -> dict:
     """{"embed", "final_norm", "layers": [...]} of row-major device tensors -> the library's layout."""
     return {"embed": pack_tensor(natural["embed"]) if natural.get("embed") is not None else None,
             "final_norm": natural["final_norm"],
-            "layers": [pack_layer(l) for l in natural["layers"]]}
+            "layers": [pack_layer(l, expert_dtype) for l in natural["layers"]]}

@@ -38,5 +38,37 @@ def build() -> str:
     return LIB
 
 
+# Host-side sanitizer build of the library for CPU-only tests of the C ABI (argument validation, workspace
+# carving, error paths): the host code of dg_api.cpp with AddressSanitizer and UndefinedBehaviorSanitizer, the
+# kernels unchanged (device code is not instrumented).  Loaded through DG_LIBRARY with the clang ASan runtime
+# preloaded; never used on a GPU.
+SAN_LIB = os.path.join(HERE, "libdg_san.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-Xarch_host",
+             "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def asan_runtime() -> str:
+    clang = os.path.join(os.path.dirname(HIPCC), "..", "llvm", "bin", "clang")
+    r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return r.stdout.strip()
+
+
+def build_sanitized() -> str:
+    """The sanitizer build, reusing the kernels' objects of the last build() (made first if missing)."""
+    if not all(os.path.exists(os.path.join(BUILD, os.path.splitext(s)[0] + ".o")) for s in SOURCES):
+        build()
+    obj = os.path.join(BUILD, "dg_api_san.o")
+    cmd = [HIPCC, *FLAGS, *SAN_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, "dg_api.cpp"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc (sanitized) failed:\n{r.stderr}")
+    objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES if s != "dg_api.cpp"] + [obj]
+    tmp = SAN_LIB + ".tmp"
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-shared-libsan", *SAN_FLAGS, "-o", tmp,
+                    *objs], check=True)
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
     print(build())

@@ -223,14 +223,20 @@ int check_cfg(const dg_config* c) {
   if (G != 1 && G != 2 && G != 4) return DG_ERR_UNSUPPORTED;
   if (c->n_experts > 256 || c->top_k > 16) return DG_ERR_UNSUPPORTED;
   if (c->canvas > 1024 || c->canvas > moe_max_rows(c->n_experts)) return DG_ERR_UNSUPPORTED;
+  if (c->expert_dtype != 0 && c->expert_dtype != DG_E4M3 && c->expert_dtype != c->dtype) return DG_ERR_INVALID;
+  if (c->expert_dtype == DG_E4M3 && (c->dtype != DG_BF16 || c->d_model % 64 || c->ffn_expert % 64))
+    return DG_ERR_UNSUPPORTED;
   return DG_OK;
 }
 
-int check_layer_weights(const dg_layer_weights& l) {
+inline bool fp8_experts(const dg_config* c) { return c->expert_dtype == DG_E4M3; }
+
+int check_layer_weights(const dg_config* c, const dg_layer_weights& l) {
   const void* p[] = {l.attn_norm, l.wqkv, l.wo, l.ffn_norm, l.w_router, l.w_gate_up, l.w_down, l.ws_gate_up,
                      l.ws_down};
   for (const void* q : p)
     if (!aligned16(q)) return DG_ERR_INVALID;
+  if (fp8_experts(c) && (!aligned16(l.w_gate_up_scale) || !aligned16(l.w_down_scale))) return DG_ERR_INVALID;
   return DG_OK;
 }
 
@@ -240,7 +246,7 @@ int check_weights(const dg_config* c, const dg_weights* w, bool need_layers, boo
   if (need_head && !aligned16(w->final_norm)) return DG_ERR_INVALID;
   if (need_layers && c->n_layers > 0) {
     if (!w->h_layers) return DG_ERR_INVALID;
-    for (int l = 0; l < c->n_layers; ++l) DG_CHECK(check_layer_weights(w->h_layers[l]));
+    for (int l = 0; l < c->n_layers; ++l) DG_CHECK(check_layer_weights(c, w->h_layers[l]));
   }
   return DG_OK;
 }
@@ -380,10 +386,16 @@ int layer_t(const dg_config* c, const dg_weights* w, int l, const Segs& sg, int6
   MoeArgs ma{};
   ma.tiles = ws.tiles; ma.n_tiles = ws.n_tiles; ma.max_tiles = moe_max_tiles(Mi, E, k); ma.perm = ws.perm;
   ma.tile_rows = ra.tile_rows;
-  ma.X = ws.Xn; ma.W = L.w_gate_up; ma.out = ws.Hp; ma.d = d; ma.F = c->ffn_expert;
-  DG_LAUNCH(DG_K_MOE_GATE_UP, s, launch_moe_gate_up<T>(ma, s));
-  ma.X = ws.Hp; ma.W = L.w_down; ma.out = ws.Yp;
-  DG_LAUNCH(DG_K_MOE_DOWN, s, launch_moe_down<T>(ma, s));
+  ma.X = ws.Xn; ma.W = L.w_gate_up; ma.out = ws.Hp; ma.d = d; ma.F = c->ffn_expert; ma.scale = L.w_gate_up_scale;
+  if (fp8_experts(c))
+    DG_LAUNCH(DG_K_MOE_GATE_UP, s, launch_moe_gate_up_f8(ma, s));
+  else
+    DG_LAUNCH(DG_K_MOE_GATE_UP, s, launch_moe_gate_up<T>(ma, s));
+  ma.X = ws.Hp; ma.W = L.w_down; ma.out = ws.Yp; ma.scale = L.w_down_scale;
+  if (fp8_experts(c))
+    DG_LAUNCH(DG_K_MOE_DOWN, s, launch_moe_down_f8(ma, s));
+  else
+    DG_LAUNCH(DG_K_MOE_DOWN, s, launch_moe_down<T>(ma, s));
 
   if (fork) DG_TRY(hipStreamWaitEvent(s, sd.join, 0));  // join: the combine reads the shared expert's output
   const T* g_next = next == Next::NextLayer ? (const T*)w->h_layers[l + 1].attn_norm
@@ -552,6 +564,72 @@ int check_sampler(const dg_config* c, const dg_sampler* sp) {
   return DG_OK;
 }
 
+// One block's passes (initial canvas, passes t = 1.. with the stop check and, if not stopping, the canvas update)
+// with an already-validated configuration; `pending` (nullable) is committed inside the first pass (kv->len grows
+// by S).  The block's tokens (the last pass's predictions) are left in wsv.pred; *st receives the status (read from
+// the device here, so it is valid when the stream reaches this point).
+int block_loop(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const dg_sampler* sp, uint32_t block,
+               const int32_t* pending, const Ws& wsv, const dg_side* side, hipStream_t s, dg_block_status* st) {
+  const int S = cfg->canvas;
+  const StopParams stp = stop_params(cfg, sp);
+  const bool fixed = sp->fixed_steps > 0;
+  const int limit = fixed ? sp->fixed_steps : sp->max_steps;
+  const bool lock = (sp->flags & DG_KEEP_LOCK) != 0;
+  uint8_t* lock_mask = lock ? wsv.lock : nullptr;  // the locked slots; cleared by the initial draw
+  CanvasArgs ca{nullptr, nullptr, nullptr, 0, nullptr, S, 0, sp->seed, block, 0, (uint32_t)cfg->vocab, wsv.canvas,
+                lock_mask};
+  DG_LAUNCH(DG_K_CANVAS_UPDATE, s, launch_canvas_update(ca, s));
+  for (int t = 1;; ++t) {
+    const PassParams pp = sampler_pass(sp, block, t);
+    if (t == 1 && pending) {
+      DG_CHECK(denoise_committing(cfg, w, kv, pending, wsv.canvas, pp, wsv.pred, wsv.conf, wsv.ent, wsv, side, s));
+      kv->len += S;  // the pending block is committed (in stream order) before every later pass
+    } else {
+      DG_CHECK(denoise(cfg, w, kv, wsv.canvas, pp, wsv.pred, wsv.conf, wsv.ent, nullptr, wsv, side, s));
+    }
+    DG_LAUNCH(DG_K_STOP_CHECK, s,
+              launch_stop_check(wsv.ent, wsv.pred, wsv.prev_pred, wsv.canvas, lock_mask, S, t, stp, wsv.status, s));
+    bool stop;
+    if (fixed) {
+      stop = t >= limit;
+    } else {
+      DG_TRY(hipMemcpyAsync(st, wsv.status, sizeof(*st), hipMemcpyDeviceToHost, s));
+      DG_TRY(hipStreamSynchronize(s));
+      stop = st->reason != DG_STOP_NONE;
+    }
+    if (stop) break;
+    ca = CanvasArgs{wsv.pred, wsv.conf, wsv.ent, (sp->flags & DG_KEEP_ENTROPY) ? 1 : 0, lock_mask, S,
+                    (int)std::min<int64_t>(S, (int64_t)t * sp->n_new), sp->seed, block, (uint32_t)t,
+                    (uint32_t)cfg->vocab, wsv.canvas, lock_mask};
+    DG_LAUNCH(DG_K_CANVAS_UPDATE, s, launch_canvas_update(ca, s));
+  }
+  if (fixed) DG_TRY(hipMemcpyAsync(st, wsv.status, sizeof(*st), hipMemcpyDeviceToHost, s));
+  return DG_OK;
+}
+
+// Greedy verify of a drafted block (validated configuration, workspace of S rows): the commit's causal forward
+// over draft at kv->len.., the argmax of every row into ar_pred, then the accepted prefix (draft[0] as drafted,
+// draft[i] while ar_pred[i - 1] == draft[i]); kv->len grows by it.  Synchronises the stream.
+int verify_rows(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const int32_t* draft, int32_t* ar_pred,
+                const Ws& wsv, const dg_side* side, hipStream_t s, int32_t* accepted, int32_t* next_token) {
+  const int S = cfg->canvas;
+  DG_CHECK(embed(cfg, w, draft, S, wsv, s));
+  const int L = cfg->n_layers;
+  for (int l = 0; l < L; ++l)
+    DG_CHECK(layer(cfg, w, l, kv, kv->len, S, S, l > 0, l + 1 < L ? Next::NextLayer : Next::Head, wsv, side, s));
+  DG_CHECK(head(cfg, w, S, argmax_pass(1.0f), ar_pred, wsv.conf, wsv.ent, L > 0, wsv, s));
+  std::vector<int32_t> hp(S), hd(S);
+  DG_TRY(hipMemcpyAsync(hp.data(), ar_pred, (size_t)S * 4, hipMemcpyDeviceToHost, s));
+  DG_TRY(hipMemcpyAsync(hd.data(), draft, (size_t)S * 4, hipMemcpyDeviceToHost, s));
+  DG_TRY(hipStreamSynchronize(s));
+  int n = 1;
+  while (n < S && hp[n - 1] == hd[n]) ++n;
+  *accepted = n;
+  *next_token = hp[n - 1];
+  kv->len += n;
+  return DG_OK;
+}
+
 }  // namespace
 
 // ====================================================================== C ABI
@@ -655,43 +733,9 @@ int dg_generate_block_overlapped(const dg_config* cfg, const dg_weights* w, dg_k
   DG_CHECK(check_ws(cfg, rows, ws, ws_bytes));
   hipStream_t s = (hipStream_t)stream;
   Ws wsv = carve(cfg, rows, (char*)ws);
-  const StopParams stp = stop_params(cfg, sp);
-  const bool fixed = sp->fixed_steps > 0;
-  const int limit = fixed ? sp->fixed_steps : sp->max_steps;
-  const bool lock = (sp->flags & DG_KEEP_LOCK) != 0;
-  uint8_t* lock_mask = lock ? wsv.lock : nullptr;  // the locked slots; cleared by the initial draw
-
-  CanvasArgs ca{nullptr, nullptr, nullptr, 0, nullptr, S, 0, sp->seed, block, 0, (uint32_t)cfg->vocab, wsv.canvas,
-                lock_mask};
-  DG_LAUNCH(DG_K_CANVAS_UPDATE, s, launch_canvas_update(ca, s));
   dg_block_status st{};
-  for (int t = 1;; ++t) {
-    const PassParams pp = sampler_pass(sp, block, t);
-    if (t == 1 && pending) {
-      DG_CHECK(denoise_committing(cfg, w, kv, pending, wsv.canvas, pp, wsv.pred, wsv.conf, wsv.ent, wsv, side, s));
-      kv->len += S;  // the pending block is committed (in stream order) before every later pass
-    } else {
-      DG_CHECK(denoise(cfg, w, kv, wsv.canvas, pp, wsv.pred, wsv.conf, wsv.ent, nullptr, wsv, side, s));
-    }
-    DG_LAUNCH(DG_K_STOP_CHECK, s,
-              launch_stop_check(wsv.ent, wsv.pred, wsv.prev_pred, wsv.canvas, lock_mask, S, t, stp, wsv.status, s));
-    bool stop;
-    if (fixed) {
-      stop = t >= limit;
-    } else {
-      DG_TRY(hipMemcpyAsync(&st, wsv.status, sizeof(st), hipMemcpyDeviceToHost, s));
-      DG_TRY(hipStreamSynchronize(s));
-      stop = st.reason != DG_STOP_NONE;
-    }
-    if (stop) break;
-    ca = CanvasArgs{wsv.pred, wsv.conf, wsv.ent, (sp->flags & DG_KEEP_ENTROPY) ? 1 : 0, lock_mask, S,
-                    (int)std::min<int64_t>(S, (int64_t)t * sp->n_new), sp->seed, block, (uint32_t)t,
-                    (uint32_t)cfg->vocab, wsv.canvas, lock_mask};
-    DG_LAUNCH(DG_K_CANVAS_UPDATE, s, launch_canvas_update(ca, s));
-  }
+  DG_CHECK(block_loop(cfg, w, kv, sp, block, pending, wsv, side, s, &st));
   DG_TRY(hipMemcpyAsync(tokens_out, wsv.pred, (size_t)S * 4, hipMemcpyDeviceToDevice, s));
-  // read the status before the commit reuses the workspace
-  if (fixed) DG_TRY(hipMemcpyAsync(&st, wsv.status, sizeof(st), hipMemcpyDeviceToHost, s));
   if (!defer_commit) {
     DG_CHECK(prefill(cfg, w, kv, tokens_out, S, ws, ws_bytes, side, s));
     kv->len += S;
@@ -838,7 +882,8 @@ int dg_generate_blocks(const dg_config* cfg, const dg_weights* w, dg_kv* kvs, in
 }
 
 int dg_verify_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const int32_t* draft, int32_t* ar_pred,
-                    int32_t* h_accepted, int32_t* h_next_token, void* ws, size_t ws_bytes, const dg_side* side, void* stream) {
+                    int32_t* h_accepted, int32_t* h_next_token, void* ws, size_t ws_bytes, const dg_side* side,
+                    void* stream) {
   DG_CHECK(check_cfg(cfg));
   DG_CHECK(check_side(side));
   DG_CHECK(check_weights(cfg, w, true, true));
@@ -846,23 +891,46 @@ int dg_verify_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const 
   const int S = cfg->canvas;
   DG_CHECK(check_kv(kv, S));
   DG_CHECK(check_ws(cfg, S, ws, ws_bytes));
+  Ws wsv = carve(cfg, S, (char*)ws);
+  return verify_rows(cfg, w, kv, draft, ar_pred, wsv, side, (hipStream_t)stream, h_accepted, h_next_token);
+}
+
+int dg_generate_speculative(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const dg_sampler* sp,
+                            uint32_t block0, int32_t first_token, int32_t n_tokens, int32_t* tokens_out,
+                            int32_t* h_accepted, dg_spec_status* h_status, void* ws, size_t ws_bytes,
+                            const dg_side* side, void* stream) {
+  DG_CHECK(check_cfg(cfg));
+  DG_CHECK(check_side(side));
+  DG_CHECK(check_weights(cfg, w, true, true));
+  DG_CHECK(check_sampler(cfg, sp));
+  if (!tokens_out || !h_status || n_tokens < 1 || first_token < 0 || first_token >= cfg->vocab)
+    return DG_ERR_INVALID;
+  const int S = cfg->canvas;
+  // every round starts with kv->len below len0 + n_tokens and needs S rows after it
+  DG_CHECK(check_kv(kv, (int64_t)n_tokens - 1 + S));
+  DG_CHECK(check_ws(cfg, S, ws, ws_bytes));
   hipStream_t s = (hipStream_t)stream;
   Ws wsv = carve(cfg, S, (char*)ws);
-  // the commit's causal forward over the draft, then the greedy prediction of every row
-  DG_CHECK(embed(cfg, w, draft, S, wsv, s));
-  const int L = cfg->n_layers;
-  for (int l = 0; l < L; ++l)
-    DG_CHECK(layer(cfg, w, l, kv, kv->len, S, S, l > 0, l + 1 < L ? Next::NextLayer : Next::Head, wsv, side, s));
-  DG_CHECK(head(cfg, w, S, argmax_pass(1.0f), ar_pred, wsv.conf, wsv.ent, L > 0, wsv, s));
-  std::vector<int32_t> hp(S), hd(S);
-  DG_TRY(hipMemcpyAsync(hp.data(), ar_pred, (size_t)S * 4, hipMemcpyDeviceToHost, s));
-  DG_TRY(hipMemcpyAsync(hd.data(), draft, (size_t)S * 4, hipMemcpyDeviceToHost, s));
+  dg_spec_status out{};
+  int32_t nxt = first_token;
+  while (out.tokens < n_tokens) {
+    dg_block_status st{};
+    DG_CHECK(block_loop(cfg, w, kv, sp, block0 + (uint32_t)out.rounds, nullptr, wsv, side, s, &st));
+    // the draft: the block's tokens with the known next token in slot 0 (wsv.canvas is free after the block)
+    DG_TRY(hipMemcpyAsync(wsv.canvas, wsv.pred, (size_t)S * 4, hipMemcpyDeviceToDevice, s));
+    DG_TRY(hipMemsetD32Async((hipDeviceptr_t)wsv.canvas, nxt, 1, s));
+    int32_t acc = 0;
+    DG_CHECK(verify_rows(cfg, w, kv, wsv.canvas, wsv.pred, wsv, side, s, &acc, &nxt));
+    const int take = std::min(acc, n_tokens - out.tokens);
+    DG_TRY(hipMemcpyAsync(tokens_out + out.tokens, wsv.canvas, (size_t)take * 4, hipMemcpyDeviceToDevice, s));
+    if (h_accepted) h_accepted[out.rounds] = acc;
+    out.tokens += take;
+    out.accepted += acc;
+    out.rounds += 1;
+  }
+  out.next_token = nxt;
   DG_TRY(hipStreamSynchronize(s));
-  int n = 1;
-  while (n < S && hp[n - 1] == hd[n]) ++n;
-  *h_accepted = n;
-  *h_next_token = hp[n - 1];
-  kv->len += n;
+  *h_status = out;
   return DG_OK;
 }
 
@@ -872,7 +940,7 @@ int dg_layer_forward(const dg_config* cfg, const dg_weights* w, int32_t layer_i,
   DG_CHECK(check_cfg(cfg));
   DG_CHECK(check_side(side));
   if (!w || !w->h_layers || layer_i < 0 || layer_i >= cfg->n_layers) return DG_ERR_INVALID;
-  DG_CHECK(check_layer_weights(w->h_layers[layer_i]));
+  DG_CHECK(check_layer_weights(cfg, w->h_layers[layer_i]));
   if (!aligned16(x_in) || !aligned16(x_out) || n < 1 || n > moe_max_rows(cfg->n_experts)) return DG_ERR_INVALID;
   if (causal != 0 && causal != 1) return DG_ERR_INVALID;
   DG_CHECK(check_kv(kv, n));
@@ -986,6 +1054,27 @@ int dg_packed_elems(int64_t rows, int64_t cols, int64_t* h_elems) {
   *h_elems = 0;
   if (rows < 1 || cols < 32 || cols % 32) return DG_ERR_INVALID;
   *h_elems = (rows + 15) / 16 * 16 * cols;
+  return DG_OK;
+}
+
+int dg_packed_bytes_e4m3(int64_t rows, int64_t cols, int64_t* h_bytes) {
+  if (!h_bytes) return DG_ERR_INVALID;
+  *h_bytes = 0;
+  if (rows < 1 || cols < 64 || cols % 64) return DG_ERR_INVALID;
+  *h_bytes = (rows + 15) / 16 * 16 * cols;
+  return DG_OK;
+}
+
+int dg_quantize_e4m3(const void* src, void* dst, float* scale, int64_t batch, int64_t rows, int64_t cols,
+                     void* stream) {
+  int64_t per = 0;
+  DG_CHECK(dg_packed_bytes_e4m3(rows, cols, &per));
+  if (batch < 1 || !aligned16(src) || !aligned16(dst) || !scale || ((uintptr_t)scale & 3u)) return DG_ERR_INVALID;
+  const uintptr_t s0 = (uintptr_t)src, s1 = s0 + (size_t)(batch * rows * cols) * 2;
+  const uintptr_t d0 = (uintptr_t)dst, d1 = d0 + (size_t)(batch * per);
+  const uintptr_t c0 = (uintptr_t)scale, c1 = c0 + (size_t)(batch * rows) * 4;
+  if ((s0 < d1 && d0 < s1) || (s0 < c1 && c0 < s1) || (d0 < c1 && c0 < d1)) return DG_ERR_INVALID;
+  DG_TRY(launch_quantize_e4m3((const bf16*)src, (uint8_t*)dst, scale, batch, rows, cols, (hipStream_t)stream));
   return DG_OK;
 }
 

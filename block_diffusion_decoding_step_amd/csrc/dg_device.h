@@ -78,6 +78,29 @@ struct Frag<float> {
   __device__ __forceinline__ float get(int j) const { return j < 4 ? lo[j] : hi[j - 4]; }
 };
 
+// FP8 (OCP E4M3) operand of two consecutive 32-wide K steps: one 16-byte load per lane, whose two 8-byte halves
+// are the lane's elements of the two steps (the FP8 pair-tiled layout).  E4M3 values are exact in bf16, so the
+// pair decodes without rounding into two bf16 fragments for the bf16 matrix core.
+struct Frag8x2 {
+  u32x4 v;
+  __device__ __forceinline__ void load(const uint8_t* p) { v = *reinterpret_cast<const u32x4*>(p); }
+  __device__ __forceinline__ void load_nt(const uint8_t* p) {
+    v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  }
+  // half h (0: first K step, 1: second) as a bf16 fragment
+  __device__ __forceinline__ Frag<bf16> half(int h) const {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const uint32_t w0 = h ? v[2] : v[0], w1 = h ? v[3] : v[1];
+    const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+    const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+    const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+    Frag<bf16> f;
+    f.v = bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+    return f;
+  }
+};
+
 // acc += A(16 x 32) * B(32 x 16) for one 32-wide K step
 __device__ __forceinline__ void mma(f32x4& acc, const Frag<bf16>& a, const Frag<bf16>& b) {
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);

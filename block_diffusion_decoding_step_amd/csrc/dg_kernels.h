@@ -61,6 +61,10 @@ template <typename T>
 hipError_t launch_embed(const int32_t* tok, const T* E, T* X, int M, int d, int V, hipStream_t s);
 template <typename T>
 hipError_t launch_pack(const T* src, T* dst, int64_t batch, int64_t rows, int64_t cols, hipStream_t s);
+// per-row E4M3 scales and codes of `batch` row-major [rows, cols] bf16 matrices (cols a multiple of 64), codes in
+// the FP8 pair-tiled layout (rows padded to 16 with zeros)
+hipError_t launch_quantize_e4m3(const bf16* src, uint8_t* dst, float* scale, int64_t batch, int64_t rows, int64_t cols,
+                                hipStream_t s);
 // Y (row-major) and / or Yt (fragment-tiled, rows padded to 16); either may be null
 template <typename T>
 hipError_t launch_rmsnorm(const T* X, const T* g, T* Y, T* Yt, int M, int d, float eps, hipStream_t s,
@@ -146,11 +150,15 @@ struct MoeArgs {
   void* out;              // gate_up: H [pairs, F]; down: Yp [pairs, d]
   int d, F;
   int tile_rows;          // as the routing's
+  const float* scale;     // FP8 weights: per-output-channel scales, gate_up [E][2F], down [E][d]
 };
 template <typename T>
 hipError_t launch_moe_gate_up(const MoeArgs& a, hipStream_t s);
 template <typename T>
 hipError_t launch_moe_down(const MoeArgs& a, hipStream_t s);
+// FP8 (E4M3) expert weights in the pair-tiled layout, bf16 activations
+hipError_t launch_moe_gate_up_f8(const MoeArgs& a, hipStream_t s);
+hipError_t launch_moe_down_f8(const MoeArgs& a, hipStream_t s);
 
 // ---- k_attn.hip
 struct AttnArgs {

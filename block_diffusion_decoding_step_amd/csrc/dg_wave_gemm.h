@@ -88,4 +88,81 @@ __device__ __forceinline__ void wave_gemm(f32x4 (&acc)[MT][NT], const T* const (
   wave_gemm_run<T, MT, NT, DEPTH, SA, SB>(acc, fa, fb, ap, bp, ksteps, sa, sb);
 }
 
+// ---------------------------------------------------------------- FP8 B operand (routed experts)
+// acc[mt][nt] += sum_k A[row(mt)][k] * B[col(nt)][k] over npairs pairs of 32-wide K steps, with A in bf16 (ap:
+// this lane's first fragment, consecutive K steps sa elements apart) and B in the FP8 pair-tiled layout (bp:
+// this lane's first 16 bytes, consecutive pairs sb bytes apart; decoded to bf16 in registers).  Same ring
+// discipline as wave_gemm: DEPTH pairs of loads in flight, clamped reloads at the end, no branches in the
+// steady state.
+template <int NT, int DEPTH, bool STREAM>
+__device__ __forceinline__ void wave_gemm_f8_fill(Frag8x2 (&f)[DEPTH][NT], const uint8_t* const (&p)[NT], int npairs,
+                                                  int stride) {
+  const int last = npairs - 1;
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      if constexpr (STREAM) f[d][nt].load_nt(p[nt] + (int64_t)stride * min(d, last));
+      else f[d][nt].load(p[nt] + (int64_t)stride * min(d, last));
+    }
+}
+
+template <int MT, int DEPTH>
+__device__ __forceinline__ void wave_gemm_f8_fill_a(Frag<bf16> (&f)[DEPTH][2][MT], const bf16* const (&p)[MT],
+                                                    int npairs, int sa) {
+  const int last = npairs - 1;
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) f[d][h][mt].load(p[mt] + (int64_t)sa * (2 * min(d, last) + h));
+}
+
+template <int MT, int NT, int DEPTH, bool SB>
+__device__ __forceinline__ void wave_gemm_f8_run(f32x4 (&acc)[MT][NT], Frag<bf16> (&fa)[DEPTH][2][MT],
+                                                 Frag8x2 (&fb)[DEPTH][NT], const bf16* const (&ap)[MT],
+                                                 const uint8_t* const (&bp)[NT], int npairs, int sa, int sb) {
+  const int last = npairs - 1;
+  int s0 = 0;
+  for (; s0 + DEPTH <= npairs; s0 += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const Frag<bf16> b0 = fb[d][nt].half(0), b1 = fb[d][nt].half(1);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          mma(acc[mt][nt], fa[d][0][mt], b0);
+          mma(acc[mt][nt], fa[d][1][mt], b1);
+        }
+      }
+      const int sn = min(s0 + DEPTH + d, last);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) fa[d][h][mt].load(ap[mt] + (int64_t)sa * (2 * sn + h));
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        if constexpr (SB) fb[d][nt].load_nt(bp[nt] + (int64_t)sb * sn);
+        else fb[d][nt].load(bp[nt] + (int64_t)sb * sn);
+      }
+    }
+  }
+  const int rem = npairs - s0;
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d)
+    if (d < rem) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const Frag<bf16> b0 = fb[d][nt].half(0), b1 = fb[d][nt].half(1);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          mma(acc[mt][nt], fa[d][0][mt], b0);
+          mma(acc[mt][nt], fa[d][1][mt], b1);
+        }
+      }
+    }
+}
+
 }  // namespace dg

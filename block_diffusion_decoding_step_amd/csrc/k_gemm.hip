@@ -415,6 +415,204 @@ __global__ __launch_bounds__(256, 2) void k_moe_down_wide(MoeArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- routed experts, FP8 weights
+// The same work units and reductions as above with the expert weights in OCP E4M3 (FP8 pair-tiled layout, one
+// float scale per output channel): each 16-byte weight load covers two K steps and is decoded to bf16 in
+// registers for the bf16 matrix core; the scale of a channel multiplies its fp32 sum before the SwiGLU (gate and
+// up channels each their own) or before the store (down).  Activations stay bf16.  Half the weight bytes of the
+// bf16 kernels, which are bound by exactly those bytes.
+struct DepthF8 {
+  static constexpr int moe1 = 3;  // pairs of K steps in flight, one 16-row M-tile
+  static constexpr int moe2 = 2;  // two M-tiles
+  static constexpr int moe4 = 1;  // three or four M-tiles (wide tiles)
+  static constexpr int down = 3;
+};
+
+template <int MT, bool NTL>
+__device__ __forceinline__ void moe_gate_up_body_f8(const MoeArgs& a, f32x4 (*red)[8][64], int e, int p0, int rows,
+                                                    int c0) {
+  constexpr int NT = 8;
+  const int lane = lane_id(), w = wave_id();
+  const int row16 = lane & 15, kq = (lane >> 4) * 8;
+  const int np = a.d / 64, q = (np + 3) / 4;
+  const int pb = min(w * q, np), pe = min(pb + q, np);
+  const bf16* X = (const bf16*)a.X;
+  const uint8_t* W = (const uint8_t*)a.W + (int64_t)e * 2 * a.F * a.d;
+  constexpr int D = MT == 1 ? DepthF8::moe1 : MT == 2 ? DepthF8::moe2 : DepthF8::moe4;
+  const uint8_t* bp[NT];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ct = min(c0 / 16 + j, a.F / 16 - 1);
+    bp[j] = W + ((int64_t)ct * np + pb) * 1024 + lane * 16;
+    bp[4 + j] = W + ((int64_t)(a.F / 16 + ct) * np + pb) * 1024 + lane * 16;
+  }
+  Frag8x2 fb[D][NT];
+  if (pe > pb) wave_gemm_f8_fill<NT, D, NTL>(fb, bp, pe - pb, 1024);
+  const bf16* ap[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int r = min(16 * mt + row16, rows - 1);
+    ap[mt] = X + (int64_t)a.perm[p0 + r] * a.d + 64 * pb + kq;
+  }
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = zero4();
+  if (pe > pb) {
+    Frag<bf16> fa[D][2][MT];
+    wave_gemm_f8_fill_a<MT, D>(fa, ap, pe - pb, 32);
+    wave_gemm_f8_run<MT, NT, D, NTL>(acc, fa, fb, ap, bp, pe - pb, 32, 1024);
+  }
+  bf16* H = (bf16*)a.out;
+  const int rq = (lane >> 4) * 4;
+  const int c = c0 + 16 * w + row16;  // wave w finishes gate tile w with up tile 4 + w
+  const float sg = a.scale[(int64_t)e * 2 * a.F + min(c, a.F - 1)];
+  const float su = a.scale[(int64_t)e * 2 * a.F + a.F + min(c, a.F - 1)];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    if (mt) __syncthreads();
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) red[w][nt][lane] = acc[mt][nt];
+    __syncthreads();
+    const f32x4 g = red[0][w][lane] + red[1][w][lane] + red[2][w][lane] + red[3][w][lane];
+    const f32x4 u = red[0][4 + w][lane] + red[1][4 + w][lane] + red[2][4 + w][lane] + red[3][4 + w][lane];
+    if (c < a.F) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rr = 16 * mt + rq + r;
+        if (rr < rows) H[(int64_t)(p0 + rr) * a.F + c] = from_f32<bf16>(silu(sg * g[r]) * (su * u[r]));
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void k_moe_gate_up_f8(MoeArgs a) {
+  __shared__ f32x4 red[4][8][64];
+  int4 tile;
+  int col;
+  if (!moe_unit(a, (a.F + 63) / 64, min(*a.n_tiles, a.max_tiles), tile, col)) return;
+  const int c0 = col * 64;
+  if (tile.w > 1) {
+    if (tile.z > 16) moe_gate_up_body_f8<2, false>(a, red, tile.x, tile.y, tile.z, c0);
+    else moe_gate_up_body_f8<1, false>(a, red, tile.x, tile.y, tile.z, c0);
+  } else {
+    if (tile.z > 16) moe_gate_up_body_f8<2, true>(a, red, tile.x, tile.y, tile.z, c0);
+    else moe_gate_up_body_f8<1, true>(a, red, tile.x, tile.y, tile.z, c0);
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void k_moe_gate_up_f8_wide(MoeArgs a) {
+  __shared__ f32x4 red[4][8][64];
+  int4 tile;
+  int col;
+  if (!moe_unit(a, (a.F + 63) / 64, min(*a.n_tiles, a.max_tiles), tile, col)) return;
+  const int c0 = col * 64;
+  if (tile.w > 1) {
+    if (tile.z > 32) moe_gate_up_body_f8<4, false>(a, red, tile.x, tile.y, tile.z, c0);
+    else if (tile.z > 16) moe_gate_up_body_f8<2, false>(a, red, tile.x, tile.y, tile.z, c0);
+    else moe_gate_up_body_f8<1, false>(a, red, tile.x, tile.y, tile.z, c0);
+  } else {
+    if (tile.z > 32) moe_gate_up_body_f8<4, true>(a, red, tile.x, tile.y, tile.z, c0);
+    else if (tile.z > 16) moe_gate_up_body_f8<2, true>(a, red, tile.x, tile.y, tile.z, c0);
+    else moe_gate_up_body_f8<1, true>(a, red, tile.x, tile.y, tile.z, c0);
+  }
+}
+
+template <int MT, bool NTL>
+__device__ __forceinline__ void moe_down_body_f8(const MoeArgs& a, int e, int p0, int rows, int c0) {
+  constexpr int NT = 4;
+  const int lane = lane_id();
+  const int row16 = lane & 15, kq = (lane >> 4) * 8;
+  const bf16* H = (const bf16*)a.X;
+  const uint8_t* W = (const uint8_t*)a.W + (int64_t)e * a.d * a.F;
+  const bf16* ap[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int r = min(16 * mt + row16, rows - 1);
+    ap[mt] = H + (int64_t)(p0 + r) * a.F + kq;
+  }
+  const int np = a.F / 64;
+  const uint8_t* bp[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) bp[nt] = W + (int64_t)min(c0 / 16 + nt, a.d / 16 - 1) * np * 1024 + lane * 16;
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = zero4();
+  constexpr int D = MT <= 2 ? DepthF8::down : DepthF8::moe4;
+  Frag8x2 fb[D][NT];
+  Frag<bf16> fa[D][2][MT];
+  wave_gemm_f8_fill<NT, D, NTL>(fb, bp, np, 1024);
+  wave_gemm_f8_fill_a<MT, D>(fa, ap, np, 32);
+  wave_gemm_f8_run<MT, NT, D, NTL>(acc, fa, fb, ap, bp, np, 32, 1024);
+  bf16* Y = (bf16*)a.out;
+  const int rq = (lane >> 4) * 4;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int c = c0 + 16 * nt + row16;
+    if (c >= a.d) continue;
+    const float sc = a.scale[(int64_t)e * a.d + c];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rr = 16 * mt + rq + r;
+        if (rr < rows) Y[(int64_t)(p0 + rr) * a.d + c] = from_f32<bf16>(sc * acc[mt][nt][r]);
+      }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_moe_down_f8(MoeArgs a) {
+  int4 tile;
+  int col;
+  if (!moe_unit(a, (a.d + 255) / 256, min(*a.n_tiles, a.max_tiles), tile, col)) return;
+  const int c0 = col * 256 + wave_id() * 64;
+  if (c0 >= a.d) return;
+  if (tile.w > 1) {
+    if (tile.z > 16) moe_down_body_f8<2, false>(a, tile.x, tile.y, tile.z, c0);
+    else moe_down_body_f8<1, false>(a, tile.x, tile.y, tile.z, c0);
+  } else {
+    if (tile.z > 16) moe_down_body_f8<2, true>(a, tile.x, tile.y, tile.z, c0);
+    else moe_down_body_f8<1, true>(a, tile.x, tile.y, tile.z, c0);
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void k_moe_down_f8_wide(MoeArgs a) {
+  int4 tile;
+  int col;
+  if (!moe_unit(a, (a.d + 255) / 256, min(*a.n_tiles, a.max_tiles), tile, col)) return;
+  const int c0 = col * 256 + wave_id() * 64;
+  if (c0 >= a.d) return;
+  if (tile.w > 1) {
+    if (tile.z > 32) moe_down_body_f8<4, false>(a, tile.x, tile.y, tile.z, c0);
+    else if (tile.z > 16) moe_down_body_f8<2, false>(a, tile.x, tile.y, tile.z, c0);
+    else moe_down_body_f8<1, false>(a, tile.x, tile.y, tile.z, c0);
+  } else {
+    if (tile.z > 32) moe_down_body_f8<4, true>(a, tile.x, tile.y, tile.z, c0);
+    else if (tile.z > 16) moe_down_body_f8<2, true>(a, tile.x, tile.y, tile.z, c0);
+    else moe_down_body_f8<1, true>(a, tile.x, tile.y, tile.z, c0);
+  }
+}
+
+hipError_t launch_moe_gate_up_f8(const MoeArgs& a, hipStream_t s) {
+  const dim3 grid(moe_grid(a.max_tiles, (a.F + 63) / 64));
+  if (a.tile_rows > kMoeTileRows)
+    hipLaunchKernelGGL(k_moe_gate_up_f8_wide, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_moe_gate_up_f8, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+hipError_t launch_moe_down_f8(const MoeArgs& a, hipStream_t s) {
+  const dim3 grid(moe_grid(a.max_tiles, (a.d + 255) / 256));
+  if (a.tile_rows > kMoeTileRows)
+    hipLaunchKernelGGL(k_moe_down_f8_wide, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_moe_down_f8, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_moe_gate_up(const MoeArgs& a, hipStream_t s) {
   const dim3 grid(moe_grid(a.max_tiles, (a.F + 63) / 64));

@@ -57,6 +57,71 @@ __global__ __launch_bounds__(256) void k_pack(const T* __restrict__ src, T* __re
   }
 }
 
+// ============================================================== FP8 (OCP E4M3) weight quantisation
+// Per-row (output channel) scale s = amax / 448 in fp32 (1 for an all-zero row); each weight w becomes the
+// E4M3 code of w / s rounded to nearest, ties to the even mantissa, magnitudes beyond 448 saturated.  E4M3 is
+// the OCP 8-bit float with 4 exponent bits (bias 7) and 3 mantissa bits, subnormals 0.mmm * 2^-6 and no
+// infinities (0x7F / 0xFF are NaN, 448 the largest finite value).
+__device__ __forceinline__ uint32_t e4m3_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u, mag = u & 0x7FFFFFFFu;
+  if (mag > 0x7F800000u) return sign | 0x7Fu;                      // NaN
+  const float a = __uint_as_float(mag);
+  if (a >= 448.f) return sign | 0x7Eu;                             // saturate
+  if (a < 0.015625f) return sign | (uint32_t)(int)rintf(a * 512.f);  // subnormal spacing 2^-9 (8 -> 2^-6)
+  int e = (int)((mag >> 23) & 0xFF) - 127 + 7;                     // biased E4M3 exponent, 1 .. 15
+  uint32_t keep = (mag >> 20) & 7u, rest = mag & 0xFFFFFu;
+  if (rest > 0x80000u || (rest == 0x80000u && (keep & 1u))) ++keep;
+  if (keep == 8u) { keep = 0u; ++e; }
+  if (e > 15 || (e == 15 && keep == 7u)) return sign | 0x7Eu;
+  return sign | ((uint32_t)e << 3) | keep;
+}
+
+// amax of each row of `batch` row-major [rows, cols] bf16 matrices -> scale; one wave per row
+__global__ __launch_bounds__(256) void k_e4m3_scales(const bf16* __restrict__ src, float* __restrict__ scale,
+                                                     int64_t n_rows, int64_t cols) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave_id();
+  if (row >= n_rows) return;
+  const bf16* p = src + row * cols;
+  float m = 0.f;
+  for (int64_t c = lane_id(); c < cols; c += 64) m = fmaxf(m, fabsf((float)p[c]));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if (lane_id() == 0) scale[row] = m > 0.f ? m / 448.f : 1.f;
+}
+
+// codes in the FP8 pair-tiled layout: 16-row x 64-column blocks of 1024 bytes; lane l's 16 bytes hold row
+// (l & 15), columns 8 (l >> 4) .. +8 of the block's first 32-wide half, then the same of its second half
+// (one 16-byte load gives a lane its A/B fragment elements of two consecutive 32-wide K steps); padded rows 0
+__global__ __launch_bounds__(256) void k_e4m3_pack(const bf16* __restrict__ src, const float* __restrict__ scale,
+                                                   uint8_t* __restrict__ dst, int64_t batch, int64_t rows,
+                                                   int64_t cols, int64_t rows_p) {
+  const int64_t kp = cols / 64;
+  const int64_t per = rows_p / 16 * kp * 64;  // 16-byte lane chunks per matrix
+  const int64_t total = batch * per;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int64_t b = i / per, rem = i % per;
+    const int lane = (int)(rem & 63);
+    const int64_t blk = rem >> 6;
+    const int64_t pk = blk % kp, rt = blk / kp;
+    const int64_t r = rt * 16 + (lane & 15), c = pk * 64 + (lane >> 4) * 8;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (r < rows) {
+      const bf16* row = src + (b * rows + r) * cols;
+      const float sc = scale[b * rows + r];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t q = e4m3_rne((float)row[c + 32 * h + j] / sc);
+          w[2 * h + j / 4] |= q << (8 * (j % 4));
+        }
+    }
+    *reinterpret_cast<uint4*>(dst + (b * rows_p * cols) + rem * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 // ============================================================== RMSNorm
 // Y = X / sqrt(mean(X^2) + eps) * g, fp32 statistics.  One workgroup per row, one thread per 8
 // consecutive columns (blockDim = 64 * ceil(d / 512)); the sum of squares is reduced in a fixed
@@ -566,6 +631,18 @@ hipError_t launch_pack(const T* src, T* dst, int64_t batch, int64_t rows, int64_
   if (g > 65536) g = 65536;
   if (g < 1) g = 1;
   hipLaunchKernelGGL(k_pack<T>, dim3((unsigned)g), dim3(256), 0, s, src, dst, batch, rows, cols, rows_p);
+  return hipGetLastError();
+}
+hipError_t launch_quantize_e4m3(const bf16* src, uint8_t* dst, float* scale, int64_t batch, int64_t rows, int64_t cols,
+                                hipStream_t s) {
+  const int64_t n_rows = batch * rows;
+  hipLaunchKernelGGL(k_e4m3_scales, dim3((unsigned)((n_rows + 3) / 4)), dim3(256), 0, s, src, scale, n_rows, cols);
+  const int64_t rows_p = (rows + 15) / 16 * 16;
+  const int64_t chunks = batch * rows_p / 16 * (cols / 64) * 64;
+  int64_t g = (chunks + 255) / 256;
+  if (g > 65536) g = 65536;
+  if (g < 1) g = 1;
+  hipLaunchKernelGGL(k_e4m3_pack, dim3((unsigned)g), dim3(256), 0, s, src, scale, dst, batch, rows, cols, rows_p);
   return hipGetLastError();
 }
 static inline int row_threads(int d) { return 64 * ((d + 511) / 512); }

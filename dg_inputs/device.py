@@ -84,7 +84,10 @@ def packed_model_weights_device(d: Dims, seed: int = recipe.WEIGHT_SEED) -> dict
                 layer[name] = torch.ones(shape, dtype=torch_dtype(d.dtype), device="cuda")
             else:
                 t = normal_tensor(shape, seed, layer_stream(l, name), recipe.WEIGHT_SIGMA, d.dtype)
-                layer[name] = dg.pack_tensor(t)
+                if d.expert_dtype == "e4m3" and name in dg.EXPERT_FIELDS:
+                    layer[name], layer[name + "_scale"] = dg.quantize_tensor_e4m3(t)
+                else:
+                    layer[name] = dg.pack_tensor(t)
                 del t
         out["layers"].append(layer)
     return out

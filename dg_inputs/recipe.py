@@ -50,6 +50,7 @@ class Dims:
     canvas: int
     dtype: str  # "f32" or "bf16"
     rms_eps: float = 1e-6
+    expert_dtype: str = ""  # "" (as dtype) or "e4m3": routed experts' weights quantised to FP8 per output channel
 
     @property
     def qkv_rows(self) -> int:
@@ -100,7 +101,13 @@ C4 = Workload(
     description="the 30-layer model over a 131072-token prefix, 4 consecutive committed blocks at T=10, bf16",
 )
 
-WORKLOADS = {w.name: w for w in (C0, C1, C2, C3, C4)}
+C3_FP8 = Workload(
+    name="full_loop_fp8", dims=replace(_BIG, expert_dtype="e4m3"), prefix=4096, n_new=26, fixed_steps=10,
+    description="the full-loop workload with the routed experts' weights in FP8 (OCP E4M3, one scale per output "
+                "channel, quantised from the same bf16 weights); everything else bf16",
+)
+
+WORKLOADS = {w.name: w for w in (C0, C1, C2, C3, C4, C3_FP8)}
 
 
 def layer_stream(layer: int, tensor: str) -> int:

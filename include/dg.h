@@ -72,7 +72,9 @@ typedef enum dg_status {
   DG_ERR_HIP = -5          /* a HIP runtime/launch call failed; see dg_last_hip_error() */
 } dg_status;
 
-typedef enum dg_dtype { DG_F32 = 0, DG_BF16 = 1 } dg_dtype;
+/* DG_E4M3: OCP 8-bit float (4 exponent bits, bias 7, 3 mantissa bits, largest value 448), only for the
+ * routed experts' weights (dg_config.expert_dtype), with one float scale per output channel. */
+typedef enum dg_dtype { DG_F32 = 0, DG_BF16 = 1, DG_E4M3 = 2 } dg_dtype;
 
 /* Why a block stopped ([P2] "How Diffusion Changes the Equation": entropy below a
  * threshold, or predictions unchanged over two consecutive passes, or 48 passes;
@@ -108,6 +110,11 @@ typedef struct dg_config {
   int32_t dtype;      /* dg_dtype: storage type of weights, activations and KV */
   float rms_eps;      /* RMSNorm epsilon */
   float rope_theta;   /* reserved; must be 0 */
+  /* Storage of the routed experts' weights (w_gate_up, w_down): 0 = dtype; DG_E4M3 = FP8 codes in the
+   * FP8 pair-tiled layout (dg_quantize_e4m3) with per-output-channel scales (dg_layer_weights
+   * w_gate_up_scale, w_down_scale); needs dtype DG_BF16 and d_model, ffn_expert multiples of 64.
+   * ([P2] "Benchmark Numbers": the headline figure runs FP8 weights; activations stay bf16 here.) */
+  int32_t expert_dtype;
 } dg_config;
 
 typedef struct dg_layer_weights {
@@ -120,6 +127,8 @@ typedef struct dg_layer_weights {
   const void* w_down;
   const void* ws_gate_up;
   const void* ws_down;
+  const float* w_gate_up_scale;  /* expert_dtype DG_E4M3: [n_experts][2*ffn_expert] (else ignored, may be NULL) */
+  const float* w_down_scale;     /* expert_dtype DG_E4M3: [n_experts][d_model] */
 } dg_layer_weights;
 
 typedef struct dg_weights {
@@ -243,6 +252,21 @@ int dg_packed_elems(int64_t rows, int64_t cols, int64_t* h_elems);
  * This is how callers bring weights into the layout dg_weights expects. */
 int dg_pack_matrix(const void* src, void* dst, int64_t batch, int64_t rows, int64_t cols, int32_t dtype,
                    void* stream);
+
+/* Bytes of the FP8 pair-tiled form of a rows x cols matrix (rows rounded up to 16; cols a positive multiple of
+ * 64, else 0 is written and DG_ERR_INVALID returned).  Host-only. */
+int dg_packed_bytes_e4m3(int64_t rows, int64_t cols, int64_t* h_bytes);
+
+/* Quantise `batch` row-major [rows, cols] bf16 matrices at src (cols a multiple of 64) to OCP E4M3 with one
+ * scale per row (output channel): scale[b * rows + r] = amax / 448 of row r (1 for an all-zero row), code =
+ * the E4M3 value nearest to w / scale (ties to the even mantissa, beyond 448 saturated; the division and the
+ * decision in float32).  Codes go to dst in the FP8 pair-tiled layout (batch * dg_packed_bytes_e4m3 bytes):
+ * with R rows padded to 16, element (r, c) is byte
+ *     ((r/16)*(cols/64) + c/64)*1024 + ((r%16) + 16*((c%32)/8))*16 + ((c%64)/32)*8 + c%8,
+ * so that one 16-byte load gives a 64-lane wave's lane its elements of two consecutive 32-wide K steps.
+ * Padded rows are zero.  src, dst 16-byte aligned, scale 4-byte aligned; no overlap. */
+int dg_quantize_e4m3(const void* src, void* dst, float* scale, int64_t batch, int64_t rows, int64_t cols,
+                     void* stream);
 
 /* Bytes of workspace needed by any call that processes up to max_tokens rows at
  * once (use cfg->canvas for denoising; a prefill chunk size for prefill/commit;
@@ -385,6 +409,30 @@ int dg_generate_blocks_overlapped(const dg_config* cfg, const dg_weights* w, dg_
  * kv->len + canvas <= capacity and a workspace of canvas rows; synchronises `stream` once. */
 int dg_verify_block(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const int32_t* draft, int32_t* ar_pred,
                     int32_t* h_accepted, int32_t* h_next_token, void* ws, size_t ws_bytes, const dg_side* side, void* stream);
+
+/* Status of dg_generate_speculative (host struct). */
+typedef struct dg_spec_status {
+  int32_t rounds;      /* drafts verified */
+  int32_t tokens;      /* tokens written to tokens_out (n_tokens) */
+  int32_t accepted;    /* draft tokens accepted over all rounds (>= tokens; the last round's surplus stays cached) */
+  int32_t next_token;  /* the causal prediction for the position after the last accepted token */
+} dg_spec_status;
+
+/* Self-speculative decoding ([P1] "The result that complicates 'faster, not smarter'": the same weights draft a
+ * block by diffusion and check it autoregressively over one shared KV cache).  first_token is the known token at
+ * position kv->len (e.g. the causal prediction after the prompt).  Each round r drafts a block by diffusion at
+ * the cache's end under `sampler` (block id block0 + r, the commit deferred), puts the known token in slot 0 of
+ * the draft and verifies it as dg_verify_block does: the accepted prefix is committed and written to tokens_out,
+ * and the causal prediction after it is the next round's known token.  Rounds run until n_tokens tokens are out
+ * (device tokens_out [n_tokens]); the output equals greedy autoregressive decoding from first_token, and the
+ * drafts decide how many tokens each causal pass confirms.  h_accepted (host, nullable, n_tokens entries)
+ * receives each round's accepted count, h_status the totals.  kv->len grows by every accepted token.  Needs
+ * kv->len + n_tokens - 1 + canvas <= capacity (DG_ERR_KV_FULL) and a workspace of canvas rows; synchronises the
+ * stream once per round.  DG_ERR_INVALID for n_tokens < 1 or first_token outside [0, vocab). */
+int dg_generate_speculative(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const dg_sampler* sampler,
+                            uint32_t block0, int32_t first_token, int32_t n_tokens, int32_t* tokens_out,
+                            int32_t* h_accepted, dg_spec_status* h_status, void* ws, size_t ws_bytes,
+                            const dg_side* side, void* stream);
 
 /* --- finer-grained calls of the same path (each is one stage of dg_denoise_step) --- */
 

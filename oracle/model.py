@@ -243,12 +243,13 @@ class Model:
             kv.append(l, k, v)
         return x, LayerTrace(idx=idx, w=rw, router_logits=rlog, gap=gap, hidden=x)
 
-    def layer_rows(self, l: int, x: np.ndarray, kv: KVCache, causal: bool, rows: np.ndarray):
+    def layer_rows(self, l: int, x: np.ndarray, kv: KVCache, causal: bool, rows: np.ndarray, return_kv=False):
         """``layer(l, x, kv, causal, append=False)`` evaluated for the rows ``rows`` only.
 
         Every row's keys and values are still formed (all of them take part in the
         attention of the rows asked for); everything after the attention is per row.
-        Returns (x_out[rows], LayerTrace of those rows)."""
+        Returns (x_out[rows], LayerTrace of those rows), and with ``return_kv`` also the
+        keys and values of all the new rows ([Hkv, n, Dh] each, as the layer stores them)."""
         d, w, rnd = self.d, self.w["layers"][l], self.rnd
         hq, hkv, dh = d.n_heads, d.n_kv_heads, d.head_dim
         rows = np.asarray(rows, dtype=np.int64)
@@ -270,7 +271,10 @@ class Model:
                        w.get("w_down_scale"))
         ys = swiglu_ffn(xn2, w["ws_gate_up"], w["ws_down"], rnd)
         xr = rnd(xr + ys + y)
-        return xr, LayerTrace(idx=idx, w=rw, router_logits=rlog, gap=gap, hidden=xr)
+        tr = LayerTrace(idx=idx, w=rw, router_logits=rlog, gap=gap, hidden=xr)
+        if return_kv:
+            return xr, tr, k, v
+        return xr, tr
 
     def embed(self, tokens) -> np.ndarray:
         return self.w["embed"][np.asarray(tokens, dtype=np.int64)]

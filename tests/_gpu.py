@@ -21,7 +21,7 @@ class Session:
         if weights is None:
             weights = gdev.packed_model_weights_device(d)
         elif not packed:
-            weights = dg.pack_weights(weights)
+            weights = dg.pack_weights(weights, d.expert_dtype)
         self.w = weights
         self.weights = dg.Weights(weights["embed"], weights["final_norm"], weights["layers"])
         cap = ((capacity + kv_capacity_round - 1) // kv_capacity_round) * kv_capacity_round
@@ -108,6 +108,25 @@ def compare_routing(g_idx: np.ndarray, g_w: np.ndarray, g_logits: np.ndarray, o_
 
 
 # ----------------------------------------------------------------------------- teacher-forced oracle checks
+# Both sides round at the same bf16 storage points, but the values before a rounding differ in the last fp32 bits,
+# so a sizeable share of the attention residual's elements land one bf16 ulp apart (measured at the full widths:
+# a median of 2.7e-3 relative to a row's largest element), which moves a token's router logits by up to ~7e-3.
+# Two consequences for comparisons that run several bf16 layers free (each side on its own outputs):
+#   * a token whose k-th and (k+1)-th router logits are closer than ROUTING_GAP may take another expert on the two
+#     sides, and its later outputs then legitimately differ: such tokens are left out of later comparisons;
+#   * the one-ulp differences of one layer's output enter the next layer's keys and values as extra error of the
+#     same order as the bar itself, so keys and values are compared free-running at layer 0 only (whose inputs
+#     are exact); every layer's keys, values and outputs are compared on the GPU's own inputs in
+#     test_gpu_teacher_forced.py, and the deeper cache rows written here are checked through the passes that read
+#     them (tokens and entropy of the next pass against the oracle on the GPU's cache).
+ROUTING_GAP = 3e-2
+# The same one-ulp differences reach the vocabulary logits of a free-running multi-layer pass: about 2e-3 per logit
+# (sqrt of the ~850 differing elements of a 2816-wide row, times one bf16 ulp of the normalised row, times the
+# 0.02 scale of the head), so the largest of a slot's 262144 logits differs by up to ~1.2e-2 (five standard
+# deviations).  The 1e-2 margin of teacher-forced comparisons is then too narrow; free-running bf16 passes of more
+# than one layer compare tokens where the oracle's top-2 margin exceeds FREE_MARGIN.
+FREE_MARGIN = 5e-2
+
 
 def gpu_cache_as_oracle(sess: Session, n_rows: int):
     """The GPU's first n_rows cache rows of every layer as an oracle KVCache (the teacher-forced context)."""
@@ -118,12 +137,17 @@ def gpu_cache_as_oracle(sess: Session, n_rows: int):
     return kv
 
 
-def check_pass_on_gpu_cache(model, kv, canvas, tokens, mean_entropy, tol, margin=1e-2) -> int:
-    """The oracle's pass over `canvas` with the cache `kv` against a GPU pass's tokens (compared where the
-    oracle's top-2 margin exceeds `margin`) and mean entropy (within tol).  Returns the slots compared."""
+def check_pass_on_gpu_cache(model, kv, canvas, tokens, mean_entropy, tol, margin=None, gap=ROUTING_GAP) -> int:
+    """The oracle's pass over `canvas` with the cache `kv` against a GPU pass's tokens, compared where the oracle's
+    top-2 margin exceeds `margin` (1e-2; FREE_MARGIN for bf16 models of more than one layer) and no layer's
+    routing of the slot sat within `gap` of a tie, and its mean entropy (within tol).  Returns the slots
+    compared."""
     from oracle import sampler as osm
-    rec, _ = osm.denoise_pass(model, kv, canvas)
-    sel = rec.margin > margin
+    if margin is None:
+        margin = FREE_MARGIN if (model.d.dtype == "bf16" and model.d.n_layers > 1) else 1e-2
+    rec, _ = osm.denoise_pass(model, kv, canvas, keep_traces=True)
+    steady = np.all([tr.gap >= gap for tr in rec.traces], axis=0)
+    sel = (rec.margin > margin) & steady
     bad = np.nonzero(sel & (np.asarray(tokens) != rec.pred))[0]
     assert bad.size == 0, f"tokens differ away from a near-tie at slots {bad[:10]}"
     ref = float(np.mean(rec.ent))
@@ -131,14 +155,35 @@ def check_pass_on_gpu_cache(model, kv, canvas, tokens, mean_entropy, tol, margin
     return int(sel.sum())
 
 
+def check_causal_rows(sess: Session, model, kv, tokens, tol, gap=ROUTING_GAP, layers=None) -> int:
+    """Run `tokens` causally through the oracle after the cache `kv` (the rows before them), layer by layer, and
+    compare the keys and values each of the first `layers` layers appends (default: all in fp32, layer 0 in
+    bf16, see above) with the GPU's cache rows at the same positions.  A row whose routing at some layer sat
+    within `gap` of a tie is left out from the next layer on.  Returns the rows left out."""
+    r0 = kv.length
+    if layers is None:
+        layers = sess.d.n_layers if sess.d.dtype == "f32" else min(1, sess.d.n_layers)
+    x = model.embed(np.asarray(tokens, dtype=np.int64))
+    keep = np.ones(len(tokens), dtype=bool)
+    for l in range(layers):
+        x, tr = model.layer(l, x, kv, causal=True, append=True)
+        gk, gv = sess.kv_numpy(l, r0 + len(tokens))
+        rk = allclose_report(gk[:, r0:][:, keep], kv.k[l][:, r0:][:, keep], *tol)
+        rv = allclose_report(gv[:, r0:][:, keep], kv.v[l][:, r0:][:, keep], *tol)
+        assert rk[0] and rv[0], (l, rk, rv, int((~keep).sum()))
+        keep = keep & (tr.gap >= gap)
+    return int((~keep).sum())
+
+
 def check_commit_on_gpu_cache(model, kv, tokens, sess: Session, tol):
     """Commit `tokens` in the oracle after the cache `kv` (the GPU's rows before them) and compare the rows it
-    appends with the GPU's cache rows at the same positions, every layer."""
-    from oracle import sampler as osm
-    r0 = kv.length
-    osm.commit(model, kv, np.asarray(tokens, dtype=np.int64))
-    for l in range(sess.d.n_layers):
-        gk, gv = sess.kv_numpy(l, kv.length)
-        rk = allclose_report(gk[:, r0:], kv.k[l][:, r0:], *tol)
-        rv = allclose_report(gv[:, r0:], kv.v[l][:, r0:], *tol)
-        assert rk[0] and rv[0], (l, rk, rv)
+    appends with the GPU's cache rows at the same positions (the layers check_causal_rows compares)."""
+    return check_causal_rows(sess, model, kv, tokens, tol)
+
+
+def check_prompt_cache(sess: Session, model, prompt, tol, gap=ROUTING_GAP):
+    """Free-running prefill parity of the GPU's cache rows [0, len(prompt)) against the oracle's prefill (the layers
+    check_causal_rows compares).  Returns the number of rows left out."""
+    from oracle import model as om
+    d = sess.d
+    return check_causal_rows(sess, model, om.KVCache(d.n_layers, d.n_kv_heads, d.head_dim), prompt, tol, gap)

@@ -18,9 +18,14 @@ def oracle_dims(d: recipe.Dims) -> om.Dims:
 
 
 def oracle_model(d: recipe.Dims, storage=None) -> om.Model:
+    """The oracle model of the seeded weights (or of `storage`); with FP8 experts their matrices are quantised by
+    the oracle's own quantiser."""
     if storage is None:
         storage = dg_inputs.model_weights_host(d)
-    return om.Model(oracle_dims(d), om.weights_to_f64(storage, d.dtype))
+    w = om.weights_to_f64(storage, d.dtype)
+    if d.expert_dtype == "e4m3":
+        w["layers"] = [om.fp8_expert_layer(l) for l in w["layers"]]
+    return om.Model(oracle_dims(d), w)
 
 
 def oracle_sampler(w: recipe.Workload, **kw) -> osm.Sampler:

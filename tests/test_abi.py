@@ -21,7 +21,7 @@ HEADER = os.path.join(ROOT, "include", "dg.h")
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(dg_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(dg_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_documented_calls():

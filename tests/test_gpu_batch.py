@@ -105,7 +105,7 @@ def test_c3_two_layers_batch_against_oracle(overlapped):
     Every sequence is checked against the oracle on the GPU's context (teacher-forced): its tokens where the
     oracle's top-2 margin exceeds 1e-2, its mean entropy, and each committed block's cache rows, every layer,
     at the bf16 bar; the prompt caches are checked free-running."""
-    from tests._gpu import check_commit_on_gpu_cache, check_pass_on_gpu_cache, gpu_cache_as_oracle
+    from tests._gpu import check_commit_on_gpu_cache, check_pass_on_gpu_cache, check_prompt_cache, gpu_cache_as_oracle
     d = replace(recipe.C3.dims, n_layers=2)
     S = d.canvas
     prefixes, calls = [512, 300, 64, 700], ([[3, 1, 4, 1], [5, 9, 2, 6]] if overlapped else [[3, 1, 4, 1]])
@@ -113,11 +113,8 @@ def test_c3_two_layers_batch_against_oracle(overlapped):
     sessions = _sessions(d, prefixes)
     model = oracle_model(d)
     for b, (s, p) in enumerate(zip(sessions, prefixes)):  # prompt caches, free-running
-        kv = om.KVCache(d.n_layers, d.n_kv_heads, d.head_dim)
-        osm.prefill(model, kv, dg_inputs.prompt_tokens(p, d.vocab, seed=b + 1))
-        for l in range(d.n_layers):
-            gk, gv = s.kv_numpy(l, p)
-            assert allclose_report(gk, kv.k[l], *BF16_TOL)[0] and allclose_report(gv, kv.v[l], *BF16_TOL)[0], (b, l)
+        out = check_prompt_cache(s, model, dg_inputs.prompt_tokens(p, d.vocab, seed=b + 1), BF16_TOL)
+        log(f"seq {b} prompt cache: {out} rows near a routing tie left out")
     n = len(sessions)
     ws_bytes = dg.dg_workspace_size(sessions[0].cfg, (2 if overlapped else 1) * n * S)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")

@@ -1,0 +1,203 @@
+"""GPU parity of the FP8 routed experts (OCP E4M3 weights, one float scale per output channel, bf16 activations)
+against the oracle's FP8 model.
+
+The pages' headline figures run FP8 weights ([P2] "DiffusionGemma 26B: How Google's Text Diffusion Model
+Generates Tokens in Parallel", "Benchmark Numbers").  Checked here:
+  * the quantiser: codes and scales bit-exact against the oracle's quantiser, on crafted rows (every E4M3 tie,
+    zero rows, saturation) and on seeded expert weights at the full widths;
+  * one full-size MoE layer (d 2816, 128 experts top-8 + shared, 2048-key prefix) with FP8 experts;
+  * a four-layer FP8 model at the full widths: one canvas pass teacher-forced layer by layer, and the head.
+Bars as for bf16: 2e-2 abs/rel on hidden states and keys/values, routing by compare_routing, argmax where the
+oracle's top-2 margin exceeds 1e-2.
+"""
+from __future__ import annotations
+
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+import block_diffusion_decoding_step_amd as dg  # noqa: E402
+import dg_inputs  # noqa: E402
+from dg_inputs import device as gdev  # noqa: E402
+from dg_inputs import recipe  # noqa: E402
+from oracle import model as om  # noqa: E402
+from oracle import numerics  # noqa: E402
+from oracle import sampler as osm  # noqa: E402
+from tests._gpu import Session, allclose_report, compare_routing, to_f64  # noqa: E402
+from tests._helpers import oracle_dims, oracle_model  # noqa: E402
+
+BF16_TOL = (2e-2, 2e-2)
+MARGIN = 1e-2
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def _untile(codes: np.ndarray, batch: int, rows: int, cols: int) -> np.ndarray:
+    """FP8 pair-tiled bytes -> row-major [batch, rows, cols] codes (the layout dg_quantize_e4m3 documents)."""
+    rp = (rows + 15) // 16 * 16
+    a = codes.reshape(batch, rp // 16, cols // 64, 4, 16, 2, 8)      # b, rt, pair, q, r%16, half, j
+    a = a.transpose(0, 1, 4, 2, 5, 3, 6).reshape(batch, rp, cols)   # c = 64 pair + 32 half + 8 q + j
+    assert np.all(a[:, rows:] == 0), "padded rows are not zero"
+    return a[:, :rows]
+
+
+def _bf16_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def _quantize_on_gpu(w_bits: np.ndarray):
+    b, r, c = w_bits.shape
+    codes, scale = dg.quantize_tensor_e4m3(_bf16_dev(w_bits))
+    torch.cuda.synchronize()
+    return _untile(codes.cpu().numpy(), b, r, c), scale.cpu().numpy().reshape(b, r)
+
+
+def _bf16_bits(x):
+    return (np.asarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_quantize_crafted_rows_bit_exact():
+    """Rows whose largest magnitude is 448 * 2^-k (so the scale is 2^-k exactly and every quotient is exact): the
+    other entries sit on every midpoint between neighbouring E4M3 values (ties to the even mantissa), a hair
+    either side of them, on the codes themselves and beyond the largest value; plus an all-zero row and a row
+    with one nonzero entry.  Codes and scales equal the oracle's bit for bit; padded rows are zero."""
+    pos = numerics.e4m3_decode(np.arange(0x7F))
+    mids = (pos[:-1] + pos[1:]) / 2
+    vals = np.concatenate([mids, -mids, pos, -pos, mids * (1 + 2 ** -7), mids * (1 - 2 ** -7)])
+    vals = numerics.bf16_round(vals)                       # exactly representable rows (bf16 storage)
+    cols = 128
+    rows = []
+    for k, chunk in enumerate(np.array_split(vals, len(vals) // (cols - 1) + 1)):
+        s = 2.0 ** -(k % 5)
+        row = np.zeros(cols)
+        row[0] = 448.0 * s
+        row[1:1 + len(chunk)] = np.clip(chunk, -448, 448) * s
+        rows.append(row)
+    rows.append(np.zeros(cols))
+    one = np.zeros(cols)
+    one[77] = -3.0e-3
+    rows.append(one)
+    w = np.stack(rows)[None].astype(np.float32)
+    bits = _bf16_bits(w)
+    codes, scale = _quantize_on_gpu(bits)
+    ref_codes, ref_scale = numerics.quantize_e4m3_rows(numerics.from_storage(bits, "bf16").astype(np.float32))
+    assert np.array_equal(scale, ref_scale)
+    bad = np.nonzero(codes != ref_codes)
+    assert bad[0].size == 0, f"{bad[0].size} codes differ, first at {[(int(i), int(j), int(k)) for i, j, k in zip(*bad)][:5]}"
+
+
+def test_quantize_seeded_expert_weights_bit_exact():
+    """The first four experts of a full-width layer's gate/up weights ([4, 1408, 2816], the seeded N(0, 0.02)
+    draw): codes and scales equal the oracle's bit for bit."""
+    d = recipe.C3.dims
+    shape = (4, 2 * d.ffn_expert, d.d_model)
+    bits = dg_inputs.normal(shape, recipe.WEIGHT_SEED, recipe.layer_stream(0, "w_gate_up"), recipe.WEIGHT_SIGMA,
+                            "bf16")
+    codes, scale = _quantize_on_gpu(bits)
+    ref_codes, ref_scale = numerics.quantize_e4m3_rows(numerics.from_storage(bits, "bf16").astype(np.float32))
+    assert np.array_equal(scale, ref_scale)
+    assert np.array_equal(codes, ref_codes)
+
+
+def test_fp8_layer_full_size():
+    """One full-size MoE layer with FP8 experts: 256 canvas rows over a 2048-key prefix (bidirectional), hidden
+    states where the routing agrees and the canvas keys/values against the oracle's FP8 layer."""
+    d = replace(recipe.C1.dims, expert_dtype="e4m3")
+    S, P = d.canvas, recipe.C1.prefix
+    log("fp8 layer: device weights")
+    w = {"embed": torch.zeros((8, d.d_model), dtype=torch.bfloat16, device="cuda"),
+         "final_norm": torch.ones(d.d_model, dtype=torch.bfloat16, device="cuda"),
+         "layers": [gdev.layer_weights_device(d, 0)]}
+    sess = Session(d, capacity=P + S, weights=w)
+    k = dg_inputs.normal((d.n_kv_heads, P, d.head_dim), recipe.INPUT_SEED, recipe.STREAM_PREFIX_K, 1.0, "bf16")
+    v = dg_inputs.normal((d.n_kv_heads, P, d.head_dim), recipe.INPUT_SEED, recipe.STREAM_PREFIX_V, 1.0, "bf16")
+    sess.k[0, :, :P, :] = _bf16_dev(k)
+    sess.v[0, :, :, :P] = _bf16_dev(v.transpose(0, 2, 1))
+    sess.kv.len = P
+    x_host = dg_inputs.hidden((S, d.d_model), "bf16")
+    x_dev = _bf16_dev(x_host)
+    y_dev = torch.empty_like(x_dev)
+    dbg = {"route_idx": torch.empty((S, d.top_k), dtype=torch.int32, device="cuda"),
+           "route_w": torch.empty((S, d.top_k), dtype=torch.float32, device="cuda"),
+           "router_logits": torch.empty((S, d.n_experts), dtype=torch.float32, device="cuda")}
+    dg.dg_layer_forward(sess.cfg, sess.weights, 0, sess.kv, x_dev, y_dev, S, 0, dbg, sess.ws, sess.ws_bytes,
+                        side=sess.side)
+    torch.cuda.synchronize()
+    log("fp8 layer: oracle")
+    lw = om.fp8_expert_layer({n: numerics.from_storage(a, "bf16") for n, a in dg_inputs.layer_weights_host(d, 0).items()})
+    model = om.Model(oracle_dims(d), {"embed": None, "final_norm": None, "layers": [lw]})
+    kv = om.KVCache(1, d.n_kv_heads, d.head_dim)
+    kv.k[0], kv.v[0] = numerics.from_storage(k, "bf16"), numerics.from_storage(v, "bf16")
+    y_ref, tr = model.layer(0, numerics.from_storage(x_host, "bf16"), kv, False, append=True)
+    same = compare_routing(dbg["route_idx"].cpu().numpy(), dbg["route_w"].cpu().numpy(),
+                           dbg["router_logits"].cpu().numpy(), tr.router_logits, tr.idx, BF16_TOL)
+    ok, worst, at = allclose_report(to_f64(y_dev)[same], y_ref[same], *BF16_TOL)
+    log(f"fp8 layer: {int((~same).sum())} routing flips at ties; worst excess {worst:+.2e}")
+    assert ok, ("hidden", worst, at)
+    assert int((~same).sum()) <= S // 20
+    gk, gv = sess.kv_numpy(0, P + S)
+    assert allclose_report(gk[:, P:], kv.k[0][:, P:], *BF16_TOL)[0]
+    assert allclose_report(gv[:, P:], kv.v[0][:, P:], *BF16_TOL)[0]
+    # the FP8 layer is a different computation from the bf16 one: its outputs move by more than the bf16 bar
+    lw16 = {n: numerics.from_storage(a, "bf16") for n, a in dg_inputs.layer_weights_host(d, 0).items()}
+    kv16 = om.KVCache(1, d.n_kv_heads, d.head_dim)
+    kv16.k[0], kv16.v[0] = kv.k[0][:, :P], kv.v[0][:, :P]
+    y16, _ = om.Model(oracle_dims(replace(d, expert_dtype="")), {"embed": None, "final_norm": None,
+                                                                  "layers": [lw16]}).layer(
+        0, numerics.from_storage(x_host, "bf16"), kv16, False, append=False)
+    assert np.max(np.abs(y16 - y_ref)) > 1e-2
+
+
+def test_fp8_four_layers_teacher_forced_and_head():
+    """A four-layer FP8 model at the full widths over a 512-token prompt: one canvas pass, each layer compared on
+    the GPU's input rows and cache (the prompt's layer-0 keys/values checked free-running), and the head on every
+    slot."""
+    from tests._gpu import check_prompt_cache
+    d = replace(recipe.C3.dims, n_layers=4, expert_dtype="e4m3")
+    P, S = 512, d.canvas
+    log("fp8 4 layers: device weights")
+    sess = Session(d, capacity=P + S, max_tokens=S)
+    prompt = dg_inputs.prompt_tokens(P, d.vocab)
+    sess.prefill(prompt)
+    canvas = osm.initial_canvas(recipe.INPUT_SEED, 0, S, d.vocab)
+    L = d.n_layers
+    dbg = {"hidden": torch.empty((L, S, d.d_model), dtype=torch.bfloat16, device="cuda"),
+           "route_idx": torch.empty((L, S, d.top_k), dtype=torch.int32, device="cuda"),
+           "route_w": torch.empty((L, S, d.top_k), dtype=torch.float32, device="cuda"),
+           "router_logits": torch.empty((L, S, d.n_experts), dtype=torch.float32, device="cuda")}
+    pred, conf, ent = sess.denoise(canvas, dbg=dbg)
+    torch.cuda.synchronize()
+    log("fp8 4 layers: oracle")
+    model = oracle_model(d)
+    left = check_prompt_cache(sess, model, prompt, BF16_TOL)
+    log(f"fp8 4 layers: prompt cache checked ({left} rows near a routing tie left out)")
+    hid = [to_f64(dbg["hidden"][l]) for l in range(L)]
+    x = model.embed(canvas)
+    for l in range(L):
+        if l:
+            x = hid[l - 1]
+        kv = om.KVCache(L, d.n_kv_heads, d.head_dim)
+        kv.k[l], kv.v[l] = sess.kv_numpy(l, P)
+        xo, tr = model.layer(l, x, kv, causal=False, append=False)
+        same = compare_routing(dbg["route_idx"][l].cpu().numpy(), dbg["route_w"][l].cpu().numpy(),
+                               dbg["router_logits"][l].cpu().numpy(), tr.router_logits, tr.idx, BF16_TOL)
+        ok, worst, at = allclose_report(hid[l][same], xo[same], *BF16_TOL)
+        log(f"fp8 layer {l}: routing flips {int((~same).sum())}; worst excess {worst:+.2e}")
+        assert ok, (l, worst, at)
+        assert int((~same).sum()) <= 4
+    opred, oconf, oent, margin = om.head_stats(hid[L - 1], model.w["final_norm"], model.w["embed"], 1.0, d.rms_eps,
+                                               numerics.bf16_round)
+    sel = margin > MARGIN
+    assert np.array_equal(pred.cpu().numpy()[sel], opred[sel])
+    assert allclose_report(to_f64(ent), oent, *BF16_TOL)[0]
+    assert allclose_report(to_f64(conf), oconf, *BF16_TOL)[0]
+    log(f"fp8 4 layers: head {int(sel.sum())}/{S} argmax compared")

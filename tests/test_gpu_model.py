@@ -234,16 +234,14 @@ def test_bf16_overlapped_commits_against_oracle():
     block is checked against the oracle on the GPU's context (teacher-forced): its tokens where the oracle's
     top-2 margin exceeds 1e-2 and its mean entropy, then each committed block's cache rows, every layer, at the
     bf16 bar."""
-    from tests._gpu import check_commit_on_gpu_cache, check_pass_on_gpu_cache, gpu_cache_as_oracle
+    from tests._gpu import check_commit_on_gpu_cache, check_pass_on_gpu_cache, check_prompt_cache, gpu_cache_as_oracle
     d = replace(recipe.C3.dims, n_layers=2)
     P, S = 384, d.canvas
     sess = Session(d, capacity=P + 4 * S, max_tokens=2 * S)
     prompt = dg_inputs.prompt_tokens(P, d.vocab)
     sess.prefill(prompt)
     model = oracle_model(d)
-    kv = om.KVCache(d.n_layers, d.n_kv_heads, d.head_dim)
-    osm.prefill(model, kv, prompt)
-    _check_kv(sess, kv, BF16_TOL)
+    log(f"prompt cache: {check_prompt_cache(sess, model, prompt, BF16_TOL)} rows near a routing tie left out")
     sp = dg.make_sampler(26, fixed_steps=1)
     outs = [sess.i32(S) for _ in range(3)]
     pending = None

@@ -64,18 +64,10 @@ def _dbg_rows(d, n, with_hidden_layers=0):
     return out
 
 
-def _kv_of_rows(x64, lw, d):
-    """Keys and values of rows x (layer input) as the layer stores them: bf16 of rms(x) g_attn W_{k,v}^T."""
-    hq, hkv, dh = d.n_heads, d.n_kv_heads, d.head_dim
-    xn = numerics.bf16_round(om.rmsnorm(x64, lw["attn_norm"], d.rms_eps))
-    kvp = xn @ lw["wqkv"][hq * dh:].T
-    n = x64.shape[0]
-    k = numerics.bf16_round(kvp[:, :hkv * dh]).reshape(n, hkv, dh).transpose(1, 0, 2)
-    v = numerics.bf16_round(kvp[:, hkv * dh:]).reshape(n, hkv, dh).transpose(1, 0, 2)
-    return k, v
-
-
-def test_c3_teacher_forced_every_layer():
+@pytest.fixture(scope="module")
+def c3_run():
+    """The GPU side, once: the prompt run layer by layer through dg_layer_forward (each layer's input rows kept),
+    then one canvas pass with per-layer dumps."""
     wl = recipe.C3
     d = wl.dims
     P, S, L = wl.prefix, d.canvas, d.n_layers
@@ -86,7 +78,7 @@ def test_c3_teacher_forced_every_layer():
                                  "bf16")
     x = emb_nat[torch.from_numpy(prompt.astype(np.int64)).cuda()].contiguous()
     del emb_nat
-    # prefill layer by layer: x_in[l] are the prompt rows entering layer l
+    # prefill layer by layer: pre_in[l] are the prompt rows entering layer l
     sample = np.array([0, 1, 2, 63, 64, 1000, 2046, 2047, 2048, 2049, 3000, 4094, 4095])
     pre_in, pre_out, pre_route = [], [], []
     for l in range(L):
@@ -111,51 +103,58 @@ def test_c3_teacher_forced_every_layer():
     dbg = _dbg_rows(d, S, with_hidden_layers=L)
     pred, conf, ent = sess.denoise(canvas, dbg=dbg)
     torch.cuda.synchronize()
-    hid = dbg["hidden"].cpu()
-    ridx, rw, rlog = (dbg[k].cpu().numpy() for k in ("route_idx", "route_w", "router_logits"))
-    kv_np = [sess.kv_numpy(l, P + S) for l in range(L)]
-    emb_rows = numerics.from_storage(dg_inputs.embed_host(d, rows=canvas), "bf16")
-    dims1 = oracle_dims(replace(d, n_layers=1))
+    run = dict(d=d, P=P, S=S, L=L, sample=sample, pre_in=pre_in, pre_out=pre_out, pre_route=pre_route,
+               hid=dbg["hidden"].cpu(), ridx=dbg["route_idx"].cpu().numpy(), rw=dbg["route_w"].cpu().numpy(),
+               rlog=dbg["router_logits"].cpu().numpy(), kv_np=[sess.kv_numpy(l, P + S) for l in range(L)],
+               emb_rows=numerics.from_storage(dg_inputs.embed_host(d, rows=canvas), "bf16"),
+               pred=pred.cpu().numpy(), conf=to_f64(conf), ent=to_f64(ent))
+    del sess
+    torch.cuda.empty_cache()
+    return run
 
-    def check_layer(l):
-        lw = {n: numerics.from_storage(a, "bf16") for n, a in dg_inputs.layer_weights_host(d, l).items()}
-        model = om.Model(dims1, {"embed": None, "final_norm": None, "layers": [lw]})
-        rep = {"layer": l}
-        # prefill: every prompt row's keys/values, sampled rows' outputs
-        x_in = pre_in[l].float().numpy().astype(np.float64)
-        k_ref, v_ref = _kv_of_rows(x_in, lw, d)
-        gk, gv = kv_np[l]
-        rep["prefill_k"] = allclose_report(gk[:, :P], k_ref, *BF16_TOL)
-        rep["prefill_v"] = allclose_report(gv[:, :P], v_ref, *BF16_TOL)
-        empty = om.KVCache(1, d.n_kv_heads, d.head_dim)
-        y_ref, tr = model.layer_rows(0, x_in, empty, True, sample)
-        r = pre_route[l]
-        same = compare_routing(r["route_idx"], r["route_w"], r["router_logits"], tr.router_logits, tr.idx, BF16_TOL)
-        y = pre_out[l].float().numpy().astype(np.float64)
-        rep["prefill_out"] = allclose_report(y[same], y_ref[same], *BF16_TOL)
-        rep["prefill_routing_flips"] = int((~same).sum())
-        del x_in, k_ref, v_ref
-        # canvas pass on the GPU's layer input and the GPU's cache of this layer
-        xc = emb_rows if l == 0 else hid[l - 1].float().numpy().astype(np.float64)
-        kv = om.KVCache(1, d.n_kv_heads, d.head_dim)
-        kv.k[0], kv.v[0] = gk[:, :P], gv[:, :P]
-        xo, tr = model.layer(0, xc, kv, causal=False, append=True)
-        same = compare_routing(ridx[l], rw[l], rlog[l], tr.router_logits, tr.idx, BF16_TOL)
-        g = hid[l].float().numpy().astype(np.float64)
-        rep["canvas_out"] = allclose_report(g[same], xo[same], *BF16_TOL)
-        rep["canvas_routing_flips"] = int((~same).sum())
-        rep["canvas_k"] = allclose_report(gk[:, P:P + S], kv.k[0][:, P:], *BF16_TOL)
-        rep["canvas_v"] = allclose_report(gv[:, P:P + S], kv.v[0][:, P:], *BF16_TOL)
-        return rep
 
-    log("C3 teacher-forced: oracle, layer by layer")
-    workers = min(4, os.cpu_count() or 1)
+def _check_layer(run, l):
+    d, P, S, sample = run["d"], run["P"], run["S"], run["sample"]
+    lw = {n: numerics.from_storage(a, "bf16") for n, a in dg_inputs.layer_weights_host(d, l).items()}
+    model = om.Model(oracle_dims(replace(d, n_layers=1)), {"embed": None, "final_norm": None, "layers": [lw]})
+    rep = {"layer": l}
+    # prefill: every prompt row's keys/values, sampled rows' outputs, on the GPU's input rows of this layer
+    x_in = run["pre_in"][l].float().numpy().astype(np.float64)
+    empty = om.KVCache(1, d.n_kv_heads, d.head_dim)
+    y_ref, tr, k_ref, v_ref = model.layer_rows(0, x_in, empty, True, sample, return_kv=True)
+    gk, gv = run["kv_np"][l]
+    rep["prefill_k"] = allclose_report(gk[:, :P], k_ref, *BF16_TOL)
+    rep["prefill_v"] = allclose_report(gv[:, :P], v_ref, *BF16_TOL)
+    r = run["pre_route"][l]
+    same = compare_routing(r["route_idx"], r["route_w"], r["router_logits"], tr.router_logits, tr.idx, BF16_TOL)
+    y = run["pre_out"][l].float().numpy().astype(np.float64)
+    rep["prefill_out"] = allclose_report(y[same], y_ref[same], *BF16_TOL)
+    rep["prefill_routing_flips"] = int((~same).sum())
+    del x_in, k_ref, v_ref
+    # canvas pass on the GPU's layer input and the GPU's cache of this layer
+    xc = run["emb_rows"] if l == 0 else run["hid"][l - 1].float().numpy().astype(np.float64)
+    kv = om.KVCache(1, d.n_kv_heads, d.head_dim)
+    kv.k[0], kv.v[0] = gk[:, :P], gv[:, :P]
+    xo, tr = model.layer(0, xc, kv, causal=False, append=True)
+    same = compare_routing(run["ridx"][l], run["rw"][l], run["rlog"][l], tr.router_logits, tr.idx, BF16_TOL)
+    g = run["hid"][l].float().numpy().astype(np.float64)
+    rep["canvas_out"] = allclose_report(g[same], xo[same], *BF16_TOL)
+    rep["canvas_routing_flips"] = int((~same).sum())
+    rep["canvas_k"] = allclose_report(gk[:, P:P + S], kv.k[0][:, P:], *BF16_TOL)
+    rep["canvas_v"] = allclose_report(gv[:, P:P + S], kv.v[0][:, P:], *BF16_TOL)
+    return rep
+
+
+@pytest.mark.parametrize("first", [0, 10, 20], ids=["layers_0_9", "layers_10_19", "layers_20_29"])
+def test_c3_teacher_forced_layers(c3_run, first):
+    """Ten layers of the benchmarked configuration, each on the GPU's own inputs (prefill and canvas pass)."""
+    layers = range(first, min(first + 10, c3_run["L"]))
     failures = []
-    with ThreadPoolExecutor(max_workers=workers) as ex:
-        for rep in ex.map(check_layer, range(L)):
+    with ThreadPoolExecutor(max_workers=min(5, os.cpu_count() or 1)) as ex:
+        for rep in ex.map(lambda l: _check_layer(c3_run, l), layers):
             bad = [k for k, v in rep.items() if isinstance(v, tuple) and not v[0]]
-            log(f"layer {rep['layer']:2d}: routing flips prefill {rep['prefill_routing_flips']}/{len(sample)} "
-                f"canvas {rep['canvas_routing_flips']}/{S}; worst excess "
+            log(f"layer {rep['layer']:2d}: routing flips prefill {rep['prefill_routing_flips']}/{len(c3_run['sample'])} "
+                f"canvas {rep['canvas_routing_flips']}/{c3_run['S']}; worst excess "
                 + " ".join(f"{k} {v[1]:+.2e}" for k, v in rep.items() if isinstance(v, tuple))
                 + (f"  FAIL {bad}" if bad else ""))
             if bad:
@@ -163,13 +162,16 @@ def test_c3_teacher_forced_every_layer():
             assert rep["canvas_routing_flips"] <= 4 and rep["prefill_routing_flips"] <= 1, rep
     assert not failures, failures
 
-    log("C3 teacher-forced: head on the GPU's final rows")
+
+def test_c3_teacher_forced_head(c3_run):
+    """The head's statistics on the GPU's final hidden rows, every slot."""
+    d, L, S = c3_run["d"], c3_run["L"], c3_run["S"]
     E = numerics.from_storage(dg_inputs.embed_host(d), "bf16")
-    opred, oconf, oent, margin = om.head_stats(hid[L - 1].float().numpy().astype(np.float64), np.ones(d.d_model), E,
-                                               1.0, d.rms_eps, numerics.bf16_round)
+    opred, oconf, oent, margin = om.head_stats(c3_run["hid"][L - 1].float().numpy().astype(np.float64),
+                                               np.ones(d.d_model), E, 1.0, d.rms_eps, numerics.bf16_round)
     sel = margin > MARGIN
-    assert np.array_equal(pred.cpu().numpy()[sel], opred[sel])
-    ok_e = allclose_report(to_f64(ent), oent, *BF16_TOL)
-    ok_c = allclose_report(to_f64(conf), oconf, *BF16_TOL)
+    assert np.array_equal(c3_run["pred"][sel], opred[sel])
+    ok_e = allclose_report(c3_run["ent"], oent, *BF16_TOL)
+    ok_c = allclose_report(c3_run["conf"], oconf, *BF16_TOL)
     log(f"head: {int(sel.sum())}/{S} argmax compared; worst excess entropy {ok_e[1]:+.2e} conf {ok_c[1]:+.2e}")
     assert ok_e[0] and ok_c[0]

@@ -144,3 +144,44 @@ def test_c0_ragged_canvas_verify():
     for l in range(d.n_layers):
         gk, gv = sess.kv_numpy(l, kv.length)
         assert allclose_report(gk, kv.k[l], *F32_TOL)[0] and allclose_report(gv, kv.v[l], *F32_TOL)[0], l
+
+
+# ----------------------------------------------------------------------------- the self-speculative loop
+
+def _moving_chain_storage(d):
+    """Seeded weights with the output projections scaled up 30 times: the layer, not the embedding, decides the
+    head's argmax, so the greedy chain moves from token to token and some diffusion drafts agree with it."""
+    st = dg_inputs.model_weights_host(d)
+    for layer in st["layers"]:
+        for n in ("wo", "w_down", "ws_down"):
+            layer[n] = (layer[n] * 30.0).astype(np.float32)
+    return st
+
+
+@pytest.mark.parametrize("canvas,vocab", [(8, 64), (32, 4096)])
+def test_c0_speculative_loop_equals_oracle(canvas, vocab):
+    """dg_generate_speculative against the oracle's loop (fp32): the same tokens (greedy autoregressive decoding
+    from the known first token), the same accepted count per round, the same committed cache."""
+    d = replace(recipe.C0.dims, canvas=canvas, vocab=vocab, n_layers=1)
+    storage = _moving_chain_storage(d)
+    n_tokens, first = 3 * canvas // 2, 7
+    sess = Session(d, capacity=16 + n_tokens + canvas + 32, weights=gdev.from_host(storage, d.dtype))
+    model = oracle_model(d, storage)
+    kv = om.KVCache(d.n_layers, d.n_kv_heads, d.head_dim)
+    prompt = dg_inputs.prompt_tokens(16, d.vocab)
+    sess.prefill(prompt)
+    osm.prefill(model, kv, prompt)
+    sp = dg.make_sampler(max(1, canvas // 4), fixed_steps=3)
+    out = sess.i32(n_tokens)
+    st, acc = dg.dg_generate_speculative(sess.cfg, sess.weights, sess.kv, sp, 5, first, n_tokens, out, sess.ws,
+                                         sess.ws_bytes, side=sess.side)
+    torch.cuda.synchronize()
+    ref = osm.generate_speculative(model, kv, osm.Sampler(n_new=max(1, canvas // 4), fixed_steps=3), block0=5,
+                                   first_token=first, n_tokens=n_tokens)
+    log(f"speculative S={canvas}: GPU rounds {st.rounds} accepted {acc}; oracle {ref.accepted}")
+    assert np.array_equal(out.cpu().numpy(), ref.tokens)
+    assert acc == ref.accepted and st.rounds == len(ref.accepted) and st.accepted == sum(ref.accepted)
+    assert st.tokens == n_tokens and sess.kv.len == kv.length
+    for l in range(d.n_layers):
+        gk, gv = sess.kv_numpy(l, kv.length)
+        assert allclose_report(gk, kv.k[l], 1e-4, 1e-4)[0] and allclose_report(gv, kv.v[l], 1e-4, 1e-4)[0]

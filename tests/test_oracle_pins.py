@@ -232,6 +232,12 @@ def test_layer_rows_equals_full_layer(causal):
     sub, trs = m.layer_rows(0, x, kv, causal, rows)
     np.testing.assert_allclose(sub, full[rows], rtol=1e-12, atol=1e-12)
     assert np.array_equal(trs.idx, trf.idx[rows])
+    kv_app = om.KVCache(1, d.n_kv_heads, d.head_dim)
+    kv_app.k[0], kv_app.v[0] = kv.k[0].copy(), kv.v[0].copy()
+    m.layer(0, x, kv_app, causal, append=True)
+    _, _, k_new, v_new = m.layer_rows(0, x, kv, causal, rows, return_kv=True)
+    np.testing.assert_array_equal(k_new, kv_app.k[0][:, 9:])
+    np.testing.assert_array_equal(v_new, kv_app.v[0][:, 9:])
 
 
 def test_rmsnorm_constant_input():
