@@ -36,7 +36,7 @@ EXPORTED = ("dg_workspace_size", "dg_prefill_kv", "dg_denoise_step", "dg_canvas_
             "dg_generate_block", "dg_generate_block_overlapped", "dg_layer_forward", "dg_vocab_head", "dg_stop_check", "dg_status_string",
             "dg_generate_blocks", "dg_generate_blocks_overlapped", "dg_verify_block", "dg_denoise_step_sampler", "dg_canvas_update_sampler", "dg_vocab_head_sampler", "dg_sampler_inv_temperature",
             "dg_last_hip_error", "dg_timing_start", "dg_timing_stop", "dg_packed_elems", "dg_pack_matrix",
-            "dg_side_create", "dg_side_destroy", "dg_generate_speculative", "dg_packed_bytes_e4m3", "dg_quantize_e4m3")
+            "dg_side_create", "dg_side_destroy", "dg_generate_speculative", "dg_packed_bytes_e4m3", "dg_quantize_e4m3", "dg_denoise_step_noalloc", "dg_noalloc_scratch_bytes")
 # kernel classes of dg_timing_* (dg_kernel in dg.h), in enum order
 KERNELS = ("embed", "rmsnorm", "gemm_qkv", "attention", "attn_merge", "gemm_o", "route",
            "moe_gate_up", "moe_down", "shared_gate_up", "shared_down", "moe_combine", "vocab_head",
@@ -140,6 +140,8 @@ _SIGS = {
                                 _P(_i32), _P(dg_spec_status), _vp, _sz, _P(dg_side), _vp],
     "dg_packed_bytes_e4m3": [_i64, _i64, _P(_i64)],
     "dg_quantize_e4m3": [_vp, _vp, _vp, _i64, _i64, _i64, _vp],
+    "dg_denoise_step_noalloc": [_P(dg_config), _P(dg_weights), _P(dg_kv), _vp, _f32, _vp, _vp, _vp, _P(dg_side), _vp],
+    "dg_noalloc_scratch_bytes": [_P(_sz)],
     "dg_side_destroy": [_P(dg_side)],
 }
 for _name, _args in _SIGS.items():
@@ -276,6 +278,19 @@ def dg_denoise_step(cfg, weights, kv, canvas, inv_temperature: float, pred, conf
     _check("dg_denoise_step", _lib.dg_denoise_step(ctypes.byref(cfg), _w(weights), _kv(kv), _ptr(canvas),
                                                    inv_temperature, _ptr(pred), _ptr(conf), _ptr(entropy), d,
                                                    _ptr(ws), ws_bytes, _side(side), _stream(stream)))
+
+
+def dg_denoise_step_noalloc(cfg, weights, kv, canvas, inv_temperature: float, pred, conf, entropy, side=None,
+                            stream=None) -> None:
+    _check("dg_denoise_step_noalloc",
+           _lib.dg_denoise_step_noalloc(ctypes.byref(cfg), _w(weights), _kv(kv), _ptr(canvas), inv_temperature,
+                                        _ptr(pred), _ptr(conf), _ptr(entropy), _side(side), _stream(stream)))
+
+
+def dg_noalloc_scratch_bytes() -> int:
+    out = ctypes.c_size_t(0)
+    _check("dg_noalloc_scratch_bytes", _lib.dg_noalloc_scratch_bytes(ctypes.byref(out)))
+    return int(out.value)
 
 
 def dg_canvas_update(cfg, pred, conf, keep_count: int, seed: int, block: int, step: int, canvas_out,

@@ -103,6 +103,32 @@ int check_side(const dg_side* side) {
     DG_TRY(expr);                 \
   } while (0)
 
+// ------------------------------------------------------------------ fixed scratch (dg_denoise_step_noalloc)
+// The workspace of dg_denoise_step_noalloc: a file-scope device array, part of the loaded code object, so that
+// the call allocates nothing.  Host code never passes the array's name to a kernel (on the host it is only a
+// stand-in for the symbol): its device address is looked up once per device with hipGetSymbolAddress, with that
+// device current, and that address is what the kernels receive.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(void** out) {
+  int dev = 0;
+  DG_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return DG_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    DG_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p || ((uintptr_t)p & 255u)) return DG_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DG_OK;
+}
+
 constexpr int64_t kPartialRows = 4096;
 constexpr int kMaxSeq = 8;  // sequences of one batched call  // attention split partials hold n_split * rows <= max(this, rows)
 
@@ -669,6 +695,29 @@ int dg_denoise_step(const dg_config* cfg, const dg_weights* w, const dg_kv* kv, 
   Ws wsv = carve(cfg, cfg->canvas, (char*)ws);
   return denoise(cfg, w, kv, canvas, argmax_pass(inv_temperature), pred, conf, entropy, dbg, wsv, side,
                  (hipStream_t)stream);
+}
+
+int dg_denoise_step_noalloc(const dg_config* cfg, const dg_weights* w, const dg_kv* kv, const int32_t* canvas,
+                            float inv_temperature, int32_t* pred, float* conf, float* entropy, const dg_side* side,
+                            void* stream) {
+  DG_CHECK(check_cfg(cfg));
+  DG_CHECK(check_side(side));
+  DG_CHECK(check_weights(cfg, w, true, true));
+  if (!canvas || !pred || !conf || !entropy) return DG_ERR_INVALID;
+  if (!(inv_temperature > 0.f)) return DG_ERR_INVALID;
+  DG_CHECK(check_kv(kv, cfg->canvas));
+  if (carve(cfg, cfg->canvas, nullptr).bytes > kScratchBytes) return DG_ERR_WORKSPACE;
+  void* base = nullptr;
+  DG_CHECK(scratch_of_current_device(&base));
+  Ws wsv = carve(cfg, cfg->canvas, (char*)base);
+  return denoise(cfg, w, kv, canvas, argmax_pass(inv_temperature), pred, conf, entropy, nullptr, wsv, side,
+                 (hipStream_t)stream);
+}
+
+int dg_noalloc_scratch_bytes(size_t* h_bytes) {
+  if (!h_bytes) return DG_ERR_INVALID;
+  *h_bytes = kScratchBytes;
+  return DG_OK;
 }
 
 int dg_denoise_step_sampler(const dg_config* cfg, const dg_weights* w, const dg_kv* kv, const dg_sampler* sampler,

@@ -13,7 +13,8 @@
  *   - Pointers are DEVICE pointers unless the name starts with h_.
  *   - The caller owns all memory (weights, KV cache, inputs, outputs, workspace)
  *     and every stream and event; the library never allocates device memory and
- *     keeps no device state beyond its loaded code objects.  Calls that run layers
+ *     keeps no device state beyond its loaded code objects (which hold the fixed
+ *     scratch of dg_denoise_step_noalloc).  Calls that run layers
  *     take an optional caller-owned dg_side (below) for the shared expert's
  *     concurrency.
  *     Calls on one caller stream must be issued from one host thread at a time.
@@ -296,6 +297,22 @@ int dg_prefill_kv(const dg_config* cfg, const dg_weights* w, dg_kv* kv, const in
 int dg_denoise_step(const dg_config* cfg, const dg_weights* w, const dg_kv* kv, const int32_t* canvas,
                     float inv_temperature, int32_t* pred, float* conf, float* entropy, const dg_debug* dbg,
                     void* ws, size_t ws_bytes, const dg_side* side, void* stream);
+
+/* dg_denoise_step for callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): no workspace argument and no allocation
+ * of any kind.  Its scratch is a fixed array of dg_noalloc_scratch_bytes() bytes (64 MiB)
+ * inside the library's code object, one per GPU, held until the process ends; a
+ * configuration whose dg_workspace_size(cfg, cfg->canvas) exceeds it is rejected with
+ * DG_ERR_WORKSPACE before any device work (the full-width 256-slot pass needs 58 MiB).
+ * Every call on one GPU shares that GPU's array and leaves its contents behind: calls that
+ * overlap on one GPU (other streams, other threads) race and give wrong results.  Outputs
+ * and other errors as dg_denoise_step (no debug dumps). */
+int dg_denoise_step_noalloc(const dg_config* cfg, const dg_weights* w, const dg_kv* kv, const int32_t* canvas,
+                            float inv_temperature, int32_t* pred, float* conf, float* entropy, const dg_side* side,
+                            void* stream);
+
+/* Bytes of the fixed scratch of dg_denoise_step_noalloc.  Host-only. */
+int dg_noalloc_scratch_bytes(size_t* h_bytes);
 
 /* Pass `step` (1-based, < 65536) of block `block` as dg_generate_block runs it under
  * `sampler` ([P2] "Architecture Details"): dg_denoise_step at that pass's temperature,

@@ -377,3 +377,22 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
                        timeout=120)
     assert r.returncode == 2 and "one MI355X" in r.stderr and r.stdout == ""
+
+
+def test_noalloc_rejects_configs_beyond_its_scratch():
+    """dg_denoise_step_noalloc runs in a fixed array of dg_noalloc_scratch_bytes() (64 MiB): a configuration whose
+    pass needs more (a 1024-slot canvas at the full widths) is refused with DG_ERR_WORKSPACE before any device
+    work; the full-width 256-slot pass fits."""
+    assert dg.dg_noalloc_scratch_bytes() == 64 << 20
+    assert dg.dg_workspace_size(dg.make_config(recipe.C3.dims), recipe.C3.dims.canvas) <= 64 << 20
+    cfg = dg.make_config(replace(recipe.C3.dims, canvas=1024))
+    assert dg.dg_workspace_size(cfg, 1024) > 64 << 20
+    w = _fake_weights(cfg.n_layers)
+    buf = _Fake(0x20000)
+    kv = dg.KV(buf, buf, capacity=4096, length=0)
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_denoise_step_noalloc(cfg, w, kv, buf, 1.0, buf, buf, buf, stream=0)
+    assert e.value.status == dg.DG_ERR_WORKSPACE
+    with pytest.raises(dg.DGError) as e:   # the usual argument checks come first
+        dg.dg_denoise_step_noalloc(dg.make_config(recipe.C3.dims), w, kv, None, 1.0, buf, buf, buf, stream=0)
+    assert e.value.status == dg.DG_ERR_INVALID
