@@ -421,11 +421,13 @@ __global__ __launch_bounds__(256, 2) void k_moe_down_wide(MoeArgs a) {
 // registers for the bf16 matrix core; the scale of a channel multiplies its fp32 sum before the SwiGLU (gate and
 // up channels each their own) or before the store (down).  Activations stay bf16.  Half the weight bytes of the
 // bf16 kernels, which are bound by exactly those bytes.
+// Pairs of K steps in flight (A/B/A timing of the full FP8 loop: (2, 1, 1) 8.53 ms per pass against 8.64-8.84
+// for (3, 2, 3); deeper rings were slower, the down projection's occupancy covers its latency better).
 struct DepthF8 {
-  static constexpr int moe1 = 3;  // pairs of K steps in flight, one 16-row M-tile
-  static constexpr int moe2 = 2;  // two M-tiles
+  static constexpr int moe1 = 2;  // one 16-row M-tile
+  static constexpr int moe2 = 1;  // two M-tiles
   static constexpr int moe4 = 1;  // three or four M-tiles (wide tiles)
-  static constexpr int down = 3;
+  static constexpr int down = 1;
 };
 
 template <int MT, bool NTL>
