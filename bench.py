@@ -51,7 +51,8 @@ sys.path.insert(0, ROOT)
 METRIC = "canvas tokens/sec at batch 1 (256-slot block, T=10) + ms/denoising step"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moe_gate_up_traffic.json")
+TRAFFIC_FILES = {"bf16": os.path.join(ROOT, "profiles", "moe_gate_up_traffic.json"),
+                 "e4m3": os.path.join(ROOT, "profiles", "moe_gate_up_f8_traffic.json")}
 
 
 def log(*a):
@@ -110,12 +111,15 @@ def pass_flops(d, keys: int, pairs: int) -> dict:
             "vocab_head": 2 * S * d.vocab * d.d_model}
 
 
-def read_traffic(bytes_per_launch: float):
-    if not os.path.exists(TRAFFIC_FILE):
+def read_traffic(d, kernel: str):
+    """Measured HBM bytes per canvas launch of the gate/up kernel from the committed counter summary of this
+    expert precision, or None when there is none or the kernel sources changed since it was taken."""
+    path = TRAFFIC_FILES["e4m3" if d.expert_dtype == "e4m3" else "bf16"]
+    if not os.path.exists(path):
         return None
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash() or t.get("kernel") != kernel:
         return None
     return t.get("bytes_per_launch")
 
@@ -535,8 +539,9 @@ def main() -> int:
     if dom == "moe_gate_up":
         g_work = gate_up_bytes(d, experts_hit, pairs)
         achieved = g_work / (g_avg * 1e-3) / 1e9
-        roof = {"kernel": "k_moe_gate_up", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(g_work),
+        kname = "k_moe_gate_up_f8" if d.expert_dtype == "e4m3" else "k_moe_gate_up"
+        roof = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic(d, kname),
                 "bytes_per_launch": g_work}
     else:
         # the timed plain passes: canvas queries over the prompt and the canvas

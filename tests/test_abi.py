@@ -396,3 +396,30 @@ def test_noalloc_rejects_configs_beyond_its_scratch():
     with pytest.raises(dg.DGError) as e:   # the usual argument checks come first
         dg.dg_denoise_step_noalloc(dg.make_config(recipe.C3.dims), w, kv, None, 1.0, buf, buf, buf, stream=0)
     assert e.value.status == dg.DG_ERR_INVALID
+
+
+def _bench_module():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("dg_bench", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_bench_accounting_host_side():
+    """bench.py's algorithmic byte counts and its lookup of the committed traffic summaries, for both expert
+    precisions: FP8 experts count one byte per weight plus the per-channel float scales; a traffic summary is
+    used only for the gate/up kernel it names and only while the kernel sources it was taken on are unchanged."""
+    b = _bench_module()
+    d16, d8 = recipe.C3.dims, recipe.C3_FP8.dims
+    assert b.expert_weight_bytes(d16) == 2.0 and b.expert_weight_bytes(d8) == 1.0
+    hit, pairs = 120.0, d16.canvas * d16.top_k
+    w16 = hit * 2 * d16.ffn_expert * d16.d_model * 2
+    w8 = hit * 2 * d8.ffn_expert * d8.d_model * 1 + hit * 2 * d8.ffn_expert * 4
+    acts = b.gate_up_bytes(d16, hit, pairs) - w16
+    assert acts > 0
+    assert b.gate_up_bytes(d8, hit, pairs) == pytest.approx(w8 + acts)
+    for d, kname in ((d16, "k_moe_gate_up"), (d8, "k_moe_gate_up_f8")):
+        t = b.read_traffic(d, kname)   # None or a plausible byte count, never an exception
+        assert t is None or 0.5 * b.gate_up_bytes(d, hit, pairs) < t < 4 * b.gate_up_bytes(d, hit, pairs)
+        assert b.read_traffic(d, "k_other") is None
