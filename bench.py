@@ -210,7 +210,7 @@ def run_batch(args, wl) -> int:
     log(f"bench: {wl.name} batch {B}; generating weights on the device")
     side = dg.Side()  # the shared expert's stream and events, owned here
     w = gdev.packed_model_weights_device(d)
-    weights = dg.Weights(w["embed"], w["final_norm"], w["layers"])
+    weights = dg.Weights(w["embed"], w["final_norm"], w["layers"], w.get("embed_scale"))
     cfg = dg.make_config(d)
     cap = ((wl.prefix + (wl.blocks + 1) * d.canvas + 31) // 32) * 32
     ws_bytes = dg.dg_workspace_size(cfg, max(2 * B * d.canvas if 2 * B * d.canvas <= 2048 else B * d.canvas, 2048))
@@ -321,7 +321,7 @@ def run_speculative(args, wl) -> int:
     side = dg.Side()
     log(f"bench: {wl.name} speculative {N} tokens; generating weights on the device")
     w = gdev.packed_model_weights_device(d)
-    weights = dg.Weights(w["embed"], w["final_norm"], w["layers"])
+    weights = dg.Weights(w["embed"], w["final_norm"], w["layers"], w.get("embed_scale"))
     cfg = dg.make_config(d)
     cap = ((wl.prefix + 2 * (N + d.canvas) + 31) // 32) * 32
     k, v = gdev.kv_tensors(d, cap)
@@ -404,7 +404,7 @@ def main() -> int:
     log(f"bench: {wl.name} on {torch.cuda.get_device_name(0)}; generating weights on the device")
     side = dg.Side()  # the shared expert's stream and events, owned here
     w = gdev.packed_model_weights_device(d)
-    weights = dg.Weights(w["embed"], w["final_norm"], w["layers"])
+    weights = dg.Weights(w["embed"], w["final_norm"], w["layers"], w.get("embed_scale"))
     cfg = dg.make_config(d)
     cap = ((wl.prefix + (wl.blocks + 1) * d.canvas + 31) // 32) * 32  # + the canvas rows of an overlapped commit
     k, v = gdev.kv_tensors(d, cap)

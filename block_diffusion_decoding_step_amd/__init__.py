@@ -59,7 +59,8 @@ class dg_config(ctypes.Structure):
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("ffn_expert", ctypes.c_int32), ("ffn_shared", ctypes.c_int32),
                 ("vocab", ctypes.c_int32), ("canvas", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float), ("expert_dtype", ctypes.c_int32)]
+                ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float), ("expert_dtype", ctypes.c_int32),
+                ("head_dtype", ctypes.c_int32)]
 
 
 class dg_layer_weights(ctypes.Structure):
@@ -70,7 +71,7 @@ class dg_layer_weights(ctypes.Structure):
 
 class dg_weights(ctypes.Structure):
     _fields_ = [("embed", ctypes.c_void_p), ("final_norm", ctypes.c_void_p),
-                ("h_layers", ctypes.POINTER(dg_layer_weights))]
+                ("h_layers", ctypes.POINTER(dg_layer_weights)), ("embed_scale", ctypes.c_void_p)]
 
 
 class dg_kv(ctypes.Structure):
@@ -215,7 +216,8 @@ def make_config(dims, dtype: Optional[str] = None, rms_eps: float = 1e-6) -> dg_
                      top_k=dims.top_k, ffn_expert=dims.ffn_expert, ffn_shared=dims.ffn_shared, vocab=dims.vocab,
                      canvas=dims.canvas, dtype=DG_BF16 if dt == "bf16" else DG_F32,
                      rms_eps=getattr(dims, "rms_eps", rms_eps), rope_theta=0.0,
-                     expert_dtype=DG_E4M3 if getattr(dims, "expert_dtype", "") == "e4m3" else 0)
+                     expert_dtype=DG_E4M3 if getattr(dims, "expert_dtype", "") == "e4m3" else 0,
+                     head_dtype=DG_E4M3 if getattr(dims, "head_dtype", "") == "e4m3" else 0)
 
 
 class Weights:
@@ -224,15 +226,16 @@ class Weights:
     LAYER_FIELDS = ("attn_norm", "wqkv", "wo", "ffn_norm", "w_router", "w_gate_up", "w_down", "ws_gate_up",
                     "ws_down", "w_gate_up_scale", "w_down_scale")
 
-    def __init__(self, embed, final_norm, layers: Sequence[Dict[str, object]]):
-        self._keep = [embed, final_norm, list(layers)]
+    def __init__(self, embed, final_norm, layers: Sequence[Dict[str, object]], embed_scale=None):
+        self._keep = [embed, final_norm, list(layers), embed_scale]
         n = len(layers)
         self._layers = (dg_layer_weights * max(n, 1))()
         for i, lw in enumerate(layers):
             for f in self.LAYER_FIELDS:
                 setattr(self._layers[i], f, _ptr(lw.get(f)))
         self.struct = dg_weights(embed=_ptr(embed), final_norm=_ptr(final_norm),
-                                 h_layers=ctypes.cast(self._layers, _P(dg_layer_weights)))
+                                 h_layers=ctypes.cast(self._layers, _P(dg_layer_weights)),
+                                 embed_scale=_ptr(embed_scale))
 
 
 class KV:
@@ -528,8 +531,15 @@ def pack_layer(layer: Dict[str, object], expert_dtype: str = "") -> Dict[str, ob
     return out
 
 
-def pack_weights(natural: dict, expert_dtype: str = "") -> dict:
-    """{"embed", "final_norm", "layers": [...]} of row-major device tensors -> the library's layout."""
-    return {"embed": pack_tensor(natural["embed"]) if natural.get("embed") is not None else None,
-            "final_norm": natural["final_norm"],
-            "layers": [pack_layer(l, expert_dtype) for l in natural["layers"]]}
+def pack_weights(natural: dict, expert_dtype: str = "", head_dtype: str = "") -> dict:
+    """{"embed", "final_norm", "layers": [...]} of row-major device tensors -> the library's layout.  With
+    head_dtype "e4m3" the tied embedding is quantised (codes + "embed_scale", one scale per vocabulary row)."""
+    out = {"final_norm": natural["final_norm"], "layers": [pack_layer(l, expert_dtype) for l in natural["layers"]]}
+    emb = natural.get("embed")
+    if emb is None:
+        out["embed"] = None
+    elif head_dtype == "e4m3":
+        out["embed"], out["embed_scale"] = quantize_tensor_e4m3(emb)
+    else:
+        out["embed"] = pack_tensor(emb)
+    return out

@@ -252,10 +252,13 @@ int check_cfg(const dg_config* c) {
   if (c->expert_dtype != 0 && c->expert_dtype != DG_E4M3 && c->expert_dtype != c->dtype) return DG_ERR_INVALID;
   if (c->expert_dtype == DG_E4M3 && (c->dtype != DG_BF16 || c->d_model % 64 || c->ffn_expert % 64))
     return DG_ERR_UNSUPPORTED;
+  if (c->head_dtype != 0 && c->head_dtype != DG_E4M3 && c->head_dtype != c->dtype) return DG_ERR_INVALID;
+  if (c->head_dtype == DG_E4M3 && (c->dtype != DG_BF16 || c->d_model % 64)) return DG_ERR_UNSUPPORTED;
   return DG_OK;
 }
 
 inline bool fp8_experts(const dg_config* c) { return c->expert_dtype == DG_E4M3; }
+inline bool fp8_head(const dg_config* c) { return c->head_dtype == DG_E4M3; }
 
 int check_layer_weights(const dg_config* c, const dg_layer_weights& l) {
   const void* p[] = {l.attn_norm, l.wqkv, l.wo, l.ffn_norm, l.w_router, l.w_gate_up, l.w_down, l.ws_gate_up,
@@ -269,6 +272,7 @@ int check_layer_weights(const dg_config* c, const dg_layer_weights& l) {
 int check_weights(const dg_config* c, const dg_weights* w, bool need_layers, bool need_head) {
   if (!w) return DG_ERR_INVALID;
   if (!aligned16(w->embed)) return DG_ERR_INVALID;
+  if (fp8_head(c) && !aligned16(w->embed_scale)) return DG_ERR_INVALID;
   if (need_head && !aligned16(w->final_norm)) return DG_ERR_INVALID;
   if (need_layers && c->n_layers > 0) {
     if (!w->h_layers) return DG_ERR_INVALID;
@@ -448,7 +452,10 @@ int layer(const dg_config* c, const dg_weights* w, int l, const dg_kv* kv, int64
 int embed(const dg_config* c, const dg_weights* w, const int32_t* tok, int64_t M, const Ws& ws, hipStream_t s,
           int64_t row0 = 0) {
   const int64_t off = row0 * c->d_model;
-  if (c->dtype == DG_BF16)
+  if (fp8_head(c))
+    DG_LAUNCH(DG_K_EMBED, s, launch_embed_f8(tok, (const uint8_t*)w->embed, w->embed_scale, (bf16*)ws.X + off, (int)M,
+                                              c->d_model, c->vocab, s));
+  else if (c->dtype == DG_BF16)
     DG_LAUNCH(DG_K_EMBED, s, launch_embed<bf16>(tok, (const bf16*)w->embed, (bf16*)ws.X + off, (int)M, c->d_model,
                                                  c->vocab, s));
   else
@@ -490,6 +497,7 @@ int head(const dg_config* c, const dg_weights* w, int64_t M, const PassParams& p
   h.part2 = ws.hpart2; h.gumbel = pp.gumbel ? 1 : 0;
   h.k0 = (uint32_t)pp.seed; h.k1 = (uint32_t)(pp.seed >> 32); h.block = pp.block; h.step = pp.step;
   h.pred = pred; h.conf = conf; h.ent = ent;
+  h.e_scale = fp8_head(c) ? w->embed_scale : nullptr;
   if (c->dtype == DG_BF16) {
     if (!normed)
       DG_LAUNCH(DG_K_RMSNORM, s, launch_rmsnorm<bf16>((const bf16*)ws.X + row0 * c->d_model, (const bf16*)w->final_norm,

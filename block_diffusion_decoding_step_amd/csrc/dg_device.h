@@ -20,6 +20,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -88,18 +89,24 @@ struct Frag8x2 {
     v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   }
   // half h (0: first K step, 1: second) as a bf16 fragment
-  __device__ __forceinline__ Frag<bf16> half(int h) const {
-    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-    const uint32_t w0 = h ? v[2] : v[0], w1 = h ? v[3] : v[1];
-    const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
-    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
-    const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
-    const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
-    Frag<bf16> f;
-    f.v = bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-    return f;
-  }
+  __device__ __forceinline__ Frag<bf16> half(int h) const;
 };
+
+// eight E4M3 codes (bytes of w in order, the low byte first) as a bf16 fragment; exact, since every E4M3
+// value is a bf16 value
+__device__ __forceinline__ Frag<bf16> fp8x8_to_bf16(u32x2 w) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true);
+  Frag<bf16> f;
+  f.v = bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  return f;
+}
+__device__ __forceinline__ Frag<bf16> Frag8x2::half(int h) const {
+  return fp8x8_to_bf16(h ? u32x2{v[2], v[3]} : u32x2{v[0], v[1]});
+}
 
 // acc += A(16 x 32) * B(32 x 16) for one 32-wide K step
 __device__ __forceinline__ void mma(f32x4& acc, const Frag<bf16>& a, const Frag<bf16>& b) {

@@ -59,6 +59,9 @@ struct CanvasArgs {
 // ---- k_misc.hip
 template <typename T>
 hipError_t launch_embed(const int32_t* tok, const T* E, T* X, int M, int d, int V, hipStream_t s);
+// X[m] = bf16(code(E[tok[m]]) * scale[tok[m]]) for an E4M3 embedding in the FP8 pair-tiled layout
+hipError_t launch_embed_f8(const int32_t* tok, const uint8_t* E, const float* scale, bf16* X, int M, int d, int V,
+                           hipStream_t s);
 template <typename T>
 hipError_t launch_pack(const T* src, T* dst, int64_t batch, int64_t rows, int64_t cols, hipStream_t s);
 // per-row E4M3 scales and codes of `batch` row-major [rows, cols] bf16 matrices (cols a multiple of 64), codes in
@@ -188,7 +191,8 @@ int attention_splits(int64_t n_keys, int q_rows, int n_heads, int n_kv_heads, in
 // ---- k_head.hip
 struct HeadArgs {
   const void* x;      // normalised hidden [n, d]
-  const void* E;      // [V, d]
+  const void* E;      // [V, d]: fragment-tiled bf16, or (e_scale != null) E4M3 codes in the FP8 pair-tiled layout
+  const float* e_scale;  // FP8 head: [V] row scales, applied to each row's fp32 dot product
   float4* part;       // [n_groups][n] partials (max, argmax or drawn token bits, Z, S1), natural units
   float2* part2;      // gumbel: [n_groups][n] (best perturbed score, scaled logit of the drawn token)
   int n, d, V;

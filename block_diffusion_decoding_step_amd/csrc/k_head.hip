@@ -338,7 +338,11 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head(HeadArgs a) {
 constexpr int kHeadKC = 2;  // K steps per X stage; the E ring holds the K steps of two stages (a loop turn):
                             // the ring slot of a K step is KC * (stage parity) + its index in the stage
 
-template <bool DRAW>
+// FP8 vocabulary (F8): E holds E4M3 codes in the FP8 pair-tiled layout; the register ring holds each K step's
+// 8 code bytes per lane and fragment (half the bytes and registers of the bf16 ring), decoded to bf16 fragments
+// when used; the fold multiplies each token's fp32 dot product by its row scale (read once per tile, at the
+// tile's first stage).
+template <bool DRAW, bool F8>
 __global__ __launch_bounds__(512, 1) void k_vocab_head_bf16(HeadArgs a) {
   using T = bf16;
   // the draw's generator needs registers: it runs with one K step per stage (a two-step E ring)
@@ -383,8 +387,32 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head_bf16(HeadArgs a) {
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) lds[buf * (STAGE / 16) + j * 512 + t] = r[j];
   };
+
+  // FP8: the row scales (times beta) of this lane's 8 tokens of the current tile
+  float sc[2][4];
+  auto scale_load = [&](int q) __attribute__((always_inline)) {
+    const int v0 = ((int)blockIdx.x + (q / nch) * G) * kHeadTokens + 32 * w + 4 * quad;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) sc[i][rr] = a.e_scale[min(v0 + 16 * i + rr, a.V - 1)] * beta;
+  };
   // E fragments of flat K step f (over this workgroup's tiles); steps past the end reload the last one
   const int nsteps = total * KC;
+  // FP8: this lane's 8 code bytes of the two fragments of flat K step f: half (step & 1) of the lane's 16 bytes
+  // in the step's 64-column block
+  const uint8_t* E8 = (const uint8_t*)a.E;
+  auto e8_load = [&](int f, u32x2 (&e)[2]) __attribute__((always_inline)) {
+    f = min(f, nsteps - 1);
+    const int tl = f / (nch * KC), st = f % (nch * KC);
+    const int tile = (int)blockIdx.x + tl * G;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int rt = min(tile * (kHeadTokens / 16) + 2 * w + i, last_rt);
+      const uint8_t* p = E8 + ((int64_t)rt * (ks / 2) + st / 2) * 1024 + lane * 16 + (st & 1) * 8;
+      e[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));  // read once per pass: streamed
+    }
+  };
   auto e_load = [&](int f, Frag<T> (&e)[2]) __attribute__((always_inline)) {
     f = min(f, nsteps - 1);
     const int tl = f / (nch * KC), s = f % (nch * KC);
@@ -417,7 +445,7 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head_bf16(HeadArgs a) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int v = v0 + 16 * i + 4 * quad + rr;
-          const float l = acc[i][j][rr] * beta;
+          const float l = acc[i][j][rr] * (F8 ? sc[i][rr] : beta);
           if (v < a.V && l > loc.m) { loc.m = l; loc.a = v; }
         }
       if (loc.m != -INFINITY) {
@@ -427,7 +455,7 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head_bf16(HeadArgs a) {
           for (int rr = 0; rr < 4; ++rr) {
             const int v = v0 + 16 * i + 4 * quad + rr;
             if (v < a.V) {
-              const float dl = acc[i][j][rr] * beta - loc.m;
+              const float dl = acc[i][j][rr] * (F8 ? sc[i][rr] : beta) - loc.m;
               const float e = exp2f(dl * 1.4426950408889634f);
               loc.z += e;
               loc.s1 += e * dl;
@@ -454,7 +482,7 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head_bf16(HeadArgs a) {
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             const int v = v0 + 16 * i + 4 * quad + rr;
-            const float l = acc[i][j][rr] * beta;
+            const float l = acc[i][j][rr] * (F8 ? sc[i][rr] : beta);
             if (v < a.V && l + gn[rr] > dl.g) dl = Draw{l + gn[rr], l, v};
           }
         }
@@ -478,9 +506,13 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head_bf16(HeadArgs a) {
     });
   };
 
-  Frag<T> ering[EDEPTH][2];
+  Frag<T> ering[F8 ? 1 : EDEPTH][2];
+  u32x2 ering8[F8 ? EDEPTH : 1][2];
 #pragma unroll
-  for (int dd = 0; dd < EDEPTH; ++dd) e_load(dd, ering[dd]);
+  for (int dd = 0; dd < EDEPTH; ++dd) {
+    if constexpr (F8) e8_load(dd, ering8[dd]);
+    else e_load(dd, ering[dd]);
+  }
   // X loads run two stages ahead of their LDS stage: stage q's data is requested at the start of stage
   // q - 2 into register set q & 1 and written to LDS buffer q & 1 at the end of stage q - 1
   uint4 r[2][LOADS];
@@ -494,10 +526,19 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head_bf16(HeadArgs a) {
   auto stage = [&](int q, auto bparity) __attribute__((always_inline)) {
     constexpr int B = decltype(bparity)::value;
     if (q + 2 < total) issue(q + 2, r[B]);
+    if constexpr (F8)
+      if (q % nch == 0) scale_load(q);
     const T* base = reinterpret_cast<const T*>(lds) + B * (STAGE / 2) + lane * 8;
 #pragma unroll
     for (int kk = 0; kk < KC; ++kk) {
-      Frag<T>(&ea)[2] = ering[KC * B + kk];
+      Frag<T> ea[2];
+      if constexpr (F8) {
+        ea[0] = fp8x8_to_bf16(ering8[KC * B + kk][0]);
+        ea[1] = fp8x8_to_bf16(ering8[KC * B + kk][1]);
+      } else {
+        ea[0] = ering[KC * B + kk][0];
+        ea[1] = ering[KC * B + kk][1];
+      }
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         Frag<T> fb[8];
@@ -508,7 +549,8 @@ __global__ __launch_bounds__(512, 1) void k_vocab_head_bf16(HeadArgs a) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) mma(acc[i][8 * half + j], ea[i], fb[j]);
       }
-      e_load(q * KC + kk + EDEPTH, ering[KC * B + kk]);
+      if constexpr (F8) e8_load(q * KC + kk + EDEPTH, ering8[KC * B + kk]);
+      else e_load(q * KC + kk + EDEPTH, ering[KC * B + kk]);
     }
     if (q % nch == nch - 1) fold_tile(q);
     if (q + 1 < total) commit(1 - B, r[1 - B]);
@@ -592,10 +634,17 @@ template <typename T>
 hipError_t launch_vocab_head(const HeadArgs& a, hipStream_t s) {
   dim3 grid(a.n_groups, (a.n + kHeadSlots - 1) / kHeadSlots);
   if constexpr (sizeof(T) == 2) {
-    if (a.gumbel)
-      hipLaunchKernelGGL(k_vocab_head_bf16<true>, grid, dim3(512), 0, s, a);
-    else
-      hipLaunchKernelGGL(k_vocab_head_bf16<false>, grid, dim3(512), 0, s, a);
+    if (a.e_scale) {
+      if (a.d % 64) return hipErrorInvalidValue;  // FP8 pair-tiled rows: whole 64-column blocks
+      if (a.gumbel)
+        hipLaunchKernelGGL((k_vocab_head_bf16<true, true>), grid, dim3(512), 0, s, a);
+      else
+        hipLaunchKernelGGL((k_vocab_head_bf16<false, true>), grid, dim3(512), 0, s, a);
+    } else if (a.gumbel) {
+      hipLaunchKernelGGL((k_vocab_head_bf16<true, false>), grid, dim3(512), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((k_vocab_head_bf16<false, false>), grid, dim3(512), 0, s, a);
+    }
   } else {
     if (a.gumbel)
       hipLaunchKernelGGL((k_vocab_head<T, true>), grid, dim3(512), 0, s, a);

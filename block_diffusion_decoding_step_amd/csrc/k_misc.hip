@@ -35,6 +35,36 @@ __global__ __launch_bounds__(256) void k_embed(const int32_t* __restrict__ tok, 
   }
 }
 
+// X[m, :] = bf16(code * s) for an E4M3 embedding in the FP8 pair-tiled layout (dg.h, dg_quantize_e4m3) with
+// one float scale per vocabulary row: the 8 codes of columns 8i .. 8i+7 are 8 contiguous bytes of the row's
+// 64-column block, decoded exactly to bf16 (every E4M3 value is a bf16 value), widened, scaled in fp32 and
+// rounded to bf16.  Tokens outside [0, V) are clamped into range.
+__global__ __launch_bounds__(256) void k_embed_f8(const int32_t* __restrict__ tok, const uint8_t* __restrict__ E,
+                                                  const float* __restrict__ scale, bf16* __restrict__ X, int M, int d,
+                                                  int V) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const int m = blockIdx.x;
+  if (m >= M) return;
+  int t = tok[m];
+  t = t < 0 ? 0 : (t >= V ? V - 1 : t);
+  const float s = scale[t];
+  const uint8_t* tile = E + (int64_t)(t >> 4) * (d / 64) * 1024;
+  for (int i = threadIdx.x; i < d / 8; i += blockDim.x) {
+    const int c = 8 * i;
+    const uint2 w = *reinterpret_cast<const uint2*>(tile + (c >> 6) * 1024 + ((t & 15) + 16 * ((c & 31) >> 3)) * 16 +
+                                                    ((c & 63) >> 5) * 8);
+    const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false);
+    const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true);
+    const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false);
+    const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true);
+    float v[8] = {(float)p0[0], (float)p0[1], (float)p1[0], (float)p1[1],
+                  (float)p2[0], (float)p2[1], (float)p3[0], (float)p3[1]};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] *= s;
+    Vec8<bf16>::store(X + (int64_t)m * d + c, v);
+  }
+}
+
 // ============================================================== weight packing
 // Row-major [rows, cols] -> fragment-tiled (see dg.h); thread i writes 8 elements:
 // fragment i/64 (row tile, K step) and lane i%64 of it.
@@ -618,6 +648,12 @@ hipError_t launch_kv_scatter(const KvScatterArgs& a, hipStream_t s) {
 }
 template hipError_t launch_kv_scatter<float>(const KvScatterArgs&, hipStream_t);
 template hipError_t launch_kv_scatter<bf16>(const KvScatterArgs&, hipStream_t);
+hipError_t launch_embed_f8(const int32_t* tok, const uint8_t* E, const float* scale, bf16* X, int M, int d, int V,
+                           hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_embed_f8, dim3(M), dim3(256), 0, s, tok, E, scale, X, M, d, V);
+  return hipGetLastError();
+}
 template <typename T>
 hipError_t launch_embed(const int32_t* tok, const T* E, T* X, int M, int d, int V, hipStream_t s) {
   hipLaunchKernelGGL(k_embed<T>, dim3(M), dim3(256), 0, s, tok, E, X, M, d, V);

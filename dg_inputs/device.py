@@ -74,8 +74,11 @@ def packed_model_weights_device(d: Dims, seed: int = recipe.WEIGHT_SEED) -> dict
     so that the peak memory is the packed model plus one natural tensor."""
     import block_diffusion_decoding_step_amd as dg
     emb = normal_tensor((d.vocab, d.d_model), seed, recipe.STREAM_EMBED, recipe.WEIGHT_SIGMA, d.dtype)
-    out = {"embed": dg.pack_tensor(emb), "final_norm": torch.ones(d.d_model, dtype=torch_dtype(d.dtype), device="cuda"),
-           "layers": []}
+    out = {"final_norm": torch.ones(d.d_model, dtype=torch_dtype(d.dtype), device="cuda"), "layers": []}
+    if d.head_dtype == "e4m3":
+        out["embed"], out["embed_scale"] = dg.quantize_tensor_e4m3(emb)
+    else:
+        out["embed"] = dg.pack_tensor(emb)
     del emb
     for l in range(d.n_layers):
         layer = {}

@@ -51,6 +51,7 @@ class Dims:
     dtype: str  # "f32" or "bf16"
     rms_eps: float = 1e-6
     expert_dtype: str = ""  # "" (as dtype) or "e4m3": routed experts' weights quantised to FP8 per output channel
+    head_dtype: str = ""    # "" (as dtype) or "e4m3": the tied embedding / head quantised to FP8 per vocabulary row
 
     @property
     def qkv_rows(self) -> int:
@@ -102,9 +103,11 @@ C4 = Workload(
 )
 
 C3_FP8 = Workload(
-    name="full_loop_fp8", dims=replace(_BIG, expert_dtype="e4m3"), prefix=4096, n_new=26, fixed_steps=10,
-    description="the full-loop workload with the routed experts' weights in FP8 (OCP E4M3, one scale per output "
-                "channel, quantised from the same bf16 weights); everything else bf16",
+    name="full_loop_fp8", dims=replace(_BIG, expert_dtype="e4m3", head_dtype="e4m3"), prefix=4096, n_new=26,
+    fixed_steps=10,
+    description="the full-loop workload with the routed experts' weights and the tied embedding / vocab head in FP8 "
+                "(OCP E4M3, one scale per output channel or vocabulary row, quantised from the same bf16 weights); "
+                "everything else bf16",
 )
 
 WORKLOADS = {w.name: w for w in (C0, C1, C2, C3, C4, C3_FP8)}

@@ -116,6 +116,11 @@ typedef struct dg_config {
    * w_gate_up_scale, w_down_scale); needs dtype DG_BF16 and d_model, ffn_expert multiples of 64.
    * ([P2] "Benchmark Numbers": the headline figure runs FP8 weights; activations stay bf16 here.) */
   int32_t expert_dtype;
+  /* Storage of the tied embedding / vocab head (dg_weights embed): 0 = dtype; DG_E4M3 = FP8 codes in the FP8
+   * pair-tiled layout (dg_quantize_e4m3 of the [vocab, d_model] matrix) with one float scale per vocabulary row
+   * (dg_weights embed_scale); the lookup yields code * scale rounded to bf16, the head scales each row's fp32 dot
+   * product.  Needs dtype DG_BF16 and d_model a multiple of 64.  ([P2] "Benchmark Numbers": FP8 weights.) */
+  int32_t head_dtype;
 } dg_config;
 
 typedef struct dg_layer_weights {
@@ -136,6 +141,7 @@ typedef struct dg_weights {
   const void* embed;                 /* [vocab, d_model], also the output head (tied) */
   const void* final_norm;            /* [d_model] */
   const dg_layer_weights* h_layers;  /* HOST array of n_layers entries of device pointers */
+  const float* embed_scale;          /* head_dtype DG_E4M3: [vocab] row scales (else ignored, may be NULL) */
 } dg_weights;
 
 /* KV cache.  len and capacity are host values; capacity must be a multiple of 32.

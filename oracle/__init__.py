@@ -54,7 +54,8 @@ Pins (tests/test_oracle_*.py, all run without a GPU):
     every tie rounded as torch's float8_e4m3fn conversion does, the format's
     fixed points (448, 2^-6, 2^-9, NaN codes), saturation, per-channel
     quantisation closed forms and error bound, scaled experts equal to the
-    dequantised FFN
+    dequantised FFN, the FP8 tied embedding dequantised per vocabulary row
+    (exact for representable rows, the E4M3 bound per row, lookup rounded)
 Parity unpinned: none of the functions above is left without a pin; the
 whole-model forward has no golden values on the pages and is pinned only
 through its parts.

@@ -204,6 +204,16 @@ def fp8_expert_layer(layer: dict) -> dict:
     return out
 
 
+def fp8_embed(weights: dict) -> dict:
+    """A float64 weight dict whose tied embedding is quantised to E4M3 with one scale per vocabulary row
+    (numerics.quantize_e4m3_rows): "embed" becomes the dequantised matrix code * scale, which both the lookup
+    (rounded to the storage type there) and the head read; the other tensors are unchanged."""
+    out = dict(weights)
+    codes, scales = e4m3_quantize(weights["embed"])
+    out["embed"] = e4m3_values(codes) * scales.astype(np.float64)[:, None]
+    return out
+
+
 class Model:
     """The denoiser: embedding, n_layers MoE blocks, final norm, tied vocab head."""
 
@@ -277,7 +287,9 @@ class Model:
         return xr, tr
 
     def embed(self, tokens) -> np.ndarray:
-        return self.w["embed"][np.asarray(tokens, dtype=np.int64)]
+        """Rows of the tied embedding, in the storage type (exact for stored rows; a dequantised FP8 row
+        code * scale is rounded there)."""
+        return self.rnd(self.w["embed"][np.asarray(tokens, dtype=np.int64)])
 
     def body(self, x: np.ndarray, kv: KVCache, causal: bool, append: bool):
         traces: List[LayerTrace] = []

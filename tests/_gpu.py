@@ -21,9 +21,10 @@ class Session:
         if weights is None:
             weights = gdev.packed_model_weights_device(d)
         elif not packed:
-            weights = dg.pack_weights(weights, d.expert_dtype)
+            weights = dg.pack_weights(weights, d.expert_dtype, d.head_dtype)
         self.w = weights
-        self.weights = dg.Weights(weights["embed"], weights["final_norm"], weights["layers"])
+        self.weights = dg.Weights(weights["embed"], weights["final_norm"], weights["layers"],
+                                 weights.get("embed_scale"))
         cap = ((capacity + kv_capacity_round - 1) // kv_capacity_round) * kv_capacity_round
         self.k, self.v = gdev.kv_tensors(d, cap)
         self.kv = dg.KV(self.k, self.v, cap, 0)

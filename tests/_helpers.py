@@ -17,14 +17,25 @@ def oracle_dims(d: recipe.Dims) -> om.Dims:
                    ffn_shared=d.ffn_shared, vocab=d.vocab, canvas=d.canvas, dtype=d.dtype, rms_eps=d.rms_eps)
 
 
-def oracle_model(d: recipe.Dims, storage=None) -> om.Model:
-    """The oracle model of the seeded weights (or of `storage`); with FP8 experts their matrices are quantised by
-    the oracle's own quantiser."""
+def oracle_model(d: recipe.Dims, storage=None, log=None) -> om.Model:
+    """The oracle model of the seeded weights (or of `storage`); with FP8 experts (or an FP8 head) their matrices
+    (or the tied embedding) are quantised by the oracle's own quantiser.  The embedding is quantised in blocks of
+    rows (each row has its own scale, so blocks give the same result), with a progress line per block through
+    `log` (the full vocabulary takes minutes in float64)."""
     if storage is None:
         storage = dg_inputs.model_weights_host(d)
     w = om.weights_to_f64(storage, d.dtype)
     if d.expert_dtype == "e4m3":
         w["layers"] = [om.fp8_expert_layer(l) for l in w["layers"]]
+    if d.head_dtype == "e4m3":
+        e = w["embed"]
+        deq = np.empty_like(e)
+        step = 16384
+        for r0 in range(0, e.shape[0], step):
+            deq[r0:r0 + step] = om.fp8_embed({"embed": e[r0:r0 + step]})["embed"]
+            if log:
+                log(f"oracle FP8 embedding: rows {min(r0 + step, e.shape[0])}/{e.shape[0]}")
+        w["embed"] = deq
     return om.Model(oracle_dims(d), w)
 
 

@@ -423,3 +423,37 @@ def test_bench_accounting_host_side():
         t = b.read_traffic(d, kname)   # None or a plausible byte count, never an exception
         assert t is None or 0.5 * b.gate_up_bytes(d, hit, pairs) < t < 4 * b.gate_up_bytes(d, hit, pairs)
         assert b.read_traffic(d, "k_other") is None
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dtype="e4m3"), dg.DG_ERR_UNSUPPORTED),                          # an fp32 model
+    (dict(dtype="bf16", head_dtype="e4m3", d_model=96), dg.DG_ERR_UNSUPPORTED),  # rows not whole 64-column blocks
+])
+def test_fp8_head_config_limits(kw, status):
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_workspace_size(_cfg(**kw), 32)
+    assert e.value.status == status
+    c = _cfg(dtype="bf16")
+    c.head_dtype = 5   # neither 0, the model's dtype nor DG_E4M3
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_workspace_size(c, 32)
+    assert e.value.status == dg.DG_ERR_INVALID
+
+
+def test_fp8_head_needs_row_scales():
+    """With head_dtype DG_E4M3 the tied embedding's row scales are part of the weights: a call without them is
+    refused before any device work; with them (and otherwise the same arguments) the weights pass validation."""
+    cfg = _cfg(dtype="bf16", head_dtype="e4m3")
+    assert dg.dg_workspace_size(cfg, cfg.canvas) > 0
+    w = _fake_weights(cfg.n_layers)
+    buf = _Fake(0x20000)
+    kv = dg.KV(buf, buf, capacity=cfg.canvas + 64, length=0)
+    ws_bytes = dg.dg_workspace_size(cfg, cfg.canvas)
+    with pytest.raises(dg.DGError) as e:
+        dg.dg_denoise_step(cfg, w, kv, buf, 1.0, buf, buf, buf, None, buf, ws_bytes, stream=0)
+    assert e.value.status == dg.DG_ERR_INVALID
+    a = _Fake(0x10000)
+    w = dg.Weights(a, a, [{f: a for f in dg.Weights.LAYER_FIELDS} for _ in range(cfg.n_layers)], embed_scale=a)
+    with pytest.raises(dg.DGError) as e:   # still refused, now for the workspace only
+        dg.dg_denoise_step(cfg, w, kv, buf, 1.0, buf, buf, buf, None, buf, ws_bytes - 256, stream=0)
+    assert e.value.status == dg.DG_ERR_WORKSPACE

@@ -1,12 +1,13 @@
-"""GPU parity of the FP8 routed experts (OCP E4M3 weights, one float scale per output channel, bf16 activations)
-against the oracle's FP8 model.
+"""GPU parity of the FP8 routed experts and the FP8 vocab head (OCP E4M3 weights, one float scale per output
+channel or vocabulary row, bf16 activations) against the oracle's FP8 model.
 
 The pages' headline figures run FP8 weights ([P2] "DiffusionGemma 26B: How Google's Text Diffusion Model
 Generates Tokens in Parallel", "Benchmark Numbers").  Checked here:
   * the quantiser: codes and scales bit-exact against the oracle's quantiser, on crafted rows (every E4M3 tie,
     zero rows, saturation) and on seeded expert weights at the full widths;
   * one full-size MoE layer (d 2816, 128 experts top-8 + shared, 2048-key prefix) with FP8 experts;
-  * a four-layer FP8 model at the full widths: one canvas pass teacher-forced layer by layer, and the head.
+  * a four-layer FP8 model at the full widths: one canvas pass teacher-forced layer by layer, and the head, with
+    the tied embedding / vocab head in bf16 and in FP8 (one scale per vocabulary row).
 Bars as for bf16: 2e-2 abs/rel on hidden states and keys/values, routing by compare_routing, argmax where the
 oracle's top-2 margin exceeds 1e-2.
 """
@@ -157,12 +158,15 @@ def test_fp8_layer_full_size():
     assert np.max(np.abs(y16 - y_ref)) > 1e-2
 
 
-def test_fp8_four_layers_teacher_forced_and_head():
+@pytest.mark.parametrize("head_dtype", ["", "e4m3"], ids=["bf16_head", "fp8_head"])
+def test_fp8_four_layers_teacher_forced_and_head(head_dtype):
     """A four-layer FP8 model at the full widths over a 512-token prompt: one canvas pass, each layer compared on
     the GPU's input rows and cache (the prompt's layer-0 keys/values checked free-running), and the head on every
-    slot."""
+    slot of the 262,144-token vocabulary.  With the FP8 head the tied embedding is E4M3 too: the prompt's and the
+    canvas's embedding rows (compared through layer 0, whose input the oracle builds from its own dequantised
+    rows) and the head's row-scaled logits."""
     from tests._gpu import check_prompt_cache
-    d = replace(recipe.C3.dims, n_layers=4, expert_dtype="e4m3")
+    d = replace(recipe.C3.dims, n_layers=4, expert_dtype="e4m3", head_dtype=head_dtype)
     P, S = 512, d.canvas
     log("fp8 4 layers: device weights")
     sess = Session(d, capacity=P + S, max_tokens=S)
@@ -177,7 +181,7 @@ def test_fp8_four_layers_teacher_forced_and_head():
     pred, conf, ent = sess.denoise(canvas, dbg=dbg)
     torch.cuda.synchronize()
     log("fp8 4 layers: oracle")
-    model = oracle_model(d)
+    model = oracle_model(d, log=log)
     left = check_prompt_cache(sess, model, prompt, BF16_TOL)
     log(f"fp8 4 layers: prompt cache checked ({left} rows near a routing tie left out)")
     hid = [to_f64(dbg["hidden"][l]) for l in range(L)]

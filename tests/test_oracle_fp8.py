@@ -139,3 +139,30 @@ def test_fp8_experts_are_the_dequantised_ffn(dtype):
     dense = rnd(rnd(gate / (1 + np.exp(-gate)) * up) @ deq_dn.T)
     np.testing.assert_allclose(got, dense, rtol=1e-12, atol=1e-13)
     assert np.max(np.abs(deq_gu - gu)) <= 2.0 ** -4 * np.max(np.abs(gu)) * 1.0001
+
+
+def test_fp8_embedding_is_the_row_dequantised_matrix():
+    """om.fp8_embed replaces the tied embedding by code * row scale (numerics.quantize_e4m3_rows, one scale per
+    vocabulary row), which the lookup rounds to the storage type and the head multiplies directly.  Rows made of
+    E4M3 values times a power of two (each holding +-448 times it) come back exactly; rows of very different sizes
+    each keep the E4M3 relative bound.  Catches: a scale per column instead of per row, a missing scale, a lookup
+    that skips the storage rounding."""
+    rng = np.random.default_rng(11)
+    pos = numerics.e4m3_decode(CODES[:0x7F])
+    vals = np.concatenate([pos, -pos])
+    rows = rng.choice(vals, size=(6, 128))
+    rows[:, 0] = 448.0
+    k = np.array([-12, -3, 0, 2, 5, -7], dtype=np.float64)
+    exact = rows * np.exp2(k)[:, None]
+    assert np.array_equal(om.fp8_embed({"embed": exact})["embed"], exact)
+    mags = np.array([1e-3, 0.02, 7.0])[:, None]
+    e = (rng.normal(size=(3, 256)) * mags).astype(np.float32).astype(np.float64)
+    deq = om.fp8_embed({"embed": e, "final_norm": None})["embed"]
+    bound = np.maximum(np.abs(e) * 2.0 ** -4, 2.0 ** -10 * np.max(np.abs(e), axis=1, keepdims=True) / 448.0)
+    assert np.all(np.abs(deq - e) <= bound * (1 + 1e-6))
+    dims = om.Dims(n_layers=0, d_model=256, n_heads=1, n_kv_heads=1, head_dim=64, n_experts=2, top_k=1,
+                   ffn_expert=32, ffn_shared=32, vocab=3, canvas=4, dtype="bf16")
+    m = om.Model(dims, {"embed": deq, "final_norm": np.ones(256), "layers": []})
+    got = m.embed([2, 0, 1])
+    assert np.array_equal(got, numerics.bf16_round(deq[[2, 0, 1]]))
+    assert not np.array_equal(got, deq[[2, 0, 1]])   # the dequantised rows are not bf16 values themselves
