@@ -28,15 +28,20 @@ def oracle_model(d: recipe.Dims, storage=None, log=None) -> om.Model:
     if d.expert_dtype == "e4m3":
         w["layers"] = [om.fp8_expert_layer(l) for l in w["layers"]]
     if d.head_dtype == "e4m3":
-        e = w["embed"]
-        deq = np.empty_like(e)
-        step = 16384
-        for r0 in range(0, e.shape[0], step):
-            deq[r0:r0 + step] = om.fp8_embed({"embed": e[r0:r0 + step]})["embed"]
-            if log:
-                log(f"oracle FP8 embedding: rows {min(r0 + step, e.shape[0])}/{e.shape[0]}")
-        w["embed"] = deq
+        w["embed"] = fp8_embedding(w["embed"], log)
     return om.Model(oracle_dims(d), w)
+
+
+def fp8_embedding(e: np.ndarray, log=None) -> np.ndarray:
+    """The oracle's FP8 (row-scaled E4M3) dequantised embedding of a float64 matrix, in blocks of rows (each row has
+    its own scale, so blocks give the same result) with a progress line per block through `log`."""
+    deq = np.empty_like(e)
+    step = 16384
+    for r0 in range(0, e.shape[0], step):
+        deq[r0:r0 + step] = om.fp8_embed({"embed": e[r0:r0 + step]})["embed"]
+        if log:
+            log(f"oracle FP8 embedding: rows {min(r0 + step, e.shape[0])}/{e.shape[0]}")
+    return deq
 
 
 def oracle_sampler(w: recipe.Workload, **kw) -> osm.Sampler:

@@ -28,7 +28,7 @@ from oracle import model as om  # noqa: E402
 from oracle import numerics  # noqa: E402
 from oracle import sampler as osm  # noqa: E402
 from tests._gpu import Session, allclose_report, to_f64  # noqa: E402
-from tests._helpers import oracle_model  # noqa: E402
+from tests._helpers import fp8_embedding, oracle_model  # noqa: E402
 
 F32_TOL = (1e-4, 1e-4)
 BF16_TOL = (2e-2, 2e-2)
@@ -212,11 +212,13 @@ def test_stop_check_and_rule_and_lock():
     assert np.array_equal(q2, expect) and r2 == dg.DG_STOP_STABLE
 
 
-def test_head_c2_bf16_gumbel_sampled_slots():
-    """Full vocabulary (256 x 262144 x 2816, bf16) with the draw at T = 0.8: sampled slots against the oracle
-    (draws where the perturbed top-2 gap exceeds 1e-2, conf and entropy within the bf16 bar); every slot by
-    invariants."""
-    d = recipe.C2.dims
+@pytest.mark.parametrize("head_dtype,vocab", [("", 262144), ("e4m3", 32768)], ids=["bf16_head", "fp8_head"])
+def test_head_c2_gumbel_sampled_slots(head_dtype, vocab):
+    """256 slots x 2816 with the draw at T = 0.8: the full 262,144-token vocabulary in bf16, and a 32,768-token one
+    in FP8 (E4M3, one scale per row; the same kernel path as the full FP8 vocabulary, whose argmax head is compared
+    in test_gpu_fp8.py): sampled slots against the oracle (draws where the perturbed top-2 gap exceeds 1e-2, conf
+    and entropy within the bf16 bar); every slot by invariants."""
+    d = replace(recipe.C2.dims, head_dtype=head_dtype, vocab=vocab)
     w = {"embed": gdev.normal_tensor((d.vocab, d.d_model), 0, recipe.STREAM_EMBED, 0.02, d.dtype),
          "final_norm": torch.ones(d.d_model, dtype=gdev.torch_dtype(d.dtype), device="cuda"), "layers": []}
     sess = Session(replace(d, n_layers=0), capacity=32, weights=w)
@@ -237,6 +239,8 @@ def test_head_c2_bf16_gumbel_sampled_slots():
     assert (pred != p0.cpu().numpy()).mean() > 0.5                  # at this temperature most draws leave the mode
     log("gumbel head C2: generating E on host for the oracle")
     E64 = numerics.from_storage(dg_inputs.embed_host(d), "bf16")
+    if head_dtype == "e4m3":
+        E64 = fp8_embedding(E64, log)
     rows = np.array([0, 1, 37, 100, 128, 200, 254, 255])
     xs = numerics.from_storage(x_host[rows], d.dtype)
     opred, oconf, oent, margin = om.head_stats(xs, np.ones(d.d_model), E64, 1.25, d.rms_eps,
