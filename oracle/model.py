@@ -27,9 +27,8 @@ from typing import List, Optional
 
 import numpy as np
 
-from .numerics import e4m3_decode as e4m3_values
 from .numerics import f32, from_storage, rounder
-from .numerics import quantize_e4m3_rows as e4m3_quantize
+from .numerics import round_e4m3_rows as e4m3_rows
 from .philox import gumbel_noise
 
 
@@ -194,23 +193,23 @@ EXPERT_MATRICES = ("w_gate_up", "w_down")
 
 def fp8_expert_layer(layer: dict) -> dict:
     """A float64 layer dict with its routed experts' matrices quantised to E4M3 with per-output-channel scales:
-    w_gate_up / w_down become the code values and w_gate_up_scale [E, 2F] / w_down_scale [E, d] their scales
-    (numerics.quantize_e4m3_rows; the other tensors are unchanged)."""
+    w_gate_up / w_down become the E4M3 values and w_gate_up_scale [E, 2F] / w_down_scale [E, d] their scales
+    (numerics.round_e4m3_rows; the other tensors are unchanged)."""
     out = dict(layer)
     for n in EXPERT_MATRICES:
-        codes, scales = e4m3_quantize(layer[n])
-        out[n] = e4m3_values(codes)
+        values, scales = e4m3_rows(layer[n])
+        out[n] = values
         out[n + "_scale"] = scales.astype(np.float64)
     return out
 
 
 def fp8_embed(weights: dict) -> dict:
     """A float64 weight dict whose tied embedding is quantised to E4M3 with one scale per vocabulary row
-    (numerics.quantize_e4m3_rows): "embed" becomes the dequantised matrix code * scale, which both the lookup
+    (numerics.round_e4m3_rows): "embed" becomes the dequantised matrix value * scale, which both the lookup
     (rounded to the storage type there) and the head read; the other tensors are unchanged."""
     out = dict(weights)
-    codes, scales = e4m3_quantize(weights["embed"])
-    out["embed"] = e4m3_values(codes) * scales.astype(np.float64)[:, None]
+    values, scales = e4m3_rows(weights["embed"])
+    out["embed"] = values * scales.astype(np.float64)[:, None]
     return out
 
 

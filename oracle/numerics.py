@@ -117,15 +117,21 @@ def e4m3_encode(values) -> np.ndarray:
     return codes.astype(np.uint8)
 
 
-def quantize_e4m3_rows(w) -> tuple:
-    """Per-row (per-output-channel) E4M3 quantisation of a weight matrix [..., rows, cols].
+def round_e4m3_rows(w) -> tuple:
+    """Per-row (per-output-channel) E4M3 quantisation of a weight matrix [..., rows, cols], as values.
 
     The scale of a row is s = amax / 448 in float32 (1 for an all-zero row); each weight is divided by s in
-    float32 and rounded to E4M3 (ties to even, saturated).  The row's dequantised weights are code * s.
-    Returns (codes uint8 [..., rows, cols], scales float32 [..., rows]).  The decisions are taken in float32,
-    the precision the quantiser kernel takes them in."""
+    float32 and rounded to E4M3 (ties to even, saturated).  The row's dequantised weights are value * s.
+    Returns (E4M3 values float64 [..., rows, cols], scales float32 [..., rows]).  The decisions are taken in
+    float32, the precision the quantiser kernel takes them in."""
     w32 = np.asarray(w, dtype=np.float32)
     amax = np.max(np.abs(w32), axis=-1)
     s = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
     quot = (w32 / s[..., None]).astype(np.float32)
-    return e4m3_encode(e4m3_round(quot.astype(np.float64))), s
+    return e4m3_round(quot.astype(np.float64)), s
+
+
+def quantize_e4m3_rows(w) -> tuple:
+    """round_e4m3_rows with the values as their codes: (codes uint8 [..., rows, cols], scales float32 [..., rows])."""
+    v, s = round_e4m3_rows(w)
+    return e4m3_encode(v), s

@@ -166,3 +166,19 @@ def test_fp8_embedding_is_the_row_dequantised_matrix():
     got = m.embed([2, 0, 1])
     assert np.array_equal(got, numerics.bf16_round(deq[[2, 0, 1]]))
     assert not np.array_equal(got, deq[[2, 0, 1]])   # the dequantised rows are not bf16 values themselves
+
+
+def test_row_values_are_the_decoded_codes():
+    """round_e4m3_rows (the values the FP8 experts and head are built from) and quantize_e4m3_rows (their codes,
+    as the quantiser kernel writes them) agree: decoding the codes gives the values bit for bit, signed zeros
+    included, and the scales are the same."""
+    rng = np.random.default_rng(3)
+    w = np.concatenate([rng.normal(size=(64, 512)) * 0.02, rng.normal(size=(4, 512)) * 1e-6,
+                        np.zeros((1, 512))]).astype(np.float32)
+    w[0, :5] = [-1e-9, 0.0, -0.0, 3.0, -3.0]
+    v, s = numerics.round_e4m3_rows(w)
+    c, s2 = numerics.quantize_e4m3_rows(w)
+    d = numerics.e4m3_decode(c)
+    assert np.array_equal(s, s2)
+    assert np.array_equal(v, d) and np.array_equal(np.signbit(v), np.signbit(d))
+    assert np.signbit(v[0, 0]) and v[0, 0] == 0.0   # a negative weight that rounds to zero keeps its sign
