@@ -205,3 +205,31 @@ def test_fp8_four_layers_teacher_forced_and_head(head_dtype):
     assert allclose_report(to_f64(ent), oent, *BF16_TOL)[0]
     assert allclose_report(to_f64(conf), oconf, *BF16_TOL)[0]
     log(f"fp8 4 layers: head {int(sel.sum())}/{S} argmax compared")
+
+
+@pytest.mark.parametrize("vocab", [5000, 4112])
+def test_fp8_head_ragged_vocabulary_all_slots(vocab):
+    """The FP8 head over a vocabulary that ends inside a 256-token tile (and, at 5000 rows, inside a 16-row
+    fragment, whose padding rows the quantiser fills with zeros): every slot against the oracle's row-scaled E4M3
+    head (argmax where the top-2 margin exceeds 1e-2, confidence and entropy at the bf16 bar)."""
+    from tests._helpers import fp8_embedding
+    d = replace(recipe.C2.dims, vocab=vocab, head_dtype="e4m3")
+    w = {"embed": gdev.normal_tensor((d.vocab, d.d_model), recipe.WEIGHT_SEED, recipe.STREAM_EMBED,
+                                     recipe.WEIGHT_SIGMA, "bf16"),
+         "final_norm": torch.ones(d.d_model, dtype=torch.bfloat16, device="cuda"), "layers": []}
+    sess = Session(replace(d, n_layers=0), capacity=32, weights=w)
+    x_host = dg_inputs.hidden((d.canvas, d.d_model), "bf16")
+    x_dev = torch.from_numpy(x_host.view(np.int16)).cuda().view(torch.bfloat16)
+    n = d.canvas
+    pred, conf, ent = sess.i32(n), sess.f32(n), sess.f32(n)
+    dg.dg_vocab_head(sess.cfg, sess.weights, x_dev, n, 1.0, pred, conf, ent, sess.ws, sess.ws_bytes)
+    torch.cuda.synchronize()
+    E = fp8_embedding(numerics.from_storage(dg_inputs.embed_host(d), "bf16"))
+    opred, oconf, oent, margin = om.head_stats(numerics.from_storage(x_host, "bf16"), np.ones(d.d_model), E, 1.0,
+                                               d.rms_eps, numerics.bf16_round)
+    sel = margin > MARGIN
+    log(f"fp8 head V={vocab}: {int(sel.sum())}/{n} argmax compared")
+    assert sel.sum() >= n // 2
+    assert np.array_equal(pred.cpu().numpy()[sel], opred[sel])
+    assert allclose_report(to_f64(conf), oconf, 1e-6, BF16_TOL[1])[0]
+    assert allclose_report(to_f64(ent), oent, *BF16_TOL)[0]
