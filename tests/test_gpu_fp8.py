@@ -7,7 +7,10 @@ Generates Tokens in Parallel", "Benchmark Numbers").  Checked here:
     zero rows, saturation) and on seeded expert weights at the full widths;
   * one full-size MoE layer (d 2816, 128 experts top-8 + shared, 2048-key prefix) with FP8 experts;
   * a four-layer FP8 model at the full widths: one canvas pass teacher-forced layer by layer, and the head, with
-    the tied embedding / vocab head in bf16 and in FP8 (one scale per vocabulary row).
+    the tied embedding / vocab head in bf16 and in FP8 (one scale per vocabulary row);
+  * the FP8 head over ragged vocabularies, every slot;
+  * a small FP8 model through the block calls: a prompt prefilled with 64-row expert tiles, then blocks whose
+    commits ride in the next block's first pass.
 Bars as for bf16: 2e-2 abs/rel on hidden states and keys/values, routing by compare_routing, argmax where the
 oracle's top-2 margin exceeds 1e-2.
 """
@@ -233,3 +236,41 @@ def test_fp8_head_ragged_vocabulary_all_slots(vocab):
     assert np.array_equal(pred.cpu().numpy()[sel], opred[sel])
     assert allclose_report(to_f64(conf), oconf, 1e-6, BF16_TOL[1])[0]
     assert allclose_report(to_f64(ent), oent, *BF16_TOL)[0]
+
+
+def test_fp8_small_widths_overlapped_blocks_against_oracle():
+    """FP8 experts and FP8 tied embedding / head at small widths (the tiny model's shapes in bf16: d 256, 8 experts
+    top-2 + shared, vocabulary 4096, canvas 32) through the block calls: a 256-token prompt prefilled in one call
+    (512 routed pairs, so 64-row expert tiles), then three blocks of one pass each through
+    dg_generate_block_overlapped, each block's commit carried by the next block's first pass (64 rows) and the last
+    one committed at its end.  Against the FP8 oracle at the bf16 bar: the prompt's layer-0 cache rows
+    free-running, every block's tokens (where the oracle's top-2 margin allows) and mean entropy on the GPU's
+    context, and each committed block's cache rows."""
+    from tests._gpu import check_commit_on_gpu_cache, check_pass_on_gpu_cache, check_prompt_cache, gpu_cache_as_oracle
+    d = replace(recipe.C0.dims, dtype="bf16", expert_dtype="e4m3", head_dtype="e4m3")
+    P, S = 256, d.canvas
+    sess = Session(d, capacity=P + 4 * S, max_tokens=max(P, 2 * S))
+    prompt = dg_inputs.prompt_tokens(P, d.vocab)
+    sess.prefill(prompt)
+    model = oracle_model(d)
+    log(f"fp8 small: prompt cache checked ({check_prompt_cache(sess, model, prompt, BF16_TOL)} rows near a "
+        f"routing tie left out)")
+    sp = dg.make_sampler(recipe.C0.n_new, fixed_steps=1)
+    outs = [sess.i32(S) for _ in range(3)]
+    pending = None
+    for b in range(3):
+        st = dg.dg_generate_block_overlapped(sess.cfg, sess.weights, sess.kv, sp, b, pending, 1 if b < 2 else 0,
+                                             outs[b], sess.ws, sess.ws_bytes, side=sess.side)
+        torch.cuda.synchronize()
+        assert (st.steps, st.reason) == (1, dg.DG_STOP_FIXED)
+        toks = outs[b].cpu().numpy()
+        if pending is not None:  # the previous block, committed inside this block's first pass
+            check_commit_on_gpu_cache(model, gpu_cache_as_oracle(sess, P + (b - 1) * S), outs[b - 1].cpu().numpy(),
+                                      sess, BF16_TOL)
+        n = check_pass_on_gpu_cache(model, gpu_cache_as_oracle(sess, P + b * S),
+                                    osm.initial_canvas(sp.seed, b, S, d.vocab), toks, st.mean_entropy, BF16_TOL)
+        log(f"fp8 small block {b}: {n}/{S} tokens compared, mean entropy {st.mean_entropy:.4f}")
+        assert n >= S // 2
+        pending = outs[b]
+    assert sess.kv.len == P + 3 * S
+    check_commit_on_gpu_cache(model, gpu_cache_as_oracle(sess, P + 2 * S), outs[2].cpu().numpy(), sess, BF16_TOL)
